@@ -1,0 +1,154 @@
+"""Seeded synthetic decode-attention inputs.
+
+This module only draws inputs; it holds none of the attention arithmetic and
+is shared by the tests, the benchmark and the smoke check (the HIP library
+and the oracle are each fed from it, and neither imports the other).
+
+Draw order for a workload (one ``torch.Generator`` seeded with its seed):
+  1. per-sequence lengths, when they are ragged;
+  2. q            [batch, heads_q, d]
+  3. for each sequence b: K[b] then V[b], each [max_kv_len, heads_kv, d];
+  4. the dominant-key positions, when the workload has them.
+Values are fp32 ``randn`` times ``std``, rounded to nearest-even into the
+storage dtype.  Shapes and distributions follow the pages' decode setting
+(one query row per (sequence, head) against a long KV cache), at the sizes of
+the five named workloads below.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    max_kv_len: int
+    dtype: str                 # storage dtype of q, K, V: "f32" | "f16" | "bf16"
+    out_dtype: str             # dtype of o (LSE is always fp32)
+    seed: int
+    std: float = 1.0           # q, K, V ~ N(0, std^2)
+    num_splits: int = 0        # 0: chosen by the library's heuristic
+    ragged: tuple | None = None  # (lo, hi): lengths ~ U{lo..hi} inclusive
+    dominant: int = 0          # keys per head set to factor * q / |q| * sqrt(d)
+    dominant_factor: float = 6.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def group(self) -> int:
+        return self.heads_q // self.heads_kv
+
+    def describe(self) -> dict:
+        d = dataclasses.asdict(self)
+        d["scale"] = self.scale
+        return d
+
+
+# The five named decode workloads.
+WORKLOADS = {
+    1: Workload("single_seq_f32_d64_n1024", batch=1, heads_q=1, heads_kv=1, head_dim=64,
+                max_kv_len=1024, dtype="f32", out_dtype="f32", seed=1, num_splits=4),
+    2: Workload("mha_bf16_b8_h32_d128_n4096", batch=8, heads_q=32, heads_kv=32, head_dim=128,
+                max_kv_len=4096, dtype="bf16", out_dtype="bf16", seed=2),
+    3: Workload("mha_bf16_b1_h32_d128_n65536_dominant16", batch=1, heads_q=32, heads_kv=32,
+                head_dim=128, max_kv_len=65536, dtype="bf16", out_dtype="bf16", seed=3,
+                dominant=16),
+    4: Workload("gqa_bf16_b16_hq64_hkv8_d128_ragged512_32768", batch=16, heads_q=64, heads_kv=8,
+                head_dim=128, max_kv_len=32768, dtype="bf16", out_dtype="bf16", seed=4,
+                ragged=(512, 32768)),
+    5: Workload("mha_f16_b4_h16_d256_n131072", batch=4, heads_q=16, heads_kv=16, head_dim=256,
+                max_kv_len=131072, dtype="f16", out_dtype="f16", seed=5, std=0.5),
+}
+
+
+def _randn(gen: torch.Generator, shape, std: float, dtype: str) -> torch.Tensor:
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(TORCH_DTYPES[dtype])
+
+
+def generate(w: Workload, poison_tail: bool = False) -> dict:
+    """Draw the workload's inputs on the CPU.
+
+    Returns a dict with q, k, v (torch CPU tensors in w.dtype), kv_lens (int32
+    tensor [batch], or None when every sequence is max_kv_len long) and
+    max_kv_len (the K/V row count actually allocated).  With poison_tail,
+    K/V rows at or beyond a sequence's length are set to NaN after the draw,
+    so any read of them shows up in the result.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed)
+    lens = None
+    n_max = w.max_kv_len
+    if w.ragged is not None:
+        lo, hi = w.ragged
+        lens = torch.randint(lo, hi + 1, (w.batch,), generator=gen, dtype=torch.int64)
+        lens = lens.to(torch.int32)
+        n_max = int(lens.max())
+    q = _randn(gen, (w.batch, w.heads_q, w.head_dim), w.std, w.dtype)
+    dt = TORCH_DTYPES[w.dtype]
+    k = torch.empty((w.batch, n_max, w.heads_kv, w.head_dim), dtype=dt)
+    v = torch.empty_like(k)
+    for b in range(w.batch):
+        k[b] = _randn(gen, (n_max, w.heads_kv, w.head_dim), w.std, w.dtype)
+        v[b] = _randn(gen, (n_max, w.heads_kv, w.head_dim), w.std, w.dtype)
+    if w.dominant:
+        if w.group != 1:
+            raise ValueError("dominant keys are defined for one query head per KV head")
+        d = w.head_dim
+        for b in range(w.batch):
+            for h in range(w.heads_kv):
+                nb = n_max if lens is None else int(lens[b])
+                pos = torch.randperm(nb, generator=gen)[: w.dominant]
+                qv = q[b, h].to(torch.float64)
+                key = (w.dominant_factor * math.sqrt(d) / qv.norm()) * qv
+                k[b, pos, h, :] = key.to(dt)
+    if poison_tail and lens is not None:
+        for b in range(w.batch):
+            k[b, int(lens[b]):] = float("nan")
+            v[b, int(lens[b]):] = float("nan")
+    return {"q": q, "k": k, "v": v, "kv_lens": lens, "max_kv_len": n_max}
+
+
+def custom(batch, heads_q, heads_kv, head_dim, max_kv_len, dtype="f32", seed=0, std=1.0,
+           lens=None, out_dtype=None, num_splits=0) -> tuple[Workload, dict]:
+    """A workload of any shape (test matrices); lens is an optional list of lengths."""
+    w = Workload(f"custom_b{batch}_hq{heads_q}_hkv{heads_kv}_d{head_dim}_n{max_kv_len}_{dtype}",
+                 batch, heads_q, heads_kv, head_dim, max_kv_len, dtype, out_dtype or dtype, seed,
+                 std=std, num_splits=num_splits)
+    inp = generate(w)
+    if lens is not None:
+        inp["kv_lens"] = torch.tensor(lens, dtype=torch.int32)
+    return w, inp
+
+
+def kv_bytes(w: Workload, kv_lens) -> int:
+    """Bytes of K and V a decode step must read: sum_b N_b * heads_kv * d * 2 * elem."""
+    elem = torch.tensor([], dtype=TORCH_DTYPES[w.dtype]).element_size()
+    total_tokens = w.batch * w.max_kv_len if kv_lens is None else int(kv_lens.sum())
+    return total_tokens * w.heads_kv * w.head_dim * 2 * elem
+
+
+def raw(t: torch.Tensor) -> np.ndarray:
+    """Storage bits of a CPU tensor as numpy (uint16 for 16-bit types, float32 for f32)."""
+    t = t.contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def dtype_name(t: torch.Tensor) -> str:
+    return {v: k for k, v in TORCH_DTYPES.items()}[t.dtype]
