@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X: µs per decode step and effective
+KV bandwidth (bytes of K and V a step must read / step time) against the
+8 TB/s HBM peak.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
+
+One "step" is one fd_decode call (split kernel + combine kernel) over one
+batch of the workload, inputs already resident in HBM.  The headline
+workload is the bf16 multi-head batch (--config 2); the other named workloads
+are timed in the same run and reported under "workloads".  Each workload keeps
+enough copies of its K/V in HBM that consecutive steps read different copies,
+so a step cannot be served from the 256 MB Infinity Cache (the 0.5 MiB fp32
+workload is cache-resident by nature and reports µs only).
+
+Printed: one JSON line on stdout.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+from decode_attention_03_amd import fd, workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective KV GB/s (% of 8 TB/s HBM peak) and µs per decode step"
+KERNEL_SOURCES = ["split_valu.hip", "split_mfma.hip", "combine.hip", "dev_common.h",
+                  "fd_internal.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Prepared:
+    """A workload resident on the GPU with pre-bound fd_decode arguments."""
+
+    def __init__(self, w: workloads.Workload, dev: torch.device, num_splits: int = 0):
+        self.w = w
+        t0 = time.time()
+        inp = workloads.generate(w)
+        self.host = inp
+        lens = inp["kv_lens"]
+        self.kv_bytes = workloads.kv_bytes(w, lens)
+        footprint = inp["k"].numel() * inp["k"].element_size() * 2
+        # copies so that consecutive steps stream different memory: with >= 1 GiB
+        # read between two reads of one copy, no step hits the Infinity Cache
+        if footprint < (64 << 20):
+            self.copies = 1
+        else:
+            self.copies = max(2, min(16, math.ceil((1 << 30) / footprint) + 1))
+        self.q = inp["q"].to(dev)
+        self.kv = []
+        for _ in range(self.copies):
+            self.kv.append((inp["k"].to(dev), inp["v"].to(dev)))
+        self.lens = None if lens is None else lens.to(dev)
+        batch, hq, hkv, d = w.batch, w.heads_q, w.heads_kv, w.head_dim
+        self.n_max = inp["max_kv_len"]
+        if num_splits == 0 and w.num_splits:
+            num_splits = w.num_splits
+        if num_splits == 0:
+            self.B, self.L = fd.choose_splits(batch, hq, hkv, self.n_max, d, inp["q"].dtype)
+        else:
+            self.B, self.L = num_splits, -(-self.n_max // num_splits)
+        self.o = torch.empty((batch, hq, d), dtype=workloads.TORCH_DTYPES[w.out_dtype],
+                             device=dev)
+        self.lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+        ws = fd.workspace_bytes(batch, hq, self.B, d)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws_bytes = ws
+        self.o_part = self.ws[: batch * hq * self.B * d * 4].view(torch.float32)
+        lse_off = ((batch * hq * self.B * d * 4 + 255) // 256) * 256
+        self.lse_part = self.ws[lse_off: lse_off + batch * hq * self.B * 4].view(torch.float32)
+        self.lib = fd.library()
+        self.stream = torch.cuda.current_stream(dev)
+        sp = ctypes.c_void_p(self.stream.cuda_stream)
+        code = {torch.float32: fd.F32, torch.float16: fd.F16, torch.bfloat16: fd.BF16}
+        self.in_code = code[self.q.dtype]
+        self.out_code = code[self.o.dtype]
+        P = ctypes.c_void_p
+        lens_p = None if self.lens is None else P(self.lens.data_ptr())
+        self.decode_args = []
+        self.split_args = []
+        for k, v in self.kv:
+            self.decode_args.append((P(self.q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                                     lens_p, batch, hq, hkv, self.n_max, d, self.in_code,
+                                     self.out_code, ctypes.c_float(w.scale), self.B, self.L,
+                                     P(self.o.data_ptr()), P(self.lse.data_ptr()),
+                                     P(self.ws.data_ptr()), self.ws_bytes, sp))
+            self.split_args.append((P(self.q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+                                    lens_p, batch, hq, hkv, self.n_max, d, self.in_code,
+                                    ctypes.c_float(w.scale), self.B, self.L,
+                                    P(self.o_part.data_ptr()), P(self.lse_part.data_ptr()), sp))
+        self.split_bytes = (self.kv_bytes + self.q.numel() * self.q.element_size()
+                            + (batch * hq * self.B * (d + 1) * 4 if self.B > 1 else 0))
+        log(f"[bench] {w.name}: B={self.B} L={self.L} copies={self.copies} "
+            f"kv={self.kv_bytes / 2**20:.1f} MiB prep={time.time() - t0:.1f}s")
+
+    def decode(self, i: int) -> None:
+        rc = self.lib.fd_decode(*self.decode_args[i % self.copies])
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    def split(self, i: int) -> None:
+        rc = self.lib.fd_decode_split(*self.split_args[i % self.copies])
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    def free(self) -> None:
+        self.kv.clear()
+        self.q = self.o = self.lse = self.ws = self.o_part = self.lse_part = None
+
+
+def time_steps(p: Prepared, steps: int, warmup: int) -> dict:
+    """Wall clock over exactly `steps` fd_decode calls (synchronized on both
+    sides), plus HIP events around each call for the median."""
+    for i in range(warmup):
+        p.decode(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        p.decode(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(p.stream)
+        p.decode(i)
+        ev[i][1].record(p.stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return {"wall_us_per_step": wall / steps * 1e6, "event_us_median": per[len(per) // 2],
+            "event_us_p10": per[len(per) // 10], "event_us_p90": per[(9 * len(per)) // 10]}
+
+
+def time_split_kernel(p: Prepared, steps: int, warmup: int) -> float:
+    """Average duration (µs) of the split kernel alone, HIP events on its stream."""
+    for i in range(warmup):
+        p.split(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(p.stream)
+        p.split(i)
+        ev[i][1].record(p.stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+
+
+def cpu_baseline(p: Prepared, budget_s: float) -> dict:
+    """The fp64 oracle on the host cores, on whole decode steps of the same
+    workload, repeated until about budget_s seconds of wall time."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    w, inp = p.w, p.host
+    lens = inp["kv_lens"]
+    args = (w.dtype, workloads.raw(inp["q"]), workloads.raw(inp["k"]), workloads.raw(inp["v"]),
+            None if lens is None else lens.numpy())
+    threads = oracle.threads()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.attention(*args, scale=w.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s or reps >= 50:
+            break
+    wall = time.perf_counter() - t0
+    us = wall / reps * 1e6
+    return {"value": round(p.kv_bytes / (us * 1e-6) / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "us_per_step": round(us, 1),
+            "sample": f"{reps} whole decode step(s) of {w.name} (every row, fp64, OpenMP over "
+                      f"(sequence, head)), {wall:.1f} s wall"}
+
+
+def traffic_from_profile(name: str, launches_bytes: int) -> dict | None:
+    """HBM bytes per split-kernel launch from a committed rocprofv3 counter
+    summary, when it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
+    us = t["wall_us_per_step"]
+    out = {"us_per_step": round(us, 2), "event_us_median": round(t["event_us_median"], 2),
+           "num_splits": p.B, "split_len": p.L, "kv_bytes": p.kv_bytes}
+    if p.copies > 1:
+        gbs = p.kv_bytes / (us * 1e-6) / 1e9
+        out["kv_GBps"] = round(gbs, 1)
+        out["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    else:
+        out["note"] = "cache-resident (0.5 MiB); µs only"
+    if split_us is not None:
+        out["split_kernel_us"] = round(split_us, 2)
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="headline workload (1-5)")
+    ap.add_argument("--num-splits", type=int, default=0, help="override the split count")
+    ap.add_argument("--only", action="store_true", help="time the headline workload only")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="oracle seconds (0: skip)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each GPU would run its own independent decode); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 5 copies of {args.copy_probe} bytes")
+        return 0
+
+    head = workloads.WORKLOADS[args.config]
+    p = Prepared(head, dev, args.num_splits)
+    t = time_steps(p, args.steps, args.warmup)
+    split_us = time_split_kernel(p, args.steps, args.warmup)
+    log(f"[bench] {head.name}: {t}")
+    us = t["wall_us_per_step"]
+    gbs = p.kv_bytes / (us * 1e-6) / 1e9
+    achieved = p.split_bytes / (split_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "split", "kernel_us": round(split_us, 2),
+                "algorithmic_bytes_per_launch": p.split_bytes}
+    prof = traffic_from_profile(head.name, p.split_bytes)
+    if prof is not None:
+        roofline["traffic"] = prof.get("hbm_bytes_per_launch")
+    cpu = cpu_baseline(p, args.cpu_budget) if args.cpu_budget > 0 else None
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "us_per_step": round(us, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head.name, "batch": head.batch, "heads_q": head.heads_q,
+                   "heads_kv": head.heads_kv, "head_dim": head.head_dim,
+                   "max_kv_len": p.n_max, "in_dtype": head.dtype, "out_dtype": head.out_dtype,
+                   "num_splits": p.B, "split_len": p.L, "kv_bytes_per_step": p.kv_bytes,
+                   "input_copies": p.copies, "parallelism": "single-gpu"},
+        "timing": {k: round(v, 2) for k, v in t.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    p.free()
+    del p
+    torch.cuda.empty_cache()
+    if not args.only:
+        others = {}
+        for c in sorted(workloads.WORKLOADS):
+            if c == args.config:
+                continue
+            w = workloads.WORKLOADS[c]
+            q = Prepared(w, dev)
+            tt = time_steps(q, args.steps, args.warmup)
+            su = time_split_kernel(q, args.steps, args.warmup)
+            others[w.name] = summarize(q, tt, su)
+            log(f"[bench] {w.name}: {others[w.name]}")
+            q.free()
+            del q
+            torch.cuda.empty_cache()
+        result["workloads"] = others
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,315 @@
+// fd_api.cpp -- the C ABI of libfd: argument validation, the split-count
+// heuristic, workspace carving and kernel dispatch.  Host code only; every
+// step of the computation runs in the HIP kernels of this library.
+//
+// Sources (pages; sections as printed on them):
+//   [P1] "FlashDecoding 数学推导" (my-webpage-adu.pages.dev, 2026-07-15)
+//   [P2] "adv04: Flash-Decoding（长序列 Decode 切分 + FlashInfer 简介）"
+//        (mini-vllm-tutorial.vercel.app)
+//   [P3] "FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法"
+//        (my-webpage-adu.pages.dev, 2026-07-16)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "fd.h"
+#include "fd_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;          // 0.1.0
+constexpr int kMaxSplits = 16384;      // combine keeps one weight per split in LDS
+constexpr int kWorkGroupsPerCU = 4;    // split-count heuristic: target WGs per CU
+constexpr int kMinSplitLenMha = 256;   // tokens; keeps partial traffic ~0.2% of K/V
+constexpr int kMaxAutoSplits = 512;
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dtype_ok(int dt) { return dt == FD_F32 || dt == FD_F16 || dt == FD_BF16; }
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+size_t elem_bytes(int dt) { return dt == FD_F32 ? 4 : 2; }
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+std::mutex g_cu_mutex;
+int g_cu_cache[64];  // 0 = not queried yet
+
+int device_cus(int *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(FD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_cu_mutex);
+    if (dev >= 0 && dev < 64 && g_cu_cache[dev] > 0) {
+        *out = g_cu_cache[dev];
+        return FD_OK;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0)
+        return fail(FD_ERR_HIP, "hipDeviceGetAttribute(compute units): %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64)
+        g_cu_cache[dev] = n;
+    *out = n;
+    return FD_OK;
+}
+
+// Checks shared by the split stage and the whole decode.
+int check_split_inputs(const void *q, const void *k, const void *v, int batch, int heads_q,
+                       int heads_kv, int max_kv_len, int head_dim, int in_dtype, float scale) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0)
+        return fail(FD_ERR_INVALID, "sizes must be positive (batch=%d heads_q=%d heads_kv=%d "
+                    "max_kv_len=%d)", batch, heads_q, heads_kv, max_kv_len);
+    if (heads_q % heads_kv != 0)
+        return fail(FD_ERR_INVALID, "heads_q (%d) is not a multiple of heads_kv (%d)", heads_q,
+                    heads_kv);
+    if (!q)
+        return fail(FD_ERR_INVALID, "q is null");
+    if (max_kv_len > 0 && (!k || !v))
+        return fail(FD_ERR_INVALID, "k or v is null");
+    if (!head_dim_ok(head_dim))
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", head_dim);
+    if (!dtype_ok(in_dtype))
+        return fail(FD_ERR_UNSUPPORTED, "in_dtype %d not supported", in_dtype);
+    if (!aligned16(q) || (max_kv_len > 0 && (!aligned16(k) || !aligned16(v))))
+        return fail(FD_ERR_UNSUPPORTED, "q, k and v must be 16-byte aligned");
+    if (!std::isfinite(scale))
+        return fail(FD_ERR_INVALID, "scale is not finite");
+    return FD_OK;
+}
+
+int check_partition(int batch, int heads_q, int max_kv_len, int num_splits, int split_len) {
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FD_ERR_INVALID, "num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+    if (split_len < 1)
+        return fail(FD_ERR_INVALID, "split_len %d < 1", split_len);
+    if ((long long)num_splits * split_len < max_kv_len)
+        return fail(FD_ERR_INVALID, "num_splits * split_len (%lld) < max_kv_len (%d)",
+                    (long long)num_splits * split_len, max_kv_len);
+    if ((long long)batch * heads_q * num_splits > 0x7fffffffLL)
+        return fail(FD_ERR_INVALID, "batch * heads_q * num_splits exceeds the launch limit");
+    return FD_OK;
+}
+
+int launch_split(const fd::SplitArgs &a, int in_dtype, hipStream_t stream) {
+    const int group = a.heads_q / a.heads_kv;
+    hipError_t e;
+    if (fd::split_mfma_supported(in_dtype, a.head_dim, group))
+        e = fd::launch_split_mfma(a, in_dtype, stream);
+    else
+        e = fd::launch_split_valu(a, in_dtype, stream);
+    if (e != hipSuccess)
+        return fail(FD_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_version(void) { return kVersion; }
+
+const char *fd_last_error(void) { return g_error.c_str(); }
+
+// Split count: [P2] §3 Q2 suggests roughly one split per 1K tokens, capped,
+// and notes the best count depends on the GPU.  Here the count is derived from
+// the GPU instead: enough (sequence, head, split) work-groups to give every
+// compute unit kWorkGroupsPerCU of them, but never splits shorter than a floor
+// that keeps the partial (o, LSE) traffic small next to the K/V bytes.
+int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                     int in_dtype, int num_cus, int *num_splits, int *split_len) {
+    if (!num_splits || !split_len)
+        return fail(FD_ERR_INVALID, "null output pointer");
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0 || heads_q % heads_kv)
+        return fail(FD_ERR_INVALID, "bad sizes (batch=%d heads_q=%d heads_kv=%d max_kv_len=%d)",
+                    batch, heads_q, heads_kv, max_kv_len);
+    if (!head_dim_ok(head_dim) || !dtype_ok(in_dtype))
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
+                    in_dtype);
+    if (num_cus <= 0) {
+        int rc = device_cus(&num_cus);
+        if (rc != FD_OK)
+            return rc;
+    }
+    if (max_kv_len == 0) {
+        *num_splits = 1;
+        *split_len = 1;
+        return FD_OK;
+    }
+    const int group = heads_q / heads_kv;
+    const bool grouped = fd::split_mfma_supported(in_dtype, head_dim, group);
+    // work-groups per split index: one per (sequence, KV head) when a group is
+    // computed together, else one per (sequence, query head)
+    const long long units = (long long)batch * (grouped ? heads_kv : heads_q);
+    const long long target = (long long)num_cus * kWorkGroupsPerCU;
+    long long b = (target + units - 1) / units;
+    const long long min_len = grouped ? 128LL * group : kMinSplitLenMha;
+    long long bmax = (max_kv_len + min_len - 1) / min_len;
+    if (bmax < 1)
+        bmax = 1;
+    if (b > bmax)
+        b = bmax;
+    if (b > kMaxAutoSplits)
+        b = kMaxAutoSplits;
+    if (b < 1)
+        b = 1;
+    long long len = (max_kv_len + b - 1) / b;
+    len = (len + 15) / 16 * 16;  // whole 16-token work-group steps
+    b = (max_kv_len + len - 1) / len;
+    *num_splits = (int)b;
+    *split_len = (int)len;
+    return FD_OK;
+}
+
+size_t fd_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim) {
+    if (batch < 1 || heads_q < 1 || num_splits <= 1 || head_dim < 1)
+        return 0;
+    const size_t rows = (size_t)batch * heads_q * num_splits;
+    return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                    int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                    int in_dtype, float scale, int num_splits, int split_len, float *o_part,
+                    float *lse_part, void *stream) {
+    int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
+                                in_dtype, scale);
+    if (rc != FD_OK)
+        return rc;
+    rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
+    if (rc != FD_OK)
+        return rc;
+    if (!o_part || !lse_part)
+        return fail(FD_ERR_INVALID, "o_part or lse_part is null");
+    if (!aligned16(o_part) || !aligned4(lse_part))
+        return fail(FD_ERR_UNSUPPORTED, "o_part must be 16-byte and lse_part 4-byte aligned");
+    fd::SplitArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kv_lens = kv_lens;
+    a.batch = batch;
+    a.heads_q = heads_q;
+    a.heads_kv = heads_kv;
+    a.max_kv_len = max_kv_len;
+    a.head_dim = head_dim;
+    a.num_splits = num_splits;
+    a.split_len = split_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    return launch_split(a, in_dtype, static_cast<hipStream_t>(stream));
+}
+
+int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_q,
+               int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream) {
+    if (batch < 1 || heads_q < 1)
+        return fail(FD_ERR_INVALID, "sizes must be positive (batch=%d heads_q=%d)", batch,
+                    heads_q);
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FD_ERR_INVALID, "num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+    if (!o_part || !lse_part || !o)
+        return fail(FD_ERR_INVALID, "o_part, lse_part or o is null");
+    if (!head_dim_ok(head_dim))
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", head_dim);
+    if (!dtype_ok(out_dtype))
+        return fail(FD_ERR_UNSUPPORTED, "out_dtype %d not supported", out_dtype);
+    if (!aligned16(o_part) || !aligned4(lse_part) || !aligned4(o) || (lse && !aligned4(lse)))
+        return fail(FD_ERR_UNSUPPORTED, "misaligned pointer");
+    if ((long long)batch * heads_q > 0x7fffffffLL)
+        return fail(FD_ERR_INVALID, "batch * heads_q exceeds the launch limit");
+    hipError_t e = fd::launch_combine(o_part, lse_part, batch * heads_q, num_splits, head_dim, o,
+                                      out_dtype, lse, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
+              int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
+              int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
+              void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
+                                in_dtype, scale);
+    if (rc != FD_OK)
+        return rc;
+    if (!o)
+        return fail(FD_ERR_INVALID, "o is null");
+    if (!dtype_ok(out_dtype) || (out_dtype != in_dtype && out_dtype != FD_F32))
+        return fail(FD_ERR_UNSUPPORTED, "out_dtype %d must equal in_dtype (%d) or be FD_F32",
+                    out_dtype, in_dtype);
+    if (!aligned4(o) || (lse && !aligned4(lse)))
+        return fail(FD_ERR_UNSUPPORTED, "o and lse must be 4-byte aligned");
+    if (num_splits < 0 || split_len < 0)
+        return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
+                    num_splits, split_len);
+    if (num_splits == 0) {
+        rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype, 0,
+                              &num_splits, &split_len);
+        if (rc != FD_OK)
+            return rc;
+    } else if (split_len == 0) {
+        split_len = max_kv_len > 0 ? (max_kv_len + num_splits - 1) / num_splits : 1;
+    }
+    rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
+    if (rc != FD_OK)
+        return rc;
+
+    fd::SplitArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.kv_lens = kv_lens;
+    a.batch = batch;
+    a.heads_q = heads_q;
+    a.heads_kv = heads_kv;
+    a.max_kv_len = max_kv_len;
+    a.head_dim = head_dim;
+    a.num_splits = num_splits;
+    a.split_len = split_len;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_dtype = out_dtype;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    if (num_splits == 1) {  // one split per row: the split stage writes o and lse itself
+        a.o = o;
+        a.lse = lse;
+        return launch_split(a, in_dtype, st);
+    }
+    const size_t need = fd_workspace_bytes(batch, heads_q, num_splits, head_dim);
+    if (!workspace || workspace_bytes < need)
+        return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+        return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    const size_t rows = (size_t)batch * heads_q * num_splits;
+    a.o_part = static_cast<float *>(workspace);
+    a.lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           round256(rows * head_dim * sizeof(float)));
+    rc = launch_split(a, in_dtype, st);
+    if (rc != FD_OK)
+        return rc;
+    hipError_t e = fd::launch_combine(a.o_part, a.lse_part, batch * heads_q, num_splits,
+                                      head_dim, o, out_dtype, lse, st);
+    if (e != hipSuccess)
+        return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+}  // extern "C"

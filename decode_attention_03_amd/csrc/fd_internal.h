@@ -1,0 +1,47 @@
+// fd_internal.h -- declarations shared by the host API and the kernel files
+// of libfd (not installed, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fd {
+
+// Element type codes (same values as the FD_* codes of the public header).
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Everything one split-stage launch needs.  Shapes follow the public layouts:
+// q [batch, heads_q, d], K/V [batch, max_kv_len, heads_kv, d].
+struct SplitArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    const int32_t *kv_lens;  // device [batch] or nullptr
+    int batch, heads_q, heads_kv, max_kv_len, head_dim;
+    int num_splits, split_len;
+    float scale_log2;        // scale * log2(e): scores are kept in the log2 domain
+    float *o_part;           // [batch, heads_q, num_splits, d]   (num_splits > 1)
+    float *lse_part;         // [batch, heads_q, num_splits]      (num_splits > 1)
+    void *o;                 // final output                       (num_splits == 1)
+    float *lse;              // final LSE, may be null             (num_splits == 1)
+    int out_dtype;
+};
+
+// VALU split kernel: one work-group per (sequence, query head, split).
+// Handles every head_dim/dtype; with heads_q > heads_kv each query head reads
+// its shared KV head on its own.
+hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t stream);
+
+// MFMA split kernel for grouped heads: one work-group per (sequence, KV head,
+// split) computing all heads_q/heads_kv query rows of the group.  Returns
+// hipErrorNotSupported for shapes it does not cover (the caller then uses the
+// VALU kernel).
+bool split_mfma_supported(int in_dtype, int head_dim, int group);
+hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
+
+// LSE merge of num_splits partials for `rows` = batch * heads_q rows.
+hipError_t launch_combine(const float *o_part, const float *lse_part, int rows, int num_splits,
+                          int head_dim, void *o, int out_dtype, float *lse, hipStream_t stream);
+
+}  // namespace fd

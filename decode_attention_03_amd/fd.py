@@ -1,0 +1,212 @@
+"""Thin Python binding of libfd (include/fd.h) over ctypes.
+
+Argument marshalling only: shapes, dtypes and devices are checked here, device
+pointers and torch's current HIP stream are handed to the C ABI, and every step
+of the computation runs in the library's HIP kernels.  PyTorch provides device
+memory and streams.  A missing or unloadable libfd.so raises; there is no
+fallback implementation.
+
+Layouts (see include/fd.h): q [batch, heads_q, d]; K/V [batch, max_kv_len,
+heads_kv, d]; kv_lens int32 [batch] on the device (None: all max_kv_len);
+o [batch, heads_q, d]; lse float32 [batch, heads_q].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfd.so")
+
+F32, F16, BF16 = 0, 1, 2
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+_CODES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTED",
+              ERR_WORKSPACE: "FD_ERR_WORKSPACE", ERR_HIP: "FD_ERR_HIP"}
+
+#: every symbol include/fd.h declares
+EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
+           "fd_decode_split", "fd_combine", "fd_decode")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FDError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_ERR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+def library() -> ctypes.CDLL:
+    """Open libfd.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        IP = ctypes.POINTER(ctypes.c_int)
+        lib.fd_version.argtypes, lib.fd_version.restype = [], I
+        lib.fd_last_error.argtypes, lib.fd_last_error.restype = [], ctypes.c_char_p
+        lib.fd_choose_splits.argtypes = [I, I, I, I, I, I, I, IP, IP]
+        lib.fd_choose_splits.restype = I
+        lib.fd_workspace_bytes.argtypes, lib.fd_workspace_bytes.restype = [I, I, I, I], S
+        lib.fd_decode_split.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P]
+        lib.fd_decode_split.restype = I
+        lib.fd_combine.argtypes = [P, P, I, I, I, I, P, I, P, P]
+        lib.fd_combine.restype = I
+        lib.fd_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, P]
+        lib.fd_decode.restype = I
+        _lib = lib
+        return lib
+
+
+def version() -> int:
+    return library().fd_version()
+
+
+def last_error() -> str:
+    return library().fd_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise FDError(rc, last_error())
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype not in _CODES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _CODES[dtype]
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _on_device(name: str, t: torch.Tensor, device: torch.device) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shapes(q, k, v, kv_lens):
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [batch, heads_q, d] and K/V [batch, N, heads_kv, d]")
+    batch, heads_q, d = q.shape
+    kb, n_max, heads_kv, kd = k.shape
+    if kb != batch or kd != d:
+        raise ValueError(f"q {tuple(q.shape)} and K {tuple(k.shape)} disagree")
+    if q.dtype != k.dtype or v.dtype != k.dtype:
+        raise TypeError("q, K and V must share one dtype")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _on_device(name, t, dev)
+    if kv_lens is not None:
+        _on_device("kv_lens", kv_lens, dev)
+        if kv_lens.dtype != torch.int32 or kv_lens.shape != (batch,):
+            raise ValueError("kv_lens must be int32 [batch]")
+    return batch, heads_q, heads_kv, n_max, d
+
+
+def choose_splits(batch: int, heads_q: int, heads_kv: int, max_kv_len: int, head_dim: int,
+                  dtype: torch.dtype, num_cus: int = 0) -> tuple[int, int]:
+    """(num_splits, split_len) from the library heuristic (num_cus 0: the device's)."""
+    b, length = ctypes.c_int(), ctypes.c_int()
+    _check(library().fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim,
+                                      _code(dtype), num_cus, ctypes.byref(b),
+                                      ctypes.byref(length)))
+    return b.value, length.value
+
+
+def workspace_bytes(batch: int, heads_q: int, num_splits: int, head_dim: int) -> int:
+    return int(library().fd_workspace_bytes(batch, heads_q, num_splits, head_dim))
+
+
+def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, scale=None,
+                 o_part=None, lse_part=None):
+    """Split stage: returns (o_part [batch, Hq, B, d] f32, lse_part [batch, Hq, B] f32)."""
+    batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
+    if split_len == 0:
+        split_len = max(1, -(-n_max // num_splits))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if o_part is None:
+        o_part = torch.empty((batch, heads_q, num_splits, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((batch, heads_q, num_splits), dtype=torch.float32, device=q.device)
+    _on_device("o_part", o_part, q.device)
+    _on_device("lse_part", lse_part, q.device)
+    if (o_part.shape != (batch, heads_q, num_splits, d) or o_part.dtype != torch.float32
+            or lse_part.shape != (batch, heads_q, num_splits) or lse_part.dtype != torch.float32):
+        raise ValueError("o_part / lse_part have the wrong shape or dtype")
+    _check(library().fd_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q,
+                                     heads_kv, n_max, d, _code(q.dtype), scale, num_splits,
+                                     split_len, _ptr(o_part), _ptr(lse_part), _stream(q.device)))
+    return o_part, lse_part
+
+
+def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True):
+    """Combine stage: LSE merge over the split axis -> (o, lse)."""
+    if o_part.dim() != 4 or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("o_part must be float32 [batch, Hq, B, d], lse_part float32 [batch, Hq, B]")
+    batch, heads_q, nb, d = o_part.shape
+    if lse_part.shape != (batch, heads_q, nb):
+        raise ValueError("lse_part shape does not match o_part")
+    dev = o_part.device
+    _on_device("o_part", o_part, dev)
+    _on_device("lse_part", lse_part, dev)
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    _on_device("o", o, dev)
+    if lse is not None:
+        _on_device("lse", lse, dev)
+    _check(library().fd_combine(_ptr(o_part), _ptr(lse_part), batch, heads_q, nb, d, _ptr(o),
+                                _code(o.dtype), _ptr(lse), _stream(dev)))
+    return o, lse
+
+
+def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len: int = 0,
+           out_dtype=None, return_lse: bool = True, workspace=None, o=None, lse=None):
+    """Whole decode step (split + combine) -> (o, lse or None).
+
+    num_splits 0 lets the library choose.  workspace (any dtype, on the device)
+    is allocated here when not given and more than one split is used.
+    """
+    batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = out_dtype or q.dtype
+    dev = q.device
+    if num_splits == 0:
+        num_splits, split_len = choose_splits(batch, heads_q, heads_kv, n_max, d, q.dtype)
+    if o is None:
+        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    need = workspace_bytes(batch, heads_q, num_splits, d)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _on_device("o", o, dev)
+    _check(library().fd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q, heads_kv,
+                               n_max, d, _code(q.dtype), _code(o.dtype), scale, num_splits,
+                               split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
+                               _stream(dev)))
+    return o, lse

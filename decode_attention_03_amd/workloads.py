@@ -4,11 +4,14 @@ This module only draws inputs; it holds none of the attention arithmetic and
 is shared by the tests, the benchmark and the smoke check (the HIP library
 and the oracle are each fed from it, and neither imports the other).
 
-Draw order for a workload (one ``torch.Generator`` seeded with its seed):
-  1. per-sequence lengths, when they are ragged;
-  2. q            [batch, heads_q, d]
-  3. for each sequence b: K[b] then V[b], each [max_kv_len, heads_kv, d];
-  4. the dominant-key positions, when the workload has them.
+Every tensor piece is drawn by its own ``torch.Generator`` whose seed is the
+first 8 bytes of SHA-256 over (workload seed, tag), so pieces can be drawn in
+parallel threads and the result does not depend on the thread count:
+  ("lens",)              per-sequence lengths, when they are ragged
+  ("q",)                 q [batch, heads_q, d]
+  ("k", b, c), ("v", b, c)
+                         K/V rows [c*CHUNK, (c+1)*CHUNK) of sequence b
+  ("dominant", b, h)     the dominant-key positions, when the workload has them
 Values are fp32 ``randn`` times ``std``, rounded to nearest-even into the
 storage dtype.  Shapes and distributions follow the pages' decode setting
 (one query row per (sequence, head) against a long KV cache), at the sizes of
@@ -16,8 +19,11 @@ the five named workloads below.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import hashlib
 import math
+import os
 
 import numpy as np
 import torch
@@ -73,6 +79,24 @@ WORKLOADS = {
 }
 
 
+CHUNK = 4096  # K/V rows per independently seeded piece
+
+
+def _gen(seed: int, *tag) -> torch.Generator:
+    digest = hashlib.sha256(repr((int(seed),) + tuple(tag)).encode()).digest()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int.from_bytes(digest[:8], "little") & ((1 << 63) - 1))
+    return g
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _randn(gen: torch.Generator, shape, std: float, dtype: str) -> torch.Tensor:
     x = torch.randn(shape, generator=gen, dtype=torch.float32)
     if std != 1.0:
@@ -89,22 +113,31 @@ def generate(w: Workload, poison_tail: bool = False) -> dict:
     K/V rows at or beyond a sequence's length are set to NaN after the draw,
     so any read of them shows up in the result.
     """
-    gen = torch.Generator(device="cpu")
-    gen.manual_seed(w.seed)
     lens = None
     n_max = w.max_kv_len
     if w.ragged is not None:
         lo, hi = w.ragged
-        lens = torch.randint(lo, hi + 1, (w.batch,), generator=gen, dtype=torch.int64)
+        lens = torch.randint(lo, hi + 1, (w.batch,), generator=_gen(w.seed, "lens"),
+                             dtype=torch.int64)
         lens = lens.to(torch.int32)
         n_max = int(lens.max())
-    q = _randn(gen, (w.batch, w.heads_q, w.head_dim), w.std, w.dtype)
+    q = _randn(_gen(w.seed, "q"), (w.batch, w.heads_q, w.head_dim), w.std, w.dtype)
     dt = TORCH_DTYPES[w.dtype]
     k = torch.empty((w.batch, n_max, w.heads_kv, w.head_dim), dtype=dt)
     v = torch.empty_like(k)
-    for b in range(w.batch):
-        k[b] = _randn(gen, (n_max, w.heads_kv, w.head_dim), w.std, w.dtype)
-        v[b] = _randn(gen, (n_max, w.heads_kv, w.head_dim), w.std, w.dtype)
+
+    def fill(job):
+        name, b, c = job
+        rows = min(CHUNK, n_max - c * CHUNK)
+        dst = k if name == "k" else v
+        dst[b, c * CHUNK: c * CHUNK + rows] = _randn(_gen(w.seed, name, b, c),
+                                                     (rows, w.heads_kv, w.head_dim), w.std,
+                                                     w.dtype)
+
+    jobs = [(name, b, c) for b in range(w.batch) for name in ("k", "v")
+            for c in range(-(-n_max // CHUNK))]
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, jobs))
     if w.dominant:
         if w.group != 1:
             raise ValueError("dominant keys are defined for one query head per KV head")
@@ -112,7 +145,7 @@ def generate(w: Workload, poison_tail: bool = False) -> dict:
         for b in range(w.batch):
             for h in range(w.heads_kv):
                 nb = n_max if lens is None else int(lens[b])
-                pos = torch.randperm(nb, generator=gen)[: w.dominant]
+                pos = torch.randperm(nb, generator=_gen(w.seed, "dominant", b, h))[: w.dominant]
                 qv = q[b, h].to(torch.float64)
                 key = (w.dominant_factor * math.sqrt(d) / qv.norm()) * qv
                 k[b, pos, h, :] = key.to(dt)

@@ -1,0 +1,129 @@
+/*
+ * fd.h -- C ABI of libfd, split-KV ("FlashDecoding") decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (pages; sections as printed on them):
+ *   [P1] "FlashDecoding 数学推导" (my-webpage-adu.pages.dev, 2026-07-15)
+ *   [P2] "adv04: Flash-Decoding（长序列 Decode 切分 + FlashInfer 简介）"
+ *        (mini-vllm-tutorial.vercel.app)
+ *   [P3] "FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法"
+ *        (my-webpage-adu.pages.dev, 2026-07-16)
+ *
+ * The operation.  For every sequence b and query head h there is one query
+ * row q[b,h,:] of length d.  Against the first N_b cached tokens of the key /
+ * value head kvh = h / (heads_q / heads_kv) it computes
+ *     o[b,h,:] = softmax(s) V,   s_j = scale * q[b,h,:] . K[b,j,kvh,:]
+ *     lse[b,h] = log sum_j exp(s_j)            (natural log)
+ * ([P1] §2.1.1; [P3] §2.1.1 and §2.3.1).  The KV range is cut into
+ * num_splits splits of split_len tokens ([P1] §2.1.3 and §2.5; [P2] §3);
+ * fd_decode_split emits one (o, LSE) pair per split ([P3] §2.3.3) and
+ * fd_combine merges them with exp(S_b - S_global) weights ([P3] §2.3.4).
+ *
+ * Layouts (row-major, innermost dimension contiguous, no padding):
+ *   q        [batch, heads_q, head_dim]              in_dtype
+ *   k, v     [batch, max_kv_len, heads_kv, head_dim] in_dtype
+ *   kv_lens  [batch] int32 (device memory), or NULL: every N_b = max_kv_len.
+ *            Values are clamped to [0, max_kv_len].
+ *   o        [batch, heads_q, head_dim]              out_dtype
+ *   lse      [batch, heads_q] float32, natural log of the scaled scores'
+ *            exp-sum; -inf for a sequence with no tokens (o is then 0).
+ *   o_part   [batch, heads_q, num_splits, head_dim]  float32
+ *   lse_part [batch, heads_q, num_splits]            float32
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers except the fd_choose_splits outputs are device pointers
+ *     on the current HIP device, 16-byte aligned.  The caller owns every
+ *     buffer; the library allocates no device memory and keeps no state
+ *     besides a cached per-device compute-unit count.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is queued on it; no call synchronizes; a call returns after the
+ *     launches are queued.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched and fd_last_error() describes the problem.
+ *   - Results are bitwise reproducible for fixed inputs, num_splits and
+ *     split_len (no atomics, fixed reduction orders).
+ *   - Accumulation is fp32 for every input dtype; outputs are rounded to
+ *     nearest-even into out_dtype.
+ *   - Supported: head_dim in {64, 128, 256}; in_dtype any FD_* code;
+ *     out_dtype equal to in_dtype or FD_F32; heads_q % heads_kv == 0.
+ */
+#ifndef FD_H_
+#define FD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+#define FD_F32 0
+#define FD_F16 1
+#define FD_BF16 2
+
+/* Return codes. */
+#define FD_OK 0
+#define FD_ERR_INVALID (-1)     /* null pointer, bad size, heads_q % heads_kv, B*L < N */
+#define FD_ERR_UNSUPPORTED (-2) /* head_dim, dtype or pointer alignment */
+#define FD_ERR_WORKSPACE (-3)   /* workspace missing or too small */
+#define FD_ERR_HIP (-4)         /* a HIP runtime call or a launch failed */
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fd_version(void);
+
+/* Message for the last non-FD_OK return on the calling thread ("" if none).
+ * The pointer stays valid until the thread's next fd_* call. */
+const char *fd_last_error(void);
+
+/* Pick the split count B and split length L for a decode launch ([P2] §3 Q2
+ * gives the rule of thumb this starts from: more splits for longer caches, up
+ * to a cap; here the count is set so the launch fills the GPU's compute
+ * units).  Host-only and deterministic.
+ *   num_cus <= 0: query the current HIP device (cached); > 0: use as given.
+ *   Outputs: *num_splits >= 1, *split_len >= 1, and
+ *            (*num_splits) * (*split_len) >= max_kv_len.
+ * Returns FD_OK, FD_ERR_INVALID (bad sizes or null outputs) or FD_ERR_HIP. */
+int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                     int in_dtype, int num_cus, int *num_splits, int *split_len);
+
+/* Bytes of workspace fd_decode needs for num_splits splits: o_part and
+ * lse_part as laid out above, each starting on a 256-byte boundary.  Returns
+ * 0 when num_splits <= 1 (fd_decode then writes o and lse directly) or on
+ * non-positive sizes. */
+size_t fd_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim);
+
+/* Split stage ([P1] §2.5 stage 1; [P3] §3.2.1 stage 1): for every
+ * (b, h, split i) with token range [i*L, min((i+1)*L, N_b)) write
+ *   o_part[b,h,i,:] = sum_j exp(s_j - m) V_j / l,
+ *   lse_part[b,h,i] = m + log l      (m = max s_j, l = sum_j exp(s_j - m)),
+ * and (0, -inf) for an empty range ([P3] §3.2.1 merge identity).
+ * num_splits >= 1, split_len >= 1, num_splits * split_len >= max_kv_len. */
+int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                    int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                    int in_dtype, float scale, int num_splits, int split_len, float *o_part,
+                    float *lse_part, void *stream);
+
+/* Combine stage ([P3] §2.3.4; [P1] §2.5 stage 2, a light reduction):
+ *   S = log sum_i exp(lse_part[b,h,i]),  o[b,h,:] = sum_i exp(lse_part[b,h,i] - S) o_part[b,h,i,:]
+ * Terms at -inf contribute nothing; if every term is -inf, o = 0 and S = -inf.
+ * lse may be NULL.  num_splits >= 1. */
+int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_q,
+               int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream);
+
+/* Whole decode step: split + combine.
+ *   num_splits == 0: B and L come from fd_choose_splits (split_len ignored).
+ *   num_splits > 0, split_len == 0: L = ceil(max_kv_len / num_splits)
+ *     ([P2] §4 chunking).  num_splits > 0, split_len > 0: used as given.
+ * With B == 1 the split stage writes o and lse itself and workspace may be
+ * NULL; otherwise workspace must hold fd_workspace_bytes(...) bytes.
+ * lse may be NULL. */
+int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
+              int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
+              int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FD_H_ */

@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+libfd.so must export every function include/fd.h declares; the split-count
+heuristic must satisfy its contract; invalid arguments must be rejected with
+the documented codes before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_03_amd import fd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fd.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return fd.library()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fd.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fd_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert declared, "no declarations parsed from include/fd.h"
+    assert sorted(fd.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.fd_version() >= 100
+    assert fd.last_error() == "" or isinstance(fd.last_error(), str)
+
+
+@pytest.mark.parametrize("batch,hq,hkv,d,dt", [
+    (1, 1, 1, 64, fd.F32), (8, 32, 32, 128, fd.BF16), (1, 32, 32, 128, fd.BF16),
+    (16, 64, 8, 128, fd.BF16), (4, 16, 16, 256, fd.F16), (2, 8, 1, 64, fd.F16),
+    (64, 64, 64, 128, fd.BF16)])
+def test_choose_splits_contract(lib, batch, hq, hkv, d, dt):
+    for n in (0, 1, 15, 16, 17, 255, 256, 1000, 1024, 4096, 65536, 131072, 1 << 20):
+        b, length = ctypes.c_int(), ctypes.c_int()
+        rc = lib.fd_choose_splits(batch, hq, hkv, n, d, dt, 256, ctypes.byref(b),
+                                  ctypes.byref(length))
+        assert rc == fd.OK
+        B, L = b.value, length.value
+        assert B >= 1 and L >= 1
+        assert B * L >= n
+        assert n == 0 or (B - 1) * L < n  # no trailing split is empty for the longest sequence
+        assert B <= 512
+        assert n == 0 or L % 16 == 0
+        again = (ctypes.c_int(), ctypes.c_int())
+        lib.fd_choose_splits(batch, hq, hkv, n, d, dt, 256, ctypes.byref(again[0]),
+                             ctypes.byref(again[1]))
+        assert (again[0].value, again[1].value) == (B, L)
+
+
+def test_choose_splits_fills_the_gpu(lib):
+    """Short caches use few splits, long ones enough to give every CU work."""
+    def splits(batch, hq, n, cus=256):
+        b, length = ctypes.c_int(), ctypes.c_int()
+        assert lib.fd_choose_splits(batch, hq, hq, n, 128, fd.BF16, cus, ctypes.byref(b),
+                                    ctypes.byref(length)) == fd.OK
+        return b.value
+    assert splits(1, 32, 65536) * 32 >= 256  # at least one work-group per CU
+    assert splits(1, 32, 65536) >= splits(1, 32, 4096)
+    assert splits(64, 64, 4096) == 1  # 4096 rows already fill the GPU
+    assert splits(1, 32, 65536, cus=64) <= splits(1, 32, 65536, cus=256)
+
+
+def test_choose_splits_rejects(lib):
+    b, length = ctypes.c_int(), ctypes.c_int()
+    assert lib.fd_choose_splits(1, 3, 2, 10, 64, 0, 256, ctypes.byref(b),
+                                ctypes.byref(length)) == fd.ERR_INVALID
+    assert lib.fd_choose_splits(1, 1, 1, 10, 96, 0, 256, ctypes.byref(b),
+                                ctypes.byref(length)) == fd.ERR_UNSUPPORTED
+    assert lib.fd_choose_splits(1, 1, 1, 10, 64, 7, 256, ctypes.byref(b),
+                                ctypes.byref(length)) == fd.ERR_UNSUPPORTED
+    assert lib.fd_choose_splits(1, 1, 1, 10, 64, 0, 256, None, None) == fd.ERR_INVALID
+
+
+def test_workspace_bytes(lib):
+    assert lib.fd_workspace_bytes(8, 32, 4, 128) == 8 * 32 * 4 * 128 * 4 + 256 * (
+        -(-(8 * 32 * 4 * 4) // 256))
+    assert lib.fd_workspace_bytes(1, 1, 1, 64) == 0
+    assert lib.fd_workspace_bytes(0, 1, 4, 64) == 0
+    ws = lib.fd_workspace_bytes(3, 5, 7, 64)
+    assert ws % 256 == 0 and ws >= 3 * 5 * 7 * 65 * 4
+
+
+def _split(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kv_lens=None, batch=1, hq=4, hkv=2, n=64, d=64, dt=fd.F32,
+             scale=0.125, B=4, L=16, o_part=FAKE, lse_part=FAKE)
+    a.update(kw)
+    return lib.fd_decode_split(a["q"], a["k"], a["v"], a["kv_lens"], a["batch"], a["hq"], a["hkv"],
+                               a["n"], a["d"], a["dt"], a["scale"], a["B"], a["L"], a["o_part"],
+                               a["lse_part"], None)
+
+
+def test_decode_split_validation(lib):
+    assert _split(lib, q=None) == fd.ERR_INVALID
+    assert _split(lib, k=None) == fd.ERR_INVALID
+    assert _split(lib, o_part=None) == fd.ERR_INVALID
+    assert _split(lib, batch=0) == fd.ERR_INVALID
+    assert _split(lib, n=-1) == fd.ERR_INVALID
+    assert _split(lib, hq=3) == fd.ERR_INVALID
+    assert _split(lib, B=3) == fd.ERR_INVALID            # 3 * 16 < 64
+    assert _split(lib, L=0) == fd.ERR_INVALID
+    assert _split(lib, B=0) == fd.ERR_INVALID
+    assert _split(lib, B=20000, L=1) == fd.ERR_INVALID
+    assert _split(lib, scale=float("nan")) == fd.ERR_INVALID
+    assert _split(lib, d=80) == fd.ERR_UNSUPPORTED
+    assert _split(lib, dt=5) == fd.ERR_UNSUPPORTED
+    assert _split(lib, k=FAKE + 8) == fd.ERR_UNSUPPORTED
+    assert _split(lib, o_part=FAKE + 4) == fd.ERR_UNSUPPORTED
+    msg = fd.last_error()
+    assert "aligned" in msg
+
+
+def _combine(lib, **kw):
+    a = dict(o_part=FAKE, lse_part=FAKE, batch=2, hq=4, B=3, d=128, o=FAKE, out=fd.BF16, lse=None)
+    a.update(kw)
+    return lib.fd_combine(a["o_part"], a["lse_part"], a["batch"], a["hq"], a["B"], a["d"], a["o"],
+                          a["out"], a["lse"], None)
+
+
+def test_combine_validation(lib):
+    assert _combine(lib, o_part=None) == fd.ERR_INVALID
+    assert _combine(lib, o=None) == fd.ERR_INVALID
+    assert _combine(lib, B=0) == fd.ERR_INVALID
+    assert _combine(lib, hq=0) == fd.ERR_INVALID
+    assert _combine(lib, d=32) == fd.ERR_UNSUPPORTED
+    assert _combine(lib, out=9) == fd.ERR_UNSUPPORTED
+    assert _combine(lib, o_part=FAKE + 4) == fd.ERR_UNSUPPORTED
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kv_lens=None, batch=1, hq=4, hkv=2, n=64, d=64, dt=fd.BF16,
+             out=fd.BF16, scale=0.125, B=4, L=0, o=FAKE, lse=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.fd_decode(a["q"], a["k"], a["v"], a["kv_lens"], a["batch"], a["hq"], a["hkv"],
+                         a["n"], a["d"], a["dt"], a["out"], a["scale"], a["B"], a["L"], a["o"],
+                         a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, o=None) == fd.ERR_INVALID
+    assert _decode(lib, B=-1) == fd.ERR_INVALID
+    assert _decode(lib, B=2, L=8) == fd.ERR_INVALID     # 16 < 64
+    assert _decode(lib, out=fd.F16) == fd.ERR_UNSUPPORTED  # neither in_dtype nor f32
+    assert _decode(lib, hkv=3) == fd.ERR_INVALID
+    # more than one split and no (or too small) workspace
+    assert _decode(lib) == fd.ERR_WORKSPACE
+    need = lib.fd_workspace_bytes(1, 4, 4, 64)
+    assert _decode(lib, ws=FAKE, ws_bytes=need - 1) == fd.ERR_WORKSPACE
+    assert _decode(lib, ws=FAKE + 8, ws_bytes=need) == fd.ERR_UNSUPPORTED
+    assert "workspace" in fd.last_error() or "aligned" in fd.last_error()

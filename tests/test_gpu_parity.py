@@ -1,0 +1,313 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Tolerances (max abs over every output element):
+  fp32 inputs        o <= 1e-5,   lse <= 1e-5
+  bf16 / fp16 inputs o <= 1.5e-2, lse <= 1e-3   (fp32 accumulation)
+Split partials are held to the same bounds.  Every input is seeded.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_03_amd import fd, workloads
+from tests.conftest import golden
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (1.5e-2, 1e-3), "bf16": (1.5e-2, 1e-3)}
+
+
+def _to(dev, inp):
+    lens = inp["kv_lens"]
+    return (inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+            None if lens is None else lens.to(dev))
+
+
+def _oracle(w, inp, rows=None, scale=None):
+    lens = inp["kv_lens"]
+    return oracle.attention(w.dtype, workloads.raw(inp["q"]), workloads.raw(inp["k"]),
+                            workloads.raw(inp["v"]), None if lens is None else lens.numpy(),
+                            scale=w.scale if scale is None else scale, rows=rows)
+
+
+def _np(t):
+    return t.float().cpu().double().numpy()
+
+
+def _assert_close(name, o, lse, ro, rl, dtype, rows=None):
+    tol_o, tol_l = TOL[dtype]
+    go = _np(o).reshape(-1, o.shape[-1])
+    gl = _np(lse).reshape(-1)
+    if rows is not None:
+        idx = [b * o.shape[1] + h for b, h in rows]
+        go, gl = go[idx], gl[idx]
+    err_o = np.abs(go - ro).max() if go.size else 0.0
+    inf_ref = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(gl), inf_ref), f"{name}: -inf LSE pattern differs"
+    err_l = np.abs(gl[~inf_ref] - rl[~inf_ref]).max() if (~inf_ref).any() else 0.0
+    print(f"{name}: max|o-ref|={err_o:.3e} max|lse-ref|={err_l:.3e}", flush=True)
+    assert np.isfinite(go).all(), f"{name}: non-finite output"
+    assert err_o <= tol_o, f"{name}: o error {err_o} > {tol_o}"
+    assert err_l <= tol_l, f"{name}: lse error {err_l} > {tol_l}"
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads at full size, in the launch configuration the
+# benchmark times (library-chosen splits unless the workload fixes them).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_named_workload_full_size(gpu, cfg):
+    w = workloads.WORKLOADS[cfg]
+    inp = workloads.generate(w)
+    q, k, v, lens = _to(gpu, inp)
+    o, lse = fd.decode(q, k, v, lens, num_splits=w.num_splits, scale=w.scale)
+    torch.cuda.synchronize()
+    del q, k, v
+    ro, rl = _oracle(w, inp)
+    _assert_close(w.name, o, lse, ro, rl, w.dtype)
+
+
+def test_dominant_keys_found(gpu):
+    """Long context with 16 dominant keys per head: LSE sits near the planted
+    score (~6|q|), and matches the oracle to 1e-3."""
+    w = workloads.WORKLOADS[3]
+    w = dataclasses.replace(w, max_kv_len=16384)
+    inp = workloads.generate(w)
+    q, k, v, lens = _to(gpu, inp)
+    o, lse = fd.decode(q, k, v, lens, scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(w, inp)
+    _assert_close("dominant16_n16384", o, lse, ro, rl, w.dtype)
+    qn = inp["q"][0].double().norm(dim=-1).numpy()
+    assert np.all(_np(lse)[0] > 6 * qn - 1.0)
+
+
+# ---------------------------------------------------------------------------
+# The pages' own test material
+# ---------------------------------------------------------------------------
+
+def test_tile_example_padded_to_d64(gpu):
+    """"FlashDecoding 数学推导" §2.4.1 worked example (d = 4) run through the
+    d = 64 kernel: q, K, V zero-padded (scores unchanged), scale 0.5 passed
+    explicitly.  The first 4 outputs match the page, the rest are 0."""
+    g = golden("tile_incremental_example.json")
+    q = torch.zeros(1, 1, 64)
+    k = torch.zeros(1, 3, 1, 64)
+    v = torch.zeros(1, 3, 1, 64)
+    q[0, 0, :4] = torch.tensor(g["q"])
+    k[0, :, 0, :4] = torch.tensor(g["K"])
+    v[0, :, 0, :4] = torch.tensor(g["V"])
+    for splits in (1, 2, 3):
+        o, lse = fd.decode(q.to(gpu), k.to(gpu), v.to(gpu), num_splits=splits, scale=0.5)
+        o = _np(o)[0, 0]
+        np.testing.assert_allclose(o[:4], g["o_trace"][-1], rtol=0, atol=5e-4)
+        assert np.all(o[4:] == 0)
+        s = np.array(g["scores"])
+        assert abs(float(lse.cpu()) - (s.max() + math.log(g["l_trace"][-1]))) < 1e-4
+        ro, rl = oracle.attention("f32", workloads.raw(q), workloads.raw(k), workloads.raw(v),
+                                  scale=0.5)
+        assert np.abs(o - ro[0]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("case", golden("split_test_matrix.json")["cases"],
+                         ids=lambda c: f"seq{c['seq']}_h{c['heads']}_d{c['d']}_s{c['splits']}")
+def test_split_test_matrix_fp32(gpu, case):
+    """"adv04: Flash-Decoding" §6 test matrix (fp32, atol 1e-5)."""
+    atol = golden("split_test_matrix.json")["atol"]
+    w, inp = workloads.custom(1, case["heads"], case["heads"], case["d"], case["seq"], dtype="f32",
+                              seed=case["seq"] * 7 + case["splits"])
+    q, k, v, lens = _to(gpu, inp)
+    o, lse = fd.decode(q, k, v, lens, num_splits=case["splits"], scale=w.scale)
+    ro, rl = _oracle(w, inp)
+    assert np.abs(_np(o).reshape(ro.shape) - ro).max() <= atol
+    assert np.abs(_np(lse).reshape(rl.shape) - rl).max() <= atol
+
+
+# ---------------------------------------------------------------------------
+# Shapes, dtypes, groups, ragged lengths
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_dtype_head_dim_matrix(gpu, dtype, d):
+    lens = [1, 15, 16, 17, 1000, 2049]
+    w, inp = workloads.custom(len(lens), 4, 4, d, max(lens), dtype=dtype, seed=d + len(dtype),
+                              lens=lens)
+    q, k, v, kl = _to(gpu, inp)
+    ro, rl = _oracle(w, inp)
+    for splits, split_len in ((0, 0), (1, 0), (3, 0), (7, 300), (40, 64)):
+        o, lse = fd.decode(q, k, v, kl, num_splits=splits, split_len=split_len, scale=w.scale)
+        _assert_close(f"{dtype}_d{d}_B{splits}_L{split_len}", o, lse, ro, rl, dtype)
+
+
+@pytest.mark.parametrize("group", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_grouped_heads(gpu, group, dtype):
+    hkv = 2
+    lens = [700, 33, 4097]
+    w, inp = workloads.custom(3, hkv * group, hkv, 128, max(lens), dtype=dtype, seed=group,
+                              lens=lens)
+    q, k, v, kl = _to(gpu, inp)
+    ro, rl = _oracle(w, inp)
+    for splits in (0, 1, 5):
+        o, lse = fd.decode(q, k, v, kl, num_splits=splits, scale=w.scale)
+        _assert_close(f"gqa{group}_{dtype}_B{splits}", o, lse, ro, rl, dtype)
+
+
+def test_out_dtype_f32_for_bf16_inputs(gpu):
+    w, inp = workloads.custom(2, 8, 8, 128, 3000, dtype="bf16", seed=21)
+    q, k, v, kl = _to(gpu, inp)
+    o, lse = fd.decode(q, k, v, kl, out_dtype=torch.float32, scale=w.scale)
+    assert o.dtype == torch.float32
+    ro, rl = _oracle(w, inp)
+    # fp32 output of bf16 inputs: no output rounding, so far inside the bf16 bound
+    assert np.abs(_np(o).reshape(ro.shape) - ro).max() <= 1e-4
+    assert np.abs(_np(lse).reshape(rl.shape) - rl).max() <= 1e-4
+
+
+# ---------------------------------------------------------------------------
+# Split stage and combine stage on their own
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,group,d", [("f32", 1, 64), ("bf16", 1, 128), ("bf16", 8, 128),
+                                           ("f16", 2, 256)])
+def test_split_partials(gpu, dtype, group, d):
+    lens = [1000, 0, 257, 64]
+    w, inp = workloads.custom(4, 2 * group, 2, d, 1000, dtype=dtype, seed=5, lens=lens)
+    q, k, v, kl = _to(gpu, inp)
+    B, L = 5, 200
+    o_part = torch.full((4, 2 * group, B, d), float("nan"), device=gpu)
+    lse_part = torch.full((4, 2 * group, B), float("nan"), device=gpu)
+    fd.decode_split(q, k, v, kl, num_splits=B, split_len=L, scale=w.scale, o_part=o_part,
+                    lse_part=lse_part)
+    rop, rlp = oracle.split_partials(dtype, workloads.raw(inp["q"]), workloads.raw(inp["k"]),
+                                     workloads.raw(inp["v"]), np.array(lens, dtype=np.int32), B,
+                                     L, scale=w.scale)
+    tol_o, tol_l = TOL[dtype]
+    gop, glp = _np(o_part), _np(lse_part)
+    assert np.isfinite(gop).all(), "an o_part slot was not written"
+    assert np.array_equal(np.isneginf(glp), np.isneginf(rlp))
+    assert not np.isnan(glp).any()
+    assert np.abs(gop - rop).max() <= tol_o
+    fin = np.isfinite(rlp)
+    assert np.abs(glp[fin] - rlp[fin]).max() <= tol_l
+    assert np.all(gop[~fin] == 0)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_combine_synthetic_partials(gpu, out, d):
+    """Combine alone on partials with empty splits, all-empty rows, a single
+    finite term and spreads over 200 in S."""
+    rng = np.random.default_rng(d)
+    batch, hq, B = 3, 5, 37
+    op = rng.standard_normal((batch, hq, B, d))
+    sp = rng.uniform(-40, 40, (batch, hq, B))
+    sp[0, 0, :] = -np.inf                      # empty row
+    sp[0, 1, :] = -np.inf
+    sp[0, 1, 17] = 3.0                         # one finite term
+    sp[1, 2, ::2] = -np.inf                    # every other split empty
+    sp[2, 3, 0] = 120.0                        # spread > 200
+    sp[2, 3, 1] = -100.0
+    op[sp == -np.inf] = 0.0
+    o_part = torch.tensor(op, dtype=torch.float32)
+    lse_part = torch.tensor(sp, dtype=torch.float32)
+    ro, rl = oracle.combine(o_part.double().numpy(), lse_part.double().numpy())
+    o, lse = fd.combine(o_part.to(gpu), lse_part.to(gpu), out_dtype=workloads.TORCH_DTYPES[out])
+    go, gl = _np(o), _np(lse)
+    tol = 1e-5 if out == "f32" else (8e-3 if out == "bf16" else 1e-3)
+    assert np.abs(go - ro).max() <= tol * max(1.0, np.abs(ro).max())
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert np.abs(gl[fin] - rl[fin]).max() <= 1e-5 * max(1.0, np.abs(rl[fin]).max())
+    assert np.all(go[0, 0] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+def test_empty_and_clamped_lengths(gpu):
+    """kv_lens of 0 give (o, lse) = (0, -inf); lengths above max_kv_len are
+    clamped to it (documented), negative ones to 0."""
+    w, inp = workloads.custom(4, 4, 2, 128, 300, dtype="bf16", seed=9)
+    q, k, v, _ = _to(gpu, inp)
+    lens = torch.tensor([0, 300, 5000, -3], dtype=torch.int32)
+    for splits in (0, 1, 4):
+        o, lse = fd.decode(q, k, v, lens.to(gpu), num_splits=splits, scale=w.scale)
+        ro, rl = _oracle(w, dict(inp, kv_lens=torch.tensor([0, 300, 300, 0], dtype=torch.int32)))
+        _assert_close(f"clamped_B{splits}", o, lse, ro, rl, "bf16")
+        assert np.all(_np(o)[[0, 3]] == 0)
+        assert np.all(np.isneginf(_np(lse)[[0, 3]]))
+
+
+def test_zero_length_cache(gpu):
+    q = torch.randn(2, 4, 64, device=gpu)
+    k = torch.empty(2, 0, 4, 64, device=gpu)
+    o, lse = fd.decode(q, k, k.clone(), scale=0.125)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_more_splits_than_tokens(gpu):
+    w, inp = workloads.custom(1, 8, 8, 64, 3, dtype="f32", seed=3)
+    q, k, v, kl = _to(gpu, inp)
+    ro, rl = _oracle(w, inp)
+    for B in (4, 16, 100):
+        o, lse = fd.decode(q, k, v, kl, num_splits=B, scale=w.scale)
+        _assert_close(f"B{B}_N3", o, lse, ro, rl, "f32")
+
+
+def test_values_past_length_are_never_read(gpu):
+    """K/V rows at or beyond a sequence's length hold NaN; the result must match
+    the oracle on the valid rows, so none of them was read."""
+    w = dataclasses.replace(workloads.WORKLOADS[4], batch=4, ragged=(1, 5000))
+    inp = workloads.generate(w, poison_tail=True)
+    q, k, v, kl = _to(gpu, inp)
+    for splits in (0, 1, 3, 9):
+        o, lse = fd.decode(q, k, v, kl, num_splits=splits, scale=w.scale)
+        ro, rl = _oracle(w, inp)
+        _assert_close(f"poisoned_tail_B{splits}", o, lse, ro, rl, "bf16")
+
+
+def test_every_partial_is_written(gpu):
+    """A NaN-filled workspace: the decode result is finite and correct, so the
+    combine only read partials the split stage wrote."""
+    w, inp = workloads.custom(3, 8, 2, 128, 2000, dtype="bf16", seed=4, lens=[2000, 10, 999])
+    q, k, v, kl = _to(gpu, inp)
+    B = 6
+    ws = torch.full((fd.workspace_bytes(3, 8, B, 128) // 4,), float("nan"), device=gpu)
+    o = torch.full((3, 8, 128), float("nan"), device=gpu, dtype=torch.bfloat16)
+    lse = torch.full((3, 8), float("nan"), device=gpu)
+    fd.decode(q, k, v, kl, num_splits=B, scale=w.scale, workspace=ws, o=o, lse=lse)
+    ro, rl = _oracle(w, inp)
+    _assert_close("nan_workspace", o, lse, ro, rl, "bf16")
+
+
+def test_deterministic(gpu):
+    w = workloads.WORKLOADS[2]
+    w = dataclasses.replace(w, batch=2)
+    inp = workloads.generate(w)
+    q, k, v, kl = _to(gpu, inp)
+    o1, l1 = fd.decode(q, k, v, kl, scale=w.scale)
+    o2, l2 = fd.decode(q, k, v, kl, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_runs_on_a_side_stream(gpu):
+    """Work is queued on torch's current stream: results are right when that is
+    a non-default stream."""
+    w, inp = workloads.custom(2, 4, 4, 128, 5000, dtype="bf16", seed=8)
+    q, k, v, kl = _to(gpu, inp)
+    s = torch.cuda.Stream(device=gpu)
+    s.wait_stream(torch.cuda.current_stream(gpu))
+    with torch.cuda.stream(s):
+        o, lse = fd.decode(q, k, v, kl, scale=w.scale)
+    s.synchronize()
+    ro, rl = _oracle(w, inp)
+    _assert_close("side_stream", o, lse, ro, rl, "bf16")
