@@ -79,7 +79,8 @@ class Prepared:
         if num_splits == 0 and w.num_splits:
             num_splits = w.num_splits
         if num_splits == 0:
-            self.B, self.L = fd.choose_splits(batch, hq, hkv, self.n_max, d, inp["q"].dtype)
+            self.B, self.L = fd.choose_splits(batch, hq, hkv, self.n_max, d, inp["q"].dtype,
+                                              ragged=lens is not None)
         else:
             self.B, self.L = num_splits, -(-self.n_max // num_splits)
         self.o = torch.empty((batch, hq, d), dtype=workloads.TORCH_DTYPES[w.out_dtype],
@@ -88,9 +89,10 @@ class Prepared:
         ws = fd.workspace_bytes(batch, hq, self.B, d)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
-        self.o_part = self.ws[: batch * hq * self.B * d * 4].view(torch.float32)
-        lse_off = ((batch * hq * self.B * d * 4 + 255) // 256) * 256
-        self.lse_part = self.ws[lse_off: lse_off + batch * hq * self.B * 4].view(torch.float32)
+        # partial buffers of the split kernel when it is timed on its own
+        # (fd_decode_split always writes partials, also for one split)
+        self.o_part = torch.empty((batch, hq, self.B, d), dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty((batch, hq, self.B), dtype=torch.float32, device=dev)
         self.lib = fd.library()
         self.stream = torch.cuda.current_stream(dev)
         sp = ctypes.c_void_p(self.stream.cuda_stream)

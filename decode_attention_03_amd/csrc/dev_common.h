@@ -42,6 +42,20 @@ __device__ __forceinline__ void unpack_word(uint32_t w, float *out) {
     }
 }
 
+// Two-wide dot product of packed 16-bit pairs accumulated in fp32
+// (v_dot2c_f32_bf16 / v_dot2c_f32_f16): acc + a.lo*b.lo + a.hi*b.hi.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    if constexpr (DT == kBF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), acc, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                      __builtin_bit_cast(f16x2_t, b), acc, false);
+}
+
 template <int DT>
 struct ElemInfo {
     static constexpr int bytes = DT == kF32 ? 4 : 2;
@@ -76,8 +90,24 @@ __device__ __forceinline__ void store_out(void *base, size_t idx, float val, int
 // Loads.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint4 ld128(const void *p) { return *static_cast<const uint4 *>(p); }
-__device__ __forceinline__ uint2 ld64(const void *p) { return *static_cast<const uint2 *>(p); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 128-/64-bit loads; NT = 1 marks them non-temporal (data read once).
+template <int NT = 0>
+__device__ __forceinline__ u32x4 ld128(const void *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    else
+        return *static_cast<const u32x4 *>(p);
+}
+template <int NT = 0>
+__device__ __forceinline__ u32x2 ld64(const void *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(static_cast<const u32x2 *>(p));
+    else
+        return *static_cast<const u32x2 *>(p);
+}
 
 // ---------------------------------------------------------------------------
 // Cross-lane reductions inside one 16-lane DPP row of a wave64.
@@ -97,6 +127,20 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: quads
     v += dpp_mov<0x141>(v);  // row_half_mirror: the two quads of each half-row
     v += dpp_mov<0x140>(v);  // row_mirror: the two half-rows
+    return v;
+}
+
+// Sum over groups of N = 4, 8 or 16 consecutive lanes (N divides a DPP row);
+// every lane of a group receives the same bits.
+template <int N>
+__device__ __forceinline__ float row_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16, "unsupported group size");
+    v += dpp_mov<0xB1>(v);       // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);       // quad_perm [2,3,0,1]
+    if constexpr (N >= 8)
+        v += dpp_mov<0x141>(v);  // row_half_mirror
+    if constexpr (N >= 16)
+        v += dpp_mov<0x140>(v);  // row_mirror
     return v;
 }
 

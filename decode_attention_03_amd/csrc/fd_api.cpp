@@ -23,9 +23,11 @@
 namespace {
 
 constexpr int kVersion = 100;          // 0.1.0
-constexpr int kMaxSplits = 16384;      // combine keeps one weight per split in LDS
-constexpr int kWorkGroupsPerCU = 4;    // split-count heuristic: target WGs per CU
-constexpr int kMinSplitLenMha = 256;   // tokens; keeps partial traffic ~0.2% of K/V
+constexpr int kMaxSplits = 8192;       // combine keeps one weight per split in LDS
+constexpr int kWorkGroupsPerCU = 2;    // resident one-wave work-groups per CU
+constexpr int kRaggedRounds = 4;       // work-group rounds aimed at for ragged batches
+constexpr int kMinSplitLenMha = 256;   // tokens; partial traffic ~0.8% of K/V at d = 128
+constexpr int kMinSplitLenPerHead = 64;  // grouped: tokens per query head of the group
 constexpr int kMaxAutoSplits = 512;
 
 thread_local std::string g_error;
@@ -91,6 +93,9 @@ int check_split_inputs(const void *q, const void *k, const void *v, int batch, i
         return fail(FD_ERR_UNSUPPORTED, "q, k and v must be 16-byte aligned");
     if (!std::isfinite(scale))
         return fail(FD_ERR_INVALID, "scale is not finite");
+    // the kernels address K/V with 32-bit offsets from a per-split base
+    if ((size_t)heads_kv * head_dim * elem_bytes(in_dtype) > ((size_t)1 << 24))
+        return fail(FD_ERR_UNSUPPORTED, "one token's K row over all heads exceeds 16 MiB");
     return FD_OK;
 }
 
@@ -128,12 +133,17 @@ int fd_version(void) { return kVersion; }
 const char *fd_last_error(void) { return g_error.c_str(); }
 
 // Split count: [P2] §3 Q2 suggests roughly one split per 1K tokens, capped,
-// and notes the best count depends on the GPU.  Here the count is derived from
-// the GPU instead: enough (sequence, head, split) work-groups to give every
-// compute unit kWorkGroupsPerCU of them, but never splits shorter than a floor
-// that keeps the partial (o, LSE) traffic small next to the K/V bytes.
+// and notes that the best count depends on the GPU.  Here it is derived from
+// the GPU: both split kernels run one-wave work-groups, at most
+// kWorkGroupsPerCU resident per CU (the request depth at which MI355X HBM
+// streams best), and a work-group costs a start-up latency, so
+//   - equal lengths: one full round, batch * units * B ~ CUs * kWorkGroupsPerCU;
+//   - ragged lengths (unknown to the host): about kRaggedRounds rounds judged
+//     by the longest sequence, so that the short and partial splits even out;
+// never with splits shorter than a floor that keeps the partial (o, LSE)
+// traffic small next to the K/V bytes.
 int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
-                     int in_dtype, int num_cus, int *num_splits, int *split_len) {
+                     int in_dtype, int ragged, int num_cus, int *num_splits, int *split_len) {
     if (!num_splits || !split_len)
         return fail(FD_ERR_INVALID, "null output pointer");
     if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0 || heads_q % heads_kv)
@@ -157,9 +167,10 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     // work-groups per split index: one per (sequence, KV head) when a group is
     // computed together, else one per (sequence, query head)
     const long long units = (long long)batch * (grouped ? heads_kv : heads_q);
-    const long long target = (long long)num_cus * kWorkGroupsPerCU;
+    const long long target =
+        (long long)num_cus * kWorkGroupsPerCU * (ragged ? kRaggedRounds : 1);
     long long b = (target + units - 1) / units;
-    const long long min_len = grouped ? 128LL * group : kMinSplitLenMha;
+    const long long min_len = grouped ? kMinSplitLenPerHead * group : kMinSplitLenMha;
     long long bmax = (max_kv_len + min_len - 1) / min_len;
     if (bmax < 1)
         bmax = 1;
@@ -170,7 +181,7 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     if (b < 1)
         b = 1;
     long long len = (max_kv_len + b - 1) / b;
-    len = (len + 15) / 16 * 16;  // whole 16-token work-group steps
+    len = (len + 15) / 16 * 16;  // whole 16-token tiles
     b = (max_kv_len + len - 1) / len;
     *num_splits = (int)b;
     *split_len = (int)len;
@@ -260,8 +271,8 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
         return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
                     num_splits, split_len);
     if (num_splits == 0) {
-        rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype, 0,
-                              &num_splits, &split_len);
+        rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                              kv_lens != nullptr, 0, &num_splits, &split_len);
         if (rc != FD_OK)
             return rc;
     } else if (split_len == 0) {

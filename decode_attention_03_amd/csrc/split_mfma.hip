@@ -1,10 +1,367 @@
-// split_mfma.hip -- grouped-query split stage on the gfx950 matrix cores.
+// split_mfma.hip -- split stage for grouped-query attention on the gfx950
+// matrix cores.
+//
+// Sources (pages; sections as printed on them):
+//   [P1] "FlashDecoding 数学推导" (my-webpage-adu.pages.dev, 2026-07-15)
+//   [P3] "FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法"
+//        (my-webpage-adu.pages.dev, 2026-07-16)
+//   [P4] "从第一性原理推导 Flash Attention：IO 复杂度、Tiling 策略与在线 Softmax 的数学工程"
+//        (www.ybb.press), §8.1 (grouped-query attention: fewer KV heads)
+//
+// When G = heads_q / heads_kv query heads share one KV head, every K and V
+// row a split reads serves G query rows, and the split step is a small dense
+// contraction: S = Q_g K_tile^T (G x tokens) and O += P V_tile.  One wave
+// (one work-group) owns one (sequence b, KV head, split i) and the tokens
+// [i*L, min((i+1)*L, N_b)) ([P1] §2.5 stage 1), in tiles of 16 tokens:
+//
+//   S^T (16 tokens x 16 heads) = K_tile (16 x d) . Q_g^T (d x 16):
+//     v_mfma_f32_16x16x32 over d.  A 128-bit load of 8 contiguous d-elements
+//     of one token is already an A-operand fragment; Q_g^T (zero beyond G
+//     heads) stays in registers.  The result leaves each lane with 4 tokens
+//     of one head.
+//   online softmax per head ([P1] §2.4.1; [P4] §3.1): the reference max m
+//     of a head only moves (and O, l are rescaled) when a score exceeds it
+//     by more than 2^8 ([P4] §3.2: any common reference gives the same
+//     result); the four lanes holding a head then agree on the new max
+//     through two shuffles.  In steady state a step costs one ballot.
+//     p = exp2(s - m) is rounded to the input type and l sums exactly the
+//     rounded weights, so the weights the matrix core applies sum to l.
+//   O (16 heads x d) += P (16 x 16 tokens) . V_tile (16 x d):
+//     v_mfma_f32_16x16x16, one per 16-wide d slice.  P is the A operand
+//     exactly as the S step left it.  V, stored row-major (tokens x d) in
+//     LDS, is read back with ds_read_b64_tr_b16, which hands each lane four
+//     tokens of one d column: the B-operand fragment.
+//
+// The split writes o = O / l and S = m + log l per query head ([P3]
+// §2.3.2-§2.3.3).  Scores are in the log2 domain (scale * log2(e) applied to
+// the fp32 MFMA result).  K/V loads are ordinary (cached) loads: a 16-token
+// A-operand tile reads each 256-byte head row as four 64-byte pieces, which
+// the L2 merges into whole lines.  The next tile's loads are issued before
+// the current tile's arithmetic; at
+// most two work-groups are resident per CU (LDS reservation), which keeps
+// the HBM request stream near its efficient depth.
 #include "dev_common.h"
 
 namespace fd {
+namespace {
 
-bool split_mfma_supported(int, int, int) { return false; }
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-hipError_t launch_split_mfma(const SplitArgs &, int, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kMaxGroup = 16;    // query heads per KV head one wave can hold
+constexpr float kRescaleGap = 8.f;  // log2 units the running max may lag
+
+template <int DT>
+struct Mma;
+
+template <>
+struct Mma<kBF16> {
+    static __device__ __forceinline__ f32x4_t s_tile(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
+                                                       0);
+    }
+    static __device__ __forceinline__ f32x4_t pv_tile(u32x2 a, s16x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), b, c, 0,
+                                                         0, 0);
+    }
+    // Round four weights to bf16 (nearest even); returns the packed pair and
+    // adds the rounded values to *sum.
+    static __device__ __forceinline__ u32x2 pack(const float *p, float *sum) {
+        const bf16x4_t v = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+        *sum += ((float)v[0] + (float)v[1]) + ((float)v[2] + (float)v[3]);
+        return __builtin_bit_cast(u32x2, v);
+    }
+};
+
+template <>
+struct Mma<kF16> {
+    static __device__ __forceinline__ f32x4_t s_tile(u32x4 a, u32x4 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t pv_tile(u32x2 a, s16x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                     __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ u32x2 pack(const float *p, float *sum) {
+        const f16x4_t v = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+        *sum += ((float)v[0] + (float)v[1]) + ((float)v[2] + (float)v[3]);
+        return __builtin_bit_cast(u32x2, v);
+    }
+};
+
+#ifndef FD_MFMA_NT
+#define FD_MFMA_NT 0
+#endif
+#ifndef FD_MFMA_STEP_KB
+#define FD_MFMA_STEP_KB 16
+#endif
+
+template <int D>
+struct Tiles {
+    static constexpr int ROW = D * 2;         // bytes of one head row (16-bit types)
+    static constexpr int NC = D / 32;         // 128-bit chunks per lane per token (K or V)
+    static constexpr int NT = D / 16;         // 16-wide d slices of O
+    // 16-token tiles per step: FD_MFMA_STEP_KB of K+V per wave and step
+    static constexpr int U = FD_MFMA_STEP_KB * 1024 / (16 * ROW * 2) > 0
+                                 ? FD_MFMA_STEP_KB * 1024 / (16 * ROW * 2)
+                                 : 1;
+    static constexpr int LDS_ROW = ROW + 32;  // padded LDS row: conflict-free transpose reads
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
+    using T = Tiles<D>;
+    constexpr int NC = T::NC, NT = T::NT, U = T::U;
+    using M = Mma<DT>;
+    __shared__ __attribute__((aligned(16))) char vlds[U][16 * T::LDS_ROW];
+
+    const int lane = threadIdx.x;
+    const int col = lane & 15;  // tile token (loads) / head (S) / d column (O)
+    const int grp = lane >> 4;  // 0..3
+    const int G = a.heads_q / a.heads_kv;
+
+    // Work-group -> (b, KV head, split), KV head fastest.
+    const int kvh = blockIdx.x % a.heads_kv;
+    const int rest = blockIdx.x / a.heads_kv;
+    const int split = rest % a.num_splits;
+    const int b = rest / a.num_splits;
+
+    int n = a.kv_lens ? a.kv_lens[b] : a.max_kv_len;
+    n = n < 0 ? 0 : (n > a.max_kv_len ? a.max_kv_len : n);
+    const long t0 = (long)split * a.split_len;
+    const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
+
+    f32x4_t oacc[NT];  // O[head 4*grp + r][16*t + col]
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_used = -INFINITY;  // reference max of head `col` (log2 domain)
+    float lsum = 0.f;          // this lane's share of l for head `col`
+
+    if (t0 < t1) {
+        // Q_g^T fragments: head `col` of the group, d = 32c + 8*grp + [0, 8).
+        u32x4 qf[NC];
+        {
+            const char *qrow = static_cast<const char *>(a.q) +
+                               ((size_t)b * a.heads_q + (size_t)kvh * G + col) * T::ROW;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                qf[c] = u32x4{0u, 0u, 0u, 0u};
+            if (col < G) {  // heads past the group stay zero (their rows are never written)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    qf[c] = ld128<0>(qrow + c * 64 + grp * 16);
+            }
+        }
+        const size_t tok_stride = (size_t)a.heads_kv * T::ROW;
+        const size_t split_base =
+            (((size_t)b * a.max_kv_len + (size_t)t0) * a.heads_kv + kvh) * T::ROW;
+        const char *kbase = static_cast<const char *>(a.k) + split_base;
+        const char *vbase = static_cast<const char *>(a.v) + split_base;
+        const uint32_t stride32 = (uint32_t)tok_stride;
+        const uint32_t lane_byte = (uint32_t)grp * 16u;
+        const int ntok = (int)(t1 - t0);
+        constexpr int kStepTok = 16 * U;
+        const int nsteps = (ntok + kStepTok - 1) / kStepTok;
+
+        // Step st: tiles u of 16 tokens t0 + st*16U + 16u + [0, 16); lane loads
+        // token `col` of each tile, d = 32c + 8*grp + [0, 8).  Tokens past the
+        // end re-read the last valid token (in bounds) and are masked later.
+        auto load_step = [&](int st, u32x4 (*kd)[NC], u32x4 (*vd)[NC]) {
+            const int sa = st < nsteps ? st : nsteps - 1;
+            const int first = sa * kStepTok;
+            const int last_rel = ntok - 1 - first;
+            const char *kb = kbase + (size_t)first * tok_stride;
+            const char *vb = vbase + (size_t)first * tok_stride;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                int rel = 16 * u + col;
+                rel = rel < last_rel ? rel : last_rel;
+                const uint32_t off = (uint32_t)rel * stride32 + lane_byte;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    kd[u][c] = ld128<FD_MFMA_NT>(kb + off + c * 64);
+                    vd[u][c] = ld128<FD_MFMA_NT>(vb + off + c * 64);
+                }
+            }
+        };
+
+        auto compute_step = [&](int st, const u32x4 (*kc)[NC], const u32x4 (*vc)[NC]) {
+            // V rows to LDS, row-major (token x d) with padded rows.
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    *reinterpret_cast<u32x4 *>(vlds[u] + col * T::LDS_ROW + c * 64 + grp * 16) =
+                        vc[u][c];
+            // S^T tiles on the matrix cores, scaled into the log2 domain.
+            float x[U][4];
+            float mx = -INFINITY;  // max of this lane's tokens
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    s = M::s_tile(kc[u][c], qf[c], s);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rel = st * kStepTok + 16 * u + 4 * grp + r;
+                    x[u][r] = rel < ntok ? s[r] * a.scale_log2 : -INFINITY;
+                    mx = fmaxf(mx, x[u][r]);
+                }
+            }
+            // The reference max of a head only has to bound its scores within
+            // 2^kRescaleGap, so the four lanes of a head synchronise (and O, l
+            // are rescaled) only when some lane's tokens outgrow it; in steady
+            // state this is a single ballot.
+            if (__ballot(mx > m_used + kRescaleGap)) {
+                float hm = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                hm = fmaxf(hm, __shfl_xor(hm, 32, 64));
+                const float m_new = fmaxf(m_used, hm);
+                const bool grow = m_new > m_used + kRescaleGap;  // same on a head's 4 lanes
+                const float alpha = grow ? fast_exp2(m_used - m_new) : 1.f;
+                if (grow)
+                    m_used = m_new;
+                lsum *= alpha;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        oacc[t][r] *= ar;
+                }
+            }
+            const float mref = m_used == -INFINITY ? 0.f : m_used;
+            __syncthreads();  // V tile visible to every lane
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[r] = fast_exp2(x[u][r] - mref);
+                const u32x2 pa = M::pack(p, &lsum);
+                const char *vrow = vlds[u] + (4 * grp + (col >> 2)) * T::LDS_ROW + (col & 3) * 8;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4_t *)(vrow + t * 32));
+                    oacc[t] = M::pv_tile(pa, vb, oacc[t]);
+                }
+            }
+            __syncthreads();  // reads done before the next step overwrites the tile
+        };
+
+        u32x4 kw[U][NC], vw[U][NC], kx[U][NC], vx[U][NC];
+        const int npairs = nsteps >> 1;
+        load_step(0, kw, vw);
+        for (int pr = 0; pr < npairs; ++pr) {
+            const int st = 2 * pr;
+            load_step(st + 1, kx, vx);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(st, kw, vw);
+            load_step(st + 2, kw, vw);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(st + 1, kx, vx);
+        }
+        if (nsteps & 1)
+            compute_step(nsteps - 1, kw, vw);
+    }
+
+    // l of head `col`: the four lanes holding it each summed their tokens.
+    float ltot = lsum + __shfl_xor(lsum, 16, 64);
+    ltot += __shfl_xor(ltot, 32, 64);
+    // Output rows: this lane holds heads 4*grp + r of O.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        const float lr = __shfl(ltot, h, 64);
+        const float mr = __shfl(m_used, h, 64);
+        if (h >= G)
+            continue;
+        const bool any = lr > 0.f;
+        const float inv = any ? 1.f / lr : 0.f;
+        const float lse = any ? (mr + fast_log2(lr)) * kLn2 : -INFINITY;
+        const size_t rowid = (size_t)b * a.heads_q + (size_t)kvh * G + h;
+        if (a.o_part) {
+            const size_t slot = rowid * a.num_splits + split;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                a.o_part[slot * D + 16 * t + col] = oacc[t][r] * inv;
+            if (col == 0)
+                a.lse_part[slot] = lse;
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                store_out(a.o, rowid * D + 16 * t + col, oacc[t][r] * inv, a.out_dtype);
+            if (col == 0 && a.lse)
+                a.lse[rowid] = lse;
+        }
+    }
+}
+
+int lds_per_cu_mfma() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess || v <= 0)
+            v = -1;
+        cached[dev] = v;
+    }
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+#ifndef FD_MFMA_WG_PER_CU
+#define FD_MFMA_WG_PER_CU 2
+#endif
+
+template <int DT, int D>
+hipError_t launch(const SplitArgs &a, hipStream_t stream) {
+    using T = Tiles<D>;
+    constexpr size_t kStatic = (size_t)T::U * 16 * T::LDS_ROW;
+    const long grid = (long)a.batch * a.heads_kv * a.num_splits;
+    size_t pad = 0;
+    const int lds = lds_per_cu_mfma();
+    if (FD_MFMA_WG_PER_CU > 0 && lds > 0) {
+        const size_t want = (size_t)lds / (FD_MFMA_WG_PER_CU + 1) + 256;
+        pad = want > kStatic ? want - kStatic : 0;
+    }
+    hipLaunchKernelGGL((split_mfma_kernel<DT, D>), dim3((unsigned)grid), dim3(64), pad, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const SplitArgs &a, hipStream_t stream) {
+    switch (a.head_dim) {
+    case 64: return launch<DT, 64>(a, stream);
+    case 128: return launch<DT, 128>(a, stream);
+    case 256: return launch<DT, 256>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool split_mfma_supported(int in_dtype, int head_dim, int group) {
+    return (in_dtype == kBF16 || in_dtype == kF16) && group >= 2 && group <= kMaxGroup &&
+           (head_dim == 64 || head_dim == 128 || head_dim == 256);
+}
+
+hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream) {
+    switch (in_dtype) {
+    case kBF16: return launch_dt<kBF16>(a, stream);
+    case kF16: return launch_dt<kF16>(a, stream);
+    default: return hipErrorNotSupported;
+    }
+}
 
 }  // namespace fd

@@ -1,5 +1,5 @@
 // split_valu.hip -- split stage of split-KV decode attention on the gfx950
-// vector ALUs (one query row per work-group).
+// vector ALUs.
 //
 // Sources (pages; sections as printed on them):
 //   [P1] "FlashDecoding 数学推导" (my-webpage-adu.pages.dev, 2026-07-15)
@@ -8,104 +8,124 @@
 //   [P4] "从第一性原理推导 Flash Attention：IO 复杂度、Tiling 策略与在线 Softmax 的数学工程"
 //        (www.ybb.press)
 //
-// One work-group (256 threads = 4 waves) owns one (sequence b, query head h,
-// split i) and the tokens [i*L, min((i+1)*L, N_b)) of KV head h / group
-// ([P1] §2.5 stage 1, step 2a).  The 64 lanes of a wave form four 16-lane
-// DPP rows; each row holds one token at a time, every lane of the row owning
-// d/16 contiguous elements of that token's K and V rows.  So one wave-wide
-// 128-bit load instruction fetches four whole 256-byte rows (d = 128, 16-bit
-// types), and the 16 rows of the work-group walk 16 consecutive tokens per
-// step.  A row reduces its q.K partial sums with four DPP adds, keeps a
-// running (m, l, o) with the online update ([P1] §2.4.1 incremental form,
-// with o left unnormalised as in the block update of [P4] §3.1), and the 16
-// row states are merged in LDS with the same rule ([P4] §3.2 merge lemma).
-// The split writes o = o_acc / l and S = m + log l ([P3] §2.3.2-§2.3.3).
+// A work-group owns one split i of one sequence b for HPW consecutive query
+// heads: tokens [i*L, min((i+1)*L, N_b)) of the KV heads those query heads
+// read ([P1] §2.5 stage 1, step 2a).  The lanes form 16-lane DPP rows; a row
+// holds one (head, token) pair at a time, every lane of the row owning d/16
+// contiguous elements of that token's K and V rows, so one 128-bit load per
+// lane fetches a whole 256-byte head row (d = 128, 16-bit types).  With
+// HPW > 1 the rows of one step read adjacent heads of the same token, i.e.
+// HPW * 256 contiguous bytes.  A row reduces its q.K partial sums with four
+// DPP adds and keeps a running (m, l, o) with the online update ([P1] §2.4.1
+// incremental form, o left unnormalised as in the block update of [P4]
+// §3.1); the rows of one head are merged in LDS with the same rule ([P4]
+// §3.2 merge lemma), and the split writes o = o_acc / l and S = m + log l
+// ([P3] §2.3.2-§2.3.3).
 //
 // Scores are kept in the log2 domain: q is pre-multiplied by scale*log2(e)
 // so every exponential is one v_exp_f32; the LSE is converted back to the
-// natural log on output.  K/V go straight from HBM to VGPRs: each lane uses
-// exactly the bytes it loads, so staging through LDS would add traffic
-// without reuse.  The next step's loads are issued before the current step's
-// arithmetic so that every wave keeps two steps of K/V in flight.
+// natural log on output.  K/V go straight from HBM to VGPRs with
+// non-temporal 128-bit loads (each byte is used once, by the lane that loads
+// it, so staging through LDS would add traffic without reuse).  The next
+// step's loads are issued before the current step's arithmetic.
+//
+// HBM efficiency on MI355X peaks when each CU has about two waves with
+// ~16 KB of loads in flight each; more concurrent requests lower the
+// achieved bandwidth.  So the launcher caps resident work-groups per CU by
+// reserving LDS (the reservation is never touched), whatever the grid size.
 #include "dev_common.h"
 
 namespace fd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = kThreads / 16;  // token slots per work-group step
+#ifndef FD_VALU_STEP_BYTES
+#define FD_VALU_STEP_BYTES 64
+#endif
 
-template <int DT, int D>
+template <int DT, int D, int LPR>
 struct Layout {
     static constexpr int E = ElemInfo<DT>::bytes;
-    static constexpr int ROW_BYTES = D * E;            // one token, one head
-    static constexpr int LANE_BYTES = ROW_BYTES / 16;  // 8, 16, 32 or 64
-    static constexpr bool HALF = LANE_BYTES == 8;      // d = 64 with 16-bit types
+    static constexpr int ROW_BYTES = D * E;             // one token, one head
+    static constexpr int LANE_BYTES = ROW_BYTES / LPR;  // 8, 16, 32 or 64
+    static constexpr bool HALF = LANE_BYTES == 8;       // one 64-bit load per lane
     static constexpr int NV = HALF ? 1 : LANE_BYTES / 16;
     static constexpr int WORDS = LANE_BYTES / 4;
-    static constexpr int EPL = D / 16;                 // elements per lane
+    static constexpr int EPL = D / LPR;                 // elements per lane
     static constexpr int PW = ElemInfo<DT>::per_word;
+    static constexpr int SPAN = LPR * 16;               // bytes one 128-bit load covers per row
+    static_assert(LANE_BYTES >= 8, "row too short for this lane count");
     // Element index held by lane `sub` in word j, sub-element e.  Full 16-byte
     // vectors are spread so that each load instruction covers whole
-    // contiguous 256-byte spans of a row.
+    // contiguous spans of a row.
     __device__ static constexpr int elem(int sub, int j, int e) {
         if (HALF)
-            return sub * 4 + j * PW + e;
-        return (j / 4) * (256 / E) + sub * (16 / E) + (j % 4) * PW + e;
+            return sub * (8 / E) + j * PW + e;
+        return (j / 4) * (SPAN / E) + sub * (16 / E) + (j % 4) * PW + e;
     }
-    // Default tokens per row per step: 64 bytes of K (and of V) per lane.
-    static constexpr int U = 64 / LANE_BYTES;
+    // Tokens per row per step: FD_VALU_STEP_BYTES of K (and as many of V)
+    // per lane.
+    static constexpr int U =
+        FD_VALU_STEP_BYTES / LANE_BYTES > 0 ? FD_VALU_STEP_BYTES / LANE_BYTES : 1;
 };
 
 // Load this lane's words of one row; `p` already includes the lane's byte
 // offset inside the row (sub * 8 or sub * 16).
-template <int DT, int D>
+template <int DT, int D, int LPR>
 __device__ __forceinline__ void load_row(const char *p, uint32_t *w) {
-    using L = Layout<DT, D>;
+    using L = Layout<DT, D, LPR>;
     if constexpr (L::HALF) {
-        uint2 x = ld64(p);
-        w[0] = x.x;
-        w[1] = x.y;
+        const u32x2 x = ld64<1>(p);
+        w[0] = x[0];
+        w[1] = x[1];
     } else {
 #pragma unroll
         for (int c = 0; c < L::NV; ++c) {
-            uint4 x = ld128(p + c * 256);
-            w[4 * c + 0] = x.x;
-            w[4 * c + 1] = x.y;
-            w[4 * c + 2] = x.z;
-            w[4 * c + 3] = x.w;
+            const u32x4 x = ld128<1>(p + c * L::SPAN);
+            w[4 * c + 0] = x[0];
+            w[4 * c + 1] = x[1];
+            w[4 * c + 2] = x[2];
+            w[4 * c + 3] = x[3];
         }
     }
 }
 
-template <int DT, int D>
+template <int DT, int D, int LPR>
 __device__ __forceinline__ void unpack_row(const uint32_t *w, float *f) {
-    using L = Layout<DT, D>;
+    using L = Layout<DT, D, LPR>;
 #pragma unroll
     for (int j = 0; j < L::WORDS; ++j)
         unpack_word<DT>(w[j], f + j * L::PW);
 }
 
-template <int DT, int D, int U>
-__global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
-    using L = Layout<DT, D>;
+template <int DT, int D, int THREADS, int HPW, int LPR>
+__global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
+    using L = Layout<DT, D, LPR>;
     constexpr int EPL = L::EPL;
     constexpr int WORDS = L::WORDS;
+    constexpr int U = L::U;
+    constexpr int kRows = THREADS / LPR;  // rows of LPR lanes
+    constexpr int TPS = kRows / HPW;     // token slots per step position
+    static_assert(kRows % HPW == 0, "HPW must divide the row count");
 
     __shared__ float sm_acc[kRows][D];
     __shared__ float sm_m[kRows];
     __shared__ float sm_l[kRows];
 
     const int tid = threadIdx.x;
-    const int sub = tid & 15;
-    const int row = tid >> 4;
+    const int sub = tid % LPR;
+    const int row = tid / LPR;
+    const int hoff = row % HPW;   // head of this row within the group
+    const int tslot = row / HPW;  // token slot of this row
 
-    // Work-group -> (b, hq, split); the query head varies fastest so that
-    // neighbouring work-groups read neighbouring head rows of the same tokens.
-    const int hq = blockIdx.x % a.heads_q;
-    const int rest = blockIdx.x / a.heads_q;
+    // Work-group -> (b, head group, split); the head group varies fastest so
+    // that neighbouring work-groups read neighbouring head rows of the same
+    // tokens.
+    const int ngroups = a.heads_q / HPW;
+    const int hg = blockIdx.x % ngroups;
+    const int rest = blockIdx.x / ngroups;
     const int split = rest % a.num_splits;
     const int b = rest / a.num_splits;
+    const int hq = hg * HPW + hoff;
     const int kvh = hq / (a.heads_q / a.heads_kv);
 
     int n = a.kv_lens ? a.kv_lens[b] : a.max_kv_len;
@@ -121,49 +141,55 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
         acc[i] = 0.f;
 
     if (t0 < t1) {
-        // q row of this head, pre-scaled into the log2 domain.
+        const uint32_t lane_byte = L::HALF ? sub * 8u : sub * 16u;
+        // q row of this row's head.  fp32: pre-scaled into the log2 domain.
+        // 16-bit types: kept packed for the two-wide dot products (the
+        // products of two bf16 or two fp16 values are exact in fp32), and the
+        // scale is applied to the reduced score instead.
+        uint32_t qw[WORDS];
         float qf[EPL];
         {
-            uint32_t qw[WORDS];
             const char *qrow = static_cast<const char *>(a.q) +
                                ((size_t)b * a.heads_q + hq) * (size_t)L::ROW_BYTES;
-            load_row<DT, D>(qrow + (L::HALF ? sub * 8 : sub * 16), qw);
-            unpack_row<DT, D>(qw, qf);
+            load_row<DT, D, LPR>(qrow + lane_byte, qw);
+            if constexpr (DT == kF32) {
+                unpack_row<DT, D, LPR>(qw, qf);
 #pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                qf[i] *= a.scale_log2;
+                for (int i = 0; i < EPL; ++i)
+                    qf[i] *= a.scale_log2;
+            }
         }
         // K/V addressing: a uniform (scalar) base per step plus a 32-bit
-        // per-lane byte offset, so the loads use the SGPR-base form and cost
-        // two VALU ops of address arithmetic each.  tok_stride < 2^24 is
-        // checked on the host, so every offset below fits in 32 bits.
+        // per-lane byte offset (token slot, head, lane), so the loads use the
+        // SGPR-base form.  One token's row over all heads is at most 16 MiB
+        // (checked on the host), so every offset below fits in 32 bits.
         const size_t tok_stride = (size_t)a.heads_kv * L::ROW_BYTES;
-        const size_t split_base =
-            (((size_t)b * a.max_kv_len + (size_t)t0) * a.heads_kv + kvh) * L::ROW_BYTES;
+        const size_t split_base = ((size_t)b * a.max_kv_len + (size_t)t0) * tok_stride;
         const char *kbase = static_cast<const char *>(a.k) + split_base;
         const char *vbase = static_cast<const char *>(a.v) + split_base;
         const uint32_t stride32 = (uint32_t)tok_stride;
-        const uint32_t lane_byte = L::HALF ? sub * 8u : sub * 16u;
+        const uint32_t lane_off = (uint32_t)kvh * (uint32_t)L::ROW_BYTES + lane_byte;
         const int ntok = (int)(t1 - t0);
-        const int nsteps = (ntok + kRows * U - 1) / (kRows * U);
+        constexpr int kStepTok = TPS * U;  // tokens per step
+        const int nsteps = (ntok + kStepTok - 1) / kStepTok;
 
         uint32_t kw[U][WORDS], vw[U][WORDS];
-        // Step `st` covers tokens t0 + st*16U + u*16 + row.  Slots past the end
-        // re-read the last valid token (always in bounds) and are masked, and
-        // a step past the last one re-reads the last step.
+        // Step `st` covers tokens t0 + st*TPS*U + u*TPS + tslot.  Slots past
+        // the end re-read the last valid token (always in bounds) and are
+        // masked, and a step past the last one re-reads the last step.
         auto load_step = [&](int st, uint32_t (*kd)[WORDS], uint32_t (*vd)[WORDS]) {
             const int sa = st < nsteps ? st : nsteps - 1;
-            const int first = sa * (kRows * U);
+            const int first = sa * kStepTok;
             const int last_rel = ntok - 1 - first;
             const char *kb = kbase + (size_t)first * tok_stride;
             const char *vb = vbase + (size_t)first * tok_stride;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                int rel = u * kRows + row;
+                int rel = u * TPS + tslot;
                 rel = rel < last_rel ? rel : last_rel;
-                const uint32_t off = (uint32_t)rel * stride32 + lane_byte;
-                load_row<DT, D>(kb + off, kd[u]);
-                load_row<DT, D>(vb + off, vd[u]);
+                const uint32_t off = (uint32_t)rel * stride32 + lane_off;
+                load_row<DT, D, LPR>(kb + off, kd[u]);
+                load_row<DT, D, LPR>(vb + off, vd[u]);
             }
         };
         // One step of arithmetic on the K/V words of step `st`.
@@ -173,14 +199,21 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
             float s[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float kf[EPL];
-                unpack_row<DT, D>(kc[u], kf);
                 float part = 0.f;
+                if constexpr (DT == kF32) {
+                    float kf[EPL];
+                    unpack_row<DT, D, LPR>(kc[u], kf);
 #pragma unroll
-                for (int i = 0; i < EPL; ++i)
-                    part = __builtin_fmaf(qf[i], kf[i], part);
-                s[u] = row16_sum(part);
-                const int rel = st * (kRows * U) + u * kRows + row;
+                    for (int i = 0; i < EPL; ++i)
+                        part = __builtin_fmaf(qf[i], kf[i], part);
+                    s[u] = row_sum<LPR>(part);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < WORDS; ++j)
+                        part = dot2<DT>(qw[j], kc[u][j], part);
+                    s[u] = row_sum<LPR>(part) * a.scale_log2;
+                }
+                const int rel = st * kStepTok + u * TPS + tslot;
                 s[u] = rel < ntok ? s[u] : -INFINITY;
             }
             // online update of (m, l, acc) by U tokens
@@ -204,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float vf[EPL];
-                unpack_row<DT, D>(vc[u], vf);
+                unpack_row<DT, D, LPR>(vc[u], vf);
 #pragma unroll
                 for (int i = 0; i < EPL; ++i)
                     acc[i] = __builtin_fmaf(p[u], vf[i], acc[i]);
@@ -235,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
             compute_step(nsteps - 1, kw, vw);
     }
 
-    // Merge the 16 row states of the work-group.
+    // Merge the TPS row states of each head.
     if (sub == 0) {
         sm_m[row] = m;
         sm_l[row] = l;
@@ -247,43 +280,106 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(SplitArgs a) {
             sm_acc[row][L::elem(sub, j, e)] = acc[j * L::PW + e];
     __syncthreads();
 
-    if (tid < D) {
+    for (int idx = tid; idx < HPW * D; idx += THREADS) {
+        const int hh = idx / D;
+        const int dd = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r)
+        for (int r = hh; r < kRows; r += HPW)
             M = fmaxf(M, sm_m[r]);
         float out = 0.f, lse = -INFINITY;
         if (M != -INFINITY) {
             float Ls = 0.f, Os = 0.f;
 #pragma unroll
-            for (int r = 0; r < kRows; ++r) {
+            for (int r = hh; r < kRows; r += HPW) {
                 const float w = fast_exp2(sm_m[r] - M);
                 Ls = __builtin_fmaf(w, sm_l[r], Ls);
-                Os = __builtin_fmaf(w, sm_acc[r][tid], Os);
+                Os = __builtin_fmaf(w, sm_acc[r][dd], Os);
             }
             out = Os / Ls;
             lse = (M + fast_log2(Ls)) * kLn2;
         }
-        const size_t rowid = (size_t)b * a.heads_q + hq;
+        const size_t rowid = (size_t)b * a.heads_q + hg * HPW + hh;
         if (a.o_part) {
             const size_t slot = rowid * a.num_splits + split;
-            a.o_part[slot * D + tid] = out;
-            if (tid == 0)
+            a.o_part[slot * D + dd] = out;
+            if (dd == 0)
                 a.lse_part[slot] = lse;
         } else {
-            store_out(a.o, rowid * D + tid, out, a.out_dtype);
-            if (tid == 0 && a.lse)
+            store_out(a.o, rowid * D + dd, out, a.out_dtype);
+            if (dd == 0 && a.lse)
                 a.lse[rowid] = lse;
         }
     }
 }
 
+// Resident work-groups per CU are capped by reserving LDS: a work-group
+// asks for just over 1/(cap+1) of the CU's LDS, so cap of them fit.
+int lds_per_cu() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess || v <= 0)
+            v = -1;
+        cached[dev] = v;
+    }
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+template <int DT, int D, int THREADS, int HPW, int LPR>
+hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
+    constexpr int kRows = THREADS / LPR;
+    constexpr size_t kStatic = sizeof(float) * (size_t)(kRows * D + 2 * kRows);
+    const long grid = (long)a.batch * (a.heads_q / HPW) * a.num_splits;
+    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR>;
+    size_t pad = 0;
+    const int lds = lds_per_cu();
+    if (wg_per_cu > 0 && lds > 0) {
+        const size_t want = (size_t)lds / (size_t)(wg_per_cu + 1) + 256;
+        pad = want > kStatic ? want - kStatic : 0;
+        if (pad > 65536) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)pad);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), pad, stream, a);
+    return hipGetLastError();
+}
+
+#ifndef FD_VALU_THREADS
+#define FD_VALU_THREADS 64
+#endif
+#ifndef FD_VALU_HPW
+#define FD_VALU_HPW 1
+#endif
+#ifndef FD_VALU_WG_PER_CU
+#define FD_VALU_WG_PER_CU 2
+#endif
+
+#ifndef FD_VALU_ROW_BYTES
+#define FD_VALU_ROW_BYTES 16  // bytes of a head row per lane (sets lanes per row)
+#endif
+
+// Lanes per token row: ROW_BYTES / FD_VALU_ROW_BYTES, clamped to [4, 16].
+template <int DT, int D>
+constexpr int lanes_per_row() {
+    constexpr int r = D * ElemInfo<DT>::bytes / FD_VALU_ROW_BYTES;
+    return r > 16 ? 16 : (r < 4 ? 4 : r);
+}
+
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
-    const long grid = (long)a.batch * a.heads_q * a.num_splits;
-    hipLaunchKernelGGL((split_valu_kernel<DT, D, Layout<DT, D>::U>), dim3((unsigned)grid),
-                       dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    constexpr int LPR = lanes_per_row<DT, D>();
+    if (FD_VALU_HPW > 1 && a.heads_q % FD_VALU_HPW == 0)
+        return launch_cfg<DT, D, FD_VALU_THREADS, FD_VALU_HPW, LPR>(a, FD_VALU_WG_PER_CU, stream);
+    return launch_cfg<DT, D, FD_VALU_THREADS, 1, LPR>(a, FD_VALU_WG_PER_CU, stream);
 }
 
 template <int DT>

@@ -56,7 +56,7 @@ def library() -> ctypes.CDLL:
         IP = ctypes.POINTER(ctypes.c_int)
         lib.fd_version.argtypes, lib.fd_version.restype = [], I
         lib.fd_last_error.argtypes, lib.fd_last_error.restype = [], ctypes.c_char_p
-        lib.fd_choose_splits.argtypes = [I, I, I, I, I, I, I, IP, IP]
+        lib.fd_choose_splits.argtypes = [I, I, I, I, I, I, I, I, IP, IP]
         lib.fd_choose_splits.restype = I
         lib.fd_workspace_bytes.argtypes, lib.fd_workspace_bytes.restype = [I, I, I, I], S
         lib.fd_decode_split.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P]
@@ -125,11 +125,11 @@ def _shapes(q, k, v, kv_lens):
 
 
 def choose_splits(batch: int, heads_q: int, heads_kv: int, max_kv_len: int, head_dim: int,
-                  dtype: torch.dtype, num_cus: int = 0) -> tuple[int, int]:
+                  dtype: torch.dtype, ragged: bool = False, num_cus: int = 0) -> tuple[int, int]:
     """(num_splits, split_len) from the library heuristic (num_cus 0: the device's)."""
     b, length = ctypes.c_int(), ctypes.c_int()
     _check(library().fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim,
-                                      _code(dtype), num_cus, ctypes.byref(b),
+                                      _code(dtype), int(bool(ragged)), num_cus, ctypes.byref(b),
                                       ctypes.byref(length)))
     return b.value, length.value
 
@@ -195,7 +195,8 @@ def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len:
     out_dtype = out_dtype or q.dtype
     dev = q.device
     if num_splits == 0:
-        num_splits, split_len = choose_splits(batch, heads_q, heads_kv, n_max, d, q.dtype)
+        num_splits, split_len = choose_splits(batch, heads_q, heads_kv, n_max, d, q.dtype,
+                                              ragged=kv_lens is not None)
     if o is None:
         o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
     if lse is None and return_lse:

@@ -136,8 +136,15 @@ def generate(w: Workload, poison_tail: bool = False) -> dict:
 
     jobs = [(name, b, c) for b in range(w.batch) for name in ("k", "v")
             for c in range(-(-n_max // CHUNK))]
-    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(fill, jobs))
+    # one torch thread per worker: the pieces already run in parallel, and
+    # nested intra-op pools would start threads per worker
+    intra = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, jobs))
+    finally:
+        torch.set_num_threads(intra)
     if w.dominant:
         if w.group != 1:
             raise ValueError("dominant keys are defined for one query head per KV head")

@@ -80,12 +80,16 @@ const char *fd_last_error(void);
  * gives the rule of thumb this starts from: more splits for longer caches, up
  * to a cap; here the count is set so the launch fills the GPU's compute
  * units).  Host-only and deterministic.
+ *   ragged:  nonzero when sequences may have different lengths (kv_lens is
+ *            given); the split length is then shortened so that short and
+ *            partial splits balance out.
  *   num_cus <= 0: query the current HIP device (cached); > 0: use as given.
  *   Outputs: *num_splits >= 1, *split_len >= 1, and
  *            (*num_splits) * (*split_len) >= max_kv_len.
- * Returns FD_OK, FD_ERR_INVALID (bad sizes or null outputs) or FD_ERR_HIP. */
+ * Returns FD_OK, FD_ERR_INVALID (bad sizes or null outputs),
+ * FD_ERR_UNSUPPORTED (head_dim or dtype) or FD_ERR_HIP. */
 int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
-                     int in_dtype, int num_cus, int *num_splits, int *split_len);
+                     int in_dtype, int ragged, int num_cus, int *num_splits, int *split_len);
 
 /* Bytes of workspace fd_decode needs for num_splits splits: o_part and
  * lse_part as laid out above, each starting on a 256-byte boundary.  Returns
@@ -112,7 +116,8 @@ int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_
                int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream);
 
 /* Whole decode step: split + combine.
- *   num_splits == 0: B and L come from fd_choose_splits (split_len ignored).
+ *   num_splits == 0: B and L come from fd_choose_splits (split_len ignored;
+ *     ragged = kv_lens != NULL).
  *   num_splits > 0, split_len == 0: L = ceil(max_kv_len / num_splits)
  *     ([P2] §4 chunking).  num_splits > 0, split_len > 0: used as given.
  * With B == 1 the split stage writes o and lse itself and workspace may be

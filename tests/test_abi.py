@@ -45,10 +45,11 @@ def test_exports_every_declared_symbol(lib):
     (1, 1, 1, 64, fd.F32), (8, 32, 32, 128, fd.BF16), (1, 32, 32, 128, fd.BF16),
     (16, 64, 8, 128, fd.BF16), (4, 16, 16, 256, fd.F16), (2, 8, 1, 64, fd.F16),
     (64, 64, 64, 128, fd.BF16)])
-def test_choose_splits_contract(lib, batch, hq, hkv, d, dt):
+@pytest.mark.parametrize("ragged", [0, 1])
+def test_choose_splits_contract(lib, batch, hq, hkv, d, dt, ragged):
     for n in (0, 1, 15, 16, 17, 255, 256, 1000, 1024, 4096, 65536, 131072, 1 << 20):
         b, length = ctypes.c_int(), ctypes.c_int()
-        rc = lib.fd_choose_splits(batch, hq, hkv, n, d, dt, 256, ctypes.byref(b),
+        rc = lib.fd_choose_splits(batch, hq, hkv, n, d, dt, ragged, 256, ctypes.byref(b),
                                   ctypes.byref(length))
         assert rc == fd.OK
         B, L = b.value, length.value
@@ -58,7 +59,7 @@ def test_choose_splits_contract(lib, batch, hq, hkv, d, dt):
         assert B <= 512
         assert n == 0 or L % 16 == 0
         again = (ctypes.c_int(), ctypes.c_int())
-        lib.fd_choose_splits(batch, hq, hkv, n, d, dt, 256, ctypes.byref(again[0]),
+        lib.fd_choose_splits(batch, hq, hkv, n, d, dt, ragged, 256, ctypes.byref(again[0]),
                              ctypes.byref(again[1]))
         assert (again[0].value, again[1].value) == (B, L)
 
@@ -67,24 +68,27 @@ def test_choose_splits_fills_the_gpu(lib):
     """Short caches use few splits, long ones enough to give every CU work."""
     def splits(batch, hq, n, cus=256):
         b, length = ctypes.c_int(), ctypes.c_int()
-        assert lib.fd_choose_splits(batch, hq, hq, n, 128, fd.BF16, cus, ctypes.byref(b),
+        assert lib.fd_choose_splits(batch, hq, hq, n, 128, fd.BF16, ragged, cus, ctypes.byref(b),
                                     ctypes.byref(length)) == fd.OK
         return b.value
+    ragged = 0
     assert splits(1, 32, 65536) * 32 >= 256  # at least one work-group per CU
     assert splits(1, 32, 65536) >= splits(1, 32, 4096)
     assert splits(64, 64, 4096) == 1  # 4096 rows already fill the GPU
     assert splits(1, 32, 65536, cus=64) <= splits(1, 32, 65536, cus=256)
+    ragged = 1
+    assert splits(16, 8, 32768) >= 4  # ragged batches get several rounds of work
 
 
 def test_choose_splits_rejects(lib):
     b, length = ctypes.c_int(), ctypes.c_int()
-    assert lib.fd_choose_splits(1, 3, 2, 10, 64, 0, 256, ctypes.byref(b),
+    assert lib.fd_choose_splits(1, 3, 2, 10, 64, 0, 0, 256, ctypes.byref(b),
                                 ctypes.byref(length)) == fd.ERR_INVALID
-    assert lib.fd_choose_splits(1, 1, 1, 10, 96, 0, 256, ctypes.byref(b),
+    assert lib.fd_choose_splits(1, 1, 1, 10, 96, 0, 0, 256, ctypes.byref(b),
                                 ctypes.byref(length)) == fd.ERR_UNSUPPORTED
-    assert lib.fd_choose_splits(1, 1, 1, 10, 64, 7, 256, ctypes.byref(b),
+    assert lib.fd_choose_splits(1, 1, 1, 10, 64, 7, 0, 256, ctypes.byref(b),
                                 ctypes.byref(length)) == fd.ERR_UNSUPPORTED
-    assert lib.fd_choose_splits(1, 1, 1, 10, 64, 0, 256, None, None) == fd.ERR_INVALID
+    assert lib.fd_choose_splits(1, 1, 1, 10, 64, 0, 0, 256, None, None) == fd.ERR_INVALID
 
 
 def test_workspace_bytes(lib):
@@ -115,7 +119,7 @@ def test_decode_split_validation(lib):
     assert _split(lib, B=3) == fd.ERR_INVALID            # 3 * 16 < 64
     assert _split(lib, L=0) == fd.ERR_INVALID
     assert _split(lib, B=0) == fd.ERR_INVALID
-    assert _split(lib, B=20000, L=1) == fd.ERR_INVALID
+    assert _split(lib, B=9000, L=1) == fd.ERR_INVALID
     assert _split(lib, scale=float("nan")) == fd.ERR_INVALID
     assert _split(lib, d=80) == fd.ERR_UNSUPPORTED
     assert _split(lib, dt=5) == fd.ERR_UNSUPPORTED
