@@ -68,6 +68,11 @@ def build(extra_flags: list[str] | None = None, verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    # every kernel stub and symbol must resolve (a host pass that silently
+    # drops a kernel stub shows up here, not at the first GPU call)
+    import ctypes
+
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -32,14 +32,21 @@
 //     LDS, is read back with ds_read_b64_tr_b16, which hands each lane four
 //     tokens of one d column: the B-operand fragment.
 //
+// Data movement: each step's K and V tiles are loaded with the same
+// pattern as the vector kernel (16-byte non-temporal loads, 16 lanes per
+// 256-byte head row, so one instruction reads whole rows), into one of two
+// register sets: while one step is staged and computed, the next step's loads
+// are in flight in the other set.  The staging writes each row to LDS with its
+// 16-byte chunks XOR-swizzled by the row index, which keeps the 128-bit
+// fragment reads of K and the transpose reads of V free of bank conflicts.
+// (Direct-to-LDS loads were measured slower here: their LDS destination is
+// opaque to the compiler's wait counting, which then allows only one batch in
+// flight per wave.)  At most two work-groups are resident per CU (LDS
+// reservation), which keeps the HBM request stream near its efficient depth.
+//
 // The split writes o = O / l and S = m + log l per query head ([P3]
 // §2.3.2-§2.3.3).  Scores are in the log2 domain (scale * log2(e) applied to
-// the fp32 MFMA result).  K/V loads are ordinary (cached) loads: a 16-token
-// A-operand tile reads each 256-byte head row as four 64-byte pieces, which
-// the L2 merges into whole lines.  The next tile's loads are issued before
-// the current tile's arithmetic; at
-// most two work-groups are resident per CU (LDS reservation), which keeps
-// the HBM request stream near its efficient depth.
+// the fp32 MFMA result).
 #include "dev_common.h"
 
 namespace fd {
@@ -95,9 +102,6 @@ struct Mma<kF16> {
     }
 };
 
-#ifndef FD_MFMA_NT
-#define FD_MFMA_NT 0
-#endif
 #ifndef FD_MFMA_STEP_KB
 #define FD_MFMA_STEP_KB 16
 #endif
@@ -105,24 +109,49 @@ struct Mma<kF16> {
 template <int D>
 struct Tiles {
     static constexpr int ROW = D * 2;         // bytes of one head row (16-bit types)
-    static constexpr int NC = D / 32;         // 128-bit chunks per lane per token (K or V)
+    static constexpr int CPR = ROW / 16;      // 16-byte chunks per row
+    static constexpr int RPI = 64 / CPR;      // rows per 1 KB direct-to-LDS instruction
+    static constexpr int NC = D / 32;         // K-dim chunks of the S product (32 elements)
     static constexpr int NT = D / 16;         // 16-wide d slices of O
+    static constexpr int TILE = 16 * ROW;     // bytes of one 16-token tile of K or V
+    static constexpr int IPT = TILE / 1024;   // direct-to-LDS instructions per tile
     // 16-token tiles per step: FD_MFMA_STEP_KB of K+V per wave and step
-    static constexpr int U = FD_MFMA_STEP_KB * 1024 / (16 * ROW * 2) > 0
-                                 ? FD_MFMA_STEP_KB * 1024 / (16 * ROW * 2)
-                                 : 1;
-    static constexpr int LDS_ROW = ROW + 32;  // padded LDS row: conflict-free transpose reads
+    static constexpr int U =
+        FD_MFMA_STEP_KB * 1024 / (2 * TILE) > 0 ? FD_MFMA_STEP_KB * 1024 / (2 * TILE) : 1;
+    static constexpr int BUF = 2 * U * TILE;  // LDS: U tiles of K, then U tiles of V
+    // Chunk swizzles: physical chunk p of row r holds logical chunk
+    // p ^ swz_k(r) in a K tile and p ^ swz_v(r) in a V tile.  gfx950 LDS has
+    // 64 four-byte banks.  Chosen from the LDS bank-conflict counter on
+    // micro-benchmarks of exactly these two access patterns (16 x 256-byte
+    // tiles): the K fragment reads (128-bit, one logical chunk in each of 16
+    // rows) run conflict-free with swz_k(r) = r, while the V transpose reads
+    // (served 32 lanes per pass: two adjacent chunks, one 16-wide d slice, in
+    // each of 8 rows) need swz_v >> 1 distinct on 8 consecutive rows, which
+    // 2*(r mod 8) + r/8 gives.  128-byte rows (d = 64) alternate between the
+    // two bank halves, so there the V condition applies to rows of one
+    // parity: 2*((r/2) mod 4) + r/8.
+    static __device__ __forceinline__ int swz_k(int r) { return r & ((CPR < 16 ? CPR : 16) - 1); }
+    static __device__ __forceinline__ int swz_v(int r) {
+        if (CPR >= 16)
+            return ((r & 7) << 1) | (r >> 3);
+        return (((r >> 1) & 3) << 1) | (r >> 3);
+    }
 };
+
+typedef __attribute__((address_space(3))) char lds_char;
 
 template <int DT, int D>
 __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
+    // The body uses LDS address-space pointers and gfx950-only builtins that
+    // the host pass cannot type; it only needs the kernel's declaration.
+#if defined(__HIP_DEVICE_COMPILE__)
     using T = Tiles<D>;
     constexpr int NC = T::NC, NT = T::NT, U = T::U;
     using M = Mma<DT>;
-    __shared__ __attribute__((aligned(16))) char vlds[U][16 * T::LDS_ROW];
+    __shared__ __attribute__((aligned(1024))) char tile_buf[T::BUF];
 
     const int lane = threadIdx.x;
-    const int col = lane & 15;  // tile token (loads) / head (S) / d column (O)
+    const int col = lane & 15;  // tile token (K reads) / head (S) / d column (O)
     const int grp = lane >> 4;  // 0..3
     const int G = a.heads_q / a.heads_kv;
 
@@ -164,42 +193,84 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
             (((size_t)b * a.max_kv_len + (size_t)t0) * a.heads_kv + kvh) * T::ROW;
         const char *kbase = static_cast<const char *>(a.k) + split_base;
         const char *vbase = static_cast<const char *>(a.v) + split_base;
-        const uint32_t stride32 = (uint32_t)tok_stride;
-        const uint32_t lane_byte = (uint32_t)grp * 16u;
         const int ntok = (int)(t1 - t0);
         constexpr int kStepTok = 16 * U;
         const int nsteps = (ntok + kStepTok - 1) / kStepTok;
 
-        // Step st: tiles u of 16 tokens t0 + st*16U + 16u + [0, 16); lane loads
-        // token `col` of each tile, d = 32c + 8*grp + [0, 8).  Tokens past the
-        // end re-read the last valid token (in bounds) and are masked later.
-        auto load_step = [&](int st, u32x4 (*kd)[NC], u32x4 (*vd)[NC]) {
+        // Direct-to-LDS loads of step st into buffer `buf` (a step past the
+        // last one re-reads the last step, so prefetches need no condition).
+        // One step's loads: for tile u and row group j, lane L reads the
+        // 16-byte chunk q = L % CPR of row r = j*RPI + L/CPR (token
+        // first + 16u + r, clamped to the last valid token; a step past the
+        // last one re-reads the last step, so prefetches need no condition).
+        struct Stage {
+            u32x4 k[U][T::IPT];
+            u32x4 v[U][T::IPT];
+        };
+        const int lrow = lane / T::CPR;  // row within a row group
+        const int lq = lane % T::CPR;    // logical chunk this lane carries
+        auto load_step = [&](int st, Stage &g) {
             const int sa = st < nsteps ? st : nsteps - 1;
             const int first = sa * kStepTok;
             const int last_rel = ntok - 1 - first;
-            const char *kb = kbase + (size_t)first * tok_stride;
-            const char *vb = vbase + (size_t)first * tok_stride;
+            const char *kb = kbase + (size_t)first * tok_stride + lq * 16;
+            const char *vb = vbase + (size_t)first * tok_stride + lq * 16;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < T::IPT; ++j) {
+                    int rel = 16 * u + j * T::RPI + lrow;
+                    rel = rel < last_rel ? rel : last_rel;
+                    const size_t off = (size_t)rel * tok_stride;
+                    g.k[u][j] = ld128<1>(kb + off);
+                    g.v[u][j] = ld128<1>(vb + off);
+                }
+        };
+        // Write a step's rows into the LDS tiles, chunks swizzled per row.
+        lds_char *const tb = (lds_char *)tile_buf;
+        auto stage = [&](const Stage &g) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < T::IPT; ++j) {
+                    const int r = j * T::RPI + lrow;
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
+                        tb + u * T::TILE + r * T::ROW + (lq ^ T::swz_k(r)) * 16) = g.k[u][j];
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
+                        tb + (U + u) * T::TILE + r * T::ROW + (lq ^ T::swz_v(r)) * 16) = g.v[u][j];
+                }
+        };
+
+        // All LDS fragments of one step: K for the S product, V (read
+        // transposed) for the PV product.
+        struct Frags {
+            u32x4 k[U][NC];
+            s16x4_t v[U][NT];
+        };
+        const int vr = 4 * grp + (col >> 2);  // V row this lane addresses for the transpose read
+        const int vq = (col & 3) >> 1;        // chunk within the 32-byte slice of a d tile
+        const int vh = (col & 1) * 8;         // half of that chunk
+        auto fetch = [&](const lds_char *buf, Frags &f) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                int rel = 16 * u + col;
-                rel = rel < last_rel ? rel : last_rel;
-                const uint32_t off = (uint32_t)rel * stride32 + lane_byte;
+                const lds_char *krow = buf + u * T::TILE + col * T::ROW;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    kd[u][c] = ld128<FD_MFMA_NT>(kb + off + c * 64);
-                    vd[u][c] = ld128<FD_MFMA_NT>(vb + off + c * 64);
+                    const int p = (4 * c + grp) ^ T::swz_k(col);
+                    f.k[u][c] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                        krow + p * 16);
+                }
+                const lds_char *vrow = buf + (U + u) * T::TILE + vr * T::ROW + vh;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int pc = (2 * t + vq) ^ T::swz_v(vr);
+                    f.v[u][t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4_t *)(vrow + pc * 16));
                 }
             }
         };
 
-        auto compute_step = [&](int st, const u32x4 (*kc)[NC], const u32x4 (*vc)[NC]) {
-            // V rows to LDS, row-major (token x d) with padded rows.
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    *reinterpret_cast<u32x4 *>(vlds[u] + col * T::LDS_ROW + c * 64 + grp * 16) =
-                        vc[u][c];
+        auto compute_step = [&](int st, const Frags &f) {
             // S^T tiles on the matrix cores, scaled into the log2 domain.
             float x[U][4];
             float mx = -INFINITY;  // max of this lane's tokens
@@ -208,7 +279,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
                 f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
-                    s = M::s_tile(kc[u][c], qf[c], s);
+                    s = M::s_tile(f.k[u][c], qf[c], s);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int rel = st * kStepTok + 16 * u + 4 * grp + r;
@@ -238,7 +309,6 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
                 }
             }
             const float mref = m_used == -INFINITY ? 0.f : m_used;
-            __syncthreads();  // V tile visible to every lane
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float p[4];
@@ -246,31 +316,40 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
                 for (int r = 0; r < 4; ++r)
                     p[r] = fast_exp2(x[u][r] - mref);
                 const u32x2 pa = M::pack(p, &lsum);
-                const char *vrow = vlds[u] + (4 * grp + (col >> 2)) * T::LDS_ROW + (col & 3) * 8;
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4_t *)(vrow + t * 32));
-                    oacc[t] = M::pv_tile(pa, vb, oacc[t]);
-                }
+                for (int t = 0; t < NT; ++t)
+                    oacc[t] = M::pv_tile(pa, f.v[u][t], oacc[t]);
             }
-            __syncthreads();  // reads done before the next step overwrites the tile
         };
 
-        u32x4 kw[U][NC], vw[U][NC], kx[U][NC], vx[U][NC];
+        // Pipeline over two register sets (as in the vector kernel): the next
+        // step's loads are issued before the current step is staged, read
+        // back as fragments and computed, so the compiler waits only for the
+        // older set.  The LDS tile is rewritten each step; one wave's LDS
+        // operations execute in order, so a step's writes follow the previous
+        // step's reads.
+        Frags f;
+        Stage ga, gb;
         const int npairs = nsteps >> 1;
-        load_step(0, kw, vw);
+        load_step(0, ga);
         for (int pr = 0; pr < npairs; ++pr) {
             const int st = 2 * pr;
-            load_step(st + 1, kx, vx);
+            load_step(st + 1, gb);
             __builtin_amdgcn_sched_barrier(0);
-            compute_step(st, kw, vw);
-            load_step(st + 2, kw, vw);
+            stage(ga);
+            fetch(tb, f);
+            compute_step(st, f);
+            load_step(st + 2, ga);
             __builtin_amdgcn_sched_barrier(0);
-            compute_step(st + 1, kx, vx);
+            stage(gb);
+            fetch(tb, f);
+            compute_step(st + 1, f);
         }
-        if (nsteps & 1)
-            compute_step(nsteps - 1, kw, vw);
+        if (nsteps & 1) {
+            stage(ga);
+            fetch(tb, f);
+            compute_step(nsteps - 1, f);
+        }
     }
 
     // l of head `col`: the four lanes holding it each summed their tokens.
@@ -303,6 +382,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
                 a.lse[rowid] = lse;
         }
     }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 int lds_per_cu_mfma() {
@@ -327,7 +407,7 @@ int lds_per_cu_mfma() {
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
-    constexpr size_t kStatic = (size_t)T::U * 16 * T::LDS_ROW;
+    constexpr size_t kStatic = (size_t)T::BUF;
     const long grid = (long)a.batch * a.heads_kv * a.num_splits;
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
