@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -32,24 +31,14 @@ if ROOT not in sys.path:
 
 import torch  # noqa: E402
 
-from decode_attention_03_amd import fd, workloads  # noqa: E402
+from decode_attention_03_amd import build, fd, workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective KV GB/s (% of 8 TB/s HBM peak) and µs per decode step"
-KERNEL_SOURCES = ["split_valu.hip", "split_mfma.hip", "combine.hip", "dev_common.h",
-                  "fd_internal.h"]
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_03_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 class Prepared:
@@ -157,18 +146,19 @@ def time_steps(p: Prepared, steps: int, warmup: int) -> dict:
 
 
 def time_split_kernel(p: Prepared, steps: int, warmup: int) -> float:
-    """Average duration (µs) of the split kernel alone, HIP events on its stream."""
+    """Average duration (µs) of the split kernel alone: HIP events on its stream
+    around `steps` back-to-back launches, divided by `steps`."""
     for i in range(warmup):
         p.split(i)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    start.record(p.stream)
     for i in range(steps):
-        ev[i][0].record(p.stream)
         p.split(i)
-        ev[i][1].record(p.stream)
+    end.record(p.stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+    return start.elapsed_time(end) / steps * 1e3
 
 
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
@@ -196,7 +186,7 @@ def cpu_baseline(p: Prepared, budget_s: float) -> dict:
                       f"(sequence, head)), {wall:.1f} s wall"}
 
 
-def traffic_from_profile(name: str, launches_bytes: int) -> dict | None:
+def traffic_from_profile(name: str) -> dict | None:
     """HBM bytes per split-kernel launch from a committed rocprofv3 counter
     summary, when it was taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
@@ -204,7 +194,7 @@ def traffic_from_profile(name: str, launches_bytes: int) -> dict | None:
         return None
     with open(path, encoding="utf-8") as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != build.source_hash(rec.get("kernel", "")):
         return None
     return rec
 
@@ -221,6 +211,10 @@ def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
         out["note"] = "cache-resident (0.5 MiB); µs only"
     if split_us is not None:
         out["split_kernel_us"] = round(split_us, 2)
+    prof = traffic_from_profile(p.w.name)
+    if prof is not None:
+        out["split_traffic_bytes_per_launch"] = prof["hbm_bytes_per_launch"]
+        out["split_algorithmic_bytes_per_launch"] = p.split_bytes
     return out
 
 
@@ -248,13 +242,15 @@ def main() -> int:
     dev = torch.device("cuda:0")
 
     if args.copy_probe:
+        # a streaming elementwise kernel (out = -in) that reads and writes
+        # exactly copy_probe bytes per dispatch: the scale for HBM counters
         n = args.copy_probe // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"[bench] copy probe: 5 copies of {args.copy_probe} bytes")
+        log(f"[bench] copy probe: 5 dispatches reading and writing {args.copy_probe} bytes each")
         return 0
 
     head = workloads.WORKLOADS[args.config]
@@ -269,7 +265,7 @@ def main() -> int:
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": "split", "kernel_us": round(split_us, 2),
                 "algorithmic_bytes_per_launch": p.split_bytes}
-    prof = traffic_from_profile(head.name, p.split_bytes)
+    prof = traffic_from_profile(head.name)
     if prof is not None:
         roofline["traffic"] = prof.get("hbm_bytes_per_launch")
     cpu = cpu_baseline(p, args.cpu_budget) if args.cpu_budget > 0 else None

@@ -8,6 +8,7 @@ the objects link into decode_attention_03_amd/libfd.so.  Every call rebuilds.
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import shutil
 import subprocess
@@ -20,6 +21,23 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfd.so")
 SOURCES = ["fd_api.cpp", "split_valu.hip", "split_mfma.hip", "combine.hip"]
 ARCH = "gfx950"
+
+#: the source files each kernel family is compiled from; a measurement taken
+#: on a kernel stays valid while these files are unchanged
+KERNEL_SOURCES = {
+    "split_valu": ["split_valu.hip", "dev_common.h", "fd_internal.h"],
+    "split_mfma": ["split_mfma.hip", "dev_common.h", "fd_internal.h"],
+    "combine": ["combine.hip", "dev_common.h", "fd_internal.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    """Short SHA-256 over the sources of one kernel family."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
