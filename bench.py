@@ -67,15 +67,22 @@ class Prepared:
         self.n_max = inp["max_kv_len"]
         if num_splits == 0 and w.num_splits:
             num_splits = w.num_splits
+        # the library's automatic plan unless the workload or the caller fixes B
+        self.auto = num_splits == 0
+        self.balanced = fd.uses_balanced_plan(hq, hkv, self.n_max, d, inp["q"].dtype,
+                                              lens is not None, num_splits)
         if num_splits == 0:
             self.B, self.L = fd.choose_splits(batch, hq, hkv, self.n_max, d, inp["q"].dtype,
                                               ragged=lens is not None)
         else:
             self.B, self.L = num_splits, -(-self.n_max // num_splits)
+        self.plan = "token-balanced" if self.balanced else "fixed-splits"
         self.o = torch.empty((batch, hq, d), dtype=workloads.TORCH_DTYPES[w.out_dtype],
                              device=dev)
         self.lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
-        ws = fd.workspace_bytes(batch, hq, self.B, d)
+        dec_b, dec_l = (0, 0) if self.auto else (self.B, self.L)
+        ws = fd.decode_workspace_bytes(batch, hq, hkv, self.n_max, d, inp["q"].dtype,
+                                       lens is not None, dec_b, dec_l)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
         # partial buffers of the split kernel when it is timed on its own
@@ -95,16 +102,24 @@ class Prepared:
         for k, v in self.kv:
             self.decode_args.append((P(self.q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
                                      lens_p, batch, hq, hkv, self.n_max, d, self.in_code,
-                                     self.out_code, ctypes.c_float(w.scale), self.B, self.L,
+                                     self.out_code, ctypes.c_float(w.scale), dec_b, dec_l,
                                      P(self.o.data_ptr()), P(self.lse.data_ptr()),
                                      P(self.ws.data_ptr()), self.ws_bytes, sp))
             self.split_args.append((P(self.q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
                                     lens_p, batch, hq, hkv, self.n_max, d, self.in_code,
                                     ctypes.c_float(w.scale), self.B, self.L,
                                     P(self.o_part.data_ptr()), P(self.lse_part.data_ptr()), sp))
-        self.split_bytes = (self.kv_bytes + self.q.numel() * self.q.element_size()
-                            + (batch * hq * self.B * (d + 1) * 4 if self.B > 1 else 0))
-        log(f"[bench] {w.name}: B={self.B} L={self.L} copies={self.copies} "
+        # algorithmic bytes of the timed split launch: K/V rows, q, and the
+        # partials written (fixed splits: B per row; balanced: at most one per
+        # work-group piece, bounded by work-groups + units, counted in full)
+        if self.balanced:
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            pieces = 2 * cus + batch * hkv
+            self.part_bytes = pieces * (hq // hkv) * (d + 1) * 4
+        else:
+            self.part_bytes = batch * hq * self.B * (d + 1) * 4 if self.B > 1 else 0
+        self.split_bytes = self.kv_bytes + self.q.numel() * self.q.element_size() + self.part_bytes
+        log(f"[bench] {w.name}: plan={self.plan} B={self.B} L={self.L} copies={self.copies} "
             f"kv={self.kv_bytes / 2**20:.1f} MiB prep={time.time() - t0:.1f}s")
 
     def decode(self, i: int) -> None:
@@ -147,15 +162,18 @@ def time_steps(p: Prepared, steps: int, warmup: int) -> dict:
 
 def time_split_kernel(p: Prepared, steps: int, warmup: int) -> float:
     """Average duration (µs) of the split kernel alone: HIP events on its stream
-    around `steps` back-to-back launches, divided by `steps`."""
+    around `steps` back-to-back launches, divided by `steps`.  The balanced
+    plan's split stage has no entry point of its own; for it the whole decode
+    (split + combine) is timed, which bounds the split kernel from above."""
+    run = p.decode if p.balanced else p.split
     for i in range(warmup):
-        p.split(i)
+        run(i)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(p.stream)
     for i in range(steps):
-        p.split(i)
+        run(i)
     end.record(p.stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps * 1e3
@@ -202,7 +220,9 @@ def traffic_from_profile(name: str) -> dict | None:
 def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
     us = t["wall_us_per_step"]
     out = {"us_per_step": round(us, 2), "event_us_median": round(t["event_us_median"], 2),
-           "num_splits": p.B, "split_len": p.L, "kv_bytes": p.kv_bytes}
+           "plan": p.plan, "kv_bytes": p.kv_bytes}
+    if not p.balanced:
+        out["num_splits"], out["split_len"] = p.B, p.L
     if p.copies > 1:
         gbs = p.kv_bytes / (us * 1e-6) / 1e9
         out["kv_GBps"] = round(gbs, 1)
@@ -210,7 +230,7 @@ def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
     else:
         out["note"] = "cache-resident (0.5 MiB); µs only"
     if split_us is not None:
-        out["split_kernel_us"] = round(split_us, 2)
+        out["split_kernel_us" if not p.balanced else "split_and_combine_us"] = round(split_us, 2)
     prof = traffic_from_profile(p.w.name)
     if prof is not None:
         out["split_traffic_bytes_per_launch"] = prof["hbm_bytes_per_launch"]
@@ -263,7 +283,8 @@ def main() -> int:
     achieved = p.split_bytes / (split_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "split", "kernel_us": round(split_us, 2),
+                "kernel": "split" if not p.balanced else "split+combine (token-balanced)",
+                "kernel_us": round(split_us, 2),
                 "algorithmic_bytes_per_launch": p.split_bytes}
     prof = traffic_from_profile(head.name)
     if prof is not None:
@@ -287,7 +308,8 @@ def main() -> int:
         "config": {"workload": head.name, "batch": head.batch, "heads_q": head.heads_q,
                    "heads_kv": head.heads_kv, "head_dim": head.head_dim,
                    "max_kv_len": p.n_max, "in_dtype": head.dtype, "out_dtype": head.out_dtype,
-                   "num_splits": p.B, "split_len": p.L, "kv_bytes_per_step": p.kv_bytes,
+                   "plan": p.plan, "num_splits": None if p.balanced else p.B,
+                   "split_len": None if p.balanced else p.L, "kv_bytes_per_step": p.kv_bytes,
                    "input_copies": p.copies, "parallelism": "single-gpu"},
         "timing": {k: round(v, 2) for k, v in t.items()},
         "roofline": roofline,

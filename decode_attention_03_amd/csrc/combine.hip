@@ -14,7 +14,13 @@
 // sums of each element are added in LDS in a fixed order, so the result is
 // reproducible.  -inf partials (empty splits) get weight 0 and contribute
 // exactly nothing; a row whose partials are all -inf yields o = 0, S = -inf.
+//
+// Two sources of partials: fixed splits ([batch, heads_q, B, d], B per row),
+// or the slots of the token-balanced partition (partition.h), where a row's
+// unit descriptor names its first slot and slot count and the row's partials
+// sit gsz rows apart.
 #include "dev_common.h"
+#include "partition.h"
 
 namespace fd {
 namespace {
@@ -35,25 +41,31 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// A row's partials: LSE i at S[i * s_stride], o_i at O + i * o_stride.
+struct RowSource {
+    const float *S;
+    const float *O;
+    int count, s_stride, o_stride;
+};
+
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const float *__restrict__ o_part, const float *__restrict__ lse_part, int num_splits, void *o,
-    int out_dtype, float *lse) {
+__device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, void *o,
+                                            int out_dtype, float *lse, float *weights) {
     constexpr int V4 = D / 4;                     // float4 slices per row
     constexpr int SP = kCombineThreads / V4;      // splits processed side by side
     constexpr int NW = kCombineThreads / 64;
-    extern __shared__ float weights[];            // num_splits entries
     __shared__ float red[NW];
     __shared__ float part[SP][D];
-    const int rowid = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const float *S = lse_part + (size_t)rowid * num_splits;
+    const float *S = src.S;
+    const int num_splits = src.count;
+    const int ss = src.s_stride;
 
     // S_max over the row
     float mx = -INFINITY;
     for (int i = tid; i < num_splits; i += kCombineThreads)
-        mx = fmaxf(mx, S[i]);
+        mx = fmaxf(mx, S[(size_t)i * ss]);
     mx = wave_max(mx);
     if (lane == 0)
         red[wave] = mx;
@@ -67,7 +79,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     float sum = 0.f;
     if (mx != -INFINITY)
         for (int i = tid; i < num_splits; i += kCombineThreads)
-            sum += fast_exp2((S[i] - mx) * kLog2e);
+            sum += fast_exp2((S[(size_t)i * ss] - mx) * kLog2e);
     sum = wave_sum(sum);
     if (lane == 0)
         red[wave] = sum;
@@ -78,13 +90,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
         sum += red[w];
     const float sg = mx == -INFINITY ? -INFINITY : mx + fast_log2(sum) * kLn2;
     for (int i = tid; i < num_splits; i += kCombineThreads)
-        weights[i] = mx == -INFINITY ? 0.f : fast_exp2((S[i] - sg) * kLog2e);
+        weights[i] = mx == -INFINITY ? 0.f : fast_exp2((S[(size_t)i * ss] - sg) * kLog2e);
     __syncthreads();
 
     // o = sum_i w_i o_i: thread (sp, c) takes splits sp, sp + SP, ... of slice c
     const int c = tid % V4;
     const int sp = tid / V4;
-    const float4 *col = reinterpret_cast<const float4 *>(o_part + (size_t)rowid * num_splits * D) + c;
+    const float4 *col = reinterpret_cast<const float4 *>(src.O) + c;
+    const size_t os = (size_t)src.o_stride / 4;  // float4 stride between partials
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     auto add = [&](float w, float4 x) {
         // weight 0 (an empty split) contributes nothing, whatever the slot holds
@@ -95,17 +108,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     };
     int i = sp;
     for (; i + 3 * SP < num_splits; i += 4 * SP) {
-        const float4 x0 = col[(size_t)i * V4];
-        const float4 x1 = col[(size_t)(i + SP) * V4];
-        const float4 x2 = col[(size_t)(i + 2 * SP) * V4];
-        const float4 x3 = col[(size_t)(i + 3 * SP) * V4];
+        const float4 x0 = col[(size_t)i * os];
+        const float4 x1 = col[(size_t)(i + SP) * os];
+        const float4 x2 = col[(size_t)(i + 2 * SP) * os];
+        const float4 x3 = col[(size_t)(i + 3 * SP) * os];
         add(weights[i], x0);
         add(weights[i + SP], x1);
         add(weights[i + 2 * SP], x2);
         add(weights[i + 3 * SP], x3);
     }
     for (; i < num_splits; i += SP)
-        add(weights[i], col[(size_t)i * V4]);
+        add(weights[i], col[(size_t)i * os]);
     part[sp][4 * c + 0] = acc.x;
     part[sp][4 * c + 1] = acc.y;
     part[sp][4 * c + 2] = acc.z;
@@ -116,10 +129,43 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 #pragma unroll
         for (int r = 0; r < SP; ++r)
             out += part[r][tid];
-        store_out(o, (size_t)rowid * D + tid, out, out_dtype);
+        store_out(o, rowid * D + tid, out, out_dtype);
         if (tid == 0 && lse)
             lse[rowid] = sg;
     }
+}
+
+// Fixed splits: row r's partials are contiguous, B of them.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float *__restrict__ o_part, const float *__restrict__ lse_part, int num_splits, void *o,
+    int out_dtype, float *lse) {
+    extern __shared__ float weights[];  // num_splits entries
+    const size_t rowid = blockIdx.x;
+    const RowSource src{lse_part + rowid * num_splits, o_part + rowid * num_splits * D, num_splits,
+                        1, D};
+    combine_row<D>(src, rowid, o, out_dtype, lse, weights);
+}
+
+// Token-balanced slots: row (b, h) of unit u = b * (heads_q / gsz) + h / gsz
+// reads slots first .. first + count - 1 of its unit's descriptor; a sequence
+// with no tokens has no descriptor and yields (0, -inf).
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_slots_kernel(SlotCombineArgs a) {
+    extern __shared__ float weights[];  // max_count entries
+    const size_t rowid = blockIdx.x;
+    const int b = (int)(rowid / a.heads_q);
+    const int h = (int)(rowid % a.heads_q);
+    const int g = h % a.gsz;
+    const size_t u = (size_t)b * (a.heads_q / a.gsz) + h / a.gsz;
+    RowSource src{a.lse_slots, a.o_slots, 0, a.gsz, a.gsz * D};
+    if (clamp_len(a.kv_lens, b, a.max_kv_len) > 0) {
+        const int first = a.unit_desc[2 * u];
+        src.count = a.unit_desc[2 * u + 1];
+        src.S = a.lse_slots + (size_t)first * a.gsz + g;
+        src.O = a.o_slots + ((size_t)first * a.gsz + g) * D;
+    }
+    combine_row<D>(src, rowid, a.o, a.out_dtype, a.lse, weights);
 }
 
 }  // namespace
@@ -139,6 +185,25 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int rows, 
     case 256:
         hipLaunchKernelGGL(combine_kernel<256>, dim3(rows), dim3(kCombineThreads), shmem, stream,
                            o_part, lse_part, num_splits, o, out_dtype, lse);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_slots(const SlotCombineArgs &c, hipStream_t stream) {
+    const size_t shmem = sizeof(float) * (size_t)c.max_count;
+    const dim3 grid((unsigned)((size_t)c.batch * c.heads_q));
+    switch (c.head_dim) {
+    case 64:
+        hipLaunchKernelGGL(combine_slots_kernel<64>, grid, dim3(kCombineThreads), shmem, stream, c);
+        break;
+    case 128:
+        hipLaunchKernelGGL(combine_slots_kernel<128>, grid, dim3(kCombineThreads), shmem, stream, c);
+        break;
+    case 256:
+        hipLaunchKernelGGL(combine_slots_kernel<256>, grid, dim3(kCombineThreads), shmem, stream, c);
         break;
     default:
         return hipErrorInvalidValue;

@@ -29,6 +29,7 @@ constexpr int kRaggedRounds = 4;       // work-group rounds aimed at for ragged 
 constexpr int kMinSplitLenMha = 256;   // tokens; partial traffic ~0.8% of K/V at d = 128
 constexpr int kMinSplitLenPerHead = 64;  // grouped: tokens per query head of the group
 constexpr int kMaxAutoSplits = 512;
+constexpr int kBalancedRounds = 1;     // token-balanced work-groups: CUs * per-CU * rounds
 
 thread_local std::string g_error;
 
@@ -124,6 +125,40 @@ int launch_split(const fd::SplitArgs &a, int in_dtype, hipStream_t stream) {
     return FD_OK;
 }
 
+// Token-balanced partition of a ragged batch (partition.h): used by
+// fd_decode's automatic plan when kv_lens is given and the grouped kernel
+// applies.  Workspace: o slots, LSE slots, unit descriptors, each 256-aligned.
+struct BalancedPlan {
+    int num_wgs = 0, units = 0, gsz = 0;
+    size_t o_bytes = 0, lse_bytes = 0, desc_bytes = 0;
+    size_t total() const { return o_bytes + lse_bytes + desc_bytes; }
+};
+
+bool balanced_applies(int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
+                      bool has_lens, int num_splits) {
+    return num_splits == 0 && has_lens && max_kv_len > 0 &&
+           fd::split_mfma_supported(in_dtype, head_dim, heads_q / heads_kv);
+}
+
+int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                  BalancedPlan *p) {
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != FD_OK)
+        return rc;
+    p->num_wgs = cus * kWorkGroupsPerCU * kBalancedRounds;
+    p->units = batch * heads_kv;
+    p->gsz = heads_q / heads_kv;
+    // positions (units * max_kv_len) times work-groups must stay within int64
+    if ((double)p->units * max_kv_len * p->num_wgs > 4.0e18)
+        return fail(FD_ERR_INVALID, "batch * heads_kv * max_kv_len too large for the balanced plan");
+    const size_t slots = (size_t)p->num_wgs + p->units;
+    p->o_bytes = round256(slots * p->gsz * head_dim * sizeof(float));
+    p->lse_bytes = round256(slots * p->gsz * sizeof(float));
+    p->desc_bytes = round256((size_t)p->units * 2 * sizeof(int));
+    return FD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,6 +228,40 @@ size_t fd_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim) 
         return 0;
     const size_t rows = (size_t)batch * heads_q * num_splits;
     return round256(rows * head_dim * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_len,
+                              int head_dim, int in_dtype, int has_kv_lens, int num_splits,
+                              int split_len, size_t *bytes) {
+    if (!bytes)
+        return fail(FD_ERR_INVALID, "null output pointer");
+    *bytes = 0;
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0 || heads_q % heads_kv)
+        return fail(FD_ERR_INVALID, "bad sizes (batch=%d heads_q=%d heads_kv=%d max_kv_len=%d)",
+                    batch, heads_q, heads_kv, max_kv_len);
+    if (!head_dim_ok(head_dim) || !dtype_ok(in_dtype))
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
+                    in_dtype);
+    if (num_splits < 0 || split_len < 0)
+        return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
+                    num_splits, split_len);
+    if (balanced_applies(heads_q, heads_kv, max_kv_len, head_dim, in_dtype, has_kv_lens != 0,
+                         num_splits)) {
+        BalancedPlan p;
+        int rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, &p);
+        if (rc != FD_OK)
+            return rc;
+        *bytes = p.total();
+        return FD_OK;
+    }
+    if (num_splits == 0) {
+        int rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                                  has_kv_lens != 0, 0, &num_splits, &split_len);
+        if (rc != FD_OK)
+            return rc;
+    }
+    *bytes = fd_workspace_bytes(batch, heads_q, num_splits, head_dim);
+    return FD_OK;
 }
 
 int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
@@ -270,6 +339,60 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
     if (num_splits < 0 || split_len < 0)
         return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
                     num_splits, split_len);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (balanced_applies(heads_q, heads_kv, max_kv_len, head_dim, in_dtype, kv_lens != nullptr,
+                         num_splits)) {
+        BalancedPlan p;
+        rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, &p);
+        if (rc != FD_OK)
+            return rc;
+        if (!workspace || workspace_bytes < p.total())
+            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total(),
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace))
+            return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+        char *ws = static_cast<char *>(workspace);
+        fd::SplitArgs a{};
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.kv_lens = kv_lens;
+        a.batch = batch;
+        a.heads_q = heads_q;
+        a.heads_kv = heads_kv;
+        a.max_kv_len = max_kv_len;
+        a.head_dim = head_dim;
+        a.num_splits = 0;
+        a.split_len = 0;
+        a.scale_log2 = scale * 1.4426950408889634f;
+        a.o_part = reinterpret_cast<float *>(ws);
+        a.lse_part = reinterpret_cast<float *>(ws + p.o_bytes);
+        a.out_dtype = out_dtype;
+        a.balanced = 1;
+        a.num_wgs = p.num_wgs;
+        a.unit_desc = reinterpret_cast<int *>(ws + p.o_bytes + p.lse_bytes);
+        rc = launch_split(a, in_dtype, st);
+        if (rc != FD_OK)
+            return rc;
+        fd::SlotCombineArgs c{};
+        c.o_slots = a.o_part;
+        c.lse_slots = a.lse_part;
+        c.unit_desc = a.unit_desc;
+        c.kv_lens = kv_lens;
+        c.batch = batch;
+        c.heads_q = heads_q;
+        c.gsz = p.gsz;
+        c.max_kv_len = max_kv_len;
+        c.head_dim = head_dim;
+        c.max_count = p.num_wgs;
+        c.o = o;
+        c.out_dtype = out_dtype;
+        c.lse = lse;
+        hipError_t e = fd::launch_combine_slots(c, st);
+        if (e != hipSuccess)
+            return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+        return FD_OK;
+    }
     if (num_splits == 0) {
         rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
                               kv_lens != nullptr, 0, &num_splits, &split_len);
@@ -296,7 +419,6 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
     a.split_len = split_len;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_dtype = out_dtype;
-    hipStream_t st = static_cast<hipStream_t>(stream);
 
     if (num_splits == 1) {  // one split per row: the split stage writes o and lse itself
         a.o = o;

@@ -21,11 +21,17 @@ struct SplitArgs {
     int batch, heads_q, heads_kv, max_kv_len, head_dim;
     int num_splits, split_len;
     float scale_log2;        // scale * log2(e): scores are kept in the log2 domain
-    float *o_part;           // [batch, heads_q, num_splits, d]   (num_splits > 1)
-    float *lse_part;         // [batch, heads_q, num_splits]      (num_splits > 1)
+    float *o_part;           // fixed splits: [batch, heads_q, num_splits, d] (num_splits > 1)
+                             // balanced: slot array [slots][gsz][d]
+    float *lse_part;         // fixed: [batch, heads_q, num_splits]; balanced: [slots][gsz]
     void *o;                 // final output                       (num_splits == 1)
     float *lse;              // final LSE, may be null             (num_splits == 1)
     int out_dtype;
+    // Token-balanced partition (partition.h), used when `balanced` is set:
+    // num_wgs work-groups, per-unit descriptors {first slot, count} in unit_desc.
+    int balanced;
+    int num_wgs;
+    int *unit_desc;
 };
 
 // VALU split kernel: one work-group per (sequence, query head, split).
@@ -43,5 +49,20 @@ hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t strea
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.
 hipError_t launch_combine(const float *o_part, const float *lse_part, int rows, int num_splits,
                           int head_dim, void *o, int out_dtype, float *lse, hipStream_t stream);
+
+// LSE merge of the slots a token-balanced split stage wrote: row (b, h) reads
+// the descriptor of unit b * (heads_q / gsz) + h / gsz (gsz query heads per
+// unit); max_count bounds any unit's slot count.
+struct SlotCombineArgs {
+    const float *o_slots;     // [slots][gsz][d]
+    const float *lse_slots;   // [slots][gsz]
+    const int *unit_desc;     // [units][2]
+    const int32_t *kv_lens;   // device [batch] or nullptr
+    int batch, heads_q, gsz, max_kv_len, head_dim, max_count;
+    void *o;
+    int out_dtype;
+    float *lse;
+};
+hipError_t launch_combine_slots(const SlotCombineArgs &c, hipStream_t stream);
 
 }  // namespace fd

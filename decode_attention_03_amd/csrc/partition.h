@@ -1,0 +1,116 @@
+// partition.h -- the token-balanced partition of a ragged batch, shared by
+// the split kernels (which walk it) and the combine kernel (which reads the
+// per-unit descriptors it leaves behind).
+//
+// The pages cut each sequence's KV range into splits of one fixed length
+// ("FlashDecoding 数学推导" (my-webpage-adu.pages.dev, 2026-07-15), §2.5
+// stage 1; "adv04: Flash-Decoding" (mini-vllm-tutorial), §4).  With ragged
+// lengths, fixed splits leave the GPU's work-groups unevenly loaded, so for
+// ragged batches the library also offers a partition that gives every
+// work-group the same number of token rows.  It is still a split-K partition
+// in the pages' sense: every (sequence, head) row's tokens are cut into
+// contiguous pieces, each piece yields an (o, LSE) pair, and the combine merges
+// a row's pieces ("FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法", §2.3.4;
+// the merge does not depend on where the cuts fall, §2.3.5).
+//
+// Definitions (all positions 64-bit):
+//   unit u = b * hx + x: one (sequence b, head x) pair reading one KV head
+//            (hx = heads_kv for the grouped kernel, heads_q for the vector one);
+//   N_b    = kv_lens[b] clamped to [0, max_kv_len];
+//   the flattened space lists units in order, unit u covering positions
+//            [S_u, S_u + N_b) with S_u = hx * (N_0 + ... + N_{b-1}) + x * N_b;
+//   T      = hx * sum_b N_b, W_eff = min(num_wgs, T);
+//   work-group w < W_eff covers [floor(w T / W_eff), floor((w+1) T / W_eff)),
+//            never empty; work-groups w >= W_eff do nothing;
+//   the piece of unit u handled by work-group w writes slot w + rank(u),
+//            rank(u) = number of non-empty units before u; a unit's pieces
+//            therefore fill consecutive slots, and slots < num_wgs + units;
+//   the work-group that handles a unit's first token writes the unit's
+//            descriptor {first slot, slot count}; units of empty sequences
+//            get none (the combine checks N_b itself).
+#pragma once
+
+#include "dev_common.h"
+
+namespace fd {
+
+__device__ __forceinline__ int clamp_len(const int32_t *kv_lens, int b, int max_kv_len) {
+    int n = kv_lens ? kv_lens[b] : max_kv_len;
+    return n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ long long wave_scan_ll(long long v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const long long y = __shfl_up(v, d, 64);
+        if (lane >= d)
+            v += y;
+    }
+    return v;
+}
+
+// Where one work-group's share of the flattened space starts.  Called by all
+// 64 lanes of the wave together; every result is the same on every lane.
+struct PieceCursor {
+    long long pos, end;  // [pos, end): this work-group's positions
+    long long total;     // T
+    int w_eff;           // W_eff
+    int b, x, t;         // unit (b, x) and token t within it at `pos`
+    int rank;            // rank of unit (b, x) among non-empty units
+};
+
+__device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch, int max_kv_len,
+                                               int hx, int w, int num_wgs, PieceCursor &c) {
+    const int lane = threadIdx.x & 63;
+    long long tok = 0;
+    for (int base = 0; base < batch; base += 64) {
+        const int i = base + lane;
+        tok += i < batch ? clamp_len(kv_lens, i, max_kv_len) : 0;
+    }
+    c.total = wave_sum_ll(tok) * hx;
+    c.w_eff = c.total < num_wgs ? (int)c.total : num_wgs;
+    if (w >= c.w_eff)
+        return false;
+    c.pos = c.total * w / c.w_eff;
+    c.end = c.total * (w + 1) / c.w_eff;
+    // the sequence whose units contain `pos`
+    long long before = 0;  // positions of the sequences before this chunk
+    int nonempty = 0;      // non-empty sequences before this chunk
+    for (int base = 0; base < batch; base += 64) {
+        const int i = base + lane;
+        const long long n = i < batch ? clamp_len(kv_lens, i, max_kv_len) : 0;
+        const long long incl = wave_scan_ll(n, lane);
+        const unsigned long long hit = __ballot(i < batch && before + hx * incl > c.pos);
+        const unsigned long long ne = __ballot(n > 0);
+        if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            const long long nb = __shfl(n, l, 64);
+            const long long start = before + hx * (__shfl(incl, l, 64) - nb);
+            const long long off = c.pos - start;
+            c.b = base + l;
+            c.x = (int)(off / nb);
+            c.t = (int)(off % nb);
+            const int ne_before = nonempty + __popcll(ne & ((1ull << l) - 1ull));
+            c.rank = ne_before * hx + c.x;
+            return true;
+        }
+        before += hx * __shfl(incl, 63, 64);
+        nonempty += __popcll(ne);
+    }
+    return false;  // not reached: pos < T lies in some non-empty sequence
+}
+
+// The work-group whose range holds position p.
+__device__ __forceinline__ int balanced_owner(long long p, long long total, int w_eff) {
+    return (int)(((p + 1) * w_eff - 1) / total);
+}
+
+}  // namespace fd

@@ -6,7 +6,7 @@
 //   [P3] "FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法"
 //        (my-webpage-adu.pages.dev, 2026-07-16)
 //   [P4] "从第一性原理推导 Flash Attention：IO 复杂度、Tiling 策略与在线 Softmax 的数学工程"
-//        (www.ybb.press), §8.1 (grouped-query attention: fewer KV heads)
+//        (www.ybb.press), §8 item 1 (grouped-query attention: fewer KV heads)
 //
 // When G = heads_q / heads_kv query heads share one KV head, every K and V
 // row a split reads serves G query rows, and the split step is a small dense
@@ -24,8 +24,9 @@
 //     by more than 2^8 ([P4] §3.2: any common reference gives the same
 //     result); the four lanes holding a head then agree on the new max
 //     through two shuffles.  In steady state a step costs one ballot.
-//     p = exp2(s - m) is rounded to the input type and l sums exactly the
-//     rounded weights, so the weights the matrix core applies sum to l.
+//     p = exp2(s - m) is rounded to the input type for the matrix core; o is
+//     normalised by the sum of the rounded weights (so the weights applied
+//     to V sum to 1) and the LSE uses the sum of the fp32 weights.
 //   O (16 heads x d) += P (16 x 16 tokens) . V_tile (16 x d):
 //     v_mfma_f32_16x16x16, one per 16-wide d slice.  P is the A operand
 //     exactly as the S step left it.  V, stored row-major (tokens x d) in
@@ -48,6 +49,7 @@
 // §2.3.2-§2.3.3).  Scores are in the log2 domain (scale * log2(e) applied to
 // the fp32 MFMA result).
 #include "dev_common.h"
+#include "partition.h"
 
 namespace fd {
 namespace {
@@ -60,7 +62,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxGroup = 16;    // query heads per KV head one wave can hold
-constexpr float kRescaleGap = 8.f;  // log2 units the running max may lag
+[[maybe_unused]] constexpr float kRescaleGap = 8.f;  // log2 units the running max may lag
 
 template <int DT>
 struct Mma;
@@ -140,38 +142,43 @@ struct Tiles {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-template <int DT, int D>
-__global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
-    // The body uses LDS address-space pointers and gfx950-only builtins that
-    // the host pass cannot type; it only needs the kernel's declaration.
+// Where a piece's results go: the normalised o of group head h at
+// o + h * o_stride (fp32) and its LSE at lse[h * lse_stride]; with o null the
+// piece is a whole row and writes the final output (a.o, a.lse) itself.
+struct PieceOut {
+    float *o;
+    float *lse;
+    int o_stride, lse_stride;
+};
+
 #if defined(__HIP_DEVICE_COMPILE__)
+// One piece: tokens [t0, t1) of KV head kvh of sequence b for the G query
+// heads sharing it.  Called by the whole wave; t0 >= t1 writes (0, -inf).
+// (Device pass only: the body uses LDS address-space pointers and gfx950-only
+// builtins that the host pass cannot type.)
+template <int DT, int D>
+__device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
+                                           long t0, long t1, const PieceOut &out) {
     using T = Tiles<D>;
     constexpr int NC = T::NC, NT = T::NT, U = T::U;
     using M = Mma<DT>;
-    __shared__ __attribute__((aligned(1024))) char tile_buf[T::BUF];
 
     const int lane = threadIdx.x;
     const int col = lane & 15;  // tile token (K reads) / head (S) / d column (O)
     const int grp = lane >> 4;  // 0..3
     const int G = a.heads_q / a.heads_kv;
 
-    // Work-group -> (b, KV head, split), KV head fastest.
-    const int kvh = blockIdx.x % a.heads_kv;
-    const int rest = blockIdx.x / a.heads_kv;
-    const int split = rest % a.num_splits;
-    const int b = rest / a.num_splits;
-
-    int n = a.kv_lens ? a.kv_lens[b] : a.max_kv_len;
-    n = n < 0 ? 0 : (n > a.max_kv_len ? a.max_kv_len : n);
-    const long t0 = (long)split * a.split_len;
-    const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
-
     f32x4_t oacc[NT];  // O[head 4*grp + r][16*t + col]
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_used = -INFINITY;  // reference max of head `col` (log2 domain)
-    float lsum = 0.f;          // this lane's share of l for head `col`
+    // This lane's share of l for head `col`, twice: over the weights as
+    // rounded for the matrix core (o is normalised by it, so the weights
+    // applied to V sum to exactly 1) and over the fp32 weights (the LSE uses
+    // it, free of the rounding).
+    float lsum = 0.f;
+    float lexact = 0.f;
 
     if (t0 < t1) {
         // Q_g^T fragments: head `col` of the group, d = 32c + 8*grp + [0, 8).
@@ -197,8 +204,6 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
         constexpr int kStepTok = 16 * U;
         const int nsteps = (ntok + kStepTok - 1) / kStepTok;
 
-        // Direct-to-LDS loads of step st into buffer `buf` (a step past the
-        // last one re-reads the last step, so prefetches need no condition).
         // One step's loads: for tile u and row group j, lane L reads the
         // 16-byte chunk q = L % CPR of row r = j*RPI + L/CPR (token
         // first + 16u + r, clamped to the last valid token; a step past the
@@ -227,7 +232,6 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
                 }
         };
         // Write a step's rows into the LDS tiles, chunks swizzled per row.
-        lds_char *const tb = (lds_char *)tile_buf;
         auto stage = [&](const Stage &g) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -300,6 +304,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
                 if (grow)
                     m_used = m_new;
                 lsum *= alpha;
+                lexact *= alpha;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float ar = __shfl(alpha, 4 * grp + r, 64);
@@ -315,6 +320,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     p[r] = fast_exp2(x[u][r] - mref);
+                lexact += (p[0] + p[1]) + (p[2] + p[3]);
                 const u32x2 pa = M::pack(p, &lsum);
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
@@ -355,31 +361,106 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
     // l of head `col`: the four lanes holding it each summed their tokens.
     float ltot = lsum + __shfl_xor(lsum, 16, 64);
     ltot += __shfl_xor(ltot, 32, 64);
+    float lex = lexact + __shfl_xor(lexact, 16, 64);
+    lex += __shfl_xor(lex, 32, 64);
     // Output rows: this lane holds heads 4*grp + r of O.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int h = 4 * grp + r;
         const float lr = __shfl(ltot, h, 64);
+        const float le = __shfl(lex, h, 64);
         const float mr = __shfl(m_used, h, 64);
         if (h >= G)
             continue;
+        // a non-empty piece has a weight >= 1 (its max score is at or above
+        // the reference), which rounds to >= 1: lr > 0 exactly when le > 0
         const bool any = lr > 0.f;
         const float inv = any ? 1.f / lr : 0.f;
-        const float lse = any ? (mr + fast_log2(lr)) * kLn2 : -INFINITY;
-        const size_t rowid = (size_t)b * a.heads_q + (size_t)kvh * G + h;
-        if (a.o_part) {
-            const size_t slot = rowid * a.num_splits + split;
+        const float lse = any ? (mr + fast_log2(le)) * kLn2 : -INFINITY;
+        if (out.o) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                a.o_part[slot * D + 16 * t + col] = oacc[t][r] * inv;
+                out.o[(size_t)h * out.o_stride + 16 * t + col] = oacc[t][r] * inv;
             if (col == 0)
-                a.lse_part[slot] = lse;
+                out.lse[(size_t)h * out.lse_stride] = lse;
         } else {
+            const size_t rowid = (size_t)b * a.heads_q + (size_t)kvh * G + h;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 store_out(a.o, rowid * D + 16 * t + col, oacc[t][r] * inv, a.out_dtype);
             if (col == 0 && a.lse)
                 a.lse[rowid] = lse;
+        }
+    }
+}
+
+#endif  // __HIP_DEVICE_COMPILE__
+
+// Fixed splits: work-group -> (b, KV head, split), KV head fastest; split i
+// covers [i*L, min((i+1)*L, N_b)).
+template <int DT, int D>
+__global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
+    const int kvh = blockIdx.x % a.heads_kv;
+    const int rest = blockIdx.x / a.heads_kv;
+    const int split = rest % a.num_splits;
+    const int b = rest / a.num_splits;
+    const int n = clamp_len(a.kv_lens, b, a.max_kv_len);
+    const long t0 = (long)split * a.split_len;
+    const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
+    const int G = a.heads_q / a.heads_kv;
+    PieceOut out{nullptr, nullptr, 0, 0};
+    if (a.o_part) {
+        const size_t row0 = (size_t)b * a.heads_q + (size_t)kvh * G;  // first head of the group
+        out.o = a.o_part + (row0 * a.num_splits + split) * D;
+        out.lse = a.lse_part + row0 * a.num_splits + split;
+        out.o_stride = a.num_splits * D;
+        out.lse_stride = a.num_splits;
+    }
+    mfma_piece<DT, D>(a, (lds_char *)tile_buf, b, kvh, t0, t1, out);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Token-balanced partition (partition.h): work-group w walks its share of the
+// flattened (sequence, KV head, token) space piece by piece; the piece of unit
+// u goes to slot w + rank(u) of the slot arrays (o [slot][G][d], LSE [slot][G]).
+template <int DT, int D>
+__global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
+    const int w = blockIdx.x;
+    const int G = a.heads_q / a.heads_kv;
+    PieceCursor c;
+    if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c))
+        return;
+    int n = clamp_len(a.kv_lens, c.b, a.max_kv_len);
+    while (true) {
+        const long long left = c.end - c.pos;
+        const int plen = left < (long long)(n - c.t) ? (int)left : n - c.t;
+        const int slot = w + c.rank;
+        const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G, D, 1};
+        mfma_piece<DT, D>(a, (lds_char *)tile_buf, c.b, c.x, c.t, (long)c.t + plen, out);
+        if (c.t == 0 && threadIdx.x == 0) {
+            const int last = balanced_owner(c.pos + n - 1, c.total, c.w_eff);
+            const size_t u = (size_t)c.b * a.heads_kv + c.x;
+            a.unit_desc[2 * u] = slot;
+            a.unit_desc[2 * u + 1] = last - w + 1;
+        }
+        c.pos += plen;
+        if (c.pos >= c.end)
+            break;
+        // next unit: the next KV head, else the next non-empty sequence
+        c.t = 0;
+        ++c.rank;
+        if (++c.x == a.heads_kv) {
+            c.x = 0;
+            do {
+                ++c.b;
+                n = c.b < a.batch ? clamp_len(a.kv_lens, c.b, a.max_kv_len) : 0;
+            } while (n == 0 && c.b < a.batch);
+            if (n == 0)
+                break;  // not reached: positions remain, so a non-empty sequence follows
         }
     }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -408,14 +489,19 @@ template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     constexpr size_t kStatic = (size_t)T::BUF;
-    const long grid = (long)a.batch * a.heads_kv * a.num_splits;
+    const long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
     if (FD_MFMA_WG_PER_CU > 0 && lds > 0) {
         const size_t want = (size_t)lds / (FD_MFMA_WG_PER_CU + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
     }
-    hipLaunchKernelGGL((split_mfma_kernel<DT, D>), dim3((unsigned)grid), dim3(64), pad, stream, a);
+    if (a.balanced)
+        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D>), dim3((unsigned)grid), dim3(64), pad,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((split_mfma_kernel<DT, D>), dim3((unsigned)grid), dim3(64), pad, stream,
+                           a);
     return hipGetLastError();
 }
 

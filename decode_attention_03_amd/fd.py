@@ -30,7 +30,7 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 
 #: every symbol include/fd.h declares
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
-           "fd_decode_split", "fd_combine", "fd_decode")
+           "fd_decode_workspace_bytes", "fd_decode_split", "fd_combine", "fd_decode")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,8 @@ def library() -> ctypes.CDLL:
         lib.fd_choose_splits.argtypes = [I, I, I, I, I, I, I, I, IP, IP]
         lib.fd_choose_splits.restype = I
         lib.fd_workspace_bytes.argtypes, lib.fd_workspace_bytes.restype = [I, I, I, I], S
+        lib.fd_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(S)]
+        lib.fd_decode_workspace_bytes.restype = I
         lib.fd_decode_split.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P]
         lib.fd_decode_split.restype = I
         lib.fd_combine.argtypes = [P, P, I, I, I, I, P, I, P, P]
@@ -138,6 +140,28 @@ def workspace_bytes(batch: int, heads_q: int, num_splits: int, head_dim: int) ->
     return int(library().fd_workspace_bytes(batch, heads_q, num_splits, head_dim))
 
 
+def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_kv_len: int,
+                           head_dim: int, dtype: torch.dtype, has_kv_lens: bool,
+                           num_splits: int = 0, split_len: int = 0) -> int:
+    """Workspace fd_decode needs for exactly these arguments (num_splits 0: the
+    library's automatic plan)."""
+    out = ctypes.c_size_t()
+    _check(library().fd_decode_workspace_bytes(batch, heads_q, heads_kv, max_kv_len, head_dim,
+                                               _code(dtype), int(bool(has_kv_lens)), num_splits,
+                                               split_len, ctypes.byref(out)))
+    return out.value
+
+
+def uses_balanced_plan(heads_q: int, heads_kv: int, max_kv_len: int, head_dim: int,
+                       dtype: torch.dtype, has_kv_lens: bool, num_splits: int = 0) -> bool:
+    """Whether fd_decode takes the token-balanced partition for these arguments
+    (the rule include/fd.h states: automatic plan, kv_lens given, grouped heads
+    2..16 on a 16-bit input type, supported head_dim)."""
+    group = heads_q // heads_kv
+    return (num_splits == 0 and has_kv_lens and max_kv_len > 0 and 2 <= group <= 16
+            and dtype in (torch.bfloat16, torch.float16) and head_dim in (64, 128, 256))
+
+
 def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, scale=None,
                  o_part=None, lse_part=None):
     """Split stage: returns (o_part [batch, Hq, B, d] f32, lse_part [batch, Hq, B] f32)."""
@@ -187,21 +211,21 @@ def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len:
            out_dtype=None, return_lse: bool = True, workspace=None, o=None, lse=None):
     """Whole decode step (split + combine) -> (o, lse or None).
 
-    num_splits 0 lets the library choose.  workspace (any dtype, on the device)
-    is allocated here when not given and more than one split is used.
+    num_splits 0 lets the library plan the partition (fixed splits from
+    fd_choose_splits, or the token-balanced partition for ragged grouped-head
+    batches).  workspace (any dtype, on the device) is allocated here when not
+    given and the plan needs one.
     """
     batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out_dtype = out_dtype or q.dtype
     dev = q.device
-    if num_splits == 0:
-        num_splits, split_len = choose_splits(batch, heads_q, heads_kv, n_max, d, q.dtype,
-                                              ragged=kv_lens is not None)
     if o is None:
         o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
-    need = workspace_bytes(batch, heads_q, num_splits, d)
+    need = decode_workspace_bytes(batch, heads_q, heads_kv, n_max, d, q.dtype,
+                                  kv_lens is not None, num_splits, split_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -41,8 +41,7 @@ from decode_attention_03_amd import build, workloads  # noqa: E402
 BENCH = os.path.join(ROOT, "bench.py")
 COPY_BYTES = 1 << 30
 # rocprofv3 kernel names -> kernel family (the source files it is built from)
-FAMILIES = (("split_valu_kernel", "split_valu"), ("split_mfma_kernel", "split_mfma"),
-            ("combine_kernel", "combine"))
+FAMILIES = (("split_valu", "split_valu"), ("split_mfma", "split_mfma"), ("combine", "combine"))
 
 
 def family_of(kernel_name: str) -> str | None:
@@ -213,7 +212,8 @@ def main() -> int:
         "",
         f"Workload: batch {w.batch}, {w.heads_q} query / {w.heads_kv} KV heads, d {w.head_dim}, "
         f"N {w.max_kv_len}{' (ragged)' if w.ragged else ''}, {w.dtype}; "
-        f"{res['config']['num_splits']} splits of {res['config']['split_len']} tokens.",
+        (f"{res['config']['num_splits']} splits of {res['config']['split_len']} tokens."
+         if res["config"].get("num_splits") else f"plan: {res['config'].get('plan')}."),
         "",
         "Made by (repository root):",
         "",

@@ -97,6 +97,16 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
  * non-positive sizes. */
 size_t fd_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim);
 
+/* Bytes of workspace fd_decode needs when called with exactly these
+ * arguments (has_kv_lens: nonzero when kv_lens will be non-NULL), including
+ * the automatic plan of num_splits == 0 described at fd_decode.  Writes 0 when
+ * no workspace is needed.  May query the current HIP device (compute units).
+ * Returns FD_OK, FD_ERR_INVALID (bad sizes, null bytes), FD_ERR_UNSUPPORTED
+ * (head_dim or dtype) or FD_ERR_HIP. */
+int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_len,
+                              int head_dim, int in_dtype, int has_kv_lens, int num_splits,
+                              int split_len, size_t *bytes);
+
 /* Split stage ([P1] §2.5 stage 1; [P3] §3.2.1 stage 1): for every
  * (b, h, split i) with token range [i*L, min((i+1)*L, N_b)) write
  *   o_part[b,h,i,:] = sum_j exp(s_j - m) V_j / l,
@@ -116,13 +126,25 @@ int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_
                int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream);
 
 /* Whole decode step: split + combine.
- *   num_splits == 0: B and L come from fd_choose_splits (split_len ignored;
- *     ragged = kv_lens != NULL).
+ *   num_splits == 0 (automatic plan, split_len ignored):
+ *     - kv_lens given and grouped heads on the matrix-core kernel (bf16/f16,
+ *       2 <= heads_q/heads_kv <= 16): a token-balanced partition.  The
+ *       (sequence, KV head, token) space of the actual lengths is cut into
+ *       equal shares, one per work-group (CUs x 2), so every work-group
+ *       streams the same number of K/V rows whatever the length mix; a share
+ *       may end inside one (sequence, head) row and continue in the next, and
+ *       each such piece yields one (o, LSE) pair that the combine merges with
+ *       the row's other pieces ([P3] §2.3.4; any cut gives the same result,
+ *       [P3] §2.3.5).  The split points depend on the lengths, so results
+ *       agree with a fixed-split run up to rounding, and are reproducible
+ *       for fixed inputs.
+ *     - otherwise: B and L from fd_choose_splits (ragged = kv_lens != NULL).
  *   num_splits > 0, split_len == 0: L = ceil(max_kv_len / num_splits)
  *     ([P2] §4 chunking).  num_splits > 0, split_len > 0: used as given.
  * With B == 1 the split stage writes o and lse itself and workspace may be
- * NULL; otherwise workspace must hold fd_workspace_bytes(...) bytes.
- * lse may be NULL. */
+ * NULL; otherwise workspace must hold the bytes fd_decode_workspace_bytes
+ * reports for the same arguments (for B >= 1 given explicitly, that is
+ * fd_workspace_bytes(batch, heads_q, B, head_dim)).  lse may be NULL. */
 int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
               int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
               int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,

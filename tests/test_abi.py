@@ -100,6 +100,26 @@ def test_workspace_bytes(lib):
     assert ws % 256 == 0 and ws >= 3 * 5 * 7 * 65 * 4
 
 
+def test_decode_workspace_bytes_explicit_splits(lib):
+    """With the split count given, fd_decode needs exactly fd_workspace_bytes
+    (no device query); bad arguments are rejected."""
+    out = ctypes.c_size_t(123)
+    for B, has_lens in ((4, 0), (4, 1), (1, 1), (37, 0)):
+        assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, has_lens, B, 0,
+                                             ctypes.byref(out)) == fd.OK
+        assert out.value == lib.fd_workspace_bytes(3, 8, B, 128)
+    assert lib.fd_decode_workspace_bytes(3, 8, 3, 1000, 128, fd.BF16, 0, 4, 0,
+                                         ctypes.byref(out)) == fd.ERR_INVALID
+    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 96, fd.BF16, 0, 4, 0,
+                                         ctypes.byref(out)) == fd.ERR_UNSUPPORTED
+    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, 7, 0, 4, 0,
+                                         ctypes.byref(out)) == fd.ERR_UNSUPPORTED
+    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, 0, -1, 0,
+                                         ctypes.byref(out)) == fd.ERR_INVALID
+    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, 0, 4, 0,
+                                         None) == fd.ERR_INVALID
+
+
 def _split(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, kv_lens=None, batch=1, hq=4, hkv=2, n=64, d=64, dt=fd.F32,
              scale=0.125, B=4, L=16, o_part=FAKE, lse_part=FAKE)
