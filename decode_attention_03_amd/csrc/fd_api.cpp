@@ -24,7 +24,7 @@ namespace {
 
 constexpr int kVersion = 100;          // 0.1.0
 constexpr int kMaxSplits = 8192;       // combine keeps one weight per split in LDS
-constexpr int kWorkGroupsPerCU = 2;    // resident one-wave work-groups per CU
+constexpr int kWorkGroupsPerCU = fd::kWavesPerCU;  // resident one-wave work-groups per CU
 constexpr int kRaggedRounds = 4;       // work-group rounds aimed at for ragged batches
 constexpr int kMinSplitLenMha = 256;   // tokens; partial traffic ~0.8% of K/V at d = 128
 constexpr int kMinSplitLenPerHead = 64;  // grouped: tokens per query head of the group
@@ -113,13 +113,22 @@ int check_partition(int batch, int heads_q, int max_kv_len, int num_splits, int 
     return FD_OK;
 }
 
-int launch_split(const fd::SplitArgs &a, int in_dtype, hipStream_t stream) {
+int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     const int group = a.heads_q / a.heads_kv;
     hipError_t e;
-    if (fd::split_mfma_supported(in_dtype, a.head_dim, group))
+    if (fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
         e = fd::launch_split_mfma(a, in_dtype, stream);
-    else
+    } else {
+        // two waves per work-group when one-wave work-groups would leave wave
+        // slots of the GPU empty
+        int cus = 0;
+        int rc = device_cus(&cus);
+        if (rc != FD_OK)
+            return rc;
+        const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
+        a.valu_waves = wgs < (long long)cus * fd::kWavesPerCU ? 2 : 1;
         e = fd::launch_split_valu(a, in_dtype, stream);
+    }
     if (e != hipSuccess)
         return fail(FD_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
@@ -214,6 +223,10 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     if (b > kMaxAutoSplits)
         b = kMaxAutoSplits;
     if (b < 1)
+        b = 1;
+    // the vector kernel runs a lone split per row with two waves, which fills
+    // the same wave slots as two splits and needs no combine stage
+    if (!grouped && !ragged && b == 2)
         b = 1;
     long long len = (max_kv_len + b - 1) / b;
     len = (len + 15) / 16 * 16;  // whole 16-token tiles

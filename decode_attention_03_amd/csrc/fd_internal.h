@@ -11,6 +11,10 @@ namespace fd {
 // Element type codes (same values as the FD_* codes of the public header).
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
+// Resident waves per CU the split kernels aim at: MI355X HBM streams best
+// with about two waves per CU, each with ~16 KB of loads in flight.
+constexpr int kWavesPerCU = 2;
+
 // Everything one split-stage launch needs.  Shapes follow the public layouts:
 // q [batch, heads_q, d], K/V [batch, max_kv_len, heads_kv, d].
 struct SplitArgs {
@@ -32,9 +36,14 @@ struct SplitArgs {
     int balanced;
     int num_wgs;
     int *unit_desc;
+    // Vector kernel only: waves per work-group (1 or 2).  Two waves share a
+    // split (and merge in LDS) when the grid has fewer work-groups than the
+    // GPU has wave slots, e.g. one split per row.
+    int valu_waves;
 };
 
-// VALU split kernel: one work-group per (sequence, query head, split).
+// VALU split kernel: one work-group (a.valu_waves waves) per (sequence, query
+// head, split).
 // Handles every head_dim/dtype; with heads_q > heads_kv each query head reads
 // its shared KV head on its own.
 hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t stream);

@@ -31,8 +31,12 @@
 //
 // HBM efficiency on MI355X peaks when each CU has about two waves with
 // ~16 KB of loads in flight each; more concurrent requests lower the
-// achieved bandwidth.  So the launcher caps resident work-groups per CU by
-// reserving LDS (the reservation is never touched), whatever the grid size.
+// achieved bandwidth.  So the launcher caps resident waves per CU at two by
+// reserving LDS (the reservation is never touched), whatever the grid size:
+// two one-wave work-groups, or one two-wave work-group whose waves take
+// alternate token slots of the same split (used when there are fewer
+// work-groups than wave slots, e.g. with one split per row, where it also
+// makes the combine stage unnecessary).
 #include "dev_common.h"
 
 namespace fd {
@@ -353,16 +357,6 @@ hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
     return hipGetLastError();
 }
 
-#ifndef FD_VALU_THREADS
-#define FD_VALU_THREADS 64
-#endif
-#ifndef FD_VALU_HPW
-#define FD_VALU_HPW 1
-#endif
-#ifndef FD_VALU_WG_PER_CU
-#define FD_VALU_WG_PER_CU 2
-#endif
-
 #ifndef FD_VALU_ROW_BYTES
 #define FD_VALU_ROW_BYTES 16  // bytes of a head row per lane (sets lanes per row)
 #endif
@@ -377,9 +371,9 @@ constexpr int lanes_per_row() {
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     constexpr int LPR = lanes_per_row<DT, D>();
-    if (FD_VALU_HPW > 1 && a.heads_q % FD_VALU_HPW == 0)
-        return launch_cfg<DT, D, FD_VALU_THREADS, FD_VALU_HPW, LPR>(a, FD_VALU_WG_PER_CU, stream);
-    return launch_cfg<DT, D, FD_VALU_THREADS, 1, LPR>(a, FD_VALU_WG_PER_CU, stream);
+    if (a.valu_waves == 2)
+        return launch_cfg<DT, D, 128, 1, LPR>(a, kWavesPerCU / 2, stream);
+    return launch_cfg<DT, D, 64, 1, LPR>(a, kWavesPerCU, stream);
 }
 
 template <int DT>

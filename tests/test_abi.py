@@ -75,6 +75,9 @@ def test_choose_splits_fills_the_gpu(lib):
     assert splits(1, 32, 65536) * 32 >= 256  # at least one work-group per CU
     assert splits(1, 32, 65536) >= splits(1, 32, 4096)
     assert splits(64, 64, 4096) == 1  # 4096 rows already fill the GPU
+    # 256 rows on 256 CUs: one split per row, run by two-wave work-groups
+    assert splits(8, 32, 4096) == 1
+    assert splits(4, 32, 4096) == 4  # 128 rows: four splits each
     assert splits(1, 32, 65536, cus=64) <= splits(1, 32, 65536, cus=256)
     ragged = 1
     assert splits(16, 8, 32768) >= 4  # ragged batches get several rounds of work
