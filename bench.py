@@ -179,6 +179,65 @@ def time_split_kernel(p: Prepared, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps * 1e3
 
 
+def time_partial_formats(w: workloads.Workload, dev: torch.device, steps: int, warmup: int) -> dict:
+    """The two partial formats the pages derive, on one workload with fixed
+    splits: LSE pair (fd_decode_split + fd_combine) against the m/l/o triple
+    (fd_decode_split_mlo + fd_combine_mlo).  HIP events over the timed region."""
+    p = Prepared(w, dev)
+    B, L = p.B, p.L
+    batch, hq, d = w.batch, w.heads_q, w.head_dim
+    shape = (batch, hq, B)
+    m_part = torch.empty(shape, dtype=torch.float32, device=dev)
+    l_part = torch.empty(shape, dtype=torch.float32, device=dev)
+    lib, P = p.lib, ctypes.c_void_p
+    sp = ctypes.c_void_p(p.stream.cuda_stream)
+    mlo_args = []
+    for a in p.split_args:  # same arguments, m_part and l_part in place of lse_part
+        mlo_args.append(tuple(a[:14]) + (P(m_part.data_ptr()), P(l_part.data_ptr()), sp))
+    comb_lse = (P(p.o_part.data_ptr()), P(p.lse_part.data_ptr()), batch, hq, B, d,
+                P(p.o.data_ptr()), p.out_code, P(p.lse.data_ptr()), sp)
+    comb_mlo = (P(p.o_part.data_ptr()), P(m_part.data_ptr()), P(l_part.data_ptr()), batch, hq,
+                B, d, P(p.o.data_ptr()), p.out_code, P(p.lse.data_ptr()), sp)
+
+    def region(fn) -> float:
+        for i in range(warmup):
+            fn(i)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(p.stream)
+        for i in range(steps):
+            fn(i)
+        end.record(p.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps * 1e3
+
+    def check(rc):
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    def lse_route(i):
+        check(lib.fd_decode_split(*p.split_args[i % p.copies]))
+        check(lib.fd_combine(*comb_lse))
+
+    def mlo_route(i):
+        check(lib.fd_decode_split_mlo(*mlo_args[i % p.copies]))
+        check(lib.fd_combine_mlo(*comb_mlo))
+
+    out = {"workload": w.name, "num_splits": B, "split_len": L,
+           "lse_route_us": round(region(lse_route), 2),
+           "mlo_route_us": round(region(mlo_route), 2),
+           "lse_split_us": round(region(lambda i: check(lib.fd_decode_split(
+               *p.split_args[i % p.copies]))), 2),
+           "mlo_split_us": round(region(lambda i: check(lib.fd_decode_split_mlo(
+               *mlo_args[i % p.copies]))), 2),
+           "lse_combine_us": round(region(lambda i: check(lib.fd_combine(*comb_lse))), 2),
+           "mlo_combine_us": round(region(lambda i: check(lib.fd_combine_mlo(*comb_mlo))), 2),
+           "partial_bytes_lse": batch * hq * B * (d + 1) * 4,
+           "partial_bytes_mlo": batch * hq * B * (d + 2) * 4}
+    p.free()
+    return out
+
+
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     """The fp64 oracle on the host cores, on whole decode steps of the same
     workload, repeated until about budget_s seconds of wall time."""
@@ -333,6 +392,12 @@ def main() -> int:
             del q
             torch.cuda.empty_cache()
         result["workloads"] = others
+        # the m/l/o partial format against the LSE pair, on the long-context
+        # workload (16 splits per row, so the combine stage does real work)
+        pf = time_partial_formats(workloads.WORKLOADS[3], dev, args.steps, args.warmup)
+        log(f"[bench] partial formats: {pf}")
+        result["partial_formats"] = pf
+        torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
     return 0
 

@@ -15,6 +15,9 @@
 // reproducible.  -inf partials (empty splits) get weight 0 and contribute
 // exactly nothing; a row whose partials are all -inf yields o = 0, S = -inf.
 //
+// The m/l/o variant merges (m, l, o) triples instead ("FlashDecoding 数学推导"
+// (my-webpage-adu.pages.dev, 2026-07-15) §2.4.2 and §2.5 stage 2).
+//
 // Two sources of partials: fixed splits ([batch, heads_q, B, d], B per row),
 // or the slots of the token-balanced partition (partition.h), where a row's
 // unit descriptor names its first slot and slot count and the row's partials
@@ -41,14 +44,16 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// A row's partials: LSE i at S[i * s_stride], o_i at O + i * o_stride.
+// A row's partials: LSE i at S[i * s_stride], o_i at O + i * o_stride.  In the
+// m/l/o format S holds m_i and L holds l_i (same stride).
 struct RowSource {
     const float *S;
     const float *O;
     int count, s_stride, o_stride;
+    const float *L;
 };
 
-template <int D>
+template <int D, bool MLO = false>
 __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, void *o,
                                             int out_dtype, float *lse, float *weights) {
     constexpr int V4 = D / 4;                     // float4 slices per row
@@ -75,22 +80,51 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
     for (int w = 1; w < NW; ++w)
         mx = fmaxf(mx, red[w]);
     __syncthreads();
-    // S_global = S_max + log sum_i exp(S_i - S_max)
-    float sum = 0.f;
-    if (mx != -INFINITY)
-        for (int i = tid; i < num_splits; i += kCombineThreads)
-            sum += fast_exp2((S[(size_t)i * ss] - mx) * kLog2e);
-    sum = wave_sum(sum);
-    if (lane == 0)
-        red[wave] = sum;
-    __syncthreads();
-    sum = 0.f;
+    float sg;
+    if constexpr (!MLO) {
+        // S_global = S_max + log sum_i exp(S_i - S_max)
+        float sum = 0.f;
+        if (mx != -INFINITY)
+            for (int i = tid; i < num_splits; i += kCombineThreads)
+                sum += fast_exp2((S[(size_t)i * ss] - mx) * kLog2e);
+        sum = wave_sum(sum);
+        if (lane == 0)
+            red[wave] = sum;
+        __syncthreads();
+        sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-        sum += red[w];
-    const float sg = mx == -INFINITY ? -INFINITY : mx + fast_log2(sum) * kLn2;
-    for (int i = tid; i < num_splits; i += kCombineThreads)
-        weights[i] = mx == -INFINITY ? 0.f : fast_exp2((S[(size_t)i * ss] - sg) * kLog2e);
+        for (int w = 0; w < NW; ++w)
+            sum += red[w];
+        sg = mx == -INFINITY ? -INFINITY : mx + fast_log2(sum) * kLn2;
+        for (int i = tid; i < num_splits; i += kCombineThreads)
+            weights[i] = mx == -INFINITY ? 0.f : fast_exp2((S[(size_t)i * ss] - sg) * kLog2e);
+    } else {
+        // m/l/o ("FlashDecoding 数学推导" §2.4.2): m_g = max m_i (mx above),
+        // l_g = sum_i exp(m_i - m_g) l_i, weights exp(m_i - m_g) l_i / l_g
+        const float *Lp = src.L;
+        float lg = 0.f;
+        if (mx != -INFINITY)
+            for (int i = tid; i < num_splits; i += kCombineThreads) {
+                const float m = S[(size_t)i * ss];
+                lg += m == -INFINITY ? 0.f : fast_exp2((m - mx) * kLog2e) * Lp[(size_t)i * ss];
+            }
+        lg = wave_sum(lg);
+        if (lane == 0)
+            red[wave] = lg;
+        __syncthreads();
+        lg = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            lg += red[w];
+        sg = mx == -INFINITY ? -INFINITY : mx + fast_log2(lg) * kLn2;
+        const float inv = mx == -INFINITY ? 0.f : 1.f / lg;
+        for (int i = tid; i < num_splits; i += kCombineThreads) {
+            const float m = S[(size_t)i * ss];
+            weights[i] = m == -INFINITY
+                             ? 0.f
+                             : fast_exp2((m - mx) * kLog2e) * Lp[(size_t)i * ss] * inv;
+        }
+    }
     __syncthreads();
 
     // o = sum_i w_i o_i: thread (sp, c) takes splits sp, sp + SP, ... of slice c
@@ -143,8 +177,20 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     extern __shared__ float weights[];  // num_splits entries
     const size_t rowid = blockIdx.x;
     const RowSource src{lse_part + rowid * num_splits, o_part + rowid * num_splits * D, num_splits,
-                        1, D};
+                        1, D, nullptr};
     combine_row<D>(src, rowid, o, out_dtype, lse, weights);
+}
+
+// m/l/o triples of fixed splits.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_mlo_kernel(
+    const float *__restrict__ o_part, const float *__restrict__ m_part,
+    const float *__restrict__ l_part, int num_splits, void *o, int out_dtype, float *lse) {
+    extern __shared__ float weights[];  // num_splits entries
+    const size_t rowid = blockIdx.x;
+    const RowSource src{m_part + rowid * num_splits, o_part + rowid * num_splits * D, num_splits,
+                        1, D, l_part + rowid * num_splits};
+    combine_row<D, true>(src, rowid, o, out_dtype, lse, weights);
 }
 
 // Token-balanced slots: row (b, h) of unit u = b * (heads_q / gsz) + h / gsz
@@ -158,7 +204,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_slots_kernel(SlotComb
     const int h = (int)(rowid % a.heads_q);
     const int g = h % a.gsz;
     const size_t u = (size_t)b * (a.heads_q / a.gsz) + h / a.gsz;
-    RowSource src{a.lse_slots, a.o_slots, 0, a.gsz, a.gsz * D};
+    RowSource src{a.lse_slots, a.o_slots, 0, a.gsz, a.gsz * D, nullptr};
     if (clamp_len(a.kv_lens, b, a.max_kv_len) > 0) {
         const int first = a.unit_desc[2 * u];
         src.count = a.unit_desc[2 * u + 1];
@@ -185,6 +231,29 @@ hipError_t launch_combine(const float *o_part, const float *lse_part, int rows, 
     case 256:
         hipLaunchKernelGGL(combine_kernel<256>, dim3(rows), dim3(kCombineThreads), shmem, stream,
                            o_part, lse_part, num_splits, o, out_dtype, lse);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_mlo(const float *o_part, const float *m_part, const float *l_part,
+                              int rows, int num_splits, int head_dim, void *o, int out_dtype,
+                              float *lse, hipStream_t stream) {
+    const size_t shmem = sizeof(float) * (size_t)num_splits;
+    switch (head_dim) {
+    case 64:
+        hipLaunchKernelGGL(combine_mlo_kernel<64>, dim3(rows), dim3(kCombineThreads), shmem, stream,
+                           o_part, m_part, l_part, num_splits, o, out_dtype, lse);
+        break;
+    case 128:
+        hipLaunchKernelGGL(combine_mlo_kernel<128>, dim3(rows), dim3(kCombineThreads), shmem,
+                           stream, o_part, m_part, l_part, num_splits, o, out_dtype, lse);
+        break;
+    case 256:
+        hipLaunchKernelGGL(combine_mlo_kernel<256>, dim3(rows), dim3(kCombineThreads), shmem,
+                           stream, o_part, m_part, l_part, num_splits, o, out_dtype, lse);
         break;
     default:
         return hipErrorInvalidValue;

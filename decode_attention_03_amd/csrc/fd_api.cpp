@@ -277,10 +277,16 @@ int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_l
     return FD_OK;
 }
 
-int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
-                    int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
-                    int in_dtype, float scale, int num_splits, int split_len, float *o_part,
-                    float *lse_part, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Split stage with either partial format: lse_part (LSE pair) or m_part and
+// l_part (m/l/o triple).
+int split_stage(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
+                int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype, float scale,
+                int num_splits, int split_len, float *o_part, float *lse_part, float *m_part,
+                float *l_part, void *stream) {
     int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
                                 in_dtype, scale);
     if (rc != FD_OK)
@@ -288,10 +294,13 @@ int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *
     rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
     if (rc != FD_OK)
         return rc;
-    if (!o_part || !lse_part)
-        return fail(FD_ERR_INVALID, "o_part or lse_part is null");
-    if (!aligned16(o_part) || !aligned4(lse_part))
-        return fail(FD_ERR_UNSUPPORTED, "o_part must be 16-byte and lse_part 4-byte aligned");
+    const bool mlo = m_part || l_part;
+    if (!o_part || (mlo ? !(m_part && l_part) : !lse_part))
+        return fail(FD_ERR_INVALID, mlo ? "o_part, m_part or l_part is null"
+                                        : "o_part or lse_part is null");
+    if (!aligned16(o_part) || (mlo ? !(aligned4(m_part) && aligned4(l_part)) : !aligned4(lse_part)))
+        return fail(FD_ERR_UNSUPPORTED,
+                    "o_part must be 16-byte and the per-split scalars 4-byte aligned");
     fd::SplitArgs a{};
     a.q = q;
     a.k = k;
@@ -306,29 +315,86 @@ int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *
     a.split_len = split_len;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.o_part = o_part;
-    a.lse_part = lse_part;
+    a.lse_part = mlo ? nullptr : lse_part;
+    a.m_part = m_part;
+    a.l_part = l_part;
     return launch_split(a, in_dtype, static_cast<hipStream_t>(stream));
 }
 
-int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_q,
-               int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream) {
+// Checks shared by both combine entry points.
+int check_combine(const float *o_part, int batch, int heads_q, int num_splits, int head_dim,
+                  const void *o, int out_dtype, const float *lse) {
     if (batch < 1 || heads_q < 1)
         return fail(FD_ERR_INVALID, "sizes must be positive (batch=%d heads_q=%d)", batch,
                     heads_q);
     if (num_splits < 1 || num_splits > kMaxSplits)
         return fail(FD_ERR_INVALID, "num_splits %d outside [1, %d]", num_splits, kMaxSplits);
-    if (!o_part || !lse_part || !o)
-        return fail(FD_ERR_INVALID, "o_part, lse_part or o is null");
+    if (!o_part || !o)
+        return fail(FD_ERR_INVALID, "o_part or o is null");
     if (!head_dim_ok(head_dim))
         return fail(FD_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", head_dim);
     if (!dtype_ok(out_dtype))
         return fail(FD_ERR_UNSUPPORTED, "out_dtype %d not supported", out_dtype);
-    if (!aligned16(o_part) || !aligned4(lse_part) || !aligned4(o) || (lse && !aligned4(lse)))
+    if (!aligned16(o_part) || !aligned4(o) || (lse && !aligned4(lse)))
         return fail(FD_ERR_UNSUPPORTED, "misaligned pointer");
     if ((long long)batch * heads_q > 0x7fffffffLL)
         return fail(FD_ERR_INVALID, "batch * heads_q exceeds the launch limit");
+    return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                    int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                    int in_dtype, float scale, int num_splits, int split_len, float *o_part,
+                    float *lse_part, void *stream) {
+    return split_stage(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim,
+                       in_dtype, scale, num_splits, split_len, o_part, lse_part, nullptr, nullptr,
+                       stream);
+}
+
+int fd_decode_split_mlo(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                        int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                        int in_dtype, float scale, int num_splits, int split_len, float *o_part,
+                        float *m_part, float *l_part, void *stream) {
+    if (!m_part || !l_part)
+        return fail(FD_ERR_INVALID, "m_part or l_part is null");
+    return split_stage(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim,
+                       in_dtype, scale, num_splits, split_len, o_part, nullptr, m_part, l_part,
+                       stream);
+}
+
+int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_q,
+               int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream) {
+    int rc = check_combine(o_part, batch, heads_q, num_splits, head_dim, o, out_dtype, lse);
+    if (rc != FD_OK)
+        return rc;
+    if (!lse_part)
+        return fail(FD_ERR_INVALID, "lse_part is null");
+    if (!aligned4(lse_part))
+        return fail(FD_ERR_UNSUPPORTED, "misaligned pointer");
     hipError_t e = fd::launch_combine(o_part, lse_part, batch * heads_q, num_splits, head_dim, o,
                                       out_dtype, lse, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
+
+int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part, int batch,
+                   int heads_q, int num_splits, int head_dim, void *o, int out_dtype, float *lse,
+                   void *stream) {
+    int rc = check_combine(o_part, batch, heads_q, num_splits, head_dim, o, out_dtype, lse);
+    if (rc != FD_OK)
+        return rc;
+    if (!m_part || !l_part)
+        return fail(FD_ERR_INVALID, "m_part or l_part is null");
+    if (!aligned4(m_part) || !aligned4(l_part))
+        return fail(FD_ERR_UNSUPPORTED, "misaligned pointer");
+    hipError_t e = fd::launch_combine_mlo(o_part, m_part, l_part, batch * heads_q, num_splits,
+                                          head_dim, o, out_dtype, lse,
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;

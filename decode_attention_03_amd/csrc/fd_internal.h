@@ -28,6 +28,11 @@ struct SplitArgs {
     float *o_part;           // fixed splits: [batch, heads_q, num_splits, d] (num_splits > 1)
                              // balanced: slot array [slots][gsz][d]
     float *lse_part;         // fixed: [batch, heads_q, num_splits]; balanced: [slots][gsz]
+    // m/l/o partial format (fixed splits only): with m_part set, each split
+    // writes its max score m (natural log domain) and l = sum exp(s - m) to
+    // m_part / l_part ([batch, heads_q, num_splits]) instead of lse_part.
+    float *m_part;
+    float *l_part;
     void *o;                 // final output                       (num_splits == 1)
     float *lse;              // final LSE, may be null             (num_splits == 1)
     int out_dtype;
@@ -58,6 +63,12 @@ hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t strea
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.
 hipError_t launch_combine(const float *o_part, const float *lse_part, int rows, int num_splits,
                           int head_dim, void *o, int out_dtype, float *lse, hipStream_t stream);
+
+// m/l/o merge of num_splits triples per row: m_g = max m, weights
+// exp(m - m_g) l / l_g with l_g = sum exp(m - m_g) l; lse = m_g + log l_g.
+hipError_t launch_combine_mlo(const float *o_part, const float *m_part, const float *l_part,
+                              int rows, int num_splits, int head_dim, void *o, int out_dtype,
+                              float *lse, hipStream_t stream);
 
 // LSE merge of the slots a token-balanced split stage wrote: row (b, h) reads
 // the descriptor of unit b * (heads_q / gsz) + h / gsz (gsz query heads per

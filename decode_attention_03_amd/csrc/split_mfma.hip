@@ -46,7 +46,8 @@
 // reservation), which keeps the HBM request stream near its efficient depth.
 //
 // The split writes o = O / l and S = m + log l per query head ([P3]
-// §2.3.2-§2.3.3).  Scores are in the log2 domain (scale * log2(e) applied to
+// §2.3.2-§2.3.3), or, in the m/l/o format, o with the split's max score m and
+// l = sum exp(s - m) ([P1] §2.4.1 direct form).  Scores are in the log2 domain (scale * log2(e) applied to
 // the fp32 MFMA result).
 #include "dev_common.h"
 #include "partition.h"
@@ -143,12 +144,14 @@ struct Tiles {
 typedef __attribute__((address_space(3))) char lds_char;
 
 // Where a piece's results go: the normalised o of group head h at
-// o + h * o_stride (fp32) and its LSE at lse[h * lse_stride]; with o null the
-// piece is a whole row and writes the final output (a.o, a.lse) itself.
+// o + h * o_stride (fp32) and its LSE at lse[h * lse_stride] (m/l/o format:
+// m there and l at l[h * lse_stride]); with o null the piece is a whole row
+// and writes the final output (a.o, a.lse) itself.
 struct PieceOut {
     float *o;
-    float *lse;
+    float *lse;  // LSE, or m of the m/l/o format when `l` is set
     int o_stride, lse_stride;
+    float *l;    // m/l/o format: l at l[h * lse_stride]; null for the LSE format
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -179,6 +182,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
     // it, free of the rounding).
     float lsum = 0.f;
     float lexact = 0.f;
+    float mtrue = -INFINITY;  // max of this lane's scores (the m/l/o format's m)
 
     if (t0 < t1) {
         // Q_g^T fragments: head `col` of the group, d = 32c + 8*grp + [0, 8).
@@ -291,6 +295,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                     mx = fmaxf(mx, x[u][r]);
                 }
             }
+            mtrue = fmaxf(mtrue, mx);
             // The reference max of a head only has to bound its scores within
             // 2^kRescaleGap, so the four lanes of a head synchronise (and O, l
             // are rescaled) only when some lane's tokens outgrow it; in steady
@@ -363,6 +368,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
     ltot += __shfl_xor(ltot, 32, 64);
     float lex = lexact + __shfl_xor(lexact, 16, 64);
     lex += __shfl_xor(lex, 32, 64);
+    float mtop = fmaxf(mtrue, __shfl_xor(mtrue, 16, 64));
+    mtop = fmaxf(mtop, __shfl_xor(mtop, 32, 64));
     // Output rows: this lane holds heads 4*grp + r of O.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -370,6 +377,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         const float lr = __shfl(ltot, h, 64);
         const float le = __shfl(lex, h, 64);
         const float mr = __shfl(m_used, h, 64);
+        const float mt = __shfl(mtop, h, 64);
         if (h >= G)
             continue;
         // a non-empty piece has a weight >= 1 (its max score is at or above
@@ -381,8 +389,15 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 out.o[(size_t)h * out.o_stride + 16 * t + col] = oacc[t][r] * inv;
-            if (col == 0)
-                out.lse[(size_t)h * out.lse_stride] = lse;
+            if (col == 0) {
+                if (out.l) {  // m/l/o triple: the piece's max score and l relative to it
+                    // (the reference max trails the max by at most 2^8: no overflow)
+                    out.lse[(size_t)h * out.lse_stride] = any ? mt * kLn2 : -INFINITY;
+                    out.l[(size_t)h * out.lse_stride] = any ? le * fast_exp2(mr - mt) : 0.f;
+                } else {
+                    out.lse[(size_t)h * out.lse_stride] = lse;
+                }
+            }
         } else {
             const size_t rowid = (size_t)b * a.heads_q + (size_t)kvh * G + h;
 #pragma unroll
@@ -410,13 +425,19 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
     const long t0 = (long)split * a.split_len;
     const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
     const int G = a.heads_q / a.heads_kv;
-    PieceOut out{nullptr, nullptr, 0, 0};
+    PieceOut out{nullptr, nullptr, 0, 0, nullptr};
     if (a.o_part) {
         const size_t row0 = (size_t)b * a.heads_q + (size_t)kvh * G;  // first head of the group
-        out.o = a.o_part + (row0 * a.num_splits + split) * D;
-        out.lse = a.lse_part + row0 * a.num_splits + split;
+        const size_t first = row0 * a.num_splits + split;
+        out.o = a.o_part + first * D;
         out.o_stride = a.num_splits * D;
         out.lse_stride = a.num_splits;
+        if (a.m_part) {
+            out.lse = a.m_part + first;
+            out.l = a.l_part + first;
+        } else {
+            out.lse = a.lse_part + first;
+        }
     }
     mfma_piece<DT, D>(a, (lds_char *)tile_buf, b, kvh, t0, t1, out);
 #endif  // __HIP_DEVICE_COMPILE__
@@ -439,7 +460,8 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
         const long long left = c.end - c.pos;
         const int plen = left < (long long)(n - c.t) ? (int)left : n - c.t;
         const int slot = w + c.rank;
-        const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G, D, 1};
+        const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G, D, 1,
+                           nullptr};
         mfma_piece<DT, D>(a, (lds_char *)tile_buf, c.b, c.x, c.t, (long)c.t + plen, out);
         if (c.t == 0 && threadIdx.x == 0) {
             const int last = balanced_owner(c.pos + n - 1, c.total, c.w_eff);

@@ -20,7 +20,8 @@
 // incremental form, o left unnormalised as in the block update of [P4]
 // §3.1); the rows of one head are merged in LDS with the same rule ([P4]
 // §3.2 merge lemma), and the split writes o = o_acc / l and S = m + log l
-// ([P3] §2.3.2-§2.3.3).
+// ([P3] §2.3.2-§2.3.3), or, in the m/l/o format, o with the split's max
+// score m and l = sum exp(s - m) ([P1] §2.4.1 direct form).
 //
 // Scores are kept in the log2 domain: q is pre-multiplied by scale*log2(e)
 // so every exponential is one v_exp_f32; the LSE is converted back to the
@@ -291,9 +292,9 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
 #pragma unroll
         for (int r = hh; r < kRows; r += HPW)
             M = fmaxf(M, sm_m[r]);
-        float out = 0.f, lse = -INFINITY;
+        float out = 0.f, lse = -INFINITY, Ls = 0.f;
         if (M != -INFINITY) {
-            float Ls = 0.f, Os = 0.f;
+            float Os = 0.f;
 #pragma unroll
             for (int r = hh; r < kRows; r += HPW) {
                 const float w = fast_exp2(sm_m[r] - M);
@@ -307,8 +308,14 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         if (a.o_part) {
             const size_t slot = rowid * a.num_splits + split;
             a.o_part[slot * D + dd] = out;
-            if (dd == 0)
-                a.lse_part[slot] = lse;
+            if (dd == 0) {
+                if (a.m_part) {  // m/l/o triple: the split's max score and l relative to it
+                    a.m_part[slot] = M == -INFINITY ? -INFINITY : M * kLn2;
+                    a.l_part[slot] = M == -INFINITY ? 0.f : Ls;
+                } else {
+                    a.lse_part[slot] = lse;
+                }
+            }
         } else {
             store_out(a.o, rowid * D + dd, out, a.out_dtype);
             if (dd == 0 && a.lse)

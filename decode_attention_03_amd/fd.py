@@ -30,7 +30,8 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 
 #: every symbol include/fd.h declares
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
-           "fd_decode_workspace_bytes", "fd_decode_split", "fd_combine", "fd_decode")
+           "fd_decode_workspace_bytes", "fd_decode_split", "fd_decode_split_mlo", "fd_combine",
+           "fd_combine_mlo", "fd_decode")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,8 +64,12 @@ def library() -> ctypes.CDLL:
         lib.fd_decode_workspace_bytes.restype = I
         lib.fd_decode_split.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P]
         lib.fd_decode_split.restype = I
+        lib.fd_decode_split_mlo.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P, P]
+        lib.fd_decode_split_mlo.restype = I
         lib.fd_combine.argtypes = [P, P, I, I, I, I, P, I, P, P]
         lib.fd_combine.restype = I
+        lib.fd_combine_mlo.argtypes = [P, P, P, I, I, I, I, P, I, P, P]
+        lib.fd_combine_mlo.restype = I
         lib.fd_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, P]
         lib.fd_decode.restype = I
         _lib = lib
@@ -182,6 +187,57 @@ def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, 
                                      heads_kv, n_max, d, _code(q.dtype), scale, num_splits,
                                      split_len, _ptr(o_part), _ptr(lse_part), _stream(q.device)))
     return o_part, lse_part
+
+
+def decode_split_mlo(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, scale=None,
+                     o_part=None, m_part=None, l_part=None):
+    """Split stage, m/l/o format: returns (o_part [batch, Hq, B, d], m_part
+    [batch, Hq, B], l_part [batch, Hq, B]), all float32."""
+    batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
+    if split_len == 0:
+        split_len = max(1, -(-n_max // num_splits))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    shape = (batch, heads_q, num_splits)
+    if o_part is None:
+        o_part = torch.empty((*shape, d), dtype=torch.float32, device=q.device)
+    if m_part is None:
+        m_part = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if l_part is None:
+        l_part = torch.empty(shape, dtype=torch.float32, device=q.device)
+    for name, t, want in (("o_part", o_part, (*shape, d)), ("m_part", m_part, shape),
+                          ("l_part", l_part, shape)):
+        _on_device(name, t, q.device)
+        if t.shape != want or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 {want}")
+    _check(library().fd_decode_split_mlo(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
+                                         heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
+                                         num_splits, split_len, _ptr(o_part), _ptr(m_part),
+                                         _ptr(l_part), _stream(q.device)))
+    return o_part, m_part, l_part
+
+
+def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return_lse=True):
+    """Combine stage, m/l/o format -> (o, lse)."""
+    if o_part.dim() != 4 or any(t.dtype != torch.float32 for t in (o_part, m_part, l_part)):
+        raise ValueError("o_part must be float32 [batch, Hq, B, d]; m_part, l_part float32 "
+                         "[batch, Hq, B]")
+    batch, heads_q, nb, d = o_part.shape
+    if m_part.shape != (batch, heads_q, nb) or l_part.shape != (batch, heads_q, nb):
+        raise ValueError("m_part / l_part shape does not match o_part")
+    dev = o_part.device
+    for name, t in (("o_part", o_part), ("m_part", m_part), ("l_part", l_part)):
+        _on_device(name, t, dev)
+    out_dtype = out_dtype or torch.float32
+    if o is None:
+        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    _on_device("o", o, dev)
+    if lse is not None:
+        _on_device("lse", lse, dev)
+    _check(library().fd_combine_mlo(_ptr(o_part), _ptr(m_part), _ptr(l_part), batch, heads_q, nb,
+                                    d, _ptr(o), _code(o.dtype), _ptr(lse), _stream(dev)))
+    return o, lse
 
 
 def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True):

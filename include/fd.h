@@ -29,6 +29,7 @@
  *            exp-sum; -inf for a sequence with no tokens (o is then 0).
  *   o_part   [batch, heads_q, num_splits, head_dim]  float32
  *   lse_part [batch, heads_q, num_splits]            float32
+ *   m_part, l_part [batch, heads_q, num_splits]      float32 (m/l/o format)
  *
  * Conventions shared by every entry point:
  *   - All pointers except the fd_choose_splits outputs are device pointers
@@ -118,12 +119,36 @@ int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *
                     int in_dtype, float scale, int num_splits, int split_len, float *o_part,
                     float *lse_part, void *stream);
 
+/* Split stage in the m/l/o format ([P1] §2.4.1 direct form; [P3] §2.2.1):
+ * for every (b, h, split i) over the same token range as fd_decode_split,
+ *   m_part[b,h,i] = m = max_j s_j             (natural-log domain, like lse)
+ *   l_part[b,h,i] = l = sum_j exp(s_j - m)
+ *   o_part[b,h,i,:] = sum_j exp(s_j - m) V_j / l,
+ * and (o, m, l) = (0, -inf, 0) for an empty range.  m + log l equals what
+ * fd_decode_split writes to lse_part.  Same arguments, conditions and errors
+ * as fd_decode_split, with m_part and l_part in place of lse_part. */
+int fd_decode_split_mlo(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                        int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                        int in_dtype, float scale, int num_splits, int split_len, float *o_part,
+                        float *m_part, float *l_part, void *stream);
+
 /* Combine stage ([P3] §2.3.4; [P1] §2.5 stage 2, a light reduction):
  *   S = log sum_i exp(lse_part[b,h,i]),  o[b,h,:] = sum_i exp(lse_part[b,h,i] - S) o_part[b,h,i,:]
  * Terms at -inf contribute nothing; if every term is -inf, o = 0 and S = -inf.
  * lse may be NULL.  num_splits >= 1. */
 int fd_combine(const float *o_part, const float *lse_part, int batch, int heads_q,
                int num_splits, int head_dim, void *o, int out_dtype, float *lse, void *stream);
+
+/* Combine stage for the m/l/o format ([P1] §2.4.2 and §2.5 stage 2; [P3]
+ * §2.2.2):
+ *   m_g = max_i m_part[b,h,i],  l_g = sum_i exp(m_part[b,h,i] - m_g) l_part[b,h,i],
+ *   o[b,h,:] = sum_i exp(m_part[b,h,i] - m_g) l_part[b,h,i] o_part[b,h,i,:] / l_g,
+ *   lse[b,h] = m_g + log l_g (may be NULL).
+ * Splits with m = -inf contribute nothing; if every split is empty, o = 0
+ * and lse = -inf.  Same conditions and errors as fd_combine. */
+int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part, int batch,
+                   int heads_q, int num_splits, int head_dim, void *o, int out_dtype, float *lse,
+                   void *stream);
 
 /* Whole decode step: split + combine.
  *   num_splits == 0 (automatic plan, split_len ignored):

@@ -152,6 +152,45 @@ def test_decode_split_validation(lib):
     assert "aligned" in msg
 
 
+def _split_mlo(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kv_lens=None, batch=1, hq=4, hkv=2, n=64, d=64, dt=fd.F32,
+             scale=0.125, B=4, L=16, o_part=FAKE, m_part=FAKE, l_part=FAKE)
+    a.update(kw)
+    return lib.fd_decode_split_mlo(a["q"], a["k"], a["v"], a["kv_lens"], a["batch"], a["hq"],
+                                   a["hkv"], a["n"], a["d"], a["dt"], a["scale"], a["B"], a["L"],
+                                   a["o_part"], a["m_part"], a["l_part"], None)
+
+
+def test_decode_split_mlo_validation(lib):
+    assert _split_mlo(lib, m_part=None) == fd.ERR_INVALID
+    assert _split_mlo(lib, l_part=None) == fd.ERR_INVALID
+    assert _split_mlo(lib, o_part=None) == fd.ERR_INVALID
+    assert _split_mlo(lib, q=None) == fd.ERR_INVALID
+    assert _split_mlo(lib, B=3) == fd.ERR_INVALID
+    assert _split_mlo(lib, d=80) == fd.ERR_UNSUPPORTED
+    assert _split_mlo(lib, m_part=FAKE + 2) == fd.ERR_UNSUPPORTED
+    assert _split_mlo(lib, l_part=FAKE + 1) == fd.ERR_UNSUPPORTED
+    assert _split_mlo(lib, o_part=FAKE + 4) == fd.ERR_UNSUPPORTED
+
+
+def _combine_mlo(lib, **kw):
+    a = dict(o_part=FAKE, m_part=FAKE, l_part=FAKE, batch=2, hq=4, B=3, d=128, o=FAKE,
+             out=fd.BF16, lse=None)
+    a.update(kw)
+    return lib.fd_combine_mlo(a["o_part"], a["m_part"], a["l_part"], a["batch"], a["hq"], a["B"],
+                              a["d"], a["o"], a["out"], a["lse"], None)
+
+
+def test_combine_mlo_validation(lib):
+    assert _combine_mlo(lib, m_part=None) == fd.ERR_INVALID
+    assert _combine_mlo(lib, l_part=None) == fd.ERR_INVALID
+    assert _combine_mlo(lib, o=None) == fd.ERR_INVALID
+    assert _combine_mlo(lib, B=0) == fd.ERR_INVALID
+    assert _combine_mlo(lib, d=32) == fd.ERR_UNSUPPORTED
+    assert _combine_mlo(lib, out=9) == fd.ERR_UNSUPPORTED
+    assert _combine_mlo(lib, m_part=FAKE + 2) == fd.ERR_UNSUPPORTED
+
+
 def _combine(lib, **kw):
     a = dict(o_part=FAKE, lse_part=FAKE, batch=2, hq=4, B=3, d=128, o=FAKE, out=fd.BF16, lse=None)
     a.update(kw)
@@ -161,6 +200,7 @@ def _combine(lib, **kw):
 
 def test_combine_validation(lib):
     assert _combine(lib, o_part=None) == fd.ERR_INVALID
+    assert _combine(lib, lse_part=None) == fd.ERR_INVALID
     assert _combine(lib, o=None) == fd.ERR_INVALID
     assert _combine(lib, B=0) == fd.ERR_INVALID
     assert _combine(lib, hq=0) == fd.ERR_INVALID
