@@ -238,6 +238,64 @@ def time_partial_formats(w: workloads.Workload, dev: torch.device, steps: int, w
     return out
 
 
+def time_paged(w: workloads.Workload, dev: torch.device, page_size: int, steps: int,
+               warmup: int) -> dict:
+    """fd_decode_paged on a workload laid out in pages of page_size tokens
+    (seeded page permutation), library plan, against the same step over the
+    contiguous cache.  Wall clock over `steps` steps; enough page-cache copies
+    that consecutive steps read different memory."""
+    inp = workloads.generate(w)
+    lens = inp["kv_lens"]  # None (every sequence full) as in the contiguous run
+    if lens is None and inp["max_kv_len"] % page_size:
+        raise ValueError("page_size must divide the cache length of a uniform workload")
+    pg = workloads.paginate(inp, page_size, seed=page_size)
+    kvb = workloads.kv_bytes(w, lens)
+    footprint = pg["k_pages"].numel() * pg["k_pages"].element_size() * 2
+    copies = 1 if footprint < (64 << 20) else max(2, min(16, math.ceil((1 << 30) / footprint) + 1))
+    q = inp["q"].to(dev)
+    kl = None if lens is None else lens.to(dev)
+    bt = pg["block_table"].to(dev)
+    pages = [(pg["k_pages"].to(dev), pg["v_pages"].to(dev)) for _ in range(copies)]
+    batch, hq, hkv, d = w.batch, w.heads_q, w.heads_kv, w.head_dim
+    ps, max_pages, num_pages = page_size, pg["max_pages"], pg["num_pages"]
+    B, L = (w.num_splits, 0) if w.num_splits else (0, 0)
+    if B:
+        L = fd._tile_split_len(max_pages * ps, B)
+    out_dt = workloads.TORCH_DTYPES[w.out_dtype]
+    o = torch.empty((batch, hq, d), dtype=out_dt, device=dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    need = fd.decode_workspace_bytes(batch, hq, hkv, max_pages * ps, d, q.dtype, kl is not None,
+                                     B, L)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    lib, P = fd.library(), ctypes.c_void_p
+    stream = torch.cuda.current_stream(dev)
+    sp = P(stream.cuda_stream)
+    code = {torch.float32: fd.F32, torch.float16: fd.F16, torch.bfloat16: fd.BF16}
+    kl_p = None if kl is None else P(kl.data_ptr())
+    args = [(P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(bt.data_ptr()), kl_p, batch,
+             hq, hkv, ps, max_pages, num_pages, d, code[q.dtype], code[out_dt],
+             ctypes.c_float(w.scale), B, L, P(o.data_ptr()), P(lse.data_ptr()), P(ws.data_ptr()),
+             need, sp) for k, v in pages]
+
+    def step(i):
+        rc = lib.fd_decode_paged(*args[i % copies])
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    del pages, q, kl, bt, o, lse, ws
+    return {"page_size": ps, "pages": num_pages, "us_per_step": round(us, 2),
+            "kv_GBps": round(kvb / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(kvb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     """The fp64 oracle on the host cores, on whole decode steps of the same
     workload, repeated until about budget_s seconds of wall time."""
@@ -398,6 +456,18 @@ def main() -> int:
         log(f"[bench] partial formats: {pf}")
         result["partial_formats"] = pf
         torch.cuda.empty_cache()
+        # the paged K/V cache (block-table indirection) on the headline and
+        # the ragged grouped workloads, 16-token pages
+        paged = {}
+        for c in (args.config, 4):
+            w = workloads.WORKLOADS[c]
+            r = time_paged(w, dev, 16, args.steps, args.warmup)
+            contiguous = (result if c == args.config else others[w.name])["us_per_step"]
+            r["contiguous_us_per_step"] = contiguous
+            paged[w.name] = r
+            log(f"[bench] paged {w.name}: {r}")
+            torch.cuda.empty_cache()
+        result["paged"] = paged
     print(json.dumps(result), flush=True)
     return 0
 

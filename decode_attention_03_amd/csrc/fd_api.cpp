@@ -113,6 +113,46 @@ int check_partition(int batch, int heads_q, int max_kv_len, int num_splits, int 
     return FD_OK;
 }
 
+// Paged K/V description, validated by check_paging.
+struct Paging {
+    const int32_t *block_table = nullptr;
+    int page_shift = 0, max_pages = 0, num_pages = 0;
+};
+
+int check_paging(const int32_t *block_table, int page_size, int max_pages, int num_pages,
+                 int heads_kv, int head_dim, int in_dtype, Paging *pg) {
+    if (!block_table)
+        return fail(FD_ERR_INVALID, "block_table is null");
+    if (!aligned4(block_table))
+        return fail(FD_ERR_UNSUPPORTED, "block_table must be 4-byte aligned");
+    if (max_pages < 1 || num_pages < 1)
+        return fail(FD_ERR_INVALID, "max_pages_per_seq (%d) and num_pages (%d) must be >= 1",
+                    max_pages, num_pages);
+    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)))
+        return fail(FD_ERR_UNSUPPORTED, "page_size %d must be a power of two in [16, 2^20]",
+                    page_size);
+    if ((long long)max_pages * page_size > 0x7fffffffLL)
+        return fail(FD_ERR_INVALID, "max_pages_per_seq * page_size exceeds the int range");
+    if (heads_kv >= 1 && head_dim_ok(head_dim) && dtype_ok(in_dtype) &&
+        (long long)page_size * heads_kv * head_dim * (long long)elem_bytes(in_dtype) >
+            (1LL << 31))
+        return fail(FD_ERR_UNSUPPORTED, "one page exceeds 2 GiB");
+    pg->block_table = block_table;
+    pg->page_shift = __builtin_ctz((unsigned)page_size);
+    pg->max_pages = max_pages;
+    pg->num_pages = num_pages;
+    return FD_OK;
+}
+
+void set_paging(fd::SplitArgs &a, const Paging *pg) {
+    if (!pg)
+        return;
+    a.block_table = pg->block_table;
+    a.page_shift = pg->page_shift;
+    a.max_pages = pg->max_pages;
+    a.num_pages = pg->num_pages;
+}
+
 int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     const int group = a.heads_q / a.heads_kv;
     hipError_t e;
@@ -286,7 +326,7 @@ namespace {
 int split_stage(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
                 int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype, float scale,
                 int num_splits, int split_len, float *o_part, float *lse_part, float *m_part,
-                float *l_part, void *stream) {
+                float *l_part, void *stream, const Paging *pg = nullptr) {
     int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
                                 in_dtype, scale);
     if (rc != FD_OK)
@@ -318,6 +358,7 @@ int split_stage(const void *q, const void *k, const void *v, const int32_t *kv_l
     a.lse_part = mlo ? nullptr : lse_part;
     a.m_part = m_part;
     a.l_part = l_part;
+    set_paging(a, pg);
     return launch_split(a, in_dtype, static_cast<hipStream_t>(stream));
 }
 
@@ -400,10 +441,15 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
     return FD_OK;
 }
 
-int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
-              int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
-              int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
-              void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The whole decode step, contiguous (pg null) or paged K/V.
+int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
+                int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
+                int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
+                void *workspace, size_t workspace_bytes, void *stream, const Paging *pg) {
     int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
                                 in_dtype, scale);
     if (rc != FD_OK)
@@ -450,6 +496,7 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
         a.balanced = 1;
         a.num_wgs = p.num_wgs;
         a.unit_desc = reinterpret_cast<int *>(ws + p.o_bytes + p.lse_bytes);
+        set_paging(a, pg);
         rc = launch_split(a, in_dtype, st);
         if (rc != FD_OK)
             return rc;
@@ -483,6 +530,9 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
     rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
     if (rc != FD_OK)
         return rc;
+    if (pg && split_len % 16 != 0)
+        return fail(FD_ERR_INVALID, "paged K/V needs split_len (%d) to be a multiple of 16",
+                    split_len);
 
     fd::SplitArgs a{};
     a.q = q;
@@ -498,6 +548,7 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
     a.split_len = split_len;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_dtype = out_dtype;
+    set_paging(a, pg);
 
     if (num_splits == 1) {  // one split per row: the split stage writes o and lse itself
         a.o = o;
@@ -522,6 +573,53 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
     if (e != hipSuccess)
         return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
+              int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
+              int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
+              void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_impl(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                       out_dtype, scale, num_splits, split_len, o, lse, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+int fd_decode_split_paged(const void *q, const void *k_pages, const void *v_pages,
+                          const int32_t *block_table, const int32_t *kv_lens, int batch,
+                          int heads_q, int heads_kv, int page_size, int max_pages_per_seq,
+                          int num_pages, int head_dim, int in_dtype, float scale, int num_splits,
+                          int split_len, float *o_part, float *lse_part, void *stream) {
+    Paging pg;
+    int rc = check_paging(block_table, page_size, max_pages_per_seq, num_pages, heads_kv,
+                          head_dim, in_dtype, &pg);
+    if (rc != FD_OK)
+        return rc;
+    if (split_len % 16 != 0)
+        return fail(FD_ERR_INVALID, "paged K/V needs split_len (%d) to be a multiple of 16",
+                    split_len);
+    return split_stage(q, k_pages, v_pages, kv_lens, batch, heads_q, heads_kv,
+                       max_pages_per_seq * page_size, head_dim, in_dtype, scale, num_splits,
+                       split_len, o_part, lse_part, nullptr, nullptr, stream, &pg);
+}
+
+int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *block_table, const int32_t *kv_lens, int batch, int heads_q,
+                    int heads_kv, int page_size, int max_pages_per_seq, int num_pages,
+                    int head_dim, int in_dtype, int out_dtype, float scale, int num_splits,
+                    int split_len, void *o, float *lse, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    Paging pg;
+    int rc = check_paging(block_table, page_size, max_pages_per_seq, num_pages, heads_kv,
+                          head_dim, in_dtype, &pg);
+    if (rc != FD_OK)
+        return rc;
+    return decode_impl(q, k_pages, v_pages, kv_lens, batch, heads_q, heads_kv,
+                       max_pages_per_seq * page_size, head_dim, in_dtype, out_dtype, scale,
+                       num_splits, split_len, o, lse, workspace, workspace_bytes, stream, &pg);
 }
 
 }  // extern "C"

@@ -41,6 +41,15 @@ struct SplitArgs {
     int balanced;
     int num_wgs;
     int *unit_desc;
+    // Paged K/V: k and v point at pages [num_pages, page_size, heads_kv, d];
+    // token t of sequence b sits in page block_table[b * max_pages + t /
+    // page_size], row t % page_size.  page_size = 1 << page_shift >= 16, so a
+    // 16-token tile never straddles two pages; max_kv_len = max_pages *
+    // page_size.  Table entries outside [0, num_pages) are clamped into it.
+    const int32_t *block_table;  // null: contiguous K/V
+    int page_shift;
+    int max_pages;
+    int num_pages;
     // Vector kernel only: waves per work-group (1 or 2).  Two waves share a
     // split (and merge in LDS) when the grid has fewer work-groups than the
     // GPU has wave slots, e.g. one split per row.

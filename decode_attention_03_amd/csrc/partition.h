@@ -7,19 +7,21 @@
 // stage 1; "adv04: Flash-Decoding" (mini-vllm-tutorial), §4).  With ragged
 // lengths, fixed splits leave the GPU's work-groups unevenly loaded, so for
 // ragged batches the library also offers a partition that gives every
-// work-group the same number of token rows.  It is still a split-K partition
+// work-group the same number of 16-token granules of K/V rows.  It is still a split-K partition
 // in the pages' sense: every (sequence, head) row's tokens are cut into
 // contiguous pieces, each piece yields an (o, LSE) pair, and the combine merges
 // a row's pieces ("FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法", §2.3.4;
 // the merge does not depend on where the cuts fall, §2.3.5).
 //
-// Definitions (all positions 64-bit):
+// Definitions (all positions 64-bit; a position is one granule of
+// kGranule = 16 tokens, so every piece starts on a 16-token tile boundary):
 //   unit u = b * hx + x: one (sequence b, head x) pair reading one KV head
 //            (hx = heads_kv for the grouped kernel, heads_q for the vector one);
-//   N_b    = kv_lens[b] clamped to [0, max_kv_len];
+//   N_b    = kv_lens[b] clamped to [0, max_kv_len], g_b = ceil(N_b / 16);
 //   the flattened space lists units in order, unit u covering positions
-//            [S_u, S_u + N_b) with S_u = hx * (N_0 + ... + N_{b-1}) + x * N_b;
-//   T      = hx * sum_b N_b, W_eff = min(num_wgs, T);
+//            [S_u, S_u + g_b) with S_u = hx * (g_0 + ... + g_{b-1}) + x * g_b;
+//            granule j of a unit is tokens [16 j, min(16 j + 16, N_b));
+//   T      = hx * sum_b g_b, W_eff = min(num_wgs, T);
 //   work-group w < W_eff covers [floor(w T / W_eff), floor((w+1) T / W_eff)),
 //            never empty; work-groups w >= W_eff do nothing;
 //   the piece of unit u handled by work-group w writes slot w + rank(u),
@@ -34,9 +36,16 @@
 
 namespace fd {
 
+constexpr int kGranule = 16;  // tokens per position of the balanced partition
+
 __device__ __forceinline__ int clamp_len(const int32_t *kv_lens, int b, int max_kv_len) {
     int n = kv_lens ? kv_lens[b] : max_kv_len;
     return n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+}
+
+// Granules of sequence b.
+__device__ __forceinline__ int granules(const int32_t *kv_lens, int b, int max_kv_len) {
+    return (clamp_len(kv_lens, b, max_kv_len) + kGranule - 1) / kGranule;
 }
 
 __device__ __forceinline__ long long wave_sum_ll(long long v) {
@@ -57,25 +66,36 @@ __device__ __forceinline__ long long wave_scan_ll(long long v, int lane) {
     return v;
 }
 
+// A wave-uniform value the compiler cannot prove uniform (it came through a
+// shuffle), moved to a scalar register so that addresses built from it stay
+// scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform(long long v) {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
 // Where one work-group's share of the flattened space starts.  Called by all
 // 64 lanes of the wave together; every result is the same on every lane.
 struct PieceCursor {
     long long pos, end;  // [pos, end): this work-group's positions
     long long total;     // T
     int w_eff;           // W_eff
-    int b, x, t;         // unit (b, x) and token t within it at `pos`
+    int b, x, t;         // unit (b, x) and granule t within it at `pos`
     int rank;            // rank of unit (b, x) among non-empty units
 };
 
 __device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch, int max_kv_len,
                                                int hx, int w, int num_wgs, PieceCursor &c) {
     const int lane = threadIdx.x & 63;
-    long long tok = 0;
+    long long gsum = 0;
     for (int base = 0; base < batch; base += 64) {
         const int i = base + lane;
-        tok += i < batch ? clamp_len(kv_lens, i, max_kv_len) : 0;
+        gsum += i < batch ? granules(kv_lens, i, max_kv_len) : 0;
     }
-    c.total = wave_sum_ll(tok) * hx;
+    c.total = uniform(wave_sum_ll(gsum) * hx);
     c.w_eff = c.total < num_wgs ? (int)c.total : num_wgs;
     if (w >= c.w_eff)
         return false;
@@ -86,7 +106,7 @@ __device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch
     int nonempty = 0;      // non-empty sequences before this chunk
     for (int base = 0; base < batch; base += 64) {
         const int i = base + lane;
-        const long long n = i < batch ? clamp_len(kv_lens, i, max_kv_len) : 0;
+        const long long n = i < batch ? granules(kv_lens, i, max_kv_len) : 0;
         const long long incl = wave_scan_ll(n, lane);
         const unsigned long long hit = __ballot(i < batch && before + hx * incl > c.pos);
         const unsigned long long ne = __ballot(n > 0);
@@ -95,11 +115,11 @@ __device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch
             const long long nb = __shfl(n, l, 64);
             const long long start = before + hx * (__shfl(incl, l, 64) - nb);
             const long long off = c.pos - start;
-            c.b = base + l;
-            c.x = (int)(off / nb);
-            c.t = (int)(off % nb);
+            c.b = uniform(base + l);
+            c.x = uniform((int)(off / nb));
+            c.t = uniform((int)(off % nb));
             const int ne_before = nonempty + __popcll(ne & ((1ull << l) - 1ull));
-            c.rank = ne_before * hx + c.x;
+            c.rank = uniform(ne_before * hx + c.x);
             return true;
         }
         before += hx * __shfl(incl, 63, 64);

@@ -159,7 +159,7 @@ struct PieceOut {
 // heads sharing it.  Called by the whole wave; t0 >= t1 writes (0, -inf).
 // (Device pass only: the body uses LDS address-space pointers and gfx950-only
 // builtins that the host pass cannot type.)
-template <int DT, int D>
+template <int DT, int D, bool PAGED>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
                                            long t0, long t1, const PieceOut &out) {
     using T = Tiles<D>;
@@ -200,10 +200,6 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             }
         }
         const size_t tok_stride = (size_t)a.heads_kv * T::ROW;
-        const size_t split_base =
-            (((size_t)b * a.max_kv_len + (size_t)t0) * a.heads_kv + kvh) * T::ROW;
-        const char *kbase = static_cast<const char *>(a.k) + split_base;
-        const char *vbase = static_cast<const char *>(a.v) + split_base;
         const int ntok = (int)(t1 - t0);
         constexpr int kStepTok = 16 * U;
         const int nsteps = (ntok + kStepTok - 1) / kStepTok;
@@ -218,22 +214,67 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         };
         const int lrow = lane / T::CPR;  // row within a row group
         const int lq = lane % T::CPR;    // logical chunk this lane carries
-        auto load_step = [&](int st, Stage &g) {
+        const size_t lane_off = (size_t)kvh * T::ROW + lq * 16;
+        // Paged K/V: the page of each of a step's U tiles, looked up one step
+        // ahead of the loads that use them (the loop below).  A tile is
+        // 16-aligned (so are t0 and the step start), so it lies in one page,
+        // also after its rows are clamped to the last valid token.
+        struct Pages {
+            int pg[U];
+        };
+        auto lookup = [&](int st, Pages &P) {
+            if constexpr (PAGED) {
+                const int sa = st < nsteps ? st : nsteps - 1;
+                const int first = sa * kStepTok;
+                const int last_rel = ntok - 1 - first;
+                // read through the constant address space: the table is never
+                // written by the kernel, and scalar loads keep it out of the
+                // in-order vector-load counter the K/V pipeline waits on
+                const __attribute__((address_space(4))) int32_t *bt =
+                    (const __attribute__((address_space(4))) int32_t *)a.block_table +
+                    (size_t)b * a.max_pages;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int rel = 16 * u < last_rel ? 16 * u : last_rel;
+                    P.pg[u] = bt[((int)t0 + first + rel) >> a.page_shift];  // clamped at use
+                }
+            }
+        };
+        auto load_step = [&](int st, const Pages &P, Stage &g) {
             const int sa = st < nsteps ? st : nsteps - 1;
             const int first = sa * kStepTok;
             const int last_rel = ntok - 1 - first;
-            const char *kb = kbase + (size_t)first * tok_stride + lq * 16;
-            const char *vb = vbase + (size_t)first * tok_stride + lq * 16;
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; ++u) {
+                // base of tile u: contiguous K/V, or the tile's page
+                const char *kb, *vb;
+                uint32_t pmask = 0xffffffffu;
+                if constexpr (!PAGED) {
+                    const size_t base =
+                        ((size_t)b * a.max_kv_len + (size_t)t0 + first) * tok_stride + lane_off;
+                    kb = static_cast<const char *>(a.k) + base;
+                    vb = static_cast<const char *>(a.v) + base;
+                } else {
+                    int pg = P.pg[u];
+                    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+                    const size_t base = ((size_t)pg << a.page_shift) * tok_stride + lane_off;
+                    kb = static_cast<const char *>(a.k) + base;
+                    vb = static_cast<const char *>(a.v) + base;
+                    pmask = (1u << a.page_shift) - 1u;
+                }
 #pragma unroll
                 for (int j = 0; j < T::IPT; ++j) {
                     int rel = 16 * u + j * T::RPI + lrow;
                     rel = rel < last_rel ? rel : last_rel;
-                    const size_t off = (size_t)rel * tok_stride;
+                    // row within the base: the step-relative token, or the
+                    // token's row within its page
+                    const uint32_t row =
+                        PAGED ? ((uint32_t)((int)t0 + first + rel) & pmask) : (uint32_t)rel;
+                    const uint32_t off = row * (uint32_t)tok_stride;
                     g.k[u][j] = ld128<1>(kb + off);
                     g.v[u][j] = ld128<1>(vb + off);
                 }
+            }
         };
         // Write a step's rows into the LDS tiles, chunks swizzled per row.
         auto stage = [&](const Stage &g) {
@@ -341,16 +382,21 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         // step's reads.
         Frags f;
         Stage ga, gb;
+        Pages pa, pb;
         const int npairs = nsteps >> 1;
-        load_step(0, ga);
+        lookup(0, pa);
+        load_step(0, pa, ga);
+        lookup(1, pb);
         for (int pr = 0; pr < npairs; ++pr) {
             const int st = 2 * pr;
-            load_step(st + 1, gb);
+            load_step(st + 1, pb, gb);
+            lookup(st + 2, pa);
             __builtin_amdgcn_sched_barrier(0);
             stage(ga);
             fetch(tb, f);
             compute_step(st, f);
-            load_step(st + 2, ga);
+            load_step(st + 2, pa, ga);
+            lookup(st + 3, pb);
             __builtin_amdgcn_sched_barrier(0);
             stage(gb);
             fetch(tb, f);
@@ -413,7 +459,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
 
 // Fixed splits: work-group -> (b, KV head, split), KV head fastest; split i
 // covers [i*L, min((i+1)*L, N_b)).
-template <int DT, int D>
+template <int DT, int D, bool PAGED>
 __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
@@ -439,14 +485,14 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
             out.lse = a.lse_part + first;
         }
     }
-    mfma_piece<DT, D>(a, (lds_char *)tile_buf, b, kvh, t0, t1, out);
+    mfma_piece<DT, D, PAGED>(a, (lds_char *)tile_buf, b, kvh, t0, t1, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 // Token-balanced partition (partition.h): work-group w walks its share of the
 // flattened (sequence, KV head, token) space piece by piece; the piece of unit
 // u goes to slot w + rank(u) of the slot arrays (o [slot][G][d], LSE [slot][G]).
-template <int DT, int D>
+template <int DT, int D, bool PAGED>
 __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
@@ -455,16 +501,19 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
     PieceCursor c;
     if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c))
         return;
-    int n = clamp_len(a.kv_lens, c.b, a.max_kv_len);
+    int n = clamp_len(a.kv_lens, c.b, a.max_kv_len);  // tokens of the current sequence
+    int ng = (n + kGranule - 1) / kGranule;            // and its granules
     while (true) {
         const long long left = c.end - c.pos;
-        const int plen = left < (long long)(n - c.t) ? (int)left : n - c.t;
+        const int plen = left < (long long)(ng - c.t) ? (int)left : ng - c.t;  // granules
         const int slot = w + c.rank;
         const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G, D, 1,
                            nullptr};
-        mfma_piece<DT, D>(a, (lds_char *)tile_buf, c.b, c.x, c.t, (long)c.t + plen, out);
+        const long t0 = (long)c.t * kGranule;
+        const long t1 = (long)(c.t + plen) * kGranule < n ? (long)(c.t + plen) * kGranule : n;
+        mfma_piece<DT, D, PAGED>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, out);
         if (c.t == 0 && threadIdx.x == 0) {
-            const int last = balanced_owner(c.pos + n - 1, c.total, c.w_eff);
+            const int last = balanced_owner(c.pos + ng - 1, c.total, c.w_eff);
             const size_t u = (size_t)c.b * a.heads_kv + c.x;
             a.unit_desc[2 * u] = slot;
             a.unit_desc[2 * u + 1] = last - w + 1;
@@ -483,6 +532,7 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
             } while (n == 0 && c.b < a.batch);
             if (n == 0)
                 break;  // not reached: positions remain, so a non-empty sequence follows
+            ng = (n + kGranule - 1) / kGranule;
         }
     }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -518,12 +568,18 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         const size_t want = (size_t)lds / (FD_MFMA_WG_PER_CU + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
     }
-    if (a.balanced)
-        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D>), dim3((unsigned)grid), dim3(64), pad,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((split_mfma_kernel<DT, D>), dim3((unsigned)grid), dim3(64), pad, stream,
-                           a);
+    const dim3 g((unsigned)grid), blk(64);
+    if (a.balanced) {
+        if (a.block_table)
+            hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, true>), g, blk, pad, stream, a);
+        else
+            hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, false>), g, blk, pad, stream, a);
+    } else {
+        if (a.block_table)
+            hipLaunchKernelGGL((split_mfma_kernel<DT, D, true>), g, blk, pad, stream, a);
+        else
+            hipLaunchKernelGGL((split_mfma_kernel<DT, D, false>), g, blk, pad, stream, a);
+    }
     return hipGetLastError();
 }
 

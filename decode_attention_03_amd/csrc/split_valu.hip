@@ -102,7 +102,7 @@ __device__ __forceinline__ void unpack_row(const uint32_t *w, float *f) {
         unpack_word<DT>(w[j], f + j * L::PW);
 }
 
-template <int DT, int D, int THREADS, int HPW, int LPR>
+template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED>
 __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     using L = Layout<DT, D, LPR>;
     constexpr int EPL = L::EPL;
@@ -166,12 +166,10 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         }
         // K/V addressing: a uniform (scalar) base per step plus a 32-bit
         // per-lane byte offset (token slot, head, lane), so the loads use the
-        // SGPR-base form.  One token's row over all heads is at most 16 MiB
-        // (checked on the host), so every offset below fits in 32 bits.
+        // SGPR-base form.  One token's row over all heads is at most 16 MiB,
+        // and a page at most 2 GiB (both checked on the host), so every offset
+        // below fits in 32 bits.
         const size_t tok_stride = (size_t)a.heads_kv * L::ROW_BYTES;
-        const size_t split_base = ((size_t)b * a.max_kv_len + (size_t)t0) * tok_stride;
-        const char *kbase = static_cast<const char *>(a.k) + split_base;
-        const char *vbase = static_cast<const char *>(a.v) + split_base;
         const uint32_t stride32 = (uint32_t)tok_stride;
         const uint32_t lane_off = (uint32_t)kvh * (uint32_t)L::ROW_BYTES + lane_byte;
         const int ntok = (int)(t1 - t0);
@@ -179,22 +177,71 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         const int nsteps = (ntok + kStepTok - 1) / kStepTok;
 
         uint32_t kw[U][WORDS], vw[U][WORDS];
+        // Paged K/V: the pages of a step's 16-token tiles, looked up one step
+        // ahead of the loads that use them (the loop below), so the table
+        // read's latency hides behind a step of arithmetic.  t0 and the step
+        // start are multiples of min(16, kStepTok), so each slot group of TPS
+        // tokens lies in one tile, hence in one page, also after clamping to
+        // the last valid token.
+        constexpr int NTILE = kStepTok >= 16 ? kStepTok / 16 : 1;
+        struct Pages {
+            int pg[NTILE];
+        };
+        auto lookup = [&](int st, Pages &P) {
+            if constexpr (PAGED) {
+                const int sa = st < nsteps ? st : nsteps - 1;
+                const int first = sa * kStepTok;
+                const int last_rel = ntok - 1 - first;
+                // read through the constant address space: the table is never
+                // written by the kernel, and scalar loads keep it out of the
+                // in-order vector-load counter the K/V pipeline waits on
+                const __attribute__((address_space(4))) int32_t *bt =
+                    (const __attribute__((address_space(4))) int32_t *)a.block_table +
+                    (size_t)b * a.max_pages;
+#pragma unroll
+                for (int j = 0; j < NTILE; ++j) {
+                    const int rel = 16 * j < last_rel ? 16 * j : last_rel;
+                    P.pg[j] = bt[((int)t0 + first + rel) >> a.page_shift];  // clamped at use
+                }
+            }
+        };
         // Step `st` covers tokens t0 + st*TPS*U + u*TPS + tslot.  Slots past
         // the end re-read the last valid token (always in bounds) and are
         // masked, and a step past the last one re-reads the last step.
-        auto load_step = [&](int st, uint32_t (*kd)[WORDS], uint32_t (*vd)[WORDS]) {
+        auto load_step = [&](int st, const Pages &P, uint32_t (*kd)[WORDS],
+                             uint32_t (*vd)[WORDS]) {
             const int sa = st < nsteps ? st : nsteps - 1;
             const int first = sa * kStepTok;
             const int last_rel = ntok - 1 - first;
-            const char *kb = kbase + (size_t)first * tok_stride;
-            const char *vb = vbase + (size_t)first * tok_stride;
+            if constexpr (!PAGED) {
+                const size_t base = ((size_t)b * a.max_kv_len + (size_t)t0 + first) * tok_stride;
+                const char *kb = static_cast<const char *>(a.k) + base;
+                const char *vb = static_cast<const char *>(a.v) + base;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                int rel = u * TPS + tslot;
-                rel = rel < last_rel ? rel : last_rel;
-                const uint32_t off = (uint32_t)rel * stride32 + lane_off;
-                load_row<DT, D, LPR>(kb + off, kd[u]);
-                load_row<DT, D, LPR>(vb + off, vd[u]);
+                for (int u = 0; u < U; ++u) {
+                    int rel = u * TPS + tslot;
+                    rel = rel < last_rel ? rel : last_rel;
+                    const uint32_t off = (uint32_t)rel * stride32 + lane_off;
+                    load_row<DT, D, LPR>(kb + off, kd[u]);
+                    load_row<DT, D, LPR>(vb + off, vd[u]);
+                }
+            } else {
+                const size_t page_stride = tok_stride << a.page_shift;
+                const uint32_t pmask = (1u << a.page_shift) - 1u;
+                const int t_first = (int)t0 + first;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int j = kStepTok >= 16 ? (u * TPS) / 16 : 0;
+                    int rel = u * TPS + tslot;
+                    rel = rel < last_rel ? rel : last_rel;
+                    const uint32_t off =
+                        ((uint32_t)(t_first + rel) & pmask) * stride32 + lane_off;
+                    int pg = P.pg[j];
+                    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+                    const size_t pbase = (size_t)pg * page_stride;
+                    load_row<DT, D, LPR>(static_cast<const char *>(a.k) + pbase + off, kd[u]);
+                    load_row<DT, D, LPR>(static_cast<const char *>(a.v) + pbase + off, vd[u]);
+                }
             }
         };
         // One step of arithmetic on the K/V words of step `st`.
@@ -259,13 +306,18 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         // for the step being computed.
         uint32_t kx[U][WORDS], vx[U][WORDS];
         const int npairs = nsteps >> 1;
-        load_step(0, kw, vw);
+        Pages pa, pb;
+        lookup(0, pa);
+        load_step(0, pa, kw, vw);
+        lookup(1, pb);
         for (int pr = 0; pr < npairs; ++pr) {
             const int st = 2 * pr;
-            load_step(st + 1, kx, vx);
+            load_step(st + 1, pb, kx, vx);
+            lookup(st + 2, pa);
             __builtin_amdgcn_sched_barrier(0);
             compute_step(st, kw, vw);
-            load_step(st + 2, kw, vw);
+            load_step(st + 2, pa, kw, vw);
+            lookup(st + 3, pb);
             __builtin_amdgcn_sched_barrier(0);
             compute_step(st + 1, kx, vx);
         }
@@ -341,12 +393,12 @@ int lds_per_cu() {
     return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-template <int DT, int D, int THREADS, int HPW, int LPR>
+template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED>
 hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
     constexpr int kRows = THREADS / LPR;
     constexpr size_t kStatic = sizeof(float) * (size_t)(kRows * D + 2 * kRows);
     const long grid = (long)a.batch * (a.heads_q / HPW) * a.num_splits;
-    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR>;
+    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR, PAGED>;
     size_t pad = 0;
     const int lds = lds_per_cu();
     if (wg_per_cu > 0 && lds > 0) {
@@ -378,9 +430,14 @@ constexpr int lanes_per_row() {
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     constexpr int LPR = lanes_per_row<DT, D>();
+    if (a.block_table) {
+        if (a.valu_waves == 2)
+            return launch_cfg<DT, D, 128, 1, LPR, true>(a, kWavesPerCU / 2, stream);
+        return launch_cfg<DT, D, 64, 1, LPR, true>(a, kWavesPerCU, stream);
+    }
     if (a.valu_waves == 2)
-        return launch_cfg<DT, D, 128, 1, LPR>(a, kWavesPerCU / 2, stream);
-    return launch_cfg<DT, D, 64, 1, LPR>(a, kWavesPerCU, stream);
+        return launch_cfg<DT, D, 128, 1, LPR, false>(a, kWavesPerCU / 2, stream);
+    return launch_cfg<DT, D, 64, 1, LPR, false>(a, kWavesPerCU, stream);
 }
 
 template <int DT>

@@ -31,7 +31,7 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 #: every symbol include/fd.h declares
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
            "fd_decode_workspace_bytes", "fd_decode_split", "fd_decode_split_mlo", "fd_combine",
-           "fd_combine_mlo", "fd_decode")
+           "fd_combine_mlo", "fd_decode", "fd_decode_split_paged", "fd_decode_paged")
 
 _lock = threading.Lock()
 _lib = None
@@ -72,6 +72,12 @@ def library() -> ctypes.CDLL:
         lib.fd_combine_mlo.restype = I
         lib.fd_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, P]
         lib.fd_decode.restype = I
+        lib.fd_decode_split_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P,
+                                              P, P]
+        lib.fd_decode_split_paged.restype = I
+        lib.fd_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, P,
+                                        P, S, P]
+        lib.fd_decode_paged.restype = I
         _lib = lib
         return lib
 
@@ -290,4 +296,82 @@ def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len:
                                n_max, d, _code(q.dtype), _code(o.dtype), scale, num_splits,
                                split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
                                _stream(dev)))
+    return o, lse
+
+
+def _tile_split_len(n: int, num_splits: int) -> int:
+    """ceil(n / num_splits) rounded up to whole 16-token tiles (paged K/V needs it)."""
+    per = -(-n // num_splits)
+    return max(16, -(-per // 16) * 16)
+
+
+def _paged_shapes(q, k_pages, v_pages, block_table, kv_lens):
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("expected q [batch, heads_q, d] and K/V pages "
+                         "[num_pages, page_size, heads_kv, d]")
+    batch, heads_q, d = q.shape
+    num_pages, page_size, heads_kv, kd = k_pages.shape
+    if kd != d:
+        raise ValueError(f"q {tuple(q.shape)} and K pages {tuple(k_pages.shape)} disagree")
+    if q.dtype != k_pages.dtype or v_pages.dtype != k_pages.dtype:
+        raise TypeError("q, K and V must share one dtype")
+    dev = q.device
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("block_table", block_table)):
+        _on_device(name, t, dev)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("block_table must be int32 [batch, max_pages_per_seq]")
+    if kv_lens is not None:
+        _on_device("kv_lens", kv_lens, dev)
+        if kv_lens.dtype != torch.int32 or kv_lens.shape != (batch,):
+            raise ValueError("kv_lens must be int32 [batch]")
+    return batch, heads_q, heads_kv, page_size, block_table.shape[1], num_pages, d
+
+
+def decode_split_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, num_splits: int,
+                       split_len: int = 0, scale=None, o_part=None, lse_part=None):
+    """Split stage over a paged K/V cache -> (o_part, lse_part), as decode_split."""
+    batch, heads_q, heads_kv, ps, max_pages, num_pages, d = _paged_shapes(
+        q, k_pages, v_pages, block_table, kv_lens)
+    if split_len == 0:
+        split_len = _tile_split_len(max_pages * ps, num_splits)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if o_part is None:
+        o_part = torch.empty((batch, heads_q, num_splits, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((batch, heads_q, num_splits), dtype=torch.float32, device=q.device)
+    _on_device("o_part", o_part, q.device)
+    _on_device("lse_part", lse_part, q.device)
+    _check(library().fd_decode_split_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
+        heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), scale, num_splits, split_len,
+        _ptr(o_part), _ptr(lse_part), _stream(q.device)))
+    return o_part, lse_part
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, scale=None,
+                 num_splits: int = 0, split_len: int = 0, out_dtype=None,
+                 return_lse: bool = True, workspace=None, o=None, lse=None):
+    """Whole decode step over a paged K/V cache -> (o, lse or None), as decode."""
+    batch, heads_q, heads_kv, ps, max_pages, num_pages, d = _paged_shapes(
+        q, k_pages, v_pages, block_table, kv_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = out_dtype or q.dtype
+    dev = q.device
+    if num_splits > 0 and split_len == 0:
+        split_len = _tile_split_len(max_pages * ps, num_splits)
+    if o is None:
+        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    need = decode_workspace_bytes(batch, heads_q, heads_kv, max_pages * ps, d, q.dtype,
+                                  kv_lens is not None, num_splits, split_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _on_device("o", o, dev)
+    _check(library().fd_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
+        heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), _code(o.dtype), scale, num_splits,
+        split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, lse

@@ -175,6 +175,39 @@ def custom(batch, heads_q, heads_kv, head_dim, max_kv_len, dtype="f32", seed=0, 
     return w, inp
 
 
+def paginate(inp: dict, page_size: int, seed: int = 0, spare_pages: int = 3) -> dict:
+    """Lay a generated workload's K/V out as a paged cache (data movement only).
+
+    Logical page j of sequence b (tokens [j*page_size, (j+1)*page_size)) goes to
+    a physical page drawn from a seeded permutation; only the pages a sequence's
+    length needs get one.  Returns k_pages / v_pages [num_pages, page_size,
+    heads_kv, d], block_table int32 [batch, max_pages] (entries past a
+    sequence's pages are -1, never read), num_pages.  Physical pages nobody
+    owns (spare_pages of them, scattered) hold NaN, so a stray read shows.
+    """
+    k, v, lens = inp["k"], inp["v"], inp["kv_lens"]
+    batch, n_max, heads_kv, d = k.shape
+    max_pages = max(1, -(-n_max // page_size))
+    eff = [n_max] * batch if lens is None else [min(max(int(x), 0), n_max) for x in lens]
+    need = [-(-n // page_size) for n in eff]
+    num_pages = sum(need) + spare_pages
+    perm = torch.randperm(num_pages, generator=_gen(seed, "pages", page_size)).tolist()
+    table = torch.full((batch, max_pages), -1, dtype=torch.int32)
+    k_pages = torch.full((num_pages, page_size, heads_kv, d), float("nan"), dtype=k.dtype)
+    v_pages = torch.full_like(k_pages, float("nan"))
+    nxt = 0
+    for b in range(batch):
+        for j in range(need[b]):
+            p = perm[nxt]
+            nxt += 1
+            table[b, j] = p
+            t0, t1 = j * page_size, min((j + 1) * page_size, n_max)
+            k_pages[p, : t1 - t0] = k[b, t0:t1]
+            v_pages[p, : t1 - t0] = v[b, t0:t1]
+    return {"k_pages": k_pages, "v_pages": v_pages, "block_table": table,
+            "num_pages": num_pages, "page_size": page_size, "max_pages": max_pages}
+
+
 def kv_bytes(w: Workload, kv_lens) -> int:
     """Bytes of K and V a decode step must read: sum_b N_b * heads_kv * d * 2 * elem."""
     elem = torch.tensor([], dtype=TORCH_DTYPES[w.dtype]).element_size()

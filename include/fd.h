@@ -175,6 +175,38 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
               int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Paged K/V cache ([P2] §5: the kernel follows a block table over
+ * non-contiguous pages instead of gathering them first; [P4] §7.1: the page
+ * offsets cost an index lookup).  Same operation as fd_decode_split /
+ * fd_decode, with K and V in pages:
+ *   k_pages, v_pages [num_pages, page_size, heads_kv, head_dim]  in_dtype
+ *   block_table      [batch, max_pages_per_seq] int32 (device): token t of
+ *                    sequence b is row t % page_size of page
+ *                    block_table[b][t / page_size].
+ *   kv_lens          as above, clamped to [0, max_pages_per_seq * page_size];
+ *                    NULL: every sequence has max_pages_per_seq * page_size.
+ * page_size is a power of two in [16, 2^20] (a 16-token tile never straddles
+ * two pages); one page is at most 2 GiB.  Only the first ceil(N_b /
+ * page_size) entries of a table row are read; an entry outside
+ * [0, num_pages) is clamped into it (memory stays in bounds, that sequence's
+ * result is then meaningless).  split_len must be a multiple of 16 (the
+ * automatic plan's is).  Workspace: fd_decode_workspace_bytes with max_kv_len
+ * = max_pages_per_seq * page_size.  Extra errors: FD_ERR_INVALID for a null
+ * block_table, max_pages_per_seq or num_pages < 1, or split_len % 16 != 0;
+ * FD_ERR_UNSUPPORTED for page_size or page bytes out of range. */
+int fd_decode_split_paged(const void *q, const void *k_pages, const void *v_pages,
+                          const int32_t *block_table, const int32_t *kv_lens, int batch,
+                          int heads_q, int heads_kv, int page_size, int max_pages_per_seq,
+                          int num_pages, int head_dim, int in_dtype, float scale, int num_splits,
+                          int split_len, float *o_part, float *lse_part, void *stream);
+
+int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                    const int32_t *block_table, const int32_t *kv_lens, int batch, int heads_q,
+                    int heads_kv, int page_size, int max_pages_per_seq, int num_pages,
+                    int head_dim, int in_dtype, int out_dtype, float scale, int num_splits,
+                    int split_len, void *o, float *lse, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -191,6 +191,36 @@ def test_combine_mlo_validation(lib):
     assert _combine_mlo(lib, m_part=FAKE + 2) == fd.ERR_UNSUPPORTED
 
 
+def _paged(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, kv_lens=None, batch=2, hq=4, hkv=2, ps=16,
+             max_pages=4, num_pages=8, d=64, dt=fd.BF16, out=fd.BF16, scale=0.125, B=2, L=32,
+             o=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.fd_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["kv_lens"], a["batch"],
+                               a["hq"], a["hkv"], a["ps"], a["max_pages"], a["num_pages"],
+                               a["d"], a["dt"], a["out"], a["scale"], a["B"], a["L"], a["o"],
+                               a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_paged_validation(lib):
+    assert _paged(lib, bt=None) == fd.ERR_INVALID
+    assert _paged(lib, bt=FAKE + 2) == fd.ERR_UNSUPPORTED
+    assert _paged(lib, ps=24) == fd.ERR_UNSUPPORTED      # not a power of two
+    assert _paged(lib, ps=8) == fd.ERR_UNSUPPORTED       # below one 16-token tile
+    assert _paged(lib, max_pages=0) == fd.ERR_INVALID
+    assert _paged(lib, num_pages=0) == fd.ERR_INVALID
+    assert _paged(lib, L=40) == fd.ERR_INVALID          # split_len not a multiple of 16
+    assert _paged(lib, max_pages=1 << 27, ps=1 << 10) == fd.ERR_INVALID  # > int range
+    assert _paged(lib, ps=1 << 20, hkv=2, hq=4, d=256, dt=fd.F32) == fd.ERR_UNSUPPORTED
+    assert _paged(lib, q=None) == fd.ERR_INVALID
+    out = lib.fd_decode_split_paged(FAKE, FAKE, FAKE, None, None, 2, 4, 2, 16, 4, 8, 64, fd.BF16,
+                                    0.125, 2, 32, FAKE, FAKE, None)
+    assert out == fd.ERR_INVALID
+    out = lib.fd_decode_split_paged(FAKE, FAKE, FAKE, FAKE, None, 2, 4, 2, 16, 4, 8, 64, fd.BF16,
+                                    0.125, 2, 24, FAKE, FAKE, None)
+    assert out == fd.ERR_INVALID
+
+
 def _combine(lib, **kw):
     a = dict(o_part=FAKE, lse_part=FAKE, batch=2, hq=4, B=3, d=128, o=FAKE, out=fd.BF16, lse=None)
     a.update(kw)
