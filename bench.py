@@ -296,6 +296,85 @@ def time_paged(w: workloads.Workload, dev: torch.device, page_size: int, steps: 
             "hbm_frac": round(kvb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+CASCADE = workloads.Workload("cascade_gqa_bf16_b16_hq64_hkv8_d128_prefix16384_suffix512_4096",
+                             batch=16, heads_q=64, heads_kv=8, head_dim=128, max_kv_len=4096,
+                             dtype="bf16", out_dtype="bf16", seed=8, ragged=(512, 4096))
+CASCADE_PREFIX = 16384
+
+
+def time_cascade(steps: int, warmup: int, dev: torch.device) -> dict:
+    """Shared-prefix decode (fd_decode_cascade: one prefix copy for the batch)
+    against fd_decode over the materialised per-sequence caches (prefix +
+    suffix each).  Wall clock over `steps` steps, several input copies so that
+    consecutive steps read different memory (within a step the prefix is
+    shared by design)."""
+    w = CASCADE
+    c = workloads.cascade(w, CASCADE_PREFIX)
+    cc = workloads.cascade_concat(c)
+    lens = c["suffix_lens"]
+    row = w.heads_kv * w.head_dim * 2 * 2  # K+V bytes of one token, all KV heads
+    logical = int(cc["kv_lens"].sum()) * row      # what the sequences attend over
+    unique = (CASCADE_PREFIX + int(lens.sum())) * row  # distinct K/V in the cascade
+    lib, P = fd.library(), ctypes.c_void_p
+    sp = P(torch.cuda.current_stream(dev).cuda_stream)
+    batch, hq, hkv, d = w.batch, w.heads_q, w.heads_kv, w.head_dim
+    q = c["q"].to(dev)
+    o = torch.empty((batch, hq, d), dtype=q.dtype, device=dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+
+    def region(run, copies):
+        for i in range(warmup):
+            run(i % copies)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(i % copies)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    def check(rc):
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    # cascade
+    footprint = unique
+    copies = max(2, min(16, math.ceil((1 << 30) / footprint) + 1))
+    sl = lens.to(dev)
+    bufs = [tuple(c[n].to(dev) for n in ("k_prefix", "v_prefix", "k_suffix", "v_suffix"))
+            for _ in range(copies)]
+    need = fd.cascade_workspace_bytes(batch, hq, hkv, CASCADE_PREFIX, c["max_suffix_len"], d,
+                                      q.dtype, True)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    cargs = [(P(q.data_ptr()), P(kp.data_ptr()), P(vp.data_ptr()), CASCADE_PREFIX,
+              P(ks.data_ptr()), P(vs.data_ptr()), P(sl.data_ptr()), batch, hq, hkv,
+              c["max_suffix_len"], d, fd.BF16, fd.BF16, ctypes.c_float(w.scale),
+              P(o.data_ptr()), P(lse.data_ptr()), P(ws.data_ptr()), need, sp)
+             for kp, vp, ks, vs in bufs]
+    us_c = region(lambda i: check(lib.fd_decode_cascade(*cargs[i])), copies)
+    del bufs, cargs, ws
+    torch.cuda.empty_cache()
+    # plain decode over the materialised caches
+    copies_p = max(2, min(16, math.ceil((1 << 30) / logical) + 1))
+    kl = cc["kv_lens"].to(dev)
+    pbufs = [(cc["k"].to(dev), cc["v"].to(dev)) for _ in range(copies_p)]
+    need = fd.decode_workspace_bytes(batch, hq, hkv, cc["max_kv_len"], d, q.dtype, True)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    pargs = [(P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()), P(kl.data_ptr()), batch, hq,
+              hkv, cc["max_kv_len"], d, fd.BF16, fd.BF16, ctypes.c_float(w.scale), 0, 0,
+              P(o.data_ptr()), P(lse.data_ptr()), P(ws.data_ptr()), need, sp)
+             for k, v in pbufs]
+    us_p = region(lambda i: check(lib.fd_decode(*pargs[i])), copies_p)
+    del pbufs, pargs, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "prefix_len": CASCADE_PREFIX,
+            "suffix_tokens": int(lens.sum()), "cascade_us_per_step": round(us_c, 2),
+            "materialised_us_per_step": round(us_p, 2), "speedup": round(us_p / us_c, 3),
+            "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+            "cascade_unique_GBps": round(unique / (us_c * 1e-6) / 1e9, 1),
+            "cascade_logical_GBps": round(logical / (us_c * 1e-6) / 1e9, 1),
+            "materialised_GBps": round(logical / (us_p * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     """The fp64 oracle on the host cores, on whole decode steps of the same
     workload, repeated until about budget_s seconds of wall time."""
@@ -468,6 +547,10 @@ def main() -> int:
             log(f"[bench] paged {w.name}: {r}")
             torch.cuda.empty_cache()
         result["paged"] = paged
+        # shared-prefix decode against the same step over materialised caches
+        casc = time_cascade(args.steps, args.warmup, dev)
+        log(f"[bench] cascade: {casc}")
+        result["cascade"] = casc
     print(json.dumps(result), flush=True)
     return 0
 

@@ -383,9 +383,136 @@ int check_combine(const float *o_part, int batch, int heads_q, int num_splits, i
     return FD_OK;
 }
 
+// Cascade plan: fixed splits for the shared prefix (B_p, uniform length) and
+// for the suffixes (B_s, ragged when suffix_lens is given); the partial buffer
+// holds B_p + B_s slots per row, prefix first.
+struct CascadePlan {
+    int bp = 0, lp = 0, bs = 1, ls = 1;
+    size_t o_bytes = 0, bytes = 0;
+};
+
+int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_suffix_len,
+                 int head_dim, int in_dtype, bool has_lens, CascadePlan *p) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || prefix_len < 0 || max_suffix_len < 0 ||
+        heads_q % heads_kv)
+        return fail(FD_ERR_INVALID,
+                    "bad sizes (batch=%d heads_q=%d heads_kv=%d prefix_len=%d max_suffix_len=%d)",
+                    batch, heads_q, heads_kv, prefix_len, max_suffix_len);
+    if (!head_dim_ok(head_dim) || !dtype_ok(in_dtype))
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
+                    in_dtype);
+    int rc;
+    if (prefix_len > 0) {
+        rc = fd_choose_splits(batch, heads_q, heads_kv, prefix_len, head_dim, in_dtype, 0, 0,
+                              &p->bp, &p->lp);
+        if (rc != FD_OK)
+            return rc;
+    }
+    if (max_suffix_len > 0) {
+        rc = fd_choose_splits(batch, heads_q, heads_kv, max_suffix_len, head_dim, in_dtype,
+                              has_lens, 0, &p->bs, &p->ls);
+        if (rc != FD_OK)
+            return rc;
+    }
+    if ((long long)p->bp + p->bs > kMaxSplits)
+        return fail(FD_ERR_INVALID, "cascade needs more than %d splits per row", kMaxSplits);
+    const size_t rows = (size_t)batch * heads_q * (size_t)(p->bp + p->bs);
+    p->o_bytes = round256(rows * head_dim * sizeof(float));
+    p->bytes = p->o_bytes + round256(rows * sizeof(float));
+    return FD_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fd_cascade_workspace_bytes(int batch, int heads_q, int heads_kv, int prefix_len,
+                               int max_suffix_len, int head_dim, int in_dtype,
+                               int has_suffix_lens, size_t *bytes) {
+    if (!bytes)
+        return fail(FD_ERR_INVALID, "null output pointer");
+    *bytes = 0;
+    CascadePlan p;
+    int rc = cascade_plan(batch, heads_q, heads_kv, prefix_len, max_suffix_len, head_dim,
+                          in_dtype, has_suffix_lens != 0, &p);
+    if (rc != FD_OK)
+        return rc;
+    *bytes = p.bytes;
+    return FD_OK;
+}
+
+int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix, int prefix_len,
+                      const void *k_suffix, const void *v_suffix, const int32_t *suffix_lens,
+                      int batch, int heads_q, int heads_kv, int max_suffix_len, int head_dim,
+                      int in_dtype, int out_dtype, float scale, void *o, float *lse,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    CascadePlan p;
+    int rc = cascade_plan(batch, heads_q, heads_kv, prefix_len, max_suffix_len, head_dim,
+                          in_dtype, suffix_lens != nullptr, &p);
+    if (rc != FD_OK)
+        return rc;
+    rc = check_split_inputs(q, k_prefix, v_prefix, batch, heads_q, heads_kv, prefix_len,
+                            head_dim, in_dtype, scale);
+    if (rc != FD_OK)
+        return rc;
+    rc = check_split_inputs(q, k_suffix, v_suffix, batch, heads_q, heads_kv, max_suffix_len,
+                            head_dim, in_dtype, scale);
+    if (rc != FD_OK)
+        return rc;
+    if (!workspace || workspace_bytes < p.bytes)
+        return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+        return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    rc = check_combine(static_cast<const float *>(workspace), batch, heads_q, p.bp + p.bs,
+                       head_dim, o, out_dtype, lse);
+    if (rc != FD_OK)
+        return rc;
+    if (out_dtype != in_dtype && out_dtype != FD_F32)
+        return fail(FD_ERR_UNSUPPORTED, "out_dtype %d must equal in_dtype (%d) or be FD_F32",
+                    out_dtype, in_dtype);
+    float *o_part = static_cast<float *>(workspace);
+    float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.o_bytes);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    fd::SplitArgs a{};
+    a.q = q;
+    a.batch = batch;
+    a.heads_q = heads_q;
+    a.heads_kv = heads_kv;
+    a.head_dim = head_dim;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    a.part_stride = p.bp + p.bs;
+    if (p.bp > 0) {  // the shared prefix, read by every sequence
+        fd::SplitArgs pa = a;
+        pa.k = k_prefix;
+        pa.v = v_prefix;
+        pa.max_kv_len = prefix_len;
+        pa.shared_kv = 1;
+        pa.num_splits = p.bp;
+        pa.split_len = p.lp;
+        rc = launch_split(pa, in_dtype, st);
+        if (rc != FD_OK)
+            return rc;
+    }
+    fd::SplitArgs sa = a;  // each sequence's own suffix
+    sa.k = k_suffix;
+    sa.v = v_suffix;
+    sa.kv_lens = suffix_lens;
+    sa.max_kv_len = max_suffix_len;
+    sa.num_splits = p.bs;
+    sa.split_len = p.ls;
+    sa.part_offset = p.bp;
+    rc = launch_split(sa, in_dtype, st);
+    if (rc != FD_OK)
+        return rc;
+    hipError_t e = fd::launch_combine(o_part, lse_part, batch * heads_q, p.bp + p.bs, head_dim, o,
+                                      out_dtype, lse, st);
+    if (e != hipSuccess)
+        return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+    return FD_OK;
+}
 
 int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
                     int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,

@@ -50,6 +50,13 @@ struct SplitArgs {
     int page_shift;
     int max_pages;
     int num_pages;
+    // Shared cache: with shared_kv set every sequence reads the same K/V
+    // ([max_kv_len, heads_kv, d], batch stride 0), as the cascade's prefix.
+    int shared_kv;
+    // Fixed-split partial slots: split i of row r is slot r * part_stride +
+    // part_offset + i (part_stride 0 means num_splits), so two launches can
+    // fill one partial buffer.
+    int part_stride, part_offset;
     // Vector kernel only: waves per work-group (1 or 2).  Two waves share a
     // split (and merge in LDS) when the grid has fewer work-groups than the
     // GPU has wave slots, e.g. one split per row.

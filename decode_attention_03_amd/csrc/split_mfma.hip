@@ -250,8 +250,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 const char *kb, *vb;
                 uint32_t pmask = 0xffffffffu;
                 if constexpr (!PAGED) {
-                    const size_t base =
-                        ((size_t)b * a.max_kv_len + (size_t)t0 + first) * tok_stride + lane_off;
+                    const size_t seq = a.shared_kv ? 0 : (size_t)b * a.max_kv_len;
+                    const size_t base = (seq + (size_t)t0 + first) * tok_stride + lane_off;
                     kb = static_cast<const char *>(a.k) + base;
                     vb = static_cast<const char *>(a.v) + base;
                 } else {
@@ -474,10 +474,11 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
     PieceOut out{nullptr, nullptr, 0, 0, nullptr};
     if (a.o_part) {
         const size_t row0 = (size_t)b * a.heads_q + (size_t)kvh * G;  // first head of the group
-        const size_t first = row0 * a.num_splits + split;
+        const int pstride = a.part_stride ? a.part_stride : a.num_splits;
+        const size_t first = row0 * pstride + a.part_offset + split;
         out.o = a.o_part + first * D;
-        out.o_stride = a.num_splits * D;
-        out.lse_stride = a.num_splits;
+        out.o_stride = pstride * D;
+        out.lse_stride = pstride;
         if (a.m_part) {
             out.lse = a.m_part + first;
             out.l = a.l_part + first;

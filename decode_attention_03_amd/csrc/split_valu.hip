@@ -214,7 +214,8 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
             const int first = sa * kStepTok;
             const int last_rel = ntok - 1 - first;
             if constexpr (!PAGED) {
-                const size_t base = ((size_t)b * a.max_kv_len + (size_t)t0 + first) * tok_stride;
+                const size_t seq = a.shared_kv ? 0 : (size_t)b * a.max_kv_len;
+                const size_t base = (seq + (size_t)t0 + first) * tok_stride;
                 const char *kb = static_cast<const char *>(a.k) + base;
                 const char *vb = static_cast<const char *>(a.v) + base;
 #pragma unroll
@@ -358,7 +359,8 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         }
         const size_t rowid = (size_t)b * a.heads_q + hg * HPW + hh;
         if (a.o_part) {
-            const size_t slot = rowid * a.num_splits + split;
+            const size_t slot =
+                rowid * (a.part_stride ? a.part_stride : a.num_splits) + a.part_offset + split;
             a.o_part[slot * D + dd] = out;
             if (dd == 0) {
                 if (a.m_part) {  // m/l/o triple: the split's max score and l relative to it

@@ -31,7 +31,8 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 #: every symbol include/fd.h declares
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
            "fd_decode_workspace_bytes", "fd_decode_split", "fd_decode_split_mlo", "fd_combine",
-           "fd_combine_mlo", "fd_decode", "fd_decode_split_paged", "fd_decode_paged")
+           "fd_combine_mlo", "fd_decode", "fd_decode_split_paged", "fd_decode_paged",
+           "fd_cascade_workspace_bytes", "fd_decode_cascade")
 
 _lock = threading.Lock()
 _lib = None
@@ -78,6 +79,11 @@ def library() -> ctypes.CDLL:
         lib.fd_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, I, P, P,
                                         P, S, P]
         lib.fd_decode_paged.restype = I
+        lib.fd_cascade_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, ctypes.POINTER(S)]
+        lib.fd_cascade_workspace_bytes.restype = I
+        lib.fd_decode_cascade.argtypes = [P, P, P, I, P, P, P, I, I, I, I, I, I, I, F, P, P, P, S,
+                                          P]
+        lib.fd_decode_cascade.restype = I
         _lib = lib
         return lib
 
@@ -374,4 +380,60 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, scale=None,
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
         heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), _code(o.dtype), scale, num_splits,
         split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
+    return o, lse
+
+
+def cascade_workspace_bytes(batch: int, heads_q: int, heads_kv: int, prefix_len: int,
+                            max_suffix_len: int, head_dim: int, dtype: torch.dtype,
+                            has_suffix_lens: bool) -> int:
+    out = ctypes.c_size_t()
+    _check(library().fd_cascade_workspace_bytes(batch, heads_q, heads_kv, prefix_len,
+                                                max_suffix_len, head_dim, _code(dtype),
+                                                int(bool(has_suffix_lens)), ctypes.byref(out)))
+    return out.value
+
+
+def decode_cascade(q, k_prefix, v_prefix, k_suffix, v_suffix, suffix_lens=None, *, scale=None,
+                   out_dtype=None, return_lse: bool = True, workspace=None, o=None, lse=None):
+    """Shared-prefix decode -> (o, lse or None).
+
+    k_prefix / v_prefix [prefix_len, heads_kv, d] (one copy for the batch),
+    k_suffix / v_suffix [batch, max_suffix_len, heads_kv, d], suffix_lens int32
+    [batch] or None.  Equals decode() over each sequence's prefix + suffix.
+    """
+    if q.dim() != 3 or k_prefix.dim() != 3 or k_suffix.dim() != 4:
+        raise ValueError("expected q [batch, Hq, d], prefix [P, Hkv, d], suffix [batch, S, Hkv, d]")
+    if v_prefix.shape != k_prefix.shape or v_suffix.shape != k_suffix.shape:
+        raise ValueError("K and V shapes differ")
+    batch, heads_q, d = q.shape
+    prefix_len, heads_kv, pd = k_prefix.shape
+    sb, max_suffix_len, sh, sd = k_suffix.shape
+    if sb != batch or sh != heads_kv or pd != d or sd != d:
+        raise ValueError("q, prefix and suffix shapes disagree")
+    if any(t.dtype != q.dtype for t in (k_prefix, v_prefix, k_suffix, v_suffix)):
+        raise TypeError("q, K and V must share one dtype")
+    dev = q.device
+    for name, t in (("q", q), ("k_prefix", k_prefix), ("v_prefix", v_prefix),
+                    ("k_suffix", k_suffix), ("v_suffix", v_suffix)):
+        _on_device(name, t, dev)
+    if suffix_lens is not None:
+        _on_device("suffix_lens", suffix_lens, dev)
+        if suffix_lens.dtype != torch.int32 or suffix_lens.shape != (batch,):
+            raise ValueError("suffix_lens must be int32 [batch]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out_dtype = out_dtype or q.dtype
+    if o is None:
+        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    need = cascade_workspace_bytes(batch, heads_q, heads_kv, prefix_len, max_suffix_len, d,
+                                   q.dtype, suffix_lens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _on_device("o", o, dev)
+    _check(library().fd_decode_cascade(
+        _ptr(q), _ptr(k_prefix), _ptr(v_prefix), prefix_len, _ptr(k_suffix), _ptr(v_suffix),
+        _ptr(suffix_lens), batch, heads_q, heads_kv, max_suffix_len, d, _code(q.dtype),
+        _code(o.dtype), scale, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, lse

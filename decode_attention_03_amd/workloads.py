@@ -175,6 +175,38 @@ def custom(batch, heads_q, heads_kv, head_dim, max_kv_len, dtype="f32", seed=0, 
     return w, inp
 
 
+def cascade(w: Workload, prefix_len: int, poison_tail: bool = False) -> dict:
+    """Shared-prefix inputs: the workload w supplies q and each sequence's
+    suffix cache (its K/V and lengths); one prefix cache of prefix_len tokens
+    [prefix_len, heads_kv, d], drawn from the same recipe with its own seed,
+    is shared by every sequence."""
+    inp = generate(w, poison_tail=poison_tail)
+    pw = Workload(w.name + f"_prefix{prefix_len}", 1, w.heads_kv, w.heads_kv, w.head_dim,
+                  prefix_len, w.dtype, w.out_dtype, seed=w.seed + 100003, std=w.std)
+    pre = generate(pw) if prefix_len > 0 else None
+    shape = (prefix_len, w.heads_kv, w.head_dim)
+    empty = torch.empty(shape, dtype=TORCH_DTYPES[w.dtype])
+    return {"q": inp["q"], "k_prefix": pre["k"][0] if pre else empty,
+            "v_prefix": pre["v"][0] if pre else empty.clone(), "k_suffix": inp["k"],
+            "v_suffix": inp["v"], "suffix_lens": inp["kv_lens"],
+            "max_suffix_len": inp["max_kv_len"], "prefix_len": prefix_len}
+
+
+def cascade_concat(c: dict) -> dict:
+    """The cascade's inputs as one cache per sequence: prefix then suffix
+    (data movement only), in generate()'s layout, for references."""
+    k_pre, v_pre = c["k_prefix"], c["v_prefix"]
+    batch, s_max = c["k_suffix"].shape[:2]
+    p = c["prefix_len"]
+    lens = c["suffix_lens"]
+    n = [s_max] * batch if lens is None else [min(max(int(x), 0), s_max) for x in lens]
+    k = torch.cat([k_pre.unsqueeze(0).expand(batch, *k_pre.shape), c["k_suffix"]], dim=1)
+    v = torch.cat([v_pre.unsqueeze(0).expand(batch, *v_pre.shape), c["v_suffix"]], dim=1)
+    return {"q": c["q"], "k": k.contiguous(), "v": v.contiguous(),
+            "kv_lens": torch.tensor([p + x for x in n], dtype=torch.int32),
+            "max_kv_len": p + s_max}
+
+
 def paginate(inp: dict, page_size: int, seed: int = 0, spare_pages: int = 3) -> dict:
     """Lay a generated workload's K/V out as a paged cache (data movement only).
 

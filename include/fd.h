@@ -207,6 +207,33 @@ int fd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
                     int split_len, void *o, float *lse, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* Cascade (shared-prefix) decode ([P2] §5: the KV cache is handled in two
+ * layers, a stable prefix shared across requests and a per-request dynamic
+ * suffix).  Every sequence b attends over its prefix-then-suffix cache
+ *   [k_prefix[0 .. prefix_len), k_suffix[b][0 .. N_b)]
+ * and the result equals fd_decode over that concatenation: the prefix and
+ * the suffix are cut into fixed splits (one shared prefix copy, read by every
+ * sequence; B_p and B_s from fd_choose_splits, the suffix as ragged when
+ * suffix_lens is given), both stages write (o, LSE) pairs into one partial
+ * buffer of B_p + B_s splits per row, and fd_combine's kernel merges them
+ * ([P3] §2.3.4; the merge is order- and cut-independent, [P3] §2.3.5).
+ *   k_prefix, v_prefix [prefix_len, heads_kv, head_dim]            in_dtype
+ *   k_suffix, v_suffix [batch, max_suffix_len, heads_kv, head_dim] in_dtype
+ *   suffix_lens        [batch] int32 (device) or NULL (all max_suffix_len),
+ *                      clamped to [0, max_suffix_len].
+ * prefix_len and max_suffix_len may be 0 (then the pointers may be NULL).
+ * The workspace must hold fd_cascade_workspace_bytes(...) bytes.  Errors as
+ * fd_decode. */
+int fd_cascade_workspace_bytes(int batch, int heads_q, int heads_kv, int prefix_len,
+                               int max_suffix_len, int head_dim, int in_dtype,
+                               int has_suffix_lens, size_t *bytes);
+
+int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix, int prefix_len,
+                      const void *k_suffix, const void *v_suffix, const int32_t *suffix_lens,
+                      int batch, int heads_q, int heads_kv, int max_suffix_len, int head_dim,
+                      int in_dtype, int out_dtype, float scale, void *o, float *lse,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

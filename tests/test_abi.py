@@ -221,6 +221,28 @@ def test_paged_validation(lib):
     assert out == fd.ERR_INVALID
 
 
+def test_cascade_validation(lib):
+    """Argument checks that come before any device query."""
+    out = ctypes.c_size_t(7)
+    assert lib.fd_cascade_workspace_bytes(0, 4, 2, 10, 10, 64, fd.BF16, 0,
+                                          ctypes.byref(out)) == fd.ERR_INVALID
+    assert lib.fd_cascade_workspace_bytes(2, 3, 2, 10, 10, 64, fd.BF16, 0,
+                                          ctypes.byref(out)) == fd.ERR_INVALID
+    assert lib.fd_cascade_workspace_bytes(2, 4, 2, -1, 10, 64, fd.BF16, 0,
+                                          ctypes.byref(out)) == fd.ERR_INVALID
+    assert lib.fd_cascade_workspace_bytes(2, 4, 2, 10, 10, 96, fd.BF16, 0,
+                                          ctypes.byref(out)) == fd.ERR_UNSUPPORTED
+    assert lib.fd_cascade_workspace_bytes(2, 4, 2, 10, 10, 64, fd.BF16, 0,
+                                          None) == fd.ERR_INVALID
+    # empty prefix and suffix: one split per row, no device query needed
+    assert lib.fd_cascade_workspace_bytes(2, 4, 2, 0, 0, 64, fd.F32, 0,
+                                          ctypes.byref(out)) == fd.OK
+    assert out.value == 256 * (-(-(2 * 4 * 64 * 4) // 256)) + 256
+    rc = lib.fd_decode_cascade(FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 2, 4, 2, 0, 64, fd.F32,
+                               fd.F32, 0.125, FAKE, None, None, 0, None)
+    assert rc == fd.ERR_WORKSPACE
+
+
 def _combine(lib, **kw):
     a = dict(o_part=FAKE, lse_part=FAKE, batch=2, hq=4, B=3, d=128, o=FAKE, out=fd.BF16, lse=None)
     a.update(kw)
