@@ -156,7 +156,7 @@ void set_paging(fd::SplitArgs &a, const Paging *pg) {
 int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     const int group = a.heads_q / a.heads_kv;
     hipError_t e;
-    if (fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
+    if (a.prefix_qt > 0 || fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
         e = fd::launch_split_mfma(a, in_dtype, stream);
     } else {
         // two waves per work-group when one-wave work-groups would leave wave
@@ -388,8 +388,37 @@ int check_combine(const float *o_part, int batch, int heads_q, int num_splits, i
 // holds B_p + B_s slots per row, prefix first.
 struct CascadePlan {
     int bp = 0, lp = 0, bs = 1, ls = 1;
+    int prefix_qt = 0;  // > 0: the prefix runs on the shared-prefix matrix-core kernel
     size_t o_bytes = 0, bytes = 0;
 };
+
+constexpr int kMinPrefixSplitLen = 256;  // tokens
+
+// Prefix splits for the shared-prefix kernel: its work-groups per split are
+// heads_kv x (query tile groups), and the split count fills the GPU's wave
+// slots once.
+int prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int head_dim,
+                CascadePlan *p) {
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != FD_OK)
+        return rc;
+    const int tiles = (int)(((long long)batch * (heads_q / heads_kv) + 15) / 16);
+    int qt = fd::split_mfma_prefix_max_qt(head_dim);
+    while (qt > 1 && qt / 2 >= tiles)
+        qt /= 2;
+    const long long per_split = (long long)heads_kv * ((tiles + qt - 1) / qt);
+    long long b = ((long long)cus * kWorkGroupsPerCU + per_split - 1) / per_split;
+    const long long bmax = (prefix_len + kMinPrefixSplitLen - 1) / kMinPrefixSplitLen;
+    b = b > bmax ? bmax : b;
+    b = b > kMaxAutoSplits ? kMaxAutoSplits : (b < 1 ? 1 : b);
+    long long len = (prefix_len + b - 1) / b;
+    len = (len + 15) / 16 * 16;
+    p->bp = (int)((prefix_len + len - 1) / len);
+    p->lp = (int)len;
+    p->prefix_qt = qt;
+    return FD_OK;
+}
 
 int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_suffix_len,
                  int head_dim, int in_dtype, bool has_lens, CascadePlan *p) {
@@ -402,7 +431,11 @@ int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_s
         return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
                     in_dtype);
     int rc;
-    if (prefix_len > 0) {
+    if (prefix_len > 0 && fd::split_mfma_prefix_supported(in_dtype, head_dim)) {
+        rc = prefix_plan(batch, heads_q, heads_kv, prefix_len, head_dim, p);
+        if (rc != FD_OK)
+            return rc;
+    } else if (prefix_len > 0) {
         rc = fd_choose_splits(batch, heads_q, heads_kv, prefix_len, head_dim, in_dtype, 0, 0,
                               &p->bp, &p->lp);
         if (rc != FD_OK)
@@ -492,6 +525,7 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
         pa.shared_kv = 1;
         pa.num_splits = p.bp;
         pa.split_len = p.lp;
+        pa.prefix_qt = p.prefix_qt;
         rc = launch_split(pa, in_dtype, st);
         if (rc != FD_OK)
             return rc;

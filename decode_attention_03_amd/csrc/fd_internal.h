@@ -53,6 +53,10 @@ struct SplitArgs {
     // Shared cache: with shared_kv set every sequence reads the same K/V
     // ([max_kv_len, heads_kv, d], batch stride 0), as the cascade's prefix.
     int shared_kv;
+    // Shared prefix on the matrix cores (shared_kv set, bf16/f16): all batch *
+    // G queries of a KV head in tiles of 16, prefix_qt tiles per work-group
+    // (1, 2 or 4); 0 selects the ordinary kernels.
+    int prefix_qt;
     // Fixed-split partial slots: split i of row r is slot r * part_stride +
     // part_offset + i (part_stride 0 means num_splits), so two launches can
     // fill one partial buffer.
@@ -74,6 +78,8 @@ hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t strea
 // hipErrorNotSupported for shapes it does not cover (the caller then uses the
 // VALU kernel).
 bool split_mfma_supported(int in_dtype, int head_dim, int group);
+bool split_mfma_prefix_supported(int in_dtype, int head_dim);
+int split_mfma_prefix_max_qt(int head_dim);  // query tiles per work-group, 1..4
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.

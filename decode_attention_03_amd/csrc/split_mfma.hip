@@ -143,60 +143,90 @@ struct Tiles {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Where a piece's results go: the normalised o of group head h at
-// o + h * o_stride (fp32) and its LSE at lse[h * lse_stride] (m/l/o format:
-// m there and l at l[h * lse_stride]); with o null the piece is a whole row
-// and writes the final output (a.o, a.lse) itself.
+// Where a piece's results go.  Partial i of query row `row` (slot h of a
+// tile when `local`) is at index (row or h) * stride + off: o at o + index * D
+// (fp32, normalised), its LSE at lse[index] (m/l/o format: m there and l at
+// l[index]).  With o null the piece covers whole rows and writes the final
+// output (a.o, a.lse) itself.
 struct PieceOut {
     float *o;
-    float *lse;  // LSE, or m of the m/l/o format when `l` is set
-    int o_stride, lse_stride;
-    float *l;    // m/l/o format: l at l[h * lse_stride]; null for the LSE format
+    float *lse;
+    float *l;
+    int stride, off;
+    bool local;
+};
+
+// The query rows one work-group serves, in tiles of 16 (the matrix-core
+// width).  Standard: the G query heads of (sequence b, KV head kvh), one
+// tile.  Shared prefix: all batch * G queries of KV head kvh, tiles tile0,
+// tile0 + 1, ...  row() is the query's row in q [batch * heads_q, d], -1 for
+// an unused slot.
+struct QMap {
+    int base;   // standard: b * heads_q + kvh * G
+    int G;
+    int nq;     // shared prefix: batch * G; 0 in the standard form
+    int tile0;
+    int heads_q, kvh;
+    __device__ __forceinline__ int row(int qt, int i) const {
+        if (nq == 0)
+            return i < G ? base + i : -1;
+        const int qi = (tile0 + qt) * 16 + i;
+        return qi < nq ? (qi / G) * heads_q + kvh * G + qi % G : -1;
+    }
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
-// One piece: tokens [t0, t1) of KV head kvh of sequence b for the G query
-// heads sharing it.  Called by the whole wave; t0 >= t1 writes (0, -inf).
-// (Device pass only: the body uses LDS address-space pointers and gfx950-only
-// builtins that the host pass cannot type.)
-template <int DT, int D, bool PAGED>
+// One piece: tokens [t0, t1) of KV head kvh of sequence b (of the shared
+// cache when a.shared_kv) for QT tiles of 16 query rows (qm).  Every K/V tile
+// staged in LDS serves all QT tiles.  Called by the whole wave; t0 >= t1
+// writes (0, -inf).  (Device pass only: the body uses LDS address-space
+// pointers and gfx950-only builtins that the host pass cannot type.)
+template <int DT, int D, bool PAGED, int QT>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
-                                           long t0, long t1, const PieceOut &out) {
+                                           long t0, long t1, const QMap &qm,
+                                           const PieceOut &out) {
     using T = Tiles<D>;
     constexpr int NC = T::NC, NT = T::NT, U = T::U;
     using M = Mma<DT>;
 
     const int lane = threadIdx.x;
-    const int col = lane & 15;  // tile token (K reads) / head (S) / d column (O)
+    const int col = lane & 15;  // tile token (K reads) / query slot (S) / d column (O)
     const int grp = lane >> 4;  // 0..3
-    const int G = a.heads_q / a.heads_kv;
 
-    f32x4_t oacc[NT];  // O[head 4*grp + r][16*t + col]
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-        oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_used = -INFINITY;  // reference max of head `col` (log2 domain)
-    // This lane's share of l for head `col`, twice: over the weights as
+    f32x4_t oacc[QT][NT];  // O[slot 4*grp + r][16*t + col] of each tile
+    float m_used[QT];      // reference max of slot `col` (log2 domain)
+    // This lane's share of l for slot `col`, twice: over the weights as
     // rounded for the matrix core (o is normalised by it, so the weights
     // applied to V sum to exactly 1) and over the fp32 weights (the LSE uses
     // it, free of the rounding).
-    float lsum = 0.f;
-    float lexact = 0.f;
-    float mtrue = -INFINITY;  // max of this lane's scores (the m/l/o format's m)
+    float lsum[QT], lexact[QT];
+    float mtrue[QT];  // max of this lane's scores (the m/l/o format's m)
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            oacc[qt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_used[qt] = -INFINITY;
+        lsum[qt] = 0.f;
+        lexact[qt] = 0.f;
+        mtrue[qt] = -INFINITY;
+    }
 
     if (t0 < t1) {
-        // Q_g^T fragments: head `col` of the group, d = 32c + 8*grp + [0, 8).
-        u32x4 qf[NC];
-        {
-            const char *qrow = static_cast<const char *>(a.q) +
-                               ((size_t)b * a.heads_q + (size_t)kvh * G + col) * T::ROW;
+        // Q^T fragments: query slot `col` of each tile, d = 32c + 8*grp + [0, 8);
+        // unused slots stay zero (their rows are never written).
+        u32x4 qf[QT][NC];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const int qr = qm.row(qt, col);
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                qf[c] = u32x4{0u, 0u, 0u, 0u};
-            if (col < G) {  // heads past the group stay zero (their rows are never written)
+                qf[qt][c] = u32x4{0u, 0u, 0u, 0u};
+            if (qr >= 0) {
+                const char *qrow = static_cast<const char *>(a.q) + (size_t)qr * T::ROW;
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
-                    qf[c] = ld128<0>(qrow + c * 64 + grp * 16);
+                    qf[qt][c] = ld128<0>(qrow + c * 64 + grp * 16);
             }
         }
         const size_t tok_stride = (size_t)a.heads_kv * T::ROW;
@@ -320,57 +350,60 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         };
 
         auto compute_step = [&](int st, const Frags &f) {
-            // S^T tiles on the matrix cores, scaled into the log2 domain.
-            float x[U][4];
-            float mx = -INFINITY;  // max of this lane's tokens
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            for (int qt = 0; qt < QT; ++qt) {
+                // S^T tiles on the matrix cores, scaled into the log2 domain.
+                float x[U][4];
+                float mx = -INFINITY;  // max of this lane's tokens
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    s = M::s_tile(f.k[u][c], qf[c], s);
+                for (int u = 0; u < U; ++u) {
+                    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rel = st * kStepTok + 16 * u + 4 * grp + r;
-                    x[u][r] = rel < ntok ? s[r] * a.scale_log2 : -INFINITY;
-                    mx = fmaxf(mx, x[u][r]);
+                    for (int c = 0; c < NC; ++c)
+                        s = M::s_tile(f.k[u][c], qf[qt][c], s);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int rel = st * kStepTok + 16 * u + 4 * grp + r;
+                        x[u][r] = rel < ntok ? s[r] * a.scale_log2 : -INFINITY;
+                        mx = fmaxf(mx, x[u][r]);
+                    }
                 }
-            }
-            mtrue = fmaxf(mtrue, mx);
-            // The reference max of a head only has to bound its scores within
-            // 2^kRescaleGap, so the four lanes of a head synchronise (and O, l
-            // are rescaled) only when some lane's tokens outgrow it; in steady
-            // state this is a single ballot.
-            if (__ballot(mx > m_used + kRescaleGap)) {
-                float hm = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                hm = fmaxf(hm, __shfl_xor(hm, 32, 64));
-                const float m_new = fmaxf(m_used, hm);
-                const bool grow = m_new > m_used + kRescaleGap;  // same on a head's 4 lanes
-                const float alpha = grow ? fast_exp2(m_used - m_new) : 1.f;
-                if (grow)
-                    m_used = m_new;
-                lsum *= alpha;
-                lexact *= alpha;
+                mtrue[qt] = fmaxf(mtrue[qt], mx);
+                // The reference max of a slot only has to bound its scores
+                // within 2^kRescaleGap, so the four lanes of a slot synchronise
+                // (and O, l are rescaled) only when some lane's tokens outgrow
+                // it; in steady state this is a single ballot.
+                if (__ballot(mx > m_used[qt] + kRescaleGap)) {
+                    float hm = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                    hm = fmaxf(hm, __shfl_xor(hm, 32, 64));
+                    const float m_new = fmaxf(m_used[qt], hm);
+                    const bool grow = m_new > m_used[qt] + kRescaleGap;  // same on a slot's 4 lanes
+                    const float alpha = grow ? fast_exp2(m_used[qt] - m_new) : 1.f;
+                    if (grow)
+                        m_used[qt] = m_new;
+                    lsum[qt] *= alpha;
+                    lexact[qt] *= alpha;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float ar = __shfl(alpha, 4 * grp + r, 64);
+                    for (int r = 0; r < 4; ++r) {
+                        const float ar = __shfl(alpha, 4 * grp + r, 64);
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            oacc[qt][t][r] *= ar;
+                    }
+                }
+                const float mref = m_used[qt] == -INFINITY ? 0.f : m_used[qt];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float p[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        p[r] = fast_exp2(x[u][r] - mref);
+                    lexact[qt] += (p[0] + p[1]) + (p[2] + p[3]);
+                    const u32x2 pa = M::pack(p, &lsum[qt]);
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
-                        oacc[t][r] *= ar;
+                        oacc[qt][t] = M::pv_tile(pa, f.v[u][t], oacc[qt][t]);
                 }
-            }
-            const float mref = m_used == -INFINITY ? 0.f : m_used;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float p[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p[r] = fast_exp2(x[u][r] - mref);
-                lexact += (p[0] + p[1]) + (p[2] + p[3]);
-                const u32x2 pa = M::pack(p, &lsum);
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    oacc[t] = M::pv_tile(pa, f.v[u][t], oacc[t]);
             }
         };
 
@@ -409,48 +442,54 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         }
     }
 
-    // l of head `col`: the four lanes holding it each summed their tokens.
-    float ltot = lsum + __shfl_xor(lsum, 16, 64);
-    ltot += __shfl_xor(ltot, 32, 64);
-    float lex = lexact + __shfl_xor(lexact, 16, 64);
-    lex += __shfl_xor(lex, 32, 64);
-    float mtop = fmaxf(mtrue, __shfl_xor(mtrue, 16, 64));
-    mtop = fmaxf(mtop, __shfl_xor(mtop, 32, 64));
-    // Output rows: this lane holds heads 4*grp + r of O.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * grp + r;
-        const float lr = __shfl(ltot, h, 64);
-        const float le = __shfl(lex, h, 64);
-        const float mr = __shfl(m_used, h, 64);
-        const float mt = __shfl(mtop, h, 64);
-        if (h >= G)
-            continue;
-        // a non-empty piece has a weight >= 1 (its max score is at or above
-        // the reference), which rounds to >= 1: lr > 0 exactly when le > 0
-        const bool any = lr > 0.f;
-        const float inv = any ? 1.f / lr : 0.f;
-        const float lse = any ? (mr + fast_log2(le)) * kLn2 : -INFINITY;
-        if (out.o) {
+    for (int qt = 0; qt < QT; ++qt) {
+        // l of slot `col`: the four lanes holding it each summed their tokens.
+        float ltot = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
+        ltot += __shfl_xor(ltot, 32, 64);
+        float lex = lexact[qt] + __shfl_xor(lexact[qt], 16, 64);
+        lex += __shfl_xor(lex, 32, 64);
+        float mtop = fmaxf(mtrue[qt], __shfl_xor(mtrue[qt], 16, 64));
+        mtop = fmaxf(mtop, __shfl_xor(mtop, 32, 64));
+        // Output rows: this lane holds slots 4*grp + r of O.
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                out.o[(size_t)h * out.o_stride + 16 * t + col] = oacc[t][r] * inv;
-            if (col == 0) {
-                if (out.l) {  // m/l/o triple: the piece's max score and l relative to it
-                    // (the reference max trails the max by at most 2^8: no overflow)
-                    out.lse[(size_t)h * out.lse_stride] = any ? mt * kLn2 : -INFINITY;
-                    out.l[(size_t)h * out.lse_stride] = any ? le * fast_exp2(mr - mt) : 0.f;
-                } else {
-                    out.lse[(size_t)h * out.lse_stride] = lse;
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * grp + r;
+            const float lr = __shfl(ltot, h, 64);
+            const float le = __shfl(lex, h, 64);
+            const float mr = __shfl(m_used[qt], h, 64);
+            const float mt = __shfl(mtop, h, 64);
+            const int row = qm.row(qt, h);
+            if (row < 0)
+                continue;
+            // a non-empty piece has a weight >= 1 (its max score is at or
+            // above the reference), which rounds to >= 1: lr > 0 exactly when
+            // le > 0
+            const bool any = lr > 0.f;
+            const float inv = any ? 1.f / lr : 0.f;
+            const float lse = any ? (mr + fast_log2(le)) * kLn2 : -INFINITY;
+            if (out.o) {
+                const size_t idx = (size_t)(out.local ? h : row) * out.stride + out.off;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    out.o[idx * D + 16 * t + col] = oacc[qt][t][r] * inv;
+                if (col == 0) {
+                    if (out.l) {  // m/l/o triple: the piece's max score and l relative to it
+                        // (the reference max trails the max by at most 2^8: no overflow)
+                        out.lse[idx] = any ? mt * kLn2 : -INFINITY;
+                        out.l[idx] = any ? le * fast_exp2(mr - mt) : 0.f;
+                    } else {
+                        out.lse[idx] = lse;
+                    }
                 }
-            }
-        } else {
-            const size_t rowid = (size_t)b * a.heads_q + (size_t)kvh * G + h;
+            } else {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                store_out(a.o, rowid * D + 16 * t + col, oacc[t][r] * inv, a.out_dtype);
-            if (col == 0 && a.lse)
-                a.lse[rowid] = lse;
+                for (int t = 0; t < NT; ++t)
+                    store_out(a.o, (size_t)row * D + 16 * t + col, oacc[qt][t][r] * inv,
+                              a.out_dtype);
+                if (col == 0 && a.lse)
+                    a.lse[row] = lse;
+            }
         }
     }
 }
@@ -471,22 +510,47 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
     const long t0 = (long)split * a.split_len;
     const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
     const int G = a.heads_q / a.heads_kv;
-    PieceOut out{nullptr, nullptr, 0, 0, nullptr};
+    const QMap qm{b * a.heads_q + kvh * G, G, 0, 0, a.heads_q, kvh};
+    PieceOut out{nullptr, nullptr, nullptr, 0, 0, false};
     if (a.o_part) {
-        const size_t row0 = (size_t)b * a.heads_q + (size_t)kvh * G;  // first head of the group
-        const int pstride = a.part_stride ? a.part_stride : a.num_splits;
-        const size_t first = row0 * pstride + a.part_offset + split;
-        out.o = a.o_part + first * D;
-        out.o_stride = pstride * D;
-        out.lse_stride = pstride;
-        if (a.m_part) {
-            out.lse = a.m_part + first;
-            out.l = a.l_part + first;
-        } else {
-            out.lse = a.lse_part + first;
-        }
+        out.o = a.o_part;
+        out.stride = a.part_stride ? a.part_stride : a.num_splits;
+        out.off = a.part_offset + split;
+        out.lse = a.m_part ? a.m_part : a.lse_part;
+        out.l = a.m_part ? a.l_part : nullptr;
     }
-    mfma_piece<DT, D, PAGED>(a, (lds_char *)tile_buf, b, kvh, t0, t1, out);
+    mfma_piece<DT, D, PAGED, 1>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Shared prefix (cascade): all batch * G queries of a KV head read the same
+// prefix split, so a work-group serves QT tiles of 16 of them from each K/V
+// tile it stages, and the work-groups sharing one (KV head, split) unit are
+// given block indices congruent mod 8: blocks are dispatched round-robin over
+// the eight XCDs, so they run on one XCD and meet the unit's K/V in its L2.
+// blockIdx -> (xcd = idx % 8, slot = idx / 8); slot -> (unit / 8 within the
+// XCD, tile group j fastest); unit = (split, KV head), KV head fastest.
+template <int DT, int D, int QT>
+__global__ __launch_bounds__(64) void split_mfma_prefix_kernel(SplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
+    const int G = a.heads_q / a.heads_kv;
+    const int nq = a.batch * G;
+    const int groups = ((nq + 15) / 16 + QT - 1) / QT;  // tile groups per unit
+    const int xcd = blockIdx.x % 8;
+    const int slot = blockIdx.x / 8;
+    const int unit = (slot / groups) * 8 + xcd;
+    const int j = slot % groups;
+    if (unit >= a.heads_kv * a.num_splits)
+        return;
+    const int kvh = unit % a.heads_kv;
+    const int split = unit / a.heads_kv;
+    const long t0 = (long)split * a.split_len;
+    const long t1 = t0 + a.split_len < a.max_kv_len ? t0 + a.split_len : a.max_kv_len;
+    const QMap qm{0, G, nq, j * QT, a.heads_q, kvh};
+    PieceOut out{a.o_part, a.lse_part, nullptr, a.part_stride ? a.part_stride : a.num_splits,
+                 a.part_offset + split, false};
+    mfma_piece<DT, D, false, QT>(a, (lds_char *)tile_buf, 0, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -508,11 +572,12 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
         const long long left = c.end - c.pos;
         const int plen = left < (long long)(ng - c.t) ? (int)left : ng - c.t;  // granules
         const int slot = w + c.rank;
-        const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G, D, 1,
-                           nullptr};
+        const QMap qm{c.b * a.heads_q + c.x * G, G, 0, 0, a.heads_q, c.x};
+        const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G,
+                           nullptr, 1, 0, true};
         const long t0 = (long)c.t * kGranule;
         const long t1 = (long)(c.t + plen) * kGranule < n ? (long)(c.t + plen) * kGranule : n;
-        mfma_piece<DT, D, PAGED>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, out);
+        mfma_piece<DT, D, PAGED, 1>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
         if (c.t == 0 && threadIdx.x == 0) {
             const int last = balanced_owner(c.pos + ng - 1, c.total, c.w_eff);
             const size_t u = (size_t)c.b * a.heads_kv + c.x;
@@ -558,11 +623,25 @@ int lds_per_cu_mfma() {
 #define FD_MFMA_WG_PER_CU 2
 #endif
 
+// Query tiles per work-group of the shared-prefix kernel that fit in the
+// register file without spilling (every tile keeps its own Q fragments, O
+// accumulators and softmax state).
+template <int D>
+constexpr int prefix_max_qt() {
+    return D == 64 ? 4 : (D == 128 ? 2 : 1);
+}
+
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     constexpr size_t kStatic = (size_t)T::BUF;
-    const long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
+    long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
+    if (a.prefix_qt > 0) {  // shared prefix: (8-aligned units) x tile groups
+        const int tiles = (a.batch * (a.heads_q / a.heads_kv) + 15) / 16;
+        const long groups = (tiles + a.prefix_qt - 1) / a.prefix_qt;
+        const long units = (long)a.heads_kv * a.num_splits;
+        grid = (units + 7) / 8 * 8 * groups;
+    }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
     if (FD_MFMA_WG_PER_CU > 0 && lds > 0) {
@@ -570,7 +649,27 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         pad = want > kStatic ? want - kStatic : 0;
     }
     const dim3 g((unsigned)grid), blk(64);
-    if (a.balanced) {
+    if (a.prefix_qt > 0) {
+        if (a.prefix_qt > prefix_max_qt<D>())
+            return hipErrorInvalidValue;
+        if (a.prefix_qt == 1)
+            hipLaunchKernelGGL((split_mfma_prefix_kernel<DT, D, 1>), g, blk, pad, stream, a);
+        else if constexpr (prefix_max_qt<D>() >= 2) {
+            if (a.prefix_qt == 2)
+                hipLaunchKernelGGL((split_mfma_prefix_kernel<DT, D, 2>), g, blk, pad, stream, a);
+            else if constexpr (prefix_max_qt<D>() >= 4) {
+                if (a.prefix_qt == 4)
+                    hipLaunchKernelGGL((split_mfma_prefix_kernel<DT, D, 4>), g, blk, pad, stream,
+                                       a);
+                else
+                    return hipErrorInvalidValue;
+            } else {
+                return hipErrorInvalidValue;
+            }
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (a.balanced) {
         if (a.block_table)
             hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, true>), g, blk, pad, stream, a);
         else
@@ -595,6 +694,20 @@ hipError_t launch_dt(const SplitArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int split_mfma_prefix_max_qt(int head_dim) {
+    switch (head_dim) {
+    case 64: return prefix_max_qt<64>();
+    case 128: return prefix_max_qt<128>();
+    case 256: return prefix_max_qt<256>();
+    default: return 0;
+    }
+}
+
+bool split_mfma_prefix_supported(int in_dtype, int head_dim) {
+    return (in_dtype == kBF16 || in_dtype == kF16) &&
+           (head_dim == 64 || head_dim == 128 || head_dim == 256);
+}
 
 bool split_mfma_supported(int in_dtype, int head_dim, int group) {
     return (in_dtype == kBF16 || in_dtype == kF16) && group >= 2 && group <= kMaxGroup &&

@@ -58,6 +58,21 @@ def test_cascade_matches_concatenated_attention(gpu, dtype, group, d, prefix_len
     _check(f"cascade_{dtype}_G{group}_d{d}_P{prefix_len}", o, lse, ro, rl, dtype)
 
 
+@pytest.mark.parametrize("dtype,group,d,batch", [("f16", 4, 64, 40), ("bf16", 8, 128, 33),
+                                                 ("bf16", 1, 256, 19)])
+def test_cascade_many_requests(gpu, dtype, group, d, batch):
+    """Many requests per shared prefix: the prefix kernel's queries span many
+    16-query tiles (partial last tile), several tiles per work-group."""
+    w = workloads.Workload("cascade_many", batch=batch, heads_q=2 * group, heads_kv=2,
+                           head_dim=d, max_kv_len=700, dtype=dtype, out_dtype=dtype,
+                           seed=batch + d, ragged=(0, 700))
+    c = workloads.cascade(w, 3000, poison_tail=True)
+    o, lse = _run(gpu, c, w)
+    torch.cuda.synchronize()
+    ro, rl = _reference(c, w)
+    _check(f"cascade_many_{dtype}_G{group}_d{d}_b{batch}", o, lse, ro, rl, dtype)
+
+
 def test_cascade_edge_cases(gpu):
     """Empty suffixes, no suffix lengths given, and an empty prefix with empty
     suffixes (o = 0, lse = -inf)."""
