@@ -51,7 +51,25 @@ struct RowSource {
     const float *O;
     int count, s_stride, o_stride;
     const float *L;
+    // optional second segment (LSE format only): partials count .. count +
+    // count2 - 1 at S2[j * s_stride2] and O2 + j * o_stride2
+    const float *S2 = nullptr;
+    const float *O2 = nullptr;
+    int count2 = 0, s_stride2 = 0, o_stride2 = 0;
 };
+
+// LSE (or m) of partial i over both segments of a row.
+__device__ __forceinline__ float row_s(const RowSource &src, int i) {
+    return i < src.count ? src.S[(size_t)i * src.s_stride]
+                         : src.S2[(size_t)(i - src.count) * src.s_stride2];
+}
+
+// Column slice c (float4) of partial i over both segments of a row.
+__device__ __forceinline__ float4 row_o(const RowSource &src, int i, int c) {
+    const float *base = i < src.count ? src.O + (size_t)i * src.o_stride
+                                      : src.O2 + (size_t)(i - src.count) * src.o_stride2;
+    return reinterpret_cast<const float4 *>(base)[c];
+}
 
 template <int D, bool MLO = false>
 __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, void *o,
@@ -64,13 +82,13 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const float *S = src.S;
-    const int num_splits = src.count;
+    const int num_splits = src.count + src.count2;
     const int ss = src.s_stride;
 
     // S_max over the row
     float mx = -INFINITY;
     for (int i = tid; i < num_splits; i += kCombineThreads)
-        mx = fmaxf(mx, S[(size_t)i * ss]);
+        mx = fmaxf(mx, row_s(src, i));
     mx = wave_max(mx);
     if (lane == 0)
         red[wave] = mx;
@@ -86,7 +104,7 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
         float sum = 0.f;
         if (mx != -INFINITY)
             for (int i = tid; i < num_splits; i += kCombineThreads)
-                sum += fast_exp2((S[(size_t)i * ss] - mx) * kLog2e);
+                sum += fast_exp2((row_s(src, i) - mx) * kLog2e);
         sum = wave_sum(sum);
         if (lane == 0)
             red[wave] = sum;
@@ -97,7 +115,7 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
             sum += red[w];
         sg = mx == -INFINITY ? -INFINITY : mx + fast_log2(sum) * kLn2;
         for (int i = tid; i < num_splits; i += kCombineThreads)
-            weights[i] = mx == -INFINITY ? 0.f : fast_exp2((S[(size_t)i * ss] - sg) * kLog2e);
+            weights[i] = mx == -INFINITY ? 0.f : fast_exp2((row_s(src, i) - sg) * kLog2e);
     } else {
         // m/l/o ("FlashDecoding 数学推导" §2.4.2): m_g = max m_i (mx above),
         // l_g = sum_i exp(m_i - m_g) l_i, weights exp(m_i - m_g) l_i / l_g
@@ -130,8 +148,7 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
     // o = sum_i w_i o_i: thread (sp, c) takes splits sp, sp + SP, ... of slice c
     const int c = tid % V4;
     const int sp = tid / V4;
-    const float4 *col = reinterpret_cast<const float4 *>(src.O) + c;
-    const size_t os = (size_t)src.o_stride / 4;  // float4 stride between partials
+
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     auto add = [&](float w, float4 x) {
         // weight 0 (an empty split) contributes nothing, whatever the slot holds
@@ -142,17 +159,17 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
     };
     int i = sp;
     for (; i + 3 * SP < num_splits; i += 4 * SP) {
-        const float4 x0 = col[(size_t)i * os];
-        const float4 x1 = col[(size_t)(i + SP) * os];
-        const float4 x2 = col[(size_t)(i + 2 * SP) * os];
-        const float4 x3 = col[(size_t)(i + 3 * SP) * os];
+        const float4 x0 = row_o(src, i, c);
+        const float4 x1 = row_o(src, i + SP, c);
+        const float4 x2 = row_o(src, i + 2 * SP, c);
+        const float4 x3 = row_o(src, i + 3 * SP, c);
         add(weights[i], x0);
         add(weights[i + SP], x1);
         add(weights[i + 2 * SP], x2);
         add(weights[i + 3 * SP], x3);
     }
     for (; i < num_splits; i += SP)
-        add(weights[i], col[(size_t)i * os]);
+        add(weights[i], row_o(src, i, c));
     part[sp][4 * c + 0] = acc.x;
     part[sp][4 * c + 1] = acc.y;
     part[sp][4 * c + 2] = acc.z;
@@ -195,7 +212,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_mlo_kernel(
 
 // Token-balanced slots: row (b, h) of unit u = b * (heads_q / gsz) + h / gsz
 // reads slots first .. first + count - 1 of its unit's descriptor; a sequence
-// with no tokens has no descriptor and yields (0, -inf).
+// with no tokens has no descriptor and contributes nothing (alone: (0, -inf)).
+// A cascade adds the row's pre_count prefix partials in front.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_slots_kernel(SlotCombineArgs a) {
     extern __shared__ float weights[];  // max_count entries
@@ -204,12 +222,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_slots_kernel(SlotComb
     const int h = (int)(rowid % a.heads_q);
     const int g = h % a.gsz;
     const size_t u = (size_t)b * (a.heads_q / a.gsz) + h / a.gsz;
-    RowSource src{a.lse_slots, a.o_slots, 0, a.gsz, a.gsz * D, nullptr};
+    // first segment: the row's fixed partials (a cascade's prefix splits), if any
+    RowSource src{a.pre_lse + rowid * a.pre_count, a.pre_o + rowid * a.pre_count * D,
+                  a.pre_count, 1, D, nullptr};
+    src.S2 = a.lse_slots;
+    src.O2 = a.o_slots;
+    src.s_stride2 = a.gsz;
+    src.o_stride2 = a.gsz * D;
     if (clamp_len(a.kv_lens, b, a.max_kv_len) > 0) {
         const int first = a.unit_desc[2 * u];
-        src.count = a.unit_desc[2 * u + 1];
-        src.S = a.lse_slots + (size_t)first * a.gsz + g;
-        src.O = a.o_slots + ((size_t)first * a.gsz + g) * D;
+        src.count2 = a.unit_desc[2 * u + 1];
+        src.S2 = a.lse_slots + (size_t)first * a.gsz + g;
+        src.O2 = a.o_slots + ((size_t)first * a.gsz + g) * D;
     }
     combine_row<D>(src, rowid, a.o, a.out_dtype, a.lse, weights);
 }
@@ -262,7 +286,7 @@ hipError_t launch_combine_mlo(const float *o_part, const float *m_part, const fl
 }
 
 hipError_t launch_combine_slots(const SlotCombineArgs &c, hipStream_t stream) {
-    const size_t shmem = sizeof(float) * (size_t)c.max_count;
+    const size_t shmem = sizeof(float) * (size_t)(c.max_count + c.pre_count);
     const dim3 grid((unsigned)((size_t)c.batch * c.heads_q));
     switch (c.head_dim) {
     case 64:

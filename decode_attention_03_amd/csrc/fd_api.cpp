@@ -389,7 +389,13 @@ int check_combine(const float *o_part, int batch, int heads_q, int num_splits, i
 struct CascadePlan {
     int bp = 0, lp = 0, bs = 1, ls = 1;
     int prefix_qt = 0;  // > 0: the prefix runs on the shared-prefix matrix-core kernel
-    size_t o_bytes = 0, bytes = 0;
+    // ragged grouped suffixes: token-balanced partition (bal), its slots merged
+    // with the prefix partials by the slot combine; bs/ls unused then
+    bool balanced = false;
+    BalancedPlan bal;
+    size_t o_bytes = 0;    // partial o of the fixed splits (prefix, and suffix if not balanced)
+    size_t lse_bytes = 0;
+    size_t bytes = 0;      // whole workspace
 };
 
 constexpr int kMinPrefixSplitLen = 256;  // tokens
@@ -408,7 +414,7 @@ int prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int head_d
     while (qt > 1 && qt / 2 >= tiles)
         qt /= 2;
     const long long per_split = (long long)heads_kv * ((tiles + qt - 1) / qt);
-    long long b = ((long long)cus * kWorkGroupsPerCU + per_split - 1) / per_split;
+    long long b = ((long long)cus * fd::kPrefixWgPerCU + per_split - 1) / per_split;
     const long long bmax = (prefix_len + kMinPrefixSplitLen - 1) / kMinPrefixSplitLen;
     b = b > bmax ? bmax : b;
     b = b > kMaxAutoSplits ? kMaxAutoSplits : (b < 1 ? 1 : b);
@@ -441,7 +447,15 @@ int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_s
         if (rc != FD_OK)
             return rc;
     }
-    if (max_suffix_len > 0) {
+    p->balanced = balanced_applies(heads_q, heads_kv, max_suffix_len, head_dim, in_dtype, has_lens,
+                                   0);
+    if (p->balanced) {
+        rc = balanced_plan(batch, heads_q, heads_kv, max_suffix_len, head_dim, &p->bal);
+        if (rc != FD_OK)
+            return rc;
+        p->bs = 0;
+        p->ls = 0;
+    } else if (max_suffix_len > 0) {
         rc = fd_choose_splits(batch, heads_q, heads_kv, max_suffix_len, head_dim, in_dtype,
                               has_lens, 0, &p->bs, &p->ls);
         if (rc != FD_OK)
@@ -451,7 +465,8 @@ int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_s
         return fail(FD_ERR_INVALID, "cascade needs more than %d splits per row", kMaxSplits);
     const size_t rows = (size_t)batch * heads_q * (size_t)(p->bp + p->bs);
     p->o_bytes = round256(rows * head_dim * sizeof(float));
-    p->bytes = p->o_bytes + round256(rows * sizeof(float));
+    p->lse_bytes = round256(rows * sizeof(float));
+    p->bytes = p->o_bytes + p->lse_bytes + (p->balanced ? p->bal.total() : 0);
     return FD_OK;
 }
 
@@ -497,15 +512,16 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
                     workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace))
         return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-    rc = check_combine(static_cast<const float *>(workspace), batch, heads_q, p.bp + p.bs,
-                       head_dim, o, out_dtype, lse);
+    rc = check_combine(static_cast<const float *>(workspace), batch, heads_q,
+                       p.bp + p.bs > 0 ? p.bp + p.bs : 1, head_dim, o, out_dtype, lse);
     if (rc != FD_OK)
         return rc;
     if (out_dtype != in_dtype && out_dtype != FD_F32)
         return fail(FD_ERR_UNSUPPORTED, "out_dtype %d must equal in_dtype (%d) or be FD_F32",
                     out_dtype, in_dtype);
-    float *o_part = static_cast<float *>(workspace);
-    float *lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.o_bytes);
+    char *ws = static_cast<char *>(workspace);
+    float *o_part = reinterpret_cast<float *>(ws);
+    float *lse_part = reinterpret_cast<float *>(ws + p.o_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
     fd::SplitArgs a{};
     a.q = q;
@@ -529,6 +545,44 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
         rc = launch_split(pa, in_dtype, st);
         if (rc != FD_OK)
             return rc;
+    }
+    if (p.balanced) {  // ragged suffixes: token-balanced pieces, then one slot combine
+        char *bws = ws + p.o_bytes + p.lse_bytes;
+        fd::SplitArgs sa = a;
+        sa.k = k_suffix;
+        sa.v = v_suffix;
+        sa.kv_lens = suffix_lens;
+        sa.max_kv_len = max_suffix_len;
+        sa.part_stride = 0;
+        sa.o_part = reinterpret_cast<float *>(bws);
+        sa.lse_part = reinterpret_cast<float *>(bws + p.bal.o_bytes);
+        sa.balanced = 1;
+        sa.num_wgs = p.bal.num_wgs;
+        sa.unit_desc = reinterpret_cast<int *>(bws + p.bal.o_bytes + p.bal.lse_bytes);
+        rc = launch_split(sa, in_dtype, st);
+        if (rc != FD_OK)
+            return rc;
+        fd::SlotCombineArgs c{};
+        c.o_slots = sa.o_part;
+        c.lse_slots = sa.lse_part;
+        c.unit_desc = sa.unit_desc;
+        c.kv_lens = suffix_lens;
+        c.batch = batch;
+        c.heads_q = heads_q;
+        c.gsz = p.bal.gsz;
+        c.max_kv_len = max_suffix_len;
+        c.head_dim = head_dim;
+        c.max_count = p.bal.num_wgs;
+        c.o = o;
+        c.out_dtype = out_dtype;
+        c.lse = lse;
+        c.pre_o = o_part;
+        c.pre_lse = lse_part;
+        c.pre_count = p.bp;
+        hipError_t e = fd::launch_combine_slots(c, st);
+        if (e != hipSuccess)
+            return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
+        return FD_OK;
     }
     fd::SplitArgs sa = a;  // each sequence's own suffix
     sa.k = k_suffix;

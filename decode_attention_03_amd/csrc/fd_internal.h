@@ -15,6 +15,13 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // with about two waves per CU, each with ~16 KB of loads in flight.
 constexpr int kWavesPerCU = 2;
 
+// Resident work-groups per CU of the shared-prefix kernel: its K/V rows are
+// read by several work-groups each, so more of them in flight per CU pays.
+#ifndef FD_PREFIX_WG_PER_CU
+#define FD_PREFIX_WG_PER_CU 4
+#endif
+constexpr int kPrefixWgPerCU = FD_PREFIX_WG_PER_CU;
+
 // Everything one split-stage launch needs.  Shapes follow the public layouts:
 // q [batch, heads_q, d], K/V [batch, max_kv_len, heads_kv, d].
 struct SplitArgs {
@@ -104,6 +111,11 @@ struct SlotCombineArgs {
     void *o;
     int out_dtype;
     float *lse;
+    // optional fixed partials merged in front of every row's slots (a
+    // cascade's prefix): [batch * heads_q, pre_count, d] and [.., pre_count]
+    const float *pre_o;
+    const float *pre_lse;
+    int pre_count;
 };
 hipError_t launch_combine_slots(const SlotCombineArgs &c, hipStream_t stream);
 

@@ -178,10 +178,11 @@ struct QMap {
 #if defined(__HIP_DEVICE_COMPILE__)
 // One piece: tokens [t0, t1) of KV head kvh of sequence b (of the shared
 // cache when a.shared_kv) for QT tiles of 16 query rows (qm).  Every K/V tile
-// staged in LDS serves all QT tiles.  Called by the whole wave; t0 >= t1
+// staged in LDS serves all QT tiles.  K/V loads carry the non-temporal hint
+// (NTLOAD) unless other work-groups will read the same rows.  Called by the whole wave; t0 >= t1
 // writes (0, -inf).  (Device pass only: the body uses LDS address-space
 // pointers and gfx950-only builtins that the host pass cannot type.)
-template <int DT, int D, bool PAGED, int QT>
+template <int DT, int D, bool PAGED, int QT, int NTLOAD = 1>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
                                            long t0, long t1, const QMap &qm,
                                            const PieceOut &out) {
@@ -301,8 +302,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                     const uint32_t row =
                         PAGED ? ((uint32_t)((int)t0 + first + rel) & pmask) : (uint32_t)rel;
                     const uint32_t off = row * (uint32_t)tok_stride;
-                    g.k[u][j] = ld128<1>(kb + off);
-                    g.v[u][j] = ld128<1>(vb + off);
+                    g.k[u][j] = ld128<NTLOAD>(kb + off);
+                    g.v[u][j] = ld128<NTLOAD>(vb + off);
                 }
             }
         };
@@ -550,7 +551,8 @@ __global__ __launch_bounds__(64) void split_mfma_prefix_kernel(SplitArgs a) {
     const QMap qm{0, G, nq, j * QT, a.heads_q, kvh};
     PieceOut out{a.o_part, a.lse_part, nullptr, a.part_stride ? a.part_stride : a.num_splits,
                  a.part_offset + split, false};
-    mfma_piece<DT, D, false, QT>(a, (lds_char *)tile_buf, 0, kvh, t0, t1, qm, out);
+    // the unit's other work-groups read the same K/V: ordinary (temporal) loads
+    mfma_piece<DT, D, false, QT, 0>(a, (lds_char *)tile_buf, 0, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -644,8 +646,9 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
-    if (FD_MFMA_WG_PER_CU > 0 && lds > 0) {
-        const size_t want = (size_t)lds / (FD_MFMA_WG_PER_CU + 1) + 256;
+    const int per_cu = a.prefix_qt > 0 ? kPrefixWgPerCU : FD_MFMA_WG_PER_CU;
+    if (per_cu > 0 && lds > 0) {
+        const size_t want = (size_t)lds / (per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
     }
     const dim3 g((unsigned)grid), blk(64);
