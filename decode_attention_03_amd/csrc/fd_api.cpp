@@ -195,7 +195,7 @@ int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head
     int rc = device_cus(&cus);
     if (rc != FD_OK)
         return rc;
-    p->num_wgs = cus * kWorkGroupsPerCU * kBalancedRounds;
+    p->num_wgs = cus * fd::kMfmaWgPerCU * kBalancedRounds;
     p->units = batch * heads_kv;
     p->gsz = heads_q / heads_kv;
     // positions (units * max_kv_len) times work-groups must stay within int64
@@ -251,8 +251,8 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     // work-groups per split index: one per (sequence, KV head) when a group is
     // computed together, else one per (sequence, query head)
     const long long units = (long long)batch * (grouped ? heads_kv : heads_q);
-    const long long target =
-        (long long)num_cus * kWorkGroupsPerCU * (ragged ? kRaggedRounds : 1);
+    const long long target = (long long)num_cus * (grouped ? fd::kMfmaWgPerCU : kWorkGroupsPerCU) *
+                             (ragged ? kRaggedRounds : 1);
     long long b = (target + units - 1) / units;
     const long long min_len = grouped ? kMinSplitLenPerHead * group : kMinSplitLenMha;
     long long bmax = (max_kv_len + min_len - 1) / min_len;

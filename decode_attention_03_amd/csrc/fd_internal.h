@@ -15,6 +15,13 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 // with about two waves per CU, each with ~16 KB of loads in flight.
 constexpr int kWavesPerCU = 2;
 
+// Resident one-wave work-groups per CU of the grouped (matrix-core) split
+// kernels; the token-balanced partition makes this many shares per CU.
+#ifndef FD_MFMA_WG_PER_CU
+#define FD_MFMA_WG_PER_CU 2
+#endif
+constexpr int kMfmaWgPerCU = FD_MFMA_WG_PER_CU;
+
 // Resident work-groups per CU of the shared-prefix kernel: its K/V rows are
 // read by several work-groups each, so more of them in flight per CU pays.
 #ifndef FD_PREFIX_WG_PER_CU

@@ -621,10 +621,6 @@ int lds_per_cu_mfma() {
     return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-#ifndef FD_MFMA_WG_PER_CU
-#define FD_MFMA_WG_PER_CU 2
-#endif
-
 // Query tiles per work-group of the shared-prefix kernel that fit in the
 // register file without spilling (every tile keeps its own Q fragments, O
 // accumulators and softmax state).
@@ -646,7 +642,7 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
-    const int per_cu = a.prefix_qt > 0 ? kPrefixWgPerCU : FD_MFMA_WG_PER_CU;
+    const int per_cu = a.prefix_qt > 0 ? kPrefixWgPerCU : kMfmaWgPerCU;
     if (per_cu > 0 && lds > 0) {
         const size_t want = (size_t)lds / (per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
