@@ -14,7 +14,10 @@ then reads the CSV files rocprofv3 wrote under RAW.  Three kinds of run:
   kernel;
 * the same two passes over ``bench.py --copy-probe BYTES`` (a streaming
   elementwise kernel that reads BYTES and writes BYTES): the calibration
-  that turns counter readings into bytes.
+  that turns counter readings into bytes;
+* one pass of rocprofv3's derived utilisation metrics (VALUBusy, MfmaUtil,
+  LdsUtil, SALUBusy: percent of the kernel's active GPU time the vector ALUs,
+  matrix cores, LDS and scalar ALU were busy) on the split kernel.
 
 Written under OUT: ``<kernel>_<workload>.md`` (trace summary and traffic),
 ``traffic_<workload>.json`` (what bench.py reports as ``roofline.traffic``,
@@ -160,6 +163,12 @@ def main() -> int:
         run(cmd, 240, log_path)
         pmc_cmds[counter] = cmd
 
+    # 2b. unit utilisation of the split kernel (derived metrics, one pass)
+    util_metrics = ("VALUBusy", "MfmaUtil", "LdsUtil", "SALUBusy")
+    util_cmd = ["rocprofv3", "--pmc", *util_metrics, "-d", raw, "-o", f"{tag}_util",
+                "--output-format", "csv", "--", *short]
+    run(util_cmd, 240, log_path)
+
     # 3. calibration on a streaming kernel of known size
     copy = [py, BENCH, "--copy-probe", str(COPY_BYTES)]
     copy_cmds = {}
@@ -186,6 +195,11 @@ def main() -> int:
             os.path.join(raw, f"{tag}_{counter}_counter_collection.csv"), counter, is_split)
         meas[counter] = {"counter_per_dispatch": v, "dispatches": n,
                          "bytes": v * cal[counter]["bytes_per_unit"]}
+    util = {}
+    for mname in util_metrics:
+        v, n, _ = counter_per_dispatch(os.path.join(raw, f"{tag}_util_counter_collection.csv"),
+                                       mname, is_split)
+        util[mname] = round(v, 2)
     fam = family_of(kname)
     roof = res["roofline"]
     alg = roof["algorithmic_bytes_per_launch"]
@@ -201,6 +215,7 @@ def main() -> int:
         "calibration": {c: {k: (round(x, 4) if isinstance(x, float) else x)
                             for k, x in d.items()} for c, d in cal.items()},
         "copy_probe_bytes": COPY_BYTES,
+        "utilisation_percent": util,
         "commands": {"fetch": shown(pmc_cmds["FETCH_SIZE"]),
                      "write": shown(pmc_cmds["WRITE_SIZE"]),
                      "copy_fetch": shown(copy_cmds["FETCH_SIZE"]),
@@ -232,6 +247,7 @@ def main() -> int:
         "    " + shown(pmc_cmds["WRITE_SIZE"]),
         "    " + shown(copy_cmds["FETCH_SIZE"]),
         "    " + shown(copy_cmds["WRITE_SIZE"]),
+        "    " + shown(util_cmd),
         "",
         "## Kernel trace (rocprofv3 --kernel-trace --stats)",
         "",
@@ -275,6 +291,15 @@ def main() -> int:
         "",
         f"HBM bytes per launch {hbm:.0f} against {alg} algorithmic bytes: "
         f"ratio {hbm / alg:.4f}.  Kernel source hash {rec['kernel_source_hash']}.",
+        "",
+        "## Unit utilisation of the split kernel (rocprofv3 derived metrics, % of active time)",
+        "",
+        "| VALUBusy | MfmaUtil | LdsUtil | SALUBusy |",
+        "|---|---|---|---|",
+        f"| {util['VALUBusy']} | {util['MfmaUtil']} | {util['LdsUtil']} | {util['SALUBusy']} |",
+        "",
+        "The kernel is bound by HBM (traffic above); these show how much of each unit's time the",
+        "streaming leaves in use.",
         "",
     ]
     md = os.path.join(out, f"{fam}_{w.name}.md")
