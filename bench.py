@@ -160,6 +160,35 @@ def time_steps(p: Prepared, steps: int, warmup: int) -> dict:
             "event_us_p10": per[len(per) // 10], "event_us_p90": per[(9 * len(per)) // 10]}
 
 
+def time_graph_steps(p: Prepared, steps: int, per_graph: int = 20) -> float:
+    """µs per decode step with `per_graph` steps captured in one HIP graph and
+    the graph replayed: the GPU-side cost of a step without the per-call host
+    overhead (what a serving loop that replays graphs pays)."""
+    s = torch.cuda.Stream(device=p.q.device)
+    s.wait_stream(torch.cuda.current_stream(p.q.device))
+    saved = p.decode_args
+    sp = ctypes.c_void_p(s.cuda_stream)
+    p.decode_args = [a[:-1] + (sp,) for a in saved]  # same arguments on the capture stream
+    try:
+        with torch.cuda.stream(s):
+            p.decode(0)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(per_graph):
+                p.decode(i)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // per_graph)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (reps * per_graph) * 1e6
+    finally:
+        p.decode_args = saved
+
+
 def time_split_kernel(p: Prepared, steps: int, warmup: int) -> float:
     """Average duration (µs) of the split kernel alone: HIP events on its stream
     around `steps` back-to-back launches, divided by `steps`.  The balanced
@@ -425,6 +454,9 @@ def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
         out["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
     else:
         out["note"] = "cache-resident (0.5 MiB); µs only"
+        # launch-bound: also the step's GPU-side time with the host overhead
+        # taken out by graph replay
+        out["graph_us_per_step"] = round(time_graph_steps(p, 200), 2)
     if split_us is not None:
         out["split_kernel_us" if not p.balanced else "split_and_combine_us"] = round(split_us, 2)
     prof = traffic_from_profile(p.w.name)

@@ -153,6 +153,23 @@ void set_paging(fd::SplitArgs &a, const Paging *pg) {
     a.num_pages = pg->num_pages;
 }
 
+// Waves per work-group when the vector kernel runs every split of a row in one
+// work-group and merges them in LDS (no combine launch, no workspace): fixed
+// splits, 2..8 of them, on a grid whose split work-groups would not even fill
+// the GPU's wave slots once.  0 when not applicable.
+int fused_waves(int batch, int heads_q, int heads_kv, int head_dim, int in_dtype,
+                int num_splits) {
+    if (num_splits < 2 || num_splits > 8 ||
+        fd::split_mfma_supported(in_dtype, head_dim, heads_q / heads_kv))
+        return 0;
+    int cus = 0;
+    if (device_cus(&cus) != FD_OK)
+        return 0;
+    if ((long long)batch * heads_q * num_splits >= (long long)cus * fd::kWavesPerCU)
+        return 0;
+    return num_splits <= 2 ? 2 : (num_splits <= 4 ? 4 : 8);
+}
+
 int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     const int group = a.heads_q / a.heads_kv;
     hipError_t e;
@@ -166,7 +183,7 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
         if (rc != FD_OK)
             return rc;
         const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
-        a.valu_waves = wgs < (long long)cus * fd::kWavesPerCU ? 2 : 1;
+        a.valu_waves = a.fused_waves > 0 ? 0 : (wgs < (long long)cus * fd::kWavesPerCU ? 2 : 1);
         e = fd::launch_split_valu(a, in_dtype, stream);
     }
     if (e != hipSuccess)
@@ -313,7 +330,9 @@ int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_l
         if (rc != FD_OK)
             return rc;
     }
-    *bytes = fd_workspace_bytes(batch, heads_q, num_splits, head_dim);
+    *bytes = fused_waves(batch, heads_q, heads_kv, head_dim, in_dtype, num_splits) > 0
+                 ? 0
+                 : fd_workspace_bytes(batch, heads_q, num_splits, head_dim);
     return FD_OK;
 }
 
@@ -766,6 +785,12 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
     set_paging(a, pg);
 
     if (num_splits == 1) {  // one split per row: the split stage writes o and lse itself
+        a.o = o;
+        a.lse = lse;
+        return launch_split(a, in_dtype, st);
+    }
+    a.fused_waves = fused_waves(batch, heads_q, heads_kv, head_dim, in_dtype, num_splits);
+    if (a.fused_waves > 0) {  // small grid: splits merged in LDS, final output directly
         a.o = o;
         a.lse = lse;
         return launch_split(a, in_dtype, st);

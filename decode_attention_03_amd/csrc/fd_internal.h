@@ -75,6 +75,10 @@ struct SplitArgs {
     // part_offset + i (part_stride 0 means num_splits), so two launches can
     // fill one partial buffer.
     int part_stride, part_offset;
+    // Vector kernel only: with fused_waves (2, 4 or 8 >= num_splits) one
+    // work-group per row runs wave w on split w and merges the splits in LDS,
+    // writing the final o / lse (a.o, a.lse); small grids only.
+    int fused_waves;
     // Vector kernel only: waves per work-group (1 or 2).  Two waves share a
     // split (and merge in LDS) when the grid has fewer work-groups than the
     // GPU has wave slots, e.g. one split per row.

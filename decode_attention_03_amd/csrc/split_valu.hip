@@ -37,7 +37,9 @@
 // two one-wave work-groups, or one two-wave work-group whose waves take
 // alternate token slots of the same split (used when there are fewer
 // work-groups than wave slots, e.g. with one split per row, where it also
-// makes the combine stage unnecessary).
+// makes the combine stage unnecessary).  When even the splits of all rows
+// leave wave slots empty, one work-group per row runs one wave per split and
+// merges the splits in LDS (FUSED), so a small decode is a single launch.
 #include "dev_common.h"
 
 namespace fd {
@@ -102,15 +104,21 @@ __device__ __forceinline__ void unpack_row(const uint32_t *w, float *f) {
         unpack_word<DT>(w[j], f + j * L::PW);
 }
 
-template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED>
+// FUSED: one work-group per (sequence, head group) whose wave w computes split
+// w (num_splits <= THREADS / 64); the LDS merge then combines the splits and
+// the work-group writes the final output (a combine stage in LDS).
+template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false>
 __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     using L = Layout<DT, D, LPR>;
     constexpr int EPL = L::EPL;
     constexpr int WORDS = L::WORDS;
     constexpr int U = L::U;
     constexpr int kRows = THREADS / LPR;  // rows of LPR lanes
-    constexpr int TPS = kRows / HPW;     // token slots per step position
-    static_assert(kRows % HPW == 0, "HPW must divide the row count");
+    constexpr int RPW = 64 / LPR;         // rows per wave
+    // token slots per step position: the work-group's rows share one split,
+    // or (FUSED) each wave's rows share that wave's split
+    constexpr int TPS = (FUSED ? RPW : kRows) / HPW;
+    static_assert(kRows % HPW == 0 && RPW % HPW == 0, "HPW must divide the row counts");
 
     __shared__ float sm_acc[kRows][D];
     __shared__ float sm_m[kRows];
@@ -119,23 +127,24 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     const int tid = threadIdx.x;
     const int sub = tid % LPR;
     const int row = tid / LPR;
-    const int hoff = row % HPW;   // head of this row within the group
-    const int tslot = row / HPW;  // token slot of this row
+    const int hoff = row % HPW;                          // head of this row within the group
+    const int tslot = (FUSED ? row % RPW : row) / HPW;  // token slot of this row
 
     // Work-group -> (b, head group, split); the head group varies fastest so
     // that neighbouring work-groups read neighbouring head rows of the same
-    // tokens.
+    // tokens.  FUSED: work-group -> (b, head group), split = wave.
     const int ngroups = a.heads_q / HPW;
     const int hg = blockIdx.x % ngroups;
     const int rest = blockIdx.x / ngroups;
-    const int split = rest % a.num_splits;
-    const int b = rest / a.num_splits;
+    const int split = FUSED ? tid / 64 : rest % a.num_splits;
+    const int b = FUSED ? rest : rest / a.num_splits;
     const int hq = hg * HPW + hoff;
     const int kvh = hq / (a.heads_q / a.heads_kv);
 
     int n = a.kv_lens ? a.kv_lens[b] : a.max_kv_len;
     n = n < 0 ? 0 : (n > a.max_kv_len ? a.max_kv_len : n);
-    const long t0 = (long)split * a.split_len;
+    // (FUSED waves past num_splits get an empty range)
+    const long t0 = split < a.num_splits ? (long)split * a.split_len : (long)n;
     const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
 
     float m = -INFINITY;  // running max of log2-domain scores in this row
@@ -395,23 +404,30 @@ int lds_per_cu() {
     return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED>
+template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false>
 hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
     constexpr int kRows = THREADS / LPR;
     constexpr size_t kStatic = sizeof(float) * (size_t)(kRows * D + 2 * kRows);
-    const long grid = (long)a.batch * (a.heads_q / HPW) * a.num_splits;
-    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR, PAGED>;
+    const long grid = (long)a.batch * (a.heads_q / HPW) * (FUSED ? 1 : a.num_splits);
+    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR, PAGED, FUSED>;
     size_t pad = 0;
     const int lds = lds_per_cu();
     if (wg_per_cu > 0 && lds > 0) {
         const size_t want = (size_t)lds / (size_t)(wg_per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
         if (pad > 65536) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)pad);
-            if (e != hipSuccess)
-                return e;
+            // once per kernel and device (the pad depends only on the device)
+            static bool raised[64];
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || !raised[dev]) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)pad);
+                if (e != hipSuccess)
+                    return e;
+                if (dev >= 0 && dev < 64)
+                    raised[dev] = true;
+            }
         }
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(THREADS), pad, stream, a);
@@ -432,6 +448,22 @@ constexpr int lanes_per_row() {
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     constexpr int LPR = lanes_per_row<DT, D>();
+    if (a.fused_waves > 0) {  // small grid: all splits of a row in one work-group
+        const bool pg = a.block_table != nullptr;
+        switch (a.fused_waves) {
+        case 2:
+            return pg ? launch_cfg<DT, D, 128, 1, LPR, true, true>(a, 0, stream)
+                      : launch_cfg<DT, D, 128, 1, LPR, false, true>(a, 0, stream);
+        case 4:
+            return pg ? launch_cfg<DT, D, 256, 1, LPR, true, true>(a, 0, stream)
+                      : launch_cfg<DT, D, 256, 1, LPR, false, true>(a, 0, stream);
+        case 8:
+            return pg ? launch_cfg<DT, D, 512, 1, LPR, true, true>(a, 0, stream)
+                      : launch_cfg<DT, D, 512, 1, LPR, false, true>(a, 0, stream);
+        default:
+            return hipErrorInvalidValue;
+        }
+    }
     if (a.block_table) {
         if (a.valu_waves == 2)
             return launch_cfg<DT, D, 128, 1, LPR, true>(a, kWavesPerCU / 2, stream);

@@ -104,13 +104,16 @@ def test_workspace_bytes(lib):
 
 
 def test_decode_workspace_bytes_explicit_splits(lib):
-    """With the split count given, fd_decode needs exactly fd_workspace_bytes
-    (no device query); bad arguments are rejected."""
+    """With the split count given, fd_decode needs fd_workspace_bytes, or
+    nothing when a small grid merges its splits in one work-group (that case
+    needs the device's CU count, so without a GPU it is never taken); bad
+    arguments are rejected."""
     out = ctypes.c_size_t(123)
     for B, has_lens in ((4, 0), (4, 1), (1, 1), (37, 0)):
         assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, has_lens, B, 0,
                                              ctypes.byref(out)) == fd.OK
-        assert out.value == lib.fd_workspace_bytes(3, 8, B, 128)
+        assert out.value in (0, lib.fd_workspace_bytes(3, 8, B, 128))
+        assert B <= 8 or out.value == lib.fd_workspace_bytes(3, 8, B, 128)
     assert lib.fd_decode_workspace_bytes(3, 8, 3, 1000, 128, fd.BF16, 0, 4, 0,
                                          ctypes.byref(out)) == fd.ERR_INVALID
     assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 96, fd.BF16, 0, 4, 0,
