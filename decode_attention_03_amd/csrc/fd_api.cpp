@@ -235,10 +235,14 @@ const char *fd_last_error(void) { return g_error.c_str(); }
 
 // Split count: [P2] §3 Q2 suggests roughly one split per 1K tokens, capped,
 // and notes that the best count depends on the GPU.  Here it is derived from
-// the GPU: both split kernels run one-wave work-groups, at most
-// kWorkGroupsPerCU resident per CU (the request depth at which MI355X HBM
-// streams best), and a work-group costs a start-up latency, so
-//   - equal lengths: one full round, batch * units * B ~ CUs * kWorkGroupsPerCU;
+// the GPU: the split kernels run one-wave work-groups (two-wave ones where the
+// grid is small), with a fixed number resident per CU (the request depth at
+// which MI355X HBM streams best: fd::kWavesPerCU for the vector kernel,
+// fd::kMfmaWgPerCU for the grouped one), and a work-group costs a start-up
+// latency, so
+//   - equal lengths: one full round, batch * units * B ~ CUs * per-CU count;
+//     a vector-kernel plan of two splits becomes one split per row run by
+//     two-wave work-groups (same wave slots, no combine stage);
 //   - ragged lengths (unknown to the host): about kRaggedRounds rounds judged
 //     by the longest sequence, so that the short and partial splits even out;
 // never with splits shorter than a floor that keeps the partial (o, LSE)
@@ -402,9 +406,10 @@ int check_combine(const float *o_part, int batch, int heads_q, int num_splits, i
     return FD_OK;
 }
 
-// Cascade plan: fixed splits for the shared prefix (B_p, uniform length) and
-// for the suffixes (B_s, ragged when suffix_lens is given); the partial buffer
-// holds B_p + B_s slots per row, prefix first.
+// Cascade plan: fixed splits for the shared prefix (B_p, uniform length);
+// the suffixes on the token-balanced partition when they are ragged and
+// grouped, else fixed splits (B_s) in the same partial buffer as the prefix
+// (B_p + B_s slots per row, prefix first).
 struct CascadePlan {
     int bp = 0, lp = 0, bs = 1, ls = 1;
     int prefix_qt = 0;  // > 0: the prefix runs on the shared-prefix matrix-core kernel

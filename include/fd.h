@@ -166,9 +166,13 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
  *     - otherwise: B and L from fd_choose_splits (ragged = kv_lens != NULL).
  *   num_splits > 0, split_len == 0: L = ceil(max_kv_len / num_splits)
  *     ([P2] §4 chunking).  num_splits > 0, split_len > 0: used as given.
- * With B == 1 the split stage writes o and lse itself and workspace may be
- * NULL; otherwise workspace must hold the bytes fd_decode_workspace_bytes
- * reports for the same arguments (for B >= 1 given explicitly, that is
+ * With B == 1 the split stage writes o and lse itself.  On the vector path
+ * (fp32 inputs, or no grouped heads) a small grid with 2 <= B <= 8 splits
+ * (batch * heads_q * B below two waves per CU) runs every split of a row in
+ * one work-group, one wave per split, and merges the splits in LDS: again a
+ * single launch that writes o and lse.  Otherwise workspace must hold the
+ * bytes fd_decode_workspace_bytes reports for the same arguments (0 in the
+ * cases above, where workspace may be NULL; for other explicit B it is
  * fd_workspace_bytes(batch, heads_q, B, head_dim)).  lse may be NULL. */
 int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
               int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
