@@ -7,7 +7,8 @@
 // stage 1; "adv04: Flash-Decoding" (mini-vllm-tutorial), §4).  With ragged
 // lengths, fixed splits leave the GPU's work-groups unevenly loaded, so for
 // ragged batches the library also offers a partition that gives every
-// work-group the same number of 16-token granules of K/V rows.  It is still a split-K partition
+// work-group the same cost: its 16-token granules of K/V rows plus a fixed
+// charge for every piece it starts.  It is still a split-K partition
 // in the pages' sense: every (sequence, head) row's tokens are cut into
 // contiguous pieces, each piece yields an (o, LSE) pair, and the combine merges
 // a row's pieces ("FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法", §2.3.4;
@@ -18,16 +19,23 @@
 //   unit u = b * hx + x: one (sequence b, head x) pair reading one KV head
 //            (hx = heads_kv for the grouped kernel, heads_q for the vector one);
 //   N_b    = kv_lens[b] clamped to [0, max_kv_len], g_b = ceil(N_b / 16);
+//   a unit of a non-empty sequence costs g_b + kPieceCost positions: the
+//            first kPieceCost stand for the fixed cost of starting a piece
+//            (loading q, filling the load pipeline, writing the partial),
+//            so that shares balance time rather than bytes; its granule j
+//            (tokens [16 j, min(16 j + 16, N_b))) is position kPieceCost + j
+//            of the unit; empty sequences cost nothing;
 //   the flattened space lists units in order, unit u covering positions
-//            [S_u, S_u + g_b) with S_u = hx * (g_0 + ... + g_{b-1}) + x * g_b;
-//            granule j of a unit is tokens [16 j, min(16 j + 16, N_b));
-//   T      = hx * sum_b g_b, W_eff = min(num_wgs, T);
+//            [S_u, S_u + g_b + kPieceCost);
+//   T      = sum of all unit costs, W_eff = min(num_wgs, T);
 //   work-group w < W_eff covers [floor(w T / W_eff), floor((w+1) T / W_eff)),
-//            never empty; work-groups w >= W_eff do nothing;
+//            never empty; work-groups w >= W_eff do nothing; a work-group's
+//            piece of unit u is the unit's granules inside its range (none
+//            when the range only touches the unit's leading cost positions);
 //   the piece of unit u handled by work-group w writes slot w + rank(u),
 //            rank(u) = number of non-empty units before u; a unit's pieces
 //            therefore fill consecutive slots, and slots < num_wgs + units;
-//   the work-group that handles a unit's first token writes the unit's
+//   the work-group that handles a unit's granule 0 writes the unit's
 //            descriptor {first slot, slot count}; units of empty sequences
 //            get none (the combine checks N_b itself).
 #pragma once
@@ -36,7 +44,11 @@
 
 namespace fd {
 
-constexpr int kGranule = 16;  // tokens per position of the balanced partition
+constexpr int kGranule = 16;   // tokens per position of the balanced partition
+#ifndef FD_PIECE_COST
+#define FD_PIECE_COST 5
+#endif
+constexpr int kPieceCost = FD_PIECE_COST;  // positions charged per unit for starting a piece
 
 __device__ __forceinline__ int clamp_len(const int32_t *kv_lens, int b, int max_kv_len) {
     int n = kv_lens ? kv_lens[b] : max_kv_len;
@@ -46,6 +58,12 @@ __device__ __forceinline__ int clamp_len(const int32_t *kv_lens, int b, int max_
 // Granules of sequence b.
 __device__ __forceinline__ int granules(const int32_t *kv_lens, int b, int max_kv_len) {
     return (clamp_len(kv_lens, b, max_kv_len) + kGranule - 1) / kGranule;
+}
+
+// Positions one unit of sequence b costs (0 for an empty sequence).
+__device__ __forceinline__ int unit_cost(const int32_t *kv_lens, int b, int max_kv_len) {
+    const int g = granules(kv_lens, b, max_kv_len);
+    return g > 0 ? g + kPieceCost : 0;
 }
 
 __device__ __forceinline__ long long wave_sum_ll(long long v) {
@@ -83,7 +101,7 @@ struct PieceCursor {
     long long pos, end;  // [pos, end): this work-group's positions
     long long total;     // T
     int w_eff;           // W_eff
-    int b, x, t;         // unit (b, x) and granule t within it at `pos`
+    int b, x, t;         // unit (b, x) and position t within it (0 .. cost - 1) at `pos`
     int rank;            // rank of unit (b, x) among non-empty units
 };
 
@@ -93,7 +111,7 @@ __device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch
     long long gsum = 0;
     for (int base = 0; base < batch; base += 64) {
         const int i = base + lane;
-        gsum += i < batch ? granules(kv_lens, i, max_kv_len) : 0;
+        gsum += i < batch ? unit_cost(kv_lens, i, max_kv_len) : 0;
     }
     c.total = uniform(wave_sum_ll(gsum) * hx);
     c.w_eff = c.total < num_wgs ? (int)c.total : num_wgs;
@@ -106,7 +124,7 @@ __device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch
     int nonempty = 0;      // non-empty sequences before this chunk
     for (int base = 0; base < batch; base += 64) {
         const int i = base + lane;
-        const long long n = i < batch ? granules(kv_lens, i, max_kv_len) : 0;
+        const long long n = i < batch ? unit_cost(kv_lens, i, max_kv_len) : 0;
         const long long incl = wave_scan_ll(n, lane);
         const unsigned long long hit = __ballot(i < batch && before + hx * incl > c.pos);
         const unsigned long long ne = __ballot(n > 0);

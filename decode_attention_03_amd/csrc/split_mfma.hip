@@ -571,22 +571,31 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
     int n = clamp_len(a.kv_lens, c.b, a.max_kv_len);  // tokens of the current sequence
     int ng = (n + kGranule - 1) / kGranule;            // and its granules
     while (true) {
+        // this work-group covers positions [c.t, c.t + avail) of unit (c.b, c.x),
+        // whose granule j is position kPieceCost + j
         const long long left = c.end - c.pos;
-        const int plen = left < (long long)(ng - c.t) ? (int)left : ng - c.t;  // granules
-        const int slot = w + c.rank;
-        const QMap qm{c.b * a.heads_q + c.x * G, G, 0, 0, a.heads_q, c.x};
-        const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G,
-                           nullptr, 1, 0, true};
-        const long t0 = (long)c.t * kGranule;
-        const long t1 = (long)(c.t + plen) * kGranule < n ? (long)(c.t + plen) * kGranule : n;
-        mfma_piece<DT, D, PAGED, 1>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
-        if (c.t == 0 && threadIdx.x == 0) {
-            const int last = balanced_owner(c.pos + ng - 1, c.total, c.w_eff);
-            const size_t u = (size_t)c.b * a.heads_kv + c.x;
-            a.unit_desc[2 * u] = slot;
-            a.unit_desc[2 * u + 1] = last - w + 1;
+        const int ucost = ng + kPieceCost;
+        const int avail = left < (long long)(ucost - c.t) ? (int)left : ucost - c.t;
+        const int lo = c.t > kPieceCost ? c.t - kPieceCost : 0;                     // granules
+        const int hi = c.t + avail - kPieceCost < ng ? c.t + avail - kPieceCost : ng;
+        if (hi > lo) {
+            const int slot = w + c.rank;
+            const QMap qm{c.b * a.heads_q + c.x * G, G, 0, 0, a.heads_q, c.x};
+            const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G,
+                               nullptr, 1, 0, true};
+            const long t0 = (long)lo * kGranule;
+            const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
+            mfma_piece<DT, D, PAGED, 1>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
+            if (lo == 0 && threadIdx.x == 0) {
+                const long long ustart = c.pos - c.t;  // the unit's first position
+                const int first = balanced_owner(ustart + kPieceCost, c.total, c.w_eff);
+                const int last = balanced_owner(ustart + kPieceCost + ng - 1, c.total, c.w_eff);
+                const size_t u = (size_t)c.b * a.heads_kv + c.x;
+                a.unit_desc[2 * u] = slot;  // this work-group owns granule 0: first == w
+                a.unit_desc[2 * u + 1] = last - first + 1;
+            }
         }
-        c.pos += plen;
+        c.pos += avail;
         if (c.pos >= c.end)
             break;
         // next unit: the next KV head, else the next non-empty sequence
