@@ -109,7 +109,7 @@ struct Mma<kF16> {
 #define FD_MFMA_STEP_KB 16
 #endif
 
-template <int D>
+template <int D, int STEP_KB = FD_MFMA_STEP_KB>
 struct Tiles {
     static constexpr int ROW = D * 2;         // bytes of one head row (16-bit types)
     static constexpr int CPR = ROW / 16;      // 16-byte chunks per row
@@ -119,8 +119,7 @@ struct Tiles {
     static constexpr int TILE = 16 * ROW;     // bytes of one 16-token tile of K or V
     static constexpr int IPT = TILE / 1024;   // direct-to-LDS instructions per tile
     // 16-token tiles per step: FD_MFMA_STEP_KB of K+V per wave and step
-    static constexpr int U =
-        FD_MFMA_STEP_KB * 1024 / (2 * TILE) > 0 ? FD_MFMA_STEP_KB * 1024 / (2 * TILE) : 1;
+    static constexpr int U = STEP_KB * 1024 / (2 * TILE) > 0 ? STEP_KB * 1024 / (2 * TILE) : 1;
     static constexpr int BUF = 2 * U * TILE;  // LDS: U tiles of K, then U tiles of V
     // Chunk swizzles: physical chunk p of row r holds logical chunk
     // p ^ swz_k(r) in a K tile and p ^ swz_v(r) in a V tile.  gfx950 LDS has
@@ -142,6 +141,15 @@ struct Tiles {
 };
 
 typedef __attribute__((address_space(3))) char lds_char;
+
+// K/V bytes per step of the shared-prefix kernel (both halves).
+#ifndef FD_PREFIX_STEP_KB
+#define FD_PREFIX_STEP_KB 16
+#endif
+#ifndef FD_PREFIX_QT128
+#define FD_PREFIX_QT128 2
+#endif
+constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;
 
 // Where a piece's results go.  Partial i of query row `row` (slot h of a
 // tile when `local`) is at index (row or h) * stride + off: o at o + index * D
@@ -182,11 +190,11 @@ struct QMap {
 // (NTLOAD) unless other work-groups will read the same rows.  Called by the whole wave; t0 >= t1
 // writes (0, -inf).  (Device pass only: the body uses LDS address-space
 // pointers and gfx950-only builtins that the host pass cannot type.)
-template <int DT, int D, bool PAGED, int QT, int NTLOAD = 1>
+template <int DT, int D, bool PAGED, int QT, int NTLOAD = 1, int STEP_KB = FD_MFMA_STEP_KB>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
                                            long t0, long t1, const QMap &qm,
                                            const PieceOut &out) {
-    using T = Tiles<D>;
+    using T = Tiles<D, STEP_KB>;
     constexpr int NC = T::NC, NT = T::NT, U = T::U;
     using M = Mma<DT>;
 
@@ -534,7 +542,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 template <int DT, int D, int QT>
 __global__ __launch_bounds__(64) void split_mfma_prefix_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
+    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D, kPrefixStepKB>::BUF];
     const int G = a.heads_q / a.heads_kv;
     const int nq = a.batch * G;
     const int groups = ((nq + 15) / 16 + QT - 1) / QT;  // tile groups per unit
@@ -552,7 +560,8 @@ __global__ __launch_bounds__(64) void split_mfma_prefix_kernel(SplitArgs a) {
     PieceOut out{a.o_part, a.lse_part, nullptr, a.part_stride ? a.part_stride : a.num_splits,
                  a.part_offset + split, false};
     // the unit's other work-groups read the same K/V: ordinary (temporal) loads
-    mfma_piece<DT, D, false, QT, 0>(a, (lds_char *)tile_buf, 0, kvh, t0, t1, qm, out);
+    mfma_piece<DT, D, false, QT, 0, kPrefixStepKB>(a, (lds_char *)tile_buf, 0, kvh, t0, t1, qm,
+                                                   out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -631,17 +640,20 @@ int lds_per_cu_mfma() {
 }
 
 // Query tiles per work-group of the shared-prefix kernel that fit in the
-// register file without spilling (every tile keeps its own Q fragments, O
-// accumulators and softmax state).
+// register file without spilling next to 16 KB steps (every tile keeps its
+// own Q fragments, O accumulators and softmax state).  Four tiles fit at
+// d = 128 with 8 KB steps, but measured slower: the smaller steps and the
+// shorter splits that the fewer work-groups need cost more than the halved
+// re-reads save.
 template <int D>
 constexpr int prefix_max_qt() {
-    return D == 64 ? 4 : (D == 128 ? 2 : 1);
+    return D == 64 ? 4 : (D == 128 ? FD_PREFIX_QT128 : 1);
 }
 
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
-    constexpr size_t kStatic = (size_t)T::BUF;
+    const size_t kStatic = a.prefix_qt > 0 ? (size_t)Tiles<D, kPrefixStepKB>::BUF : (size_t)T::BUF;
     long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
     if (a.prefix_qt > 0) {  // shared prefix: (8-aligned units) x tile groups
         const int tiles = (a.batch * (a.heads_q / a.heads_kv) + 15) / 16;
