@@ -183,7 +183,9 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
         if (rc != FD_OK)
             return rc;
         const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
-        a.valu_waves = a.fused_waves > 0 ? 0 : (wgs < (long long)cus * fd::kWavesPerCU ? 2 : 1);
+        a.valu_waves = a.fused_waves > 0
+                           ? 0
+                           : (wgs < (long long)cus * fd::kWavesPerCU ? fd::kWavesPerCU : 1);
         e = fd::launch_split_valu(a, in_dtype, stream);
     }
     if (e != hipSuccess)
@@ -285,9 +287,10 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
         b = kMaxAutoSplits;
     if (b < 1)
         b = 1;
-    // the vector kernel runs a lone split per row with two waves, which fills
-    // the same wave slots as two splits and needs no combine stage
-    if (!grouped && !ragged && b == 2)
+    // the vector kernel runs a lone split per row with one multi-wave
+    // work-group per CU, which fills the same wave slots as up to kWavesPerCU
+    // splits and needs no combine stage
+    if (!grouped && !ragged && b >= 2 && b <= fd::kWavesPerCU)
         b = 1;
     long long len = (max_kv_len + b - 1) / b;
     len = (len + 15) / 16 * 16;  // whole 16-token tiles

@@ -13,7 +13,10 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
 // Resident waves per CU the split kernels aim at: MI355X HBM streams best
 // with about two waves per CU, each with ~16 KB of loads in flight.
-constexpr int kWavesPerCU = 2;
+#ifndef FD_WAVES_PER_CU
+#define FD_WAVES_PER_CU 2
+#endif
+constexpr int kWavesPerCU = FD_WAVES_PER_CU;
 
 // Resident one-wave work-groups per CU of the grouped (matrix-core) split
 // kernels; the token-balanced partition makes this many shares per CU.
@@ -79,7 +82,8 @@ struct SplitArgs {
     // work-group per row runs wave w on split w and merges the splits in LDS,
     // writing the final o / lse (a.o, a.lse); small grids only.
     int fused_waves;
-    // Vector kernel only: waves per work-group (1 or 2).  Two waves share a
+    // Vector kernel only: waves per work-group (1, or kWavesPerCU for one
+    // work-group per CU).  Two waves share a
     // split (and merge in LDS) when the grid has fewer work-groups than the
     // GPU has wave slots, e.g. one split per row.
     int valu_waves;

@@ -465,12 +465,12 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         }
     }
     if (a.block_table) {
-        if (a.valu_waves == 2)
-            return launch_cfg<DT, D, 128, 1, LPR, true>(a, kWavesPerCU / 2, stream);
+        if (a.valu_waves > 1)
+            return launch_cfg<DT, D, 64 * kWavesPerCU, 1, LPR, true>(a, 1, stream);
         return launch_cfg<DT, D, 64, 1, LPR, true>(a, kWavesPerCU, stream);
     }
-    if (a.valu_waves == 2)
-        return launch_cfg<DT, D, 128, 1, LPR, false>(a, kWavesPerCU / 2, stream);
+    if (a.valu_waves > 1)
+        return launch_cfg<DT, D, 64 * kWavesPerCU, 1, LPR, false>(a, 1, stream);
     return launch_cfg<DT, D, 64, 1, LPR, false>(a, kWavesPerCU, stream);
 }
 
