@@ -42,8 +42,10 @@
 // fragment reads of K and the transpose reads of V free of bank conflicts.
 // (Direct-to-LDS loads were measured slower here: their LDS destination is
 // opaque to the compiler's wait counting, which then allows only one batch in
-// flight per wave.)  At most two work-groups are resident per CU (LDS
-// reservation), which keeps the HBM request stream near its efficient depth.
+// flight per wave.)  Steps are 8 KB of K+V per wave (one 16-token tile of
+// each at d = 128) and at most kMfmaWgPerCU = 3 work-groups are resident per CU
+// (LDS reservation), which keeps the HBM request stream near its efficient
+// depth (measured against 2 or 4 per CU and 16 KB steps).
 //
 // The split writes o = O / l and S = m + log l per query head ([P3]
 // §2.3.2-§2.3.3), or, in the m/l/o format, o with the split's max score m and
@@ -106,7 +108,7 @@ struct Mma<kF16> {
 };
 
 #ifndef FD_MFMA_STEP_KB
-#define FD_MFMA_STEP_KB 16
+#define FD_MFMA_STEP_KB 8
 #endif
 
 template <int D, int STEP_KB = FD_MFMA_STEP_KB>
