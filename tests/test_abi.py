@@ -285,3 +285,12 @@ def test_decode_validation(lib):
     assert _decode(lib, ws=FAKE, ws_bytes=need - 1) == fd.ERR_WORKSPACE
     assert _decode(lib, ws=FAKE + 8, ws_bytes=need) == fd.ERR_UNSUPPORTED
     assert "workspace" in fd.last_error() or "aligned" in fd.last_error()
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    """No fallback: with libfd.so missing, the binding raises instead of
+    computing anything some other way."""
+    monkeypatch.setattr(fd, "LIB_PATH", str(tmp_path / "missing" / "libfd.so"))
+    monkeypatch.setattr(fd, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        fd.library()

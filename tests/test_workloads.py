@@ -59,3 +59,41 @@ def test_dominant_keys_construction():
         assert torch.allclose(top[: w.dominant], expect.expand(w.dominant), rtol=2e-2)
         assert top[w.dominant] < 0.5 * expect
     assert math.isclose(w.scale, 1 / math.sqrt(128))
+
+
+def test_paginate_round_trip():
+    """Every valid token's K/V row sits at block_table[b][t // ps], row t % ps;
+    unused table entries are -1 and no physical page is handed out twice."""
+    w, inp = workloads.custom(4, 4, 2, 64, 100, dtype="bf16", seed=3, lens=[100, 0, 37, 16])
+    for ps in (16, 32, 128):
+        pg = workloads.paginate(inp, ps, seed=ps)
+        table = pg["block_table"]
+        assert table.shape == (4, -(-100 // ps)) and table.dtype == torch.int32
+        used = table[table >= 0].tolist()
+        assert len(used) == len(set(used)) and all(0 <= p < pg["num_pages"] for p in used)
+        for b, n in enumerate([100, 0, 37, 16]):
+            assert (table[b, -(-n // ps):] == -1).all()
+            for t in range(n):
+                p = int(table[b, t // ps])
+                assert torch.equal(pg["k_pages"][p, t % ps], inp["k"][b, t])
+                assert torch.equal(pg["v_pages"][p, t % ps], inp["v"][b, t])
+        spare = sorted(set(range(pg["num_pages"])) - set(used))
+        assert spare and all(torch.isnan(pg["k_pages"][p].float()).all() for p in spare)
+
+
+def test_cascade_inputs_and_concatenation():
+    """The cascade's prefix is shared and distinct from every suffix; the
+    concatenation puts the prefix first and sums the lengths."""
+    w = workloads.Workload("cascade_cpu", batch=3, heads_q=8, heads_kv=2, head_dim=64,
+                           max_kv_len=50, dtype="bf16", out_dtype="bf16", seed=9, ragged=(0, 50))
+    c = workloads.cascade(w, 20)
+    assert c["k_prefix"].shape == (20, 2, 64) and c["prefix_len"] == 20
+    cc = workloads.cascade_concat(c)
+    lens = c["suffix_lens"].tolist()
+    assert cc["kv_lens"].tolist() == [20 + n for n in lens]
+    for b in range(3):
+        assert torch.equal(cc["k"][b, :20], c["k_prefix"])
+        assert torch.equal(cc["v"][b, 20:20 + lens[b]], c["v_suffix"][b, :lens[b]])
+    assert not torch.equal(c["k_prefix"][:1], c["k_suffix"][0, :1])
+    c0 = workloads.cascade(w, 0)
+    assert c0["k_prefix"].shape == (0, 2, 64)
