@@ -21,7 +21,7 @@ constexpr int kWavesPerCU = FD_WAVES_PER_CU;
 // Resident one-wave work-groups per CU of the grouped (matrix-core) split
 // kernels; the token-balanced partition makes this many shares per CU.
 #ifndef FD_MFMA_WG_PER_CU
-#define FD_MFMA_WG_PER_CU 3
+#define FD_MFMA_WG_PER_CU 2
 #endif
 constexpr int kMfmaWgPerCU = FD_MFMA_WG_PER_CU;
 

@@ -43,9 +43,11 @@
 // (Direct-to-LDS loads were measured slower here: their LDS destination is
 // opaque to the compiler's wait counting, which then allows only one batch in
 // flight per wave.)  Steps are 8 KB of K+V per wave (one 16-token tile of
-// each at d = 128) and at most kMfmaWgPerCU = 3 work-groups are resident per CU
-// (LDS reservation), which keeps the HBM request stream near its efficient
-// depth (measured against 2 or 4 per CU and 16 KB steps).
+// each at d = 128) and at most kMfmaWgPerCU = 2 work-groups are resident per CU
+// (LDS reservation), as in the vector kernel: fewer concurrent request streams
+// keep HBM nearer its efficient depth.  (Measured against 3 or 4 per CU, 16 KB
+// steps, a third register set of loads in flight, and K fragments loaded
+// straight from HBM without the LDS round trip, each slower.)
 //
 // The split writes o = O / l and S = m + log l per query head ([P3]
 // §2.3.2-§2.3.3), or, in the m/l/o format, o with the split's max score m and
