@@ -428,6 +428,54 @@ def time_cascade(steps: int, warmup: int, dev: torch.device) -> dict:
             "materialised_GBps": round(logical / (us_p * 1e-6) / 1e9, 1)}
 
 
+SHARDS = 8
+SHARD = workloads.Workload("mha_bf16_b1_h32_d128_n8192_shard_of_65536", batch=1, heads_q=32,
+                           heads_kv=32, head_dim=128, max_kv_len=65536 // SHARDS, dtype="bf16",
+                           out_dtype="f32", seed=9)
+
+
+def time_shard(steps: int, warmup: int, dev: torch.device) -> dict:
+    """One GPU's share of the 64K-context workload sharded over SHARDS GPUs
+    along the sequence: fd_decode over 8192 tokens with fp32 (o, LSE) output
+    (what that GPU would send to the rows' owner), and the owner's fd_combine
+    over SHARDS such pairs per row.  The exchange itself is not measured."""
+    p = Prepared(SHARD, dev)
+    t = time_steps(p, steps, warmup)
+    shard_us = t["wall_us_per_step"]
+    batch, hq, d = SHARD.batch, SHARD.heads_q, SHARD.head_dim
+    o_part = torch.zeros((batch, hq, SHARDS, d), dtype=torch.float32, device=dev)
+    lse_part = torch.zeros((batch, hq, SHARDS), dtype=torch.float32, device=dev)
+    o = torch.empty((batch, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    P = ctypes.c_void_p
+    args = (P(o_part.data_ptr()), P(lse_part.data_ptr()), batch, hq, SHARDS, d, P(o.data_ptr()),
+            fd.BF16, P(lse.data_ptr()), P(p.stream.cuda_stream))
+
+    def comb(i):
+        rc = p.lib.fd_combine(*args)
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    settle(comb)
+    for i in range(warmup):
+        comb(i)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(p.stream)
+    for i in range(steps):
+        comb(i)
+    end.record(p.stream)
+    torch.cuda.synchronize()
+    comb_us = start.elapsed_time(end) / steps * 1e3
+    out = {"workload": SHARD.name, "shards": SHARDS, "plan": p.plan, "num_splits": p.B,
+           "shard_us_per_step": round(shard_us, 2),
+           "shard_kv_GBps": round(p.kv_bytes / (shard_us * 1e-6) / 1e9, 1),
+           "owner_combine_us": round(comb_us, 2),
+           "exchange_bytes_per_gpu": batch * hq * (d + 1) * 4}
+    p.free()
+    return out
+
+
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     """The fp64 oracle on the host cores, on whole decode steps of the same
     workload, repeated until about budget_s seconds of wall time."""
@@ -608,6 +656,11 @@ def main() -> int:
         casc = time_cascade(args.steps, args.warmup, dev)
         log(f"[bench] cascade: {casc}")
         result["cascade"] = casc
+        torch.cuda.empty_cache()
+        # one GPU's share of the long-context workload under sequence sharding
+        shard = time_shard(args.steps, args.warmup, dev)
+        log(f"[bench] shard: {shard}")
+        result["shard"] = shard
     print(json.dumps(result), flush=True)
     return 0
 
