@@ -26,8 +26,8 @@ ARCH = "gfx950"
 #: on a kernel stays valid while these files are unchanged
 KERNEL_SOURCES = {
     "split_valu": ["split_valu.hip", "dev_common.h", "fd_internal.h"],
-    "split_mfma": ["split_mfma.hip", "dev_common.h", "fd_internal.h"],
-    "combine": ["combine.hip", "dev_common.h", "fd_internal.h"],
+    "split_mfma": ["split_mfma.hip", "partition.h", "dev_common.h", "fd_internal.h"],
+    "combine": ["combine.hip", "partition.h", "dev_common.h", "fd_internal.h"],
 }
 
 
