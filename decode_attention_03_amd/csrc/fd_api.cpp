@@ -74,8 +74,9 @@ int device_cus(int *out) {
 }
 
 // Checks shared by the split stage and the whole decode.
-int check_split_inputs(const void *q, const void *k, const void *v, int batch, int heads_q,
-                       int heads_kv, int max_kv_len, int head_dim, int in_dtype, float scale) {
+int check_split_inputs(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                       int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                       int in_dtype, float scale) {
     if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0)
         return fail(FD_ERR_INVALID, "sizes must be positive (batch=%d heads_q=%d heads_kv=%d "
                     "max_kv_len=%d)", batch, heads_q, heads_kv, max_kv_len);
@@ -92,6 +93,8 @@ int check_split_inputs(const void *q, const void *k, const void *v, int batch, i
         return fail(FD_ERR_UNSUPPORTED, "in_dtype %d not supported", in_dtype);
     if (!aligned16(q) || (max_kv_len > 0 && (!aligned16(k) || !aligned16(v))))
         return fail(FD_ERR_UNSUPPORTED, "q, k and v must be 16-byte aligned");
+    if (kv_lens && !aligned4(kv_lens))
+        return fail(FD_ERR_UNSUPPORTED, "kv_lens must be 4-byte aligned");
     if (!std::isfinite(scale))
         return fail(FD_ERR_INVALID, "scale is not finite");
     // the kernels address K/V with 32-bit offsets from a per-split base
@@ -353,7 +356,7 @@ int split_stage(const void *q, const void *k, const void *v, const int32_t *kv_l
                 int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype, float scale,
                 int num_splits, int split_len, float *o_part, float *lse_part, float *m_part,
                 float *l_part, void *stream, const Paging *pg = nullptr) {
-    int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
+    int rc = check_split_inputs(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim,
                                 in_dtype, scale);
     if (rc != FD_OK)
         return rc;
@@ -526,12 +529,12 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
                           in_dtype, suffix_lens != nullptr, &p);
     if (rc != FD_OK)
         return rc;
-    rc = check_split_inputs(q, k_prefix, v_prefix, batch, heads_q, heads_kv, prefix_len,
+    rc = check_split_inputs(q, k_prefix, v_prefix, nullptr, batch, heads_q, heads_kv, prefix_len,
                             head_dim, in_dtype, scale);
     if (rc != FD_OK)
         return rc;
-    rc = check_split_inputs(q, k_suffix, v_suffix, batch, heads_q, heads_kv, max_suffix_len,
-                            head_dim, in_dtype, scale);
+    rc = check_split_inputs(q, k_suffix, v_suffix, suffix_lens, batch, heads_q, heads_kv,
+                            max_suffix_len, head_dim, in_dtype, scale);
     if (rc != FD_OK)
         return rc;
     if (!workspace || workspace_bytes < p.bytes)
@@ -692,7 +695,7 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
                 int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
                 int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
                 void *workspace, size_t workspace_bytes, void *stream, const Paging *pg) {
-    int rc = check_split_inputs(q, k, v, batch, heads_q, heads_kv, max_kv_len, head_dim,
+    int rc = check_split_inputs(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim,
                                 in_dtype, scale);
     if (rc != FD_OK)
         return rc;
@@ -768,6 +771,8 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
             return rc;
     } else if (split_len == 0) {
         split_len = max_kv_len > 0 ? (max_kv_len + num_splits - 1) / num_splits : 1;
+        if (pg)  // whole 16-token tiles
+            split_len = (split_len + 15) / 16 * 16;
     }
     rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
     if (rc != FD_OK)

@@ -195,9 +195,11 @@ def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, 
     if (o_part.shape != (batch, heads_q, num_splits, d) or o_part.dtype != torch.float32
             or lse_part.shape != (batch, heads_q, num_splits) or lse_part.dtype != torch.float32):
         raise ValueError("o_part / lse_part have the wrong shape or dtype")
-    _check(library().fd_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q,
-                                     heads_kv, n_max, d, _code(q.dtype), scale, num_splits,
-                                     split_len, _ptr(o_part), _ptr(lse_part), _stream(q.device)))
+    with torch.cuda.device(q.device):  # launches go to the current device
+        _check(library().fd_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
+                                         heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
+                                         num_splits, split_len, _ptr(o_part), _ptr(lse_part),
+                                         _stream(q.device)))
     return o_part, lse_part
 
 
@@ -221,10 +223,11 @@ def decode_split_mlo(q, k, v, kv_lens=None, *, num_splits: int, split_len: int =
         _on_device(name, t, q.device)
         if t.shape != want or t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32 {want}")
-    _check(library().fd_decode_split_mlo(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
-                                         heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
-                                         num_splits, split_len, _ptr(o_part), _ptr(m_part),
-                                         _ptr(l_part), _stream(q.device)))
+    with torch.cuda.device(q.device):  # launches go to the current device
+        _check(library().fd_decode_split_mlo(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
+                                             heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
+                                             num_splits, split_len, _ptr(o_part), _ptr(m_part),
+                                             _ptr(l_part), _stream(q.device)))
     return o_part, m_part, l_part
 
 
@@ -237,6 +240,8 @@ def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return
     if m_part.shape != (batch, heads_q, nb) or l_part.shape != (batch, heads_q, nb):
         raise ValueError("m_part / l_part shape does not match o_part")
     dev = o_part.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
     for name, t in (("o_part", o_part), ("m_part", m_part), ("l_part", l_part)):
         _on_device(name, t, dev)
     out_dtype = out_dtype or torch.float32
@@ -247,19 +252,24 @@ def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return
     _on_device("o", o, dev)
     if lse is not None:
         _on_device("lse", lse, dev)
-    _check(library().fd_combine_mlo(_ptr(o_part), _ptr(m_part), _ptr(l_part), batch, heads_q, nb,
-                                    d, _ptr(o), _code(o.dtype), _ptr(lse), _stream(dev)))
+    with torch.cuda.device(dev):  # launches go to the current device
+        _check(library().fd_combine_mlo(_ptr(o_part), _ptr(m_part), _ptr(l_part), batch,
+                                        heads_q, nb, d, _ptr(o), _code(o.dtype), _ptr(lse),
+                                        _stream(dev)))
     return o, lse
 
 
 def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True):
     """Combine stage: LSE merge over the split axis -> (o, lse)."""
     if o_part.dim() != 4 or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
-        raise ValueError("o_part must be float32 [batch, Hq, B, d], lse_part float32 [batch, Hq, B]")
+        raise ValueError("o_part must be float32 [batch, Hq, B, d], "
+                         "lse_part float32 [batch, Hq, B]")
     batch, heads_q, nb, d = o_part.shape
     if lse_part.shape != (batch, heads_q, nb):
         raise ValueError("lse_part shape does not match o_part")
     dev = o_part.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
     _on_device("o_part", o_part, dev)
     _on_device("lse_part", lse_part, dev)
     out_dtype = out_dtype or torch.float32
@@ -270,8 +280,9 @@ def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True)
     _on_device("o", o, dev)
     if lse is not None:
         _on_device("lse", lse, dev)
-    _check(library().fd_combine(_ptr(o_part), _ptr(lse_part), batch, heads_q, nb, d, _ptr(o),
-                                _code(o.dtype), _ptr(lse), _stream(dev)))
+    with torch.cuda.device(dev):  # launches go to the current device
+        _check(library().fd_combine(_ptr(o_part), _ptr(lse_part), batch, heads_q, nb, d, _ptr(o),
+                                    _code(o.dtype), _ptr(lse), _stream(dev)))
     return o, lse
 
 
@@ -292,16 +303,18 @@ def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len:
         o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
-    need = decode_workspace_bytes(batch, heads_q, heads_kv, n_max, d, q.dtype,
-                                  kv_lens is not None, num_splits, split_len)
+    with torch.cuda.device(dev):  # the plan depends on this device's compute units
+        need = decode_workspace_bytes(batch, heads_q, heads_kv, n_max, d, q.dtype,
+                                      kv_lens is not None, num_splits, split_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _on_device("o", o, dev)
-    _check(library().fd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q, heads_kv,
-                               n_max, d, _code(q.dtype), _code(o.dtype), scale, num_splits,
-                               split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes,
-                               _stream(dev)))
+    with torch.cuda.device(dev):  # launches go to the current device
+        _check(library().fd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q,
+                                   heads_kv, n_max, d, _code(q.dtype), _code(o.dtype), scale,
+                                   num_splits, split_len, _ptr(o), _ptr(lse), _ptr(workspace),
+                                   ws_bytes, _stream(dev)))
     return o, lse
 
 
@@ -322,6 +335,8 @@ def _paged_shapes(q, k_pages, v_pages, block_table, kv_lens):
     if q.dtype != k_pages.dtype or v_pages.dtype != k_pages.dtype:
         raise TypeError("q, K and V must share one dtype")
     dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
                     ("block_table", block_table)):
         _on_device(name, t, dev)
@@ -348,10 +363,11 @@ def decode_split_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, num_sp
         lse_part = torch.empty((batch, heads_q, num_splits), dtype=torch.float32, device=q.device)
     _on_device("o_part", o_part, q.device)
     _on_device("lse_part", lse_part, q.device)
-    _check(library().fd_decode_split_paged(
-        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
-        heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), scale, num_splits, split_len,
-        _ptr(o_part), _ptr(lse_part), _stream(q.device)))
+    with torch.cuda.device(q.device):  # launches go to the current device
+        _check(library().fd_decode_split_paged(
+            _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
+            heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), scale, num_splits, split_len,
+            _ptr(o_part), _ptr(lse_part), _stream(q.device)))
     return o_part, lse_part
 
 
@@ -364,22 +380,22 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, scale=None,
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out_dtype = out_dtype or q.dtype
     dev = q.device
-    if num_splits > 0 and split_len == 0:
-        split_len = _tile_split_len(max_pages * ps, num_splits)
     if o is None:
         o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
-    need = decode_workspace_bytes(batch, heads_q, heads_kv, max_pages * ps, d, q.dtype,
-                                  kv_lens is not None, num_splits, split_len)
+    with torch.cuda.device(dev):  # the plan depends on this device's compute units
+        need = decode_workspace_bytes(batch, heads_q, heads_kv, max_pages * ps, d, q.dtype,
+                                      kv_lens is not None, num_splits, split_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _on_device("o", o, dev)
-    _check(library().fd_decode_paged(
-        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
-        heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), _code(o.dtype), scale, num_splits,
-        split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
+    with torch.cuda.device(dev):  # launches go to the current device
+        _check(library().fd_decode_paged(
+            _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch,
+            heads_q, heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), _code(o.dtype), scale,
+            num_splits, split_len, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, lse
 
 
@@ -413,6 +429,8 @@ def decode_cascade(q, k_prefix, v_prefix, k_suffix, v_suffix, suffix_lens=None, 
     if any(t.dtype != q.dtype for t in (k_prefix, v_prefix, k_suffix, v_suffix)):
         raise TypeError("q, K and V must share one dtype")
     dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
     for name, t in (("q", q), ("k_prefix", k_prefix), ("v_prefix", v_prefix),
                     ("k_suffix", k_suffix), ("v_suffix", v_suffix)):
         _on_device(name, t, dev)
@@ -426,14 +444,16 @@ def decode_cascade(q, k_prefix, v_prefix, k_suffix, v_suffix, suffix_lens=None, 
         o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
         lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
-    need = cascade_workspace_bytes(batch, heads_q, heads_kv, prefix_len, max_suffix_len, d,
-                                   q.dtype, suffix_lens is not None)
+    with torch.cuda.device(dev):  # the plan depends on this device's compute units
+        need = cascade_workspace_bytes(batch, heads_q, heads_kv, prefix_len, max_suffix_len, d,
+                                       q.dtype, suffix_lens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
     _on_device("o", o, dev)
-    _check(library().fd_decode_cascade(
-        _ptr(q), _ptr(k_prefix), _ptr(v_prefix), prefix_len, _ptr(k_suffix), _ptr(v_suffix),
-        _ptr(suffix_lens), batch, heads_q, heads_kv, max_suffix_len, d, _code(q.dtype),
-        _code(o.dtype), scale, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
+    with torch.cuda.device(dev):  # launches go to the current device
+        _check(library().fd_decode_cascade(
+            _ptr(q), _ptr(k_prefix), _ptr(v_prefix), prefix_len, _ptr(k_suffix), _ptr(v_suffix),
+            _ptr(suffix_lens), batch, heads_q, heads_kv, max_suffix_len, d, _code(q.dtype),
+            _code(o.dtype), scale, _ptr(o), _ptr(lse), _ptr(workspace), ws_bytes, _stream(dev)))
     return o, lse

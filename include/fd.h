@@ -32,8 +32,11 @@
  *   m_part, l_part [batch, heads_q, num_splits]      float32 (m/l/o format)
  *
  * Conventions shared by every entry point:
- *   - All pointers except the fd_choose_splits outputs are device pointers
- *     on the current HIP device, 16-byte aligned.  The caller owns every
+ *   - All pointers except the fd_choose_splits and workspace-size outputs
+ *     are device pointers on the current HIP device.  q, k, v, o_part and
+ *     workspace are 16-byte aligned; o, lse, lse_part, m_part, l_part,
+ *     kv_lens and block_table 4-byte aligned (FD_ERR_UNSUPPORTED
+ *     otherwise).  The caller owns every
  *     buffer; the library allocates no device memory and keeps no state
  *     besides a cached per-device compute-unit count.
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  All
@@ -194,7 +197,8 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
  * page_size) entries of a table row are read; an entry outside
  * [0, num_pages) is clamped into it (memory stays in bounds, that sequence's
  * result is then meaningless).  split_len must be a multiple of 16 (the
- * automatic plan's is).  Workspace: fd_decode_workspace_bytes with max_kv_len
+ * automatic plan's is; fd_decode_paged given num_splits > 0 and split_len ==
+ * 0 rounds ceil(N / num_splits) up to one).  Workspace: fd_decode_workspace_bytes with max_kv_len
  * = max_pages_per_seq * page_size.  Extra errors: FD_ERR_INVALID for a null
  * block_table, max_pages_per_seq or num_pages < 1, or split_len % 16 != 0;
  * FD_ERR_UNSUPPORTED for page_size or page bytes out of range. */

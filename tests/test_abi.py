@@ -151,6 +151,7 @@ def test_decode_split_validation(lib):
     assert _split(lib, dt=5) == fd.ERR_UNSUPPORTED
     assert _split(lib, k=FAKE + 8) == fd.ERR_UNSUPPORTED
     assert _split(lib, o_part=FAKE + 4) == fd.ERR_UNSUPPORTED
+    assert _split(lib, kv_lens=FAKE + 2) == fd.ERR_UNSUPPORTED
     msg = fd.last_error()
     assert "aligned" in msg
 
@@ -279,6 +280,7 @@ def test_decode_validation(lib):
     assert _decode(lib, B=2, L=8) == fd.ERR_INVALID     # 16 < 64
     assert _decode(lib, out=fd.F16) == fd.ERR_UNSUPPORTED  # neither in_dtype nor f32
     assert _decode(lib, hkv=3) == fd.ERR_INVALID
+    assert _decode(lib, kv_lens=FAKE + 2) == fd.ERR_UNSUPPORTED
     # more than one split and no (or too small) workspace
     assert _decode(lib) == fd.ERR_WORKSPACE
     need = lib.fd_workspace_bytes(1, 4, 4, 64)
@@ -294,3 +296,25 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fd, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         fd.library()
+
+
+def test_binding_rejects_host_tensors():
+    """Host (CPU) tensors are refused before anything reaches the library."""
+    import torch
+
+    q = torch.zeros(1, 4, 64)
+    k = torch.zeros(1, 16, 2, 64)
+    with pytest.raises(ValueError, match="HIP device"):
+        fd.decode(q, k, k)
+    with pytest.raises(ValueError, match="HIP device"):
+        fd.decode_split(q, k, k, num_splits=2)
+    pages = torch.zeros(2, 16, 2, 64)
+    table = torch.zeros(1, 2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="HIP device"):
+        fd.decode_paged(q, pages, pages, table)
+    with pytest.raises(ValueError, match="HIP device"):
+        fd.decode_cascade(q, k[0], k[0], k, k)
+    with pytest.raises(ValueError, match="HIP device"):
+        fd.combine(torch.zeros(1, 4, 2, 64), torch.zeros(1, 4, 2))
+    with pytest.raises(ValueError, match="HIP device"):
+        fd.combine_mlo(torch.zeros(1, 4, 2, 64), torch.zeros(1, 4, 2), torch.zeros(1, 4, 2))
