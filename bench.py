@@ -495,10 +495,22 @@ def cpu_baseline(p: Prepared, budget_s: float) -> dict:
             break
     wall = time.perf_counter() - t0
     us = wall / reps * 1e6
-    return {"value": round(p.kv_bytes / (us * 1e-6) / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "us_per_step": round(us, 1),
-            "sample": f"{reps} whole decode step(s) of {w.name} (every row, fp64, OpenMP over "
-                      f"(sequence, head)), {wall:.1f} s wall"}
+    out = {"value": round(p.kv_bytes / (us * 1e-6) / 1e9, 3), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "us_per_step": round(us, 1),
+           "sample": f"{reps} whole decode step(s) of {w.name} (every row, fp64, OpenMP over "
+                     f"(sequence, head)), {wall:.1f} s wall"}
+    # the same oracle on one thread, one step, for reference
+    oracle.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.attention(*args, scale=w.scale)
+        one = time.perf_counter() - t1
+    finally:
+        oracle.set_threads(threads)
+    out["one_thread"] = {"value": round(p.kv_bytes / one / 1e9, 3), "unit": "GB/s",
+                         "us_per_step": round(one * 1e6, 1),
+                         "sample": f"1 whole decode step of {w.name} on 1 thread"}
+    return out
 
 
 def traffic_from_profile(name: str) -> dict | None:
