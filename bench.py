@@ -624,6 +624,7 @@ def main() -> int:
                    "plan": p.plan, "num_splits": None if p.balanced else p.B,
                    "split_len": None if p.balanced else p.L, "kv_bytes_per_step": p.kv_bytes,
                    "input_copies": p.copies, "parallelism": "single-gpu"},
+        "inputs_sha256": workloads.digest(p.host),
         "timing": {k: round(v, 2) for k, v in t.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -640,6 +641,7 @@ def main() -> int:
             tt = time_steps(q, args.steps, args.warmup)
             su = time_split_kernel(q, args.steps, args.warmup)
             others[w.name] = summarize(q, tt, su)
+            others[w.name]["inputs_sha256"] = workloads.digest(q.host)
             log(f"[bench] {w.name}: {others[w.name]}")
             q.free()
             del q

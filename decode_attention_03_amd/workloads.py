@@ -247,6 +247,21 @@ def kv_bytes(w: Workload, kv_lens) -> int:
     return total_tokens * w.heads_kv * w.head_dim * 2 * elem
 
 
+def digest(inp: dict) -> dict:
+    """SHA-256 (first 16 hex digits) of each generated tensor's bytes, so that
+    a run can name exactly which inputs it used."""
+    out = {}
+    for name in ("q", "k", "v", "kv_lens"):
+        t = inp.get(name)
+        if t is None:
+            continue
+        h = hashlib.sha256()
+        arr = raw(t) if t.is_floating_point() else t.contiguous().numpy()
+        h.update(memoryview(np.ascontiguousarray(arr)).cast("B"))
+        out[name] = h.hexdigest()[:16]
+    return out
+
+
 def raw(t: torch.Tensor) -> np.ndarray:
     """Storage bits of a CPU tensor as numpy (uint16 for 16-bit types, float32 for f32)."""
     t = t.contiguous()

@@ -97,3 +97,14 @@ def test_cascade_inputs_and_concatenation():
     assert not torch.equal(c["k_prefix"][:1], c["k_suffix"][0, :1])
     c0 = workloads.cascade(w, 0)
     assert c0["k_prefix"].shape == (0, 2, 64)
+
+
+def test_digest_names_the_inputs():
+    w = workloads.WORKLOADS[1]
+    a, b = workloads.digest(workloads.generate(w)), workloads.digest(workloads.generate(w))
+    assert a == b and set(a) == {"q", "k", "v"}
+    c = workloads.digest(workloads.generate(dataclasses.replace(w, seed=w.seed + 1)))
+    assert all(a[n] != c[n] for n in a)
+    r = workloads.digest(workloads.generate(
+        dataclasses.replace(workloads.WORKLOADS[4], batch=2, ragged=(3, 40))))
+    assert "kv_lens" in r
