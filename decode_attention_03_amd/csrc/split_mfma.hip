@@ -36,10 +36,12 @@
 // Data movement: each step's K and V tiles are loaded with the same
 // pattern as the vector kernel (16-byte non-temporal loads, 16 lanes per
 // 256-byte head row, so one instruction reads whole rows), into one of two
-// register sets: while one step is staged and computed, the next step's loads
-// are in flight in the other set.  The staging writes each row to LDS with its
-// 16-byte chunks XOR-swizzled by the row index, which keeps the 128-bit
-// fragment reads of K and the transpose reads of V free of bank conflicts.
+// register sets; up to d = 128 a set is refilled with the loads two steps
+// ahead as soon as its rows are staged in LDS, so two steps of loads stay in
+// flight while a step is read back and computed.  The staging writes each row
+// to LDS with its 16-byte chunks XOR-swizzled by the row index, which keeps
+// the 128-bit fragment reads of K and the transpose reads of V free of bank
+// conflicts.
 // (Direct-to-LDS loads were measured slower here: their LDS destination is
 // opaque to the compiler's wait counting, which then allows only one batch in
 // flight per wave.)  Steps are 8 KB of K+V per wave (one 16-token tile of
@@ -258,10 +260,10 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         const int lrow = lane / T::CPR;  // row within a row group
         const int lq = lane % T::CPR;    // logical chunk this lane carries
         const size_t lane_off = (size_t)kvh * T::ROW + lq * 16;
-        // Paged K/V: the page of each of a step's U tiles, looked up one step
-        // ahead of the loads that use them (the loop below).  A tile is
-        // 16-aligned (so are t0 and the step start), so it lies in one page,
-        // also after its rows are clamped to the last valid token.
+        // Paged K/V: the page of each of a step's U tiles, read before the
+        // step's loads (see the loop below for when).  A tile is 16-aligned
+        // (so are t0 and the step start), so it lies in one page, also after
+        // its rows are clamped to the last valid token.
         struct Pages {
             int pg[U];
         };
@@ -283,6 +285,16 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 }
             }
         };
+        // Addressing: a base per tile (sequence and step start, or the tile's
+        // page) plus a 32-bit per-lane row offset.  Paged, the base is uniform
+        // and the lane's column offset joins the 32-bit part, so the loads
+        // take the scalar-base form (measured 5 % faster there; contiguous,
+        // a per-lane 64-bit base measured slightly faster).  One token's row
+        // over all heads is at most 16 MiB and a page at most 2 GiB (both
+        // checked on the host), so the offsets fit in 32 bits.
+        const uint32_t stride32 = (uint32_t)tok_stride;
+        const uint32_t lane_off32 = PAGED ? (uint32_t)lane_off : 0u;
+        const size_t lane_off64 = PAGED ? 0 : lane_off;
         auto load_step = [&](int st, const Pages &P, Stage &g) {
             const int sa = st < nsteps ? st : nsteps - 1;
             const int first = sa * kStepTok;
@@ -290,21 +302,19 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 // base of tile u: contiguous K/V, or the tile's page
-                const char *kb, *vb;
+                size_t base;
                 uint32_t pmask = 0xffffffffu;
                 if constexpr (!PAGED) {
                     const size_t seq = a.shared_kv ? 0 : (size_t)b * a.max_kv_len;
-                    const size_t base = (seq + (size_t)t0 + first) * tok_stride + lane_off;
-                    kb = static_cast<const char *>(a.k) + base;
-                    vb = static_cast<const char *>(a.v) + base;
+                    base = (seq + (size_t)t0 + first) * tok_stride;
                 } else {
                     int pg = P.pg[u];
                     pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-                    const size_t base = ((size_t)pg << a.page_shift) * tok_stride + lane_off;
-                    kb = static_cast<const char *>(a.k) + base;
-                    vb = static_cast<const char *>(a.v) + base;
+                    base = ((size_t)pg << a.page_shift) * tok_stride;
                     pmask = (1u << a.page_shift) - 1u;
                 }
+                const char *kb = static_cast<const char *>(a.k) + base + lane_off64;
+                const char *vb = static_cast<const char *>(a.v) + base + lane_off64;
 #pragma unroll
                 for (int j = 0; j < T::IPT; ++j) {
                     int rel = 16 * u + j * T::RPI + lrow;
@@ -313,12 +323,13 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                     // token's row within its page
                     const uint32_t row =
                         PAGED ? ((uint32_t)((int)t0 + first + rel) & pmask) : (uint32_t)rel;
-                    const uint32_t off = row * (uint32_t)tok_stride;
+                    const uint32_t off = row * stride32 + lane_off32;
                     g.k[u][j] = ld128<NTLOAD>(kb + off);
                     g.v[u][j] = ld128<NTLOAD>(vb + off);
                 }
             }
         };
+
         // Write a step's rows into the LDS tiles, chunks swizzled per row.
         auto stage = [&](const Stage &g) {
 #pragma unroll
@@ -420,33 +431,70 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             }
         };
 
-        // Pipeline over two register sets (as in the vector kernel): the next
-        // step's loads are issued before the current step is staged, read
-        // back as fragments and computed, so the compiler waits only for the
-        // older set.  The LDS tile is rewritten each step; one wave's LDS
-        // operations execute in order, so a step's writes follow the previous
-        // step's reads.
+        // Pipeline over two register sets.  A step's rows leave their
+        // registers as soon as they are staged in LDS, so the loads two steps
+        // ahead go into those registers right then, before the step's
+        // fragments are read back and computed: two steps of loads stay in
+        // flight throughout.  (Issuing them after the arithmetic instead
+        // measured 1-3 % slower at d = 128.)  At d = 256 that keeps 128 more
+        // registers live across the arithmetic than the register file holds
+        // without spilling, so there the next step's loads are issued when
+        // the current step starts (one to two steps in flight).  Paged K/V:
+        // a step's table entries are scalar loads, and a wave's LDS reads are
+        // waited on with the same counter (which then cannot tell them apart),
+        // so each lookup is issued after a step's arithmetic, once that
+        // step's fragment reads have been waited on: it has the next staging
+        // (which waits for that step's rows) to arrive.  The LDS tile is
+        // rewritten each step;
+        // one wave's LDS operations execute in order, so a step's writes
+        // follow the previous step's reads.
         Frags f;
         Stage ga, gb;
         Pages pa, pb;
         const int npairs = nsteps >> 1;
         lookup(0, pa);
-        load_step(0, pa, ga);
         lookup(1, pb);
-        for (int pr = 0; pr < npairs; ++pr) {
-            const int st = 2 * pr;
-            load_step(st + 1, pb, gb);
-            lookup(st + 2, pa);
-            __builtin_amdgcn_sched_barrier(0);
-            stage(ga);
-            fetch(tb, f);
-            compute_step(st, f);
-            load_step(st + 2, pa, ga);
-            lookup(st + 3, pb);
-            __builtin_amdgcn_sched_barrier(0);
-            stage(gb);
-            fetch(tb, f);
-            compute_step(st + 1, f);
+        load_step(0, pa, ga);
+        if constexpr (D <= 128) {
+            load_step(1, pb, gb);
+            lookup(2, pa);
+            for (int pr = 0; pr < npairs; ++pr) {
+                const int st = 2 * pr;
+                stage(ga);
+                __builtin_amdgcn_sched_barrier(0);
+                load_step(st + 2, pa, ga);
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(tb, f);
+                compute_step(st, f);
+                if constexpr (PAGED)
+                    __builtin_amdgcn_sched_barrier(0);
+                lookup(st + 3, pb);
+                stage(gb);
+                __builtin_amdgcn_sched_barrier(0);
+                load_step(st + 3, pb, gb);
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(tb, f);
+                compute_step(st + 1, f);
+                if constexpr (PAGED)
+                    __builtin_amdgcn_sched_barrier(0);
+                lookup(st + 4, pa);
+            }
+        } else {
+            for (int pr = 0; pr < npairs; ++pr) {
+                const int st = 2 * pr;
+                load_step(st + 1, pb, gb);
+                lookup(st + 2, pa);
+                __builtin_amdgcn_sched_barrier(0);
+                stage(ga);
+                fetch(tb, f);
+                compute_step(st, f);
+                load_step(st + 2, pa, ga);
+                lookup(st + 3, pb);
+                __builtin_amdgcn_sched_barrier(0);
+                stage(gb);
+                fetch(tb, f);
+                compute_step(st + 1, f);
+            }
         }
         if (nsteps & 1) {
             stage(ga);
