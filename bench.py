@@ -3,7 +3,7 @@
 KV bandwidth (bytes of K and V a step must read / step time) against the
 8 TB/s HBM peak.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--section S]
 
 One "step" is one fd_decode call (split kernel + combine kernel) over one
 batch of the workload, inputs already resident in HBM.  The headline
@@ -354,7 +354,7 @@ CASCADE = workloads.Workload("cascade_gqa_bf16_b16_hq64_hkv8_d128_prefix16384_su
 CASCADE_PREFIX = 16384
 
 
-def time_cascade(steps: int, warmup: int, dev: torch.device) -> dict:
+def time_cascade(steps: int, warmup: int, dev: torch.device, materialised: bool = True) -> dict:
     """Shared-prefix decode (fd_decode_cascade: one prefix copy for the batch)
     against fd_decode over the materialised per-sequence caches (prefix +
     suffix each).  Wall clock over `steps` steps, several input copies so that
@@ -406,6 +406,12 @@ def time_cascade(steps: int, warmup: int, dev: torch.device) -> dict:
     us_c = region(lambda i: check(lib.fd_decode_cascade(*cargs[i])), copies)
     del bufs, cargs, ws
     torch.cuda.empty_cache()
+    if not materialised:
+        return {"workload": w.name, "prefix_len": CASCADE_PREFIX,
+                "suffix_tokens": int(lens.sum()), "cascade_us_per_step": round(us_c, 2),
+                "logical_kv_bytes": logical, "unique_kv_bytes": unique,
+                "prefix_kv_bytes": CASCADE_PREFIX * row,
+                "cascade_unique_GBps": round(unique / (us_c * 1e-6) / 1e9, 1)}
     # plain decode over the materialised caches
     copies_p = max(2, min(16, math.ceil((1 << 30) / logical) + 1))
     kl = cc["kv_lens"].to(dev)
@@ -561,6 +567,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="oracle seconds (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--section", choices=("cascade", "paged", "shard"), default=None,
+                    help="time only this section of the full run and print its JSON (profiling)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -583,6 +591,17 @@ def main() -> int:
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         log(f"[bench] copy probe: 5 dispatches reading and writing {args.copy_probe} bytes each")
+        return 0
+
+    if args.section:
+        if args.section == "cascade":
+            sec = time_cascade(args.steps, args.warmup, dev, materialised=False)
+        elif args.section == "shard":
+            sec = time_shard(args.steps, args.warmup, dev)
+        else:  # the paged step of the ragged grouped workload, 16-token pages
+            w = workloads.WORKLOADS[4]
+            sec = {"workload": w.name, **time_paged(w, dev, 16, args.steps, args.warmup)}
+        print(json.dumps({"section": args.section, **sec}), flush=True)
         return 0
 
     head = workloads.WORKLOADS[args.config]

@@ -19,6 +19,10 @@ then reads the CSV files rocprofv3 wrote under RAW.  Three kinds of run:
   LdsUtil, SALUBusy: percent of the kernel's active GPU time the vector ALUs,
   matrix cores, LDS and scalar ALU were busy) on the split kernel.
 
+With ``--section S`` it profiles one extra section of ``bench.py`` instead
+(cascade, paged, shard): the kernel trace plus HBM bytes per dispatch of
+every kernel the section launches, in ``<S>_<workload>.md``.
+
 Written under OUT: ``<kernel>_<workload>.md`` (trace summary and traffic),
 ``traffic_<workload>.json`` (what bench.py reports as ``roofline.traffic``,
 keyed by the hash of the kernel's sources so that it lapses when the kernel
@@ -127,7 +131,11 @@ def main() -> int:
     ap.add_argument("--pmc-steps", type=int, default=3)
     ap.add_argument("--skip-copy", action="store_true",
                     help="reuse the copy calibration already in RAW")
+    ap.add_argument("--section", choices=("cascade", "paged", "shard"), default=None,
+                    help="profile one section of bench.py instead of a named workload")
     args = ap.parse_args()
+    if args.section:
+        return section_main(args)
 
     w = workloads.WORKLOADS[args.config]
     raw = os.path.abspath(args.raw)
@@ -303,6 +311,106 @@ def main() -> int:
         "",
     ]
     md = os.path.join(out, f"{fam}_{w.name}.md")
+    with open(md, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines))
+    print(f"[prof] wrote {md}", file=sys.stderr, flush=True)
+    return 0
+
+
+def calibrate(raw: str, skip: bool, log_path: str) -> tuple[dict, dict]:
+    """Copy-probe passes (FETCH_SIZE, WRITE_SIZE): bytes per counter unit."""
+    copy = [sys.executable, BENCH, "--copy-probe", str(COPY_BYTES)]
+    cmds, cal = {}, {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmd = ["rocprofv3", "--pmc", counter, "-d", raw, "-o", f"copy_{counter}",
+               "--output-format", "csv", "--", *copy]
+        if not skip:
+            run(cmd, 120, log_path)
+        cmds[counter] = cmd
+        v, n, cname = counter_per_dispatch(
+            os.path.join(raw, f"copy_{counter}_counter_collection.csv"), counter)
+        cal[counter] = {"kernel": cname, "counter_per_dispatch": v, "dispatches": n,
+                        "bytes_per_unit": COPY_BYTES / v}
+    return cal, cmds
+
+
+def section_main(args) -> int:
+    """Kernel trace and HBM bytes per dispatch of every kernel that one bench.py
+    section launches (cascade: the shared-prefix kernel, the suffix kernel and
+    the combine; paged: the ragged grouped workload over 16-token pages;
+    shard: one GPU's share of the long-context workload and the merge)."""
+    raw = os.path.abspath(args.raw)
+    out = os.path.abspath(args.out)
+    os.makedirs(raw, exist_ok=True)
+    os.makedirs(out, exist_ok=True)
+    sec = args.section
+    log_path = os.path.join(raw, f"section_{sec}.log")
+    py = sys.executable
+
+    def shown(cmd: list[str]) -> str:
+        return " ".join(cmd).replace(raw, "RAW").replace(ROOT + "/", "")
+
+    bench_cmd = [py, BENCH, "--section", sec]
+    res = last_json_line(run(bench_cmd, 300, log_path))
+    trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "-d", raw, "-o", f"{sec}_trace",
+                 "--output-format", "csv", "--", *bench_cmd]
+    run(trace_cmd, 300, log_path)
+    stats = trace_stats(os.path.join(raw, f"{sec}_trace_kernel_trace.csv"))
+    short = [py, BENCH, "--section", sec, "--steps", str(args.pmc_steps), "--warmup", "1"]
+    pmc_cmds = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmd = ["rocprofv3", "--pmc", counter, "-d", raw, "-o", f"{sec}_{counter}",
+               "--output-format", "csv", "--", *short]
+        run(cmd, 240, log_path)
+        pmc_cmds[counter] = cmd
+    cal, copy_cmds = calibrate(raw, args.skip_copy, log_path)
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = os.path.join(raw, f"{sec}_{counter}_counter_collection.csv")
+        names = sorted({r["Kernel_Name"] for r in read_csv(path) if r["Counter_Name"] == counter})
+        for name in names:
+            v, n, _ = counter_per_dispatch(path, counter, lambda k, name=name: k == name)
+            per.setdefault(name, {})[counter] = v * cal[counter]["bytes_per_unit"]
+    lines = [
+        f"# bench.py section `{sec}`: {res.get('workload', '')}",
+        "",
+        "Made by (repository root):",
+        "",
+        f"    python3 -m decode_attention_03_amd.rocprof_summary --section {sec} --raw RAW "
+        "--out profiles",
+        "",
+        "which runs, from /tmp:",
+        "",
+        "    " + shown(bench_cmd),
+        "    " + shown(trace_cmd),
+        "    " + shown(pmc_cmds["FETCH_SIZE"]),
+        "    " + shown(pmc_cmds["WRITE_SIZE"]),
+        "    " + shown(copy_cmds["FETCH_SIZE"]),
+        "    " + shown(copy_cmds["WRITE_SIZE"]),
+        "",
+        "bench.py section result (same command, not under the profiler):",
+        "",
+        "    " + json.dumps(res),
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats) and HBM bytes per dispatch",
+        "",
+        "HBM bytes: FETCH_SIZE and WRITE_SIZE per dispatch (one counter per pass), scaled by what "
+        f"the same counters read for a copy kernel of {COPY_BYTES} bytes each way "
+        f"({cal['FETCH_SIZE']['bytes_per_unit']:.2f} and "
+        f"{cal['WRITE_SIZE']['bytes_per_unit']:.2f} bytes per unit).",
+        "",
+        "| kernel | calls | avg µs | min µs | max µs | share | HBM read B | HBM write B |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for r in stats:
+        b = per.get(r["kernel"], {})
+        rd = f"{b['FETCH_SIZE']:.0f}" if "FETCH_SIZE" in b else ""
+        wr = f"{b['WRITE_SIZE']:.0f}" if "WRITE_SIZE" in b else ""
+        lines.append(f"| `{r['kernel']}` | {r['calls']} | {r['avg_us']:.2f} | {r['min_us']:.2f} | "
+                     f"{r['max_us']:.2f} | {100 * r['share']:.1f} % | {rd} | {wr} |")
+    lines.append("")
+    wname = res.get("workload", sec)
+    md = os.path.join(out, (wname if wname.startswith(sec + "_") else f"{sec}_{wname}") + ".md")
     with open(md, "w", encoding="utf-8") as f:
         f.write("\n".join(lines))
     print(f"[prof] wrote {md}", file=sys.stderr, flush=True)
