@@ -10,6 +10,7 @@
   an explicit count at that cap.
 - Many sequences (more units than work-groups in the balanced partition, and
   most work-groups spanning several units), and many heads.
+- Query groups larger than one matrix-core tile (32 query heads per KV head).
 """
 import numpy as np
 import pytest
@@ -110,3 +111,15 @@ def test_many_heads(gpu):
     for splits in (0, 1, 4):
         o, lse = _run(gpu, inp, w, num_splits=splits)
         _check(f"hq128_hkv64_B{splits}", o, lse, inp, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_groups_larger_than_a_matrix_tile(gpu, dtype):
+    """32 query heads per KV head: past the 16 rows of one matrix-core tile,
+    so the vector kernel runs each query head on its own; ragged lengths,
+    automatic plan and explicit splits."""
+    lens = [2500, 1, 0, 777]
+    w, inp = workloads.custom(4, 64, 2, 128, max(lens), dtype=dtype, seed=67, lens=lens)
+    for splits in (0, 1, 5):
+        o, lse = _run(gpu, inp, w, num_splits=splits)
+        _check(f"G32_{dtype}_B{splits}", o, lse, inp, w)
