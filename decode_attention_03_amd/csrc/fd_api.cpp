@@ -28,6 +28,11 @@ constexpr int kWorkGroupsPerCU = fd::kWavesPerCU;  // resident one-wave work-gro
 constexpr int kRaggedRounds = 4;       // work-group rounds aimed at for ragged batches
 constexpr int kMinSplitLenMha = 256;   // tokens; partial traffic ~0.8% of K/V at d = 128
 constexpr int kMinSplitLenPerHead = 64;  // grouped: tokens per query head of the group
+// Groups past one tile: at least this many tokens per query head, so that a
+// split's partials (written and read back: G (d + 1) 4-byte values twice) stay
+// within about a quarter of its K/V bytes; a long floor would leave these
+// small-K/V, many-query shapes with too few work-groups.
+constexpr int kMinSplitLenPerHeadTiled = 8;
 constexpr int kMaxAutoSplits = 512;
 constexpr int kBalancedRounds = 1;     // token-balanced work-groups: CUs * per-CU * rounds
 
@@ -156,6 +161,23 @@ void set_paging(fd::SplitArgs &a, const Paging *pg) {
     a.num_pages = pg->num_pages;
 }
 
+// Groups of more than one matrix-core tile of query heads (bf16/f16): the
+// tiled kernel, which reads each K/V row once for all of them.
+bool large_group(int in_dtype, int head_dim, int group) {
+    return group >= 2 && !fd::split_mfma_supported(in_dtype, head_dim, group) &&
+           fd::split_mfma_tiled_supported(in_dtype, head_dim);
+}
+
+// Query tiles per work-group of the tiled kernel for nq queries per KV head:
+// the most that fit, but no more than there are tiles.
+int tiled_qt(int head_dim, long long nq) {
+    const long long tiles = (nq + 15) / 16;
+    int qt = fd::split_mfma_tile_max_qt(head_dim);
+    while (qt > 1 && qt / 2 >= tiles)
+        qt /= 2;
+    return qt;
+}
+
 // Waves per work-group when the vector kernel runs every split of a row in one
 // work-group and merges them in LDS (no combine launch, no workspace): fixed
 // splits, 2..8 of them, on a grid whose split work-groups would not even fill
@@ -163,7 +185,8 @@ void set_paging(fd::SplitArgs &a, const Paging *pg) {
 int fused_waves(int batch, int heads_q, int heads_kv, int head_dim, int in_dtype,
                 int num_splits) {
     if (num_splits < 2 || num_splits > 8 ||
-        fd::split_mfma_supported(in_dtype, head_dim, heads_q / heads_kv))
+        fd::split_mfma_supported(in_dtype, head_dim, heads_q / heads_kv) ||
+        large_group(in_dtype, head_dim, heads_q / heads_kv))
         return 0;
     int cus = 0;
     if (device_cus(&cus) != FD_OK)
@@ -176,7 +199,10 @@ int fused_waves(int batch, int heads_q, int heads_kv, int head_dim, int in_dtype
 int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     const int group = a.heads_q / a.heads_kv;
     hipError_t e;
-    if (a.prefix_qt > 0 || fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
+    if (a.tile_qt > 0 || fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
+        e = fd::launch_split_mfma(a, in_dtype, stream);
+    } else if (large_group(in_dtype, a.head_dim, group)) {
+        a.tile_qt = tiled_qt(a.head_dim, group);
         e = fd::launch_split_mfma(a, in_dtype, stream);
     } else {
         // two waves per work-group when one-wave work-groups would leave wave
@@ -274,13 +300,23 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     }
     const int group = heads_q / heads_kv;
     const bool grouped = fd::split_mfma_supported(in_dtype, head_dim, group);
+    const bool tiled = large_group(in_dtype, head_dim, group);
     // work-groups per split index: one per (sequence, KV head) when a group is
-    // computed together, else one per (sequence, query head)
-    const long long units = (long long)batch * (grouped ? heads_kv : heads_q);
-    const long long target = (long long)num_cus * (grouped ? fd::kMfmaWgPerCU : kWorkGroupsPerCU) *
-                             (ragged ? kRaggedRounds : 1);
+    // computed together, one per (sequence, KV head, tile group) when it takes
+    // several tiles, else one per (sequence, query head)
+    long long units = (long long)batch * (grouped ? heads_kv : heads_q);
+    int per_cu = grouped ? fd::kMfmaWgPerCU : kWorkGroupsPerCU;
+    if (tiled) {
+        const long long tiles = (group + 15) / 16;
+        const int qt = tiled_qt(head_dim, group);
+        units = (long long)batch * heads_kv * ((tiles + qt - 1) / qt);
+        per_cu = fd::kPrefixWgPerCU;
+    }
+    const long long target = (long long)num_cus * per_cu * (ragged ? kRaggedRounds : 1);
     long long b = (target + units - 1) / units;
-    const long long min_len = grouped ? kMinSplitLenPerHead * group : kMinSplitLenMha;
+    long long min_len = grouped ? kMinSplitLenPerHead * group : kMinSplitLenMha;
+    if (tiled && (long long)kMinSplitLenPerHeadTiled * group > min_len)
+        min_len = (long long)kMinSplitLenPerHeadTiled * group;
     long long bmax = (max_kv_len + min_len - 1) / min_len;
     if (bmax < 1)
         bmax = 1;
@@ -293,7 +329,7 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     // the vector kernel runs a lone split per row with one multi-wave
     // work-group per CU, which fills the same wave slots as up to kWavesPerCU
     // splits and needs no combine stage
-    if (!grouped && !ragged && b >= 2 && b <= fd::kWavesPerCU)
+    if (!grouped && !tiled && !ragged && b >= 2 && b <= fd::kWavesPerCU)
         b = 1;
     long long len = (max_kv_len + b - 1) / b;
     len = (len + 15) / 16 * 16;  // whole 16-token tiles
@@ -418,7 +454,7 @@ int check_combine(const float *o_part, int batch, int heads_q, int num_splits, i
 // (B_p + B_s slots per row, prefix first).
 struct CascadePlan {
     int bp = 0, lp = 0, bs = 1, ls = 1;
-    int prefix_qt = 0;  // > 0: the prefix runs on the shared-prefix matrix-core kernel
+    int tile_qt = 0;  // > 0: the prefix runs on the tiled matrix-core kernel
     // ragged grouped suffixes: token-balanced partition (bal), its slots merged
     // with the prefix partials by the slot combine; bs/ls unused then
     bool balanced = false;
@@ -430,19 +466,18 @@ struct CascadePlan {
 
 constexpr int kMinPrefixSplitLen = 256;  // tokens
 
-// Prefix splits for the shared-prefix kernel: its work-groups per split are
-// heads_kv x (query tile groups), and the split count fills the GPU's wave
-// slots once.
+// Prefix splits for the tiled kernel over the shared prefix: its work-groups
+// per split are heads_kv x (query tile groups), and the split count fills
+// the GPU's wave slots once.
 int prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int head_dim,
                 CascadePlan *p) {
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != FD_OK)
         return rc;
-    const int tiles = (int)(((long long)batch * (heads_q / heads_kv) + 15) / 16);
-    int qt = fd::split_mfma_prefix_max_qt(head_dim);
-    while (qt > 1 && qt / 2 >= tiles)
-        qt /= 2;
+    const long long nq = (long long)batch * (heads_q / heads_kv);
+    const long long tiles = (nq + 15) / 16;
+    const int qt = tiled_qt(head_dim, nq);
     const long long per_split = (long long)heads_kv * ((tiles + qt - 1) / qt);
     long long b = ((long long)cus * fd::kPrefixWgPerCU + per_split - 1) / per_split;
     const long long bmax = (prefix_len + kMinPrefixSplitLen - 1) / kMinPrefixSplitLen;
@@ -452,7 +487,7 @@ int prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int head_d
     len = (len + 15) / 16 * 16;
     p->bp = (int)((prefix_len + len - 1) / len);
     p->lp = (int)len;
-    p->prefix_qt = qt;
+    p->tile_qt = qt;
     return FD_OK;
 }
 
@@ -467,7 +502,7 @@ int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_s
         return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
                     in_dtype);
     int rc;
-    if (prefix_len > 0 && fd::split_mfma_prefix_supported(in_dtype, head_dim)) {
+    if (prefix_len > 0 && fd::split_mfma_tiled_supported(in_dtype, head_dim)) {
         rc = prefix_plan(batch, heads_q, heads_kv, prefix_len, head_dim, p);
         if (rc != FD_OK)
             return rc;
@@ -571,7 +606,7 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
         pa.shared_kv = 1;
         pa.num_splits = p.bp;
         pa.split_len = p.lp;
-        pa.prefix_qt = p.prefix_qt;
+        pa.tile_qt = p.tile_qt;
         rc = launch_split(pa, in_dtype, st);
         if (rc != FD_OK)
             return rc;

@@ -25,8 +25,9 @@ constexpr int kWavesPerCU = FD_WAVES_PER_CU;
 #endif
 constexpr int kMfmaWgPerCU = FD_MFMA_WG_PER_CU;
 
-// Resident work-groups per CU of the shared-prefix kernel: its K/V rows are
-// read by several work-groups each, so more of them in flight per CU pays.
+// Resident work-groups per CU of the tiled kernel (shared prefix, groups of
+// more than 16 query heads): its K/V rows are read by several work-groups
+// each, so more of them in flight per CU pays.
 #ifndef FD_PREFIX_WG_PER_CU
 #define FD_PREFIX_WG_PER_CU 4
 #endif
@@ -70,10 +71,13 @@ struct SplitArgs {
     // Shared cache: with shared_kv set every sequence reads the same K/V
     // ([max_kv_len, heads_kv, d], batch stride 0), as the cascade's prefix.
     int shared_kv;
-    // Shared prefix on the matrix cores (shared_kv set, bf16/f16): all batch *
-    // G queries of a KV head in tiles of 16, prefix_qt tiles per work-group
-    // (1, 2 or 4); 0 selects the ordinary kernels.
-    int prefix_qt;
+    // Query tiles on the matrix cores (bf16/f16): the queries of a KV head in
+    // tiles of 16 rows, tile_qt tiles per work-group (1, 2 or 4), several
+    // work-groups per (KV head, split) when there are more tiles.  With
+    // shared_kv set (the cascade's prefix) the queries are all batch * G of
+    // the KV head; otherwise the G queries of one sequence (groups larger
+    // than one tile).  0 selects the one-tile kernels.
+    int tile_qt;
     // Fixed-split partial slots: split i of row r is slot r * part_stride +
     // part_offset + i (part_stride 0 means num_splits), so two launches can
     // fill one partial buffer.
@@ -90,18 +94,20 @@ struct SplitArgs {
 };
 
 // VALU split kernel: one work-group (a.valu_waves waves) per (sequence, query
-// head, split).
-// Handles every head_dim/dtype; with heads_q > heads_kv each query head reads
-// its shared KV head on its own.
+// head, split).  Handles every head_dim/dtype; used for one query head per
+// KV head and for fp32 (with heads_q > heads_kv each query head reads its
+// shared KV head on its own).
 hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
-// MFMA split kernel for grouped heads: one work-group per (sequence, KV head,
-// split) computing all heads_q/heads_kv query rows of the group.  Returns
-// hipErrorNotSupported for shapes it does not cover (the caller then uses the
-// VALU kernel).
+// MFMA split kernels for grouped heads (bf16/f16): one work-group per
+// (sequence, KV head, split) computing all G <= 16 query rows of the group in
+// one tile; with tile_qt set, the tiled kernel (16-query tiles, several
+// work-groups per unit).
 bool split_mfma_supported(int in_dtype, int head_dim, int group);
-bool split_mfma_prefix_supported(int in_dtype, int head_dim);
-int split_mfma_prefix_max_qt(int head_dim);  // query tiles per work-group, 1..4
+// The tiled kernel: any group size (per sequence: groups larger than one
+// tile; shared prefix: any).
+bool split_mfma_tiled_supported(int in_dtype, int head_dim);
+int split_mfma_tile_max_qt(int head_dim);  // query tiles per work-group, 1..4
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.

@@ -10,9 +10,11 @@
 //
 // When G = heads_q / heads_kv query heads share one KV head, every K and V
 // row a split reads serves G query rows, and the split step is a small dense
-// contraction: S = Q_g K_tile^T (G x tokens) and O += P V_tile.  One wave
-// (one work-group) owns one (sequence b, KV head, split i) and the tokens
-// [i*L, min((i+1)*L, N_b)) ([P1] §2.5 stage 1), in tiles of 16 tokens:
+// contraction: S = Q_g K_tile^T (G x tokens) and O += P V_tile.  For G <= 16
+// one wave (one work-group) owns one (sequence b, KV head, split i) and the
+// tokens [i*L, min((i+1)*L, N_b)) ([P1] §2.5 stage 1), in tiles of 16
+// tokens (larger groups, and a prefix shared by the whole batch, use the
+// tiled kernel further down: 16-query tiles, several per work-group):
 //
 //   S^T (16 tokens x 16 heads) = K_tile (16 x d) . Q_g^T (d x 16):
 //     v_mfma_f32_16x16x32 over d.  A 128-bit load of 8 contiguous d-elements
@@ -148,14 +150,14 @@ struct Tiles {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-// K/V bytes per step of the shared-prefix kernel (both halves).
+// K/V bytes per step of the tiled kernel (both halves).
 #ifndef FD_PREFIX_STEP_KB
 #define FD_PREFIX_STEP_KB 16
 #endif
 #ifndef FD_PREFIX_QT128
 #define FD_PREFIX_QT128 2
 #endif
-constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;
+constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the tiled kernel
 
 // Where a piece's results go.  Partial i of query row `row` (slot h of a
 // tile when `local`) is at index (row or h) * stride + off: o at o + index * D
@@ -171,21 +173,22 @@ struct PieceOut {
 };
 
 // The query rows one work-group serves, in tiles of 16 (the matrix-core
-// width).  Standard: the G query heads of (sequence b, KV head kvh), one
-// tile.  Shared prefix: all batch * G queries of KV head kvh, tiles tile0,
-// tile0 + 1, ...  row() is the query's row in q [batch * heads_q, d], -1 for
-// an unused slot.
+// width).  One tile: the G <= 16 query heads of (sequence b, KV head kvh).
+// Tiled: the queries of KV head kvh numbered qi = 0 .. nq - 1 (the G heads of
+// sequence b, or for a shared prefix all batch * G queries, sequence
+// qi / G), tiles tile0, tile0 + 1, ...  row() is the query's row in
+// q [batch * heads_q, d], -1 for an unused slot.
 struct QMap {
-    int base;   // standard: b * heads_q + kvh * G
+    int base;   // one tile: b * heads_q + kvh * G; tiled: b * heads_q (0 for a shared prefix)
     int G;
-    int nq;     // shared prefix: batch * G; 0 in the standard form
+    int nq;     // tiled: queries of the KV head (G, or batch * G for a shared prefix); 0: one tile
     int tile0;
     int heads_q, kvh;
     __device__ __forceinline__ int row(int qt, int i) const {
         if (nq == 0)
             return i < G ? base + i : -1;
         const int qi = (tile0 + qt) * 16 + i;
-        return qi < nq ? (qi / G) * heads_q + kvh * G + qi % G : -1;
+        return qi < nq ? base + (qi / G) * heads_q + kvh * G + qi % G : -1;
     }
 };
 
@@ -584,35 +587,50 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Shared prefix (cascade): all batch * G queries of a KV head read the same
-// prefix split, so a work-group serves QT tiles of 16 of them from each K/V
-// tile it stages, and the work-groups sharing one (KV head, split) unit are
-// given block indices congruent mod 8: blocks are dispatched round-robin over
-// the eight XCDs, so they run on one XCD and meet the unit's K/V in its L2.
-// blockIdx -> (xcd = idx % 8, slot = idx / 8); slot -> (unit / 8 within the
-// XCD, tile group j fastest); unit = (split, KV head), KV head fastest.
-template <int DT, int D, int QT>
-__global__ __launch_bounds__(64) void split_mfma_prefix_kernel(SplitArgs a) {
+// Query tiles: all queries of a KV head that read the same K/V, in tiles of
+// 16, QT tiles per work-group; a (KV head, split) unit with more tiles gets
+// several work-groups.  Two uses: a shared prefix (cascade), whose batch * G
+// queries all read the prefix, and groups of more than 16 query heads per KV
+// head (up to multi-query attention), whose G queries read their sequence's
+// K/V.  Each work-group serves its QT tiles from every K/V tile it stages,
+// and the work-groups sharing one unit are given block indices congruent mod
+// 8: blocks are dispatched round-robin over the eight XCDs, so they run on
+// one XCD and meet the unit's K/V in its L2.  blockIdx -> (xcd = idx % 8,
+// slot = idx / 8); slot -> (unit / 8 within the XCD, tile group j fastest);
+// unit = (sequence, split, KV head), KV head fastest (one sequence for a
+// shared prefix).  The K/V loads are ordinary (temporal) loads, as other
+// work-groups may read the same rows.
+template <int DT, int D, int QT, bool PAGED>
+__global__ __launch_bounds__(64) void split_mfma_tiled_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D, kPrefixStepKB>::BUF];
     const int G = a.heads_q / a.heads_kv;
-    const int nq = a.batch * G;
+    const int nq = a.shared_kv ? a.batch * G : G;
     const int groups = ((nq + 15) / 16 + QT - 1) / QT;  // tile groups per unit
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
     const int unit = (slot / groups) * 8 + xcd;
     const int j = slot % groups;
-    if (unit >= a.heads_kv * a.num_splits)
+    const int seqs = a.shared_kv ? 1 : a.batch;
+    if (unit >= seqs * a.heads_kv * a.num_splits)
         return;
     const int kvh = unit % a.heads_kv;
-    const int split = unit / a.heads_kv;
+    const int rest = unit / a.heads_kv;
+    const int split = rest % a.num_splits;
+    const int b = rest / a.num_splits;
+    const int n = a.shared_kv ? a.max_kv_len : clamp_len(a.kv_lens, b, a.max_kv_len);
     const long t0 = (long)split * a.split_len;
-    const long t1 = t0 + a.split_len < a.max_kv_len ? t0 + a.split_len : a.max_kv_len;
-    const QMap qm{0, G, nq, j * QT, a.heads_q, kvh};
-    PieceOut out{a.o_part, a.lse_part, nullptr, a.part_stride ? a.part_stride : a.num_splits,
-                 a.part_offset + split, false};
-    // the unit's other work-groups read the same K/V: ordinary (temporal) loads
-    mfma_piece<DT, D, false, QT, 0, kPrefixStepKB>(a, (lds_char *)tile_buf, 0, kvh, t0, t1, qm,
+    const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
+    const QMap qm{a.shared_kv ? 0 : b * a.heads_q, G, nq, j * QT, a.heads_q, kvh};
+    PieceOut out{nullptr, nullptr, nullptr, 0, 0, false};
+    if (a.o_part) {
+        out.o = a.o_part;
+        out.stride = a.part_stride ? a.part_stride : a.num_splits;
+        out.off = a.part_offset + split;
+        out.lse = a.m_part ? a.m_part : a.lse_part;
+        out.l = a.m_part ? a.l_part : nullptr;
+    }
+    mfma_piece<DT, D, PAGED, QT, 0, kPrefixStepKB>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm,
                                                    out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -691,53 +709,57 @@ int lds_per_cu_mfma() {
     return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-// Query tiles per work-group of the shared-prefix kernel that fit in the
-// register file without spilling next to 16 KB steps (every tile keeps its
+// Query tiles per work-group of the tiled kernel that fit in the register
+// file without spilling next to 16 KB steps (every tile keeps its
 // own Q fragments, O accumulators and softmax state).  Four tiles fit at
 // d = 128 with 8 KB steps, but measured slower: the smaller steps and the
 // shorter splits that the fewer work-groups need cost more than the halved
 // re-reads save.
 template <int D>
-constexpr int prefix_max_qt() {
+constexpr int tile_max_qt() {
     return D == 64 ? 4 : (D == 128 ? FD_PREFIX_QT128 : 1);
+}
+
+// The tiled kernel for QT query tiles per work-group, paged or contiguous.
+template <int DT, int D, int QT>
+void launch_tiled(const SplitArgs &a, dim3 g, dim3 blk, size_t pad, hipStream_t stream) {
+    if (a.block_table)
+        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, true>), g, blk, pad, stream, a);
+    else
+        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false>), g, blk, pad, stream, a);
 }
 
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
-    const size_t kStatic = a.prefix_qt > 0 ? (size_t)Tiles<D, kPrefixStepKB>::BUF : (size_t)T::BUF;
+    const size_t kStatic = a.tile_qt > 0 ? (size_t)Tiles<D, kPrefixStepKB>::BUF : (size_t)T::BUF;
     long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
-    if (a.prefix_qt > 0) {  // shared prefix: (8-aligned units) x tile groups
-        const int tiles = (a.batch * (a.heads_q / a.heads_kv) + 15) / 16;
-        const long groups = (tiles + a.prefix_qt - 1) / a.prefix_qt;
-        const long units = (long)a.heads_kv * a.num_splits;
+    if (a.tile_qt > 0) {  // query tiles: (8-aligned units) x tile groups
+        const long nq = (long)(a.shared_kv ? a.batch : 1) * (a.heads_q / a.heads_kv);
+        const long tiles = (nq + 15) / 16;
+        const long groups = (tiles + a.tile_qt - 1) / a.tile_qt;
+        const long units = (long)(a.shared_kv ? 1 : a.batch) * a.heads_kv * a.num_splits;
         grid = (units + 7) / 8 * 8 * groups;
+        if (grid > 0x7fffffffL)
+            return hipErrorInvalidValue;
     }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
-    const int per_cu = a.prefix_qt > 0 ? kPrefixWgPerCU : kMfmaWgPerCU;
+    const int per_cu = a.tile_qt > 0 ? kPrefixWgPerCU : kMfmaWgPerCU;
     if (per_cu > 0 && lds > 0) {
         const size_t want = (size_t)lds / (per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
     }
     const dim3 g((unsigned)grid), blk(64);
-    if (a.prefix_qt > 0) {
-        if (a.prefix_qt > prefix_max_qt<D>())
-            return hipErrorInvalidValue;
-        if (a.prefix_qt == 1)
-            hipLaunchKernelGGL((split_mfma_prefix_kernel<DT, D, 1>), g, blk, pad, stream, a);
-        else if constexpr (prefix_max_qt<D>() >= 2) {
-            if (a.prefix_qt == 2)
-                hipLaunchKernelGGL((split_mfma_prefix_kernel<DT, D, 2>), g, blk, pad, stream, a);
-            else if constexpr (prefix_max_qt<D>() >= 4) {
-                if (a.prefix_qt == 4)
-                    hipLaunchKernelGGL((split_mfma_prefix_kernel<DT, D, 4>), g, blk, pad, stream,
-                                       a);
-                else
-                    return hipErrorInvalidValue;
-            } else {
-                return hipErrorInvalidValue;
-            }
+    if (a.tile_qt > 0) {
+        if (a.tile_qt == 1) {
+            launch_tiled<DT, D, 1>(a, g, blk, pad, stream);
+        } else if (a.tile_qt == 2 && tile_max_qt<D>() >= 2) {
+            if constexpr (tile_max_qt<D>() >= 2)
+                launch_tiled<DT, D, 2>(a, g, blk, pad, stream);
+        } else if (a.tile_qt == 4 && tile_max_qt<D>() >= 4) {
+            if constexpr (tile_max_qt<D>() >= 4)
+                launch_tiled<DT, D, 4>(a, g, blk, pad, stream);
         } else {
             return hipErrorInvalidValue;
         }
@@ -767,16 +789,16 @@ hipError_t launch_dt(const SplitArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-int split_mfma_prefix_max_qt(int head_dim) {
+int split_mfma_tile_max_qt(int head_dim) {
     switch (head_dim) {
-    case 64: return prefix_max_qt<64>();
-    case 128: return prefix_max_qt<128>();
-    case 256: return prefix_max_qt<256>();
+    case 64: return tile_max_qt<64>();
+    case 128: return tile_max_qt<128>();
+    case 256: return tile_max_qt<256>();
     default: return 0;
     }
 }
 
-bool split_mfma_prefix_supported(int in_dtype, int head_dim) {
+bool split_mfma_tiled_supported(int in_dtype, int head_dim) {
     return (in_dtype == kBF16 || in_dtype == kF16) &&
            (head_dim == 64 || head_dim == 128 || head_dim == 256);
 }

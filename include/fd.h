@@ -155,8 +155,8 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
 
 /* Whole decode step: split + combine.
  *   num_splits == 0 (automatic plan, split_len ignored):
- *     - kv_lens given and grouped heads on the matrix-core kernel (bf16/f16,
- *       2 <= heads_q/heads_kv <= 16): a token-balanced partition.  The
+ *     - kv_lens given and grouped heads on the one-tile matrix-core kernel
+ *       (bf16/f16, 2 <= heads_q/heads_kv <= 16): a token-balanced partition.  The
  *       (sequence, KV head, token) space of the actual lengths is cut into
  *       equal shares, one per work-group (CUs x 2), so every work-group
  *       streams the same number of K/V rows whatever the length mix; a share
@@ -169,6 +169,9 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
  *     - otherwise: B and L from fd_choose_splits (ragged = kv_lens != NULL).
  *   num_splits > 0, split_len == 0: L = ceil(max_kv_len / num_splits)
  *     ([P2] §4 chunking).  num_splits > 0, split_len > 0: used as given.
+ * Grouped heads in bf16/f16 run on the matrix cores: up to 16 query heads per
+ * KV head in one tile, larger groups (up to multi-query attention) in tiles
+ * of 16 that read each K/V row once for all of them.
  * With B == 1 the split stage writes o and lse itself.  On the vector path
  * (fp32 inputs, or no grouped heads) a small grid with 2 <= B <= 8 splits
  * (batch * heads_q * B below two waves per CU) runs every split of a row in

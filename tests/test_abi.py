@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 @pytest.mark.parametrize("batch,hq,hkv,d,dt", [
     (1, 1, 1, 64, fd.F32), (8, 32, 32, 128, fd.BF16), (1, 32, 32, 128, fd.BF16),
     (16, 64, 8, 128, fd.BF16), (4, 16, 16, 256, fd.F16), (2, 8, 1, 64, fd.F16),
-    (64, 64, 64, 128, fd.BF16)])
+    (64, 64, 64, 128, fd.BF16), (4, 64, 1, 128, fd.BF16), (2, 128, 2, 64, fd.F16)])
 @pytest.mark.parametrize("ragged", [0, 1])
 def test_choose_splits_contract(lib, batch, hq, hkv, d, dt, ragged):
     for n in (0, 1, 15, 16, 17, 255, 256, 1000, 1024, 4096, 65536, 131072, 1 << 20):

@@ -113,13 +113,38 @@ def test_many_heads(gpu):
         _check(f"hq128_hkv64_B{splits}", o, lse, inp, w)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_groups_larger_than_a_matrix_tile(gpu, dtype):
-    """32 query heads per KV head: past the 16 rows of one matrix-core tile,
-    so the vector kernel runs each query head on its own; ragged lengths,
-    automatic plan and explicit splits."""
+@pytest.mark.parametrize("dtype,group,hkv,d", [("bf16", 32, 2, 128), ("f16", 64, 1, 64),
+                                               ("bf16", 128, 1, 128), ("f16", 24, 2, 256),
+                                               ("bf16", 17, 3, 128)])
+def test_groups_larger_than_a_matrix_tile(gpu, dtype, group, hkv, d):
+    """More than 16 query heads per KV head (up to multi-query attention): the
+    group is cut into tiles of 16 (the last one partial for 17 and 24) and
+    every tile reads the same K/V rows; ragged lengths, automatic plan,
+    explicit splits, one split (direct output), and the split stage's
+    partials in both formats against the oracle's."""
     lens = [2500, 1, 0, 777]
-    w, inp = workloads.custom(4, 64, 2, 128, max(lens), dtype=dtype, seed=67, lens=lens)
+    w, inp = workloads.custom(4, group * hkv, hkv, d, max(lens), dtype=dtype,
+                              seed=67 + group + d, lens=lens)
     for splits in (0, 1, 5):
         o, lse = _run(gpu, inp, w, num_splits=splits)
-        _check(f"G32_{dtype}_B{splits}", o, lse, inp, w)
+        _check(f"G{group}_{dtype}_d{d}_B{splits}", o, lse, inp, w)
+    q, k, v = inp["q"].to(gpu), inp["k"].to(gpu), inp["v"].to(gpu)
+    kl = inp["kv_lens"].to(gpu)
+    B, L = 6, 432
+    o_part, lse_part = fd.decode_split(q, k, v, kl, num_splits=B, split_len=L, scale=w.scale)
+    o_m, m_part, l_part = fd.decode_split_mlo(q, k, v, kl, num_splits=B, split_len=L,
+                                              scale=w.scale)
+    torch.cuda.synchronize()
+    rop, rlp, rmp, rll = oracle.split_partials(dtype, workloads.raw(inp["q"]),
+                                               workloads.raw(inp["k"]), workloads.raw(inp["v"]),
+                                               np.array(lens, dtype=np.int32), B, L,
+                                               scale=w.scale, with_mlo=True)
+    tol_o, tol_l = TOL[dtype]
+    fin = np.isfinite(rlp)
+    assert np.abs(o_part.cpu().double().numpy() - rop).max() <= tol_o
+    assert np.array_equal(np.isneginf(lse_part.cpu().numpy()), ~fin)
+    assert np.abs(lse_part.cpu().double().numpy()[fin] - rlp[fin]).max() <= tol_l
+    assert np.abs(o_m.cpu().double().numpy() - rop).max() <= tol_o
+    gm, gl = m_part.cpu().double().numpy(), l_part.cpu().double().numpy()
+    # the triple's own S = m + log l against the oracle's LSE
+    assert np.abs((gm + np.log(np.where(fin, gl, 1.0)))[fin] - rlp[fin]).max() <= tol_l

@@ -66,7 +66,7 @@ def test_paged_named_workloads(gpu, cfg, page_size):
 
 
 @pytest.mark.parametrize("dtype,group,d", [("f32", 1, 64), ("bf16", 1, 128), ("bf16", 8, 128),
-                                           ("f16", 4, 256), ("f16", 2, 64)])
+                                           ("f16", 4, 256), ("f16", 2, 64), ("bf16", 32, 128)])
 @pytest.mark.parametrize("page_size", [16, 32, 1024])
 def test_paged_split_bitwise_equal_contiguous(gpu, dtype, group, d, page_size):
     """Same split count and length: paged partials equal contiguous partials
@@ -93,7 +93,7 @@ def test_paged_split_bitwise_equal_contiguous(gpu, dtype, group, d, page_size):
     assert np.abs(lp_p.cpu().double().numpy()[fin] - rlp[fin]).max() <= tol_l
 
 
-@pytest.mark.parametrize("group", [1, 8])
+@pytest.mark.parametrize("group", [1, 8, 40])
 def test_paged_decode_plans(gpu, group):
     """Whole decode over pages: automatic plan (balanced for grouped ragged),
     one split, and explicit split counts, against the oracle; page size larger
