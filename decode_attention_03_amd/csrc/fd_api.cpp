@@ -199,7 +199,7 @@ int fused_waves(int batch, int heads_q, int heads_kv, int head_dim, int in_dtype
 int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     const int group = a.heads_q / a.heads_kv;
     hipError_t e;
-    if (a.tile_qt > 0 || fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
+    if (a.balanced || a.tile_qt > 0 || fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
         e = fd::launch_split_mfma(a, in_dtype, stream);
     } else if (large_group(in_dtype, a.head_dim, group)) {
         a.tile_qt = tiled_qt(a.head_dim, group);
@@ -233,8 +233,11 @@ struct BalancedPlan {
 
 bool balanced_applies(int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
                       bool has_lens, int num_splits) {
+    const int group = heads_q / heads_kv;
     return num_splits == 0 && has_lens && max_kv_len > 0 &&
-           fd::split_mfma_supported(in_dtype, head_dim, heads_q / heads_kv);
+           (fd::split_mfma_supported(in_dtype, head_dim, group) ||
+            (large_group(in_dtype, head_dim, group) &&
+             group <= fd::split_mfma_balanced_max_group(head_dim)));
 }
 
 int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,

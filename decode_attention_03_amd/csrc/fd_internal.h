@@ -108,6 +108,9 @@ bool split_mfma_supported(int in_dtype, int head_dim, int group);
 // tile; shared prefix: any).
 bool split_mfma_tiled_supported(int in_dtype, int head_dim);
 int split_mfma_tile_max_qt(int head_dim);  // query tiles per work-group, 1..4
+// Largest group the token-balanced kernel takes (all of a unit's query tiles
+// in one work-group).
+int split_mfma_balanced_max_group(int head_dim);
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.

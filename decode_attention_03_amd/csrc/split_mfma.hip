@@ -173,21 +173,24 @@ struct PieceOut {
 };
 
 // The query rows one work-group serves, in tiles of 16 (the matrix-core
-// width).  One tile: the G <= 16 query heads of (sequence b, KV head kvh).
+// width).  nq == 0: the G query heads of (sequence b, KV head kvh), in
+// ceil(G / 16) tiles (one for G <= 16).
 // Tiled: the queries of KV head kvh numbered qi = 0 .. nq - 1 (the G heads of
 // sequence b, or for a shared prefix all batch * G queries, sequence
 // qi / G), tiles tile0, tile0 + 1, ...  row() is the query's row in
 // q [batch * heads_q, d], -1 for an unused slot.
 struct QMap {
-    int base;   // one tile: b * heads_q + kvh * G; tiled: b * heads_q (0 for a shared prefix)
+    int base;   // a group's own tiles: b * heads_q + kvh * G; tiled: b * heads_q (0 for a
+                // shared prefix)
     int G;
-    int nq;     // tiled: queries of the KV head (G, or batch * G for a shared prefix); 0: one tile
+    int nq;     // tiled: queries of the KV head (G, or batch * G for a shared prefix); 0: the
+                // G heads of (b, kvh) from base
     int tile0;
     int heads_q, kvh;
     __device__ __forceinline__ int row(int qt, int i) const {
-        if (nq == 0)
-            return i < G ? base + i : -1;
         const int qi = (tile0 + qt) * 16 + i;
+        if (nq == 0)
+            return qi < G ? base + qi : -1;
         return qi < nq ? base + (qi / G) * heads_q + kvh * G + qi % G : -1;
     }
 };
@@ -533,7 +536,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             const float inv = any ? 1.f / lr : 0.f;
             const float lse = any ? (mr + fast_log2(le)) * kLn2 : -INFINITY;
             if (out.o) {
-                const size_t idx = (size_t)(out.local ? h : row) * out.stride + out.off;
+                const size_t idx =
+                    (size_t)(out.local ? (qm.tile0 + qt) * 16 + h : row) * out.stride + out.off;
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
                     out.o[idx * D + 16 * t + col] = oacc[qt][t][r] * inv;
@@ -638,7 +642,8 @@ __global__ __launch_bounds__(64) void split_mfma_tiled_kernel(SplitArgs a) {
 // Token-balanced partition (partition.h): work-group w walks its share of the
 // flattened (sequence, KV head, token) space piece by piece; the piece of unit
 // u goes to slot w + rank(u) of the slot arrays (o [slot][G][d], LSE [slot][G]).
-template <int DT, int D, bool PAGED>
+// The G query heads of a unit take QT = ceil(G / 16) tiles.
+template <int DT, int D, bool PAGED, int QT>
 __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
@@ -664,7 +669,7 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
                                nullptr, 1, 0, true};
             const long t0 = (long)lo * kGranule;
             const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
-            mfma_piece<DT, D, PAGED, 1>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
+            mfma_piece<DT, D, PAGED, QT>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
             if (lo == 0 && threadIdx.x == 0) {
                 const long long ustart = c.pos - c.t;  // the unit's first position
                 const int first = balanced_owner(ustart + kPieceCost, c.total, c.w_eff);
@@ -729,6 +734,15 @@ void launch_tiled(const SplitArgs &a, dim3 g, dim3 blk, size_t pad, hipStream_t 
         hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false>), g, blk, pad, stream, a);
 }
 
+// The token-balanced kernel for QT query tiles per unit, paged or contiguous.
+template <int DT, int D, int QT>
+void launch_balanced(const SplitArgs &a, dim3 g, dim3 blk, size_t pad, hipStream_t stream) {
+    if (a.block_table)
+        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, true, QT>), g, blk, pad, stream, a);
+    else
+        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, false, QT>), g, blk, pad, stream, a);
+}
+
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
@@ -764,10 +778,15 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
             return hipErrorInvalidValue;
         }
     } else if (a.balanced) {
-        if (a.block_table)
-            hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, true>), g, blk, pad, stream, a);
-        else
-            hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, false>), g, blk, pad, stream, a);
+        const int qt = (a.heads_q / a.heads_kv + 15) / 16;
+        if (qt == 1) {
+            launch_balanced<DT, D, 1>(a, g, blk, pad, stream);
+        } else if (qt == 2 && tile_max_qt<D>() >= 2) {
+            if constexpr (tile_max_qt<D>() >= 2)
+                launch_balanced<DT, D, 2>(a, g, blk, pad, stream);
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
         if (a.block_table)
             hipLaunchKernelGGL((split_mfma_kernel<DT, D, true>), g, blk, pad, stream, a);
@@ -796,6 +815,15 @@ int split_mfma_tile_max_qt(int head_dim) {
     case 256: return tile_max_qt<256>();
     default: return 0;
     }
+}
+
+// Up to two tiles: with four (64 heads at d = 64, multi-query) the pieces are
+// bound by their arithmetic, and the tiled kernel's fixed splits at four
+// work-groups per CU measured 5 % faster on a ragged batch than the balanced
+// plan's two.
+int split_mfma_balanced_max_group(int head_dim) {
+    const int qt = split_mfma_tile_max_qt(head_dim);
+    return 16 * (qt < 2 ? qt : 2);
 }
 
 bool split_mfma_tiled_supported(int in_dtype, int head_dim) {

@@ -172,11 +172,13 @@ def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_kv_len: 
 def uses_balanced_plan(heads_q: int, heads_kv: int, max_kv_len: int, head_dim: int,
                        dtype: torch.dtype, has_kv_lens: bool, num_splits: int = 0) -> bool:
     """Whether fd_decode takes the token-balanced partition for these arguments
-    (the rule include/fd.h states: automatic plan, kv_lens given, grouped heads
-    2..16 on a 16-bit input type, supported head_dim)."""
+    (the rule include/fd.h states: automatic plan, kv_lens given, a 16-bit
+    input type, a supported head_dim, and 2 to 32 / 32 / 16 query heads per
+    KV head at d = 64 / 128 / 256)."""
     group = heads_q // heads_kv
-    return (num_splits == 0 and has_kv_lens and max_kv_len > 0 and 2 <= group <= 16
-            and dtype in (torch.bfloat16, torch.float16) and head_dim in (64, 128, 256))
+    max_group = {64: 32, 128: 32, 256: 16}.get(head_dim, 0)
+    return (num_splits == 0 and has_kv_lens and max_kv_len > 0 and 2 <= group <= max_group
+            and dtype in (torch.bfloat16, torch.float16))
 
 
 def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, scale=None,

@@ -5,7 +5,8 @@ The partition cuts the flattened (sequence, KV head, token) space into equal
 shares; these cases aim at its corners: empty sequences between full ones,
 every sequence empty, fewer positions than work-groups, more than 64
 sequences (the in-kernel prefix scan runs over several 64-lane chunks), one
-sequence spread over hundreds of pieces, clamped lengths.  K/V rows past each
+sequence spread over hundreds of pieces, clamped lengths, and groups of 17 to
+32 query heads per KV head (two query tiles per piece).  K/V rows past each
 length are NaN and the workspace starts NaN-filled, so a read past a length or
 of an unwritten slot shows up as a wrong or non-finite result.
 """
@@ -29,6 +30,11 @@ CASES = [
     ("one_long_row", 3, 1, 16, 256, "f16", 40000, [1, 40000, 2]),
     ("clamped", 4, 4, 8, 128, "bf16", 300, [0, 300, 5000, -3]),
     ("group2_d256", 6, 3, 2, 256, "bf16", 3000, [2999, 1, 1500, 0, 3000, 64]),
+    # groups past one 16-query tile: every tile of a unit in the one work-group
+    ("group32_d128", 6, 2, 32, 128, "bf16", 6000, [6000, 0, 17, 4099, 1, 2500]),
+    ("group32_d64_mqa", 9, 1, 32, 64, "f16", 3000, [3000, 2, 0, 1777, 3000, 64, 500, 0, 2999]),
+    ("group24_d64", 5, 2, 24, 64, "bf16", 2000, [1999, 0, 300, 2000, 33]),
+    ("group17_d128", 4, 3, 17, 128, "f16", 2500, [2500, 1, 1024, 0]),
 ]
 
 
