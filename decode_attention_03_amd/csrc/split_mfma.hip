@@ -57,6 +57,8 @@
 // §2.3.2-§2.3.3), or, in the m/l/o format, o with the split's max score m and
 // l = sum exp(s - m) ([P1] §2.4.1 direct form).  Scores are in the log2 domain (scale * log2(e) applied to
 // the fp32 MFMA result).
+#include <atomic>
+
 #include "dev_common.h"
 #include "partition.h"
 
@@ -700,18 +702,19 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
 }
 
 int lds_per_cu_mfma() {
-    static int cached[64];
+    // per device; several host threads may fill an entry at once (same value)
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 0;
-    if (cached[dev] == 0) {
-        int v = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
                 hipSuccess || v <= 0)
             v = -1;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev] > 0 ? cached[dev] : 0;
+    return v > 0 ? v : 0;
 }
 
 // Query tiles per work-group of the tiled kernel that fit in the register

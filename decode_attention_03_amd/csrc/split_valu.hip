@@ -40,6 +40,8 @@
 // makes the combine stage unnecessary).  When even the splits of all rows
 // leave wave slots empty, one work-group per row runs one wave per split and
 // merges the splits in LDS (FUSED), so a small decode is a single launch.
+#include <atomic>
+
 #include "dev_common.h"
 
 namespace fd {
@@ -390,18 +392,19 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
 // Resident work-groups per CU are capped by reserving LDS: a work-group
 // asks for just over 1/(cap+1) of the CU's LDS, so cap of them fit.
 int lds_per_cu() {
-    static int cached[64];
+    // per device; several host threads may fill an entry at once (same value)
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 0;
-    if (cached[dev] == 0) {
-        int v = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
                 hipSuccess || v <= 0)
             v = -1;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev] > 0 ? cached[dev] : 0;
+    return v > 0 ? v : 0;
 }
 
 template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false>
@@ -417,16 +420,17 @@ hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
         pad = want > kStatic ? want - kStatic : 0;
         if (pad > 65536) {
             // once per kernel and device (the pad depends only on the device)
-            static bool raised[64];
+            static std::atomic<bool> raised[64];
             int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || !raised[dev]) {
+            if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 ||
+                !raised[dev].load(std::memory_order_relaxed)) {
                 hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize,
                                                    (int)pad);
                 if (e != hipSuccess)
                     return e;
                 if (dev >= 0 && dev < 64)
-                    raised[dev] = true;
+                    raised[dev].store(true, std::memory_order_relaxed);
             }
         }
     }

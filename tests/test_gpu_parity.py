@@ -311,3 +311,42 @@ def test_runs_on_a_side_stream(gpu):
     s.synchronize()
     ro, rl = _oracle(w, inp)
     _assert_close("side_stream", o, lse, ro, rl, "bf16")
+
+
+def test_concurrent_host_threads(gpu):
+    """Several host threads call the library at once, each on its own stream
+    (the per-device caches are filled concurrently on first use): every
+    result equals the single-threaded one bit for bit."""
+    import threading
+
+    cases = [workloads.custom(3, 16, 2, 128, 1500, dtype="bf16", seed=71, lens=[1500, 9, 700]),
+             workloads.custom(2, 8, 8, 64, 900, dtype="f32", seed=72),
+             workloads.custom(4, 32, 4, 256, 600, dtype="f16", seed=73, lens=[600, 0, 1, 333])]
+    dev_inputs = [(_to(gpu, inp), w) for w, inp in cases]
+    expected = []
+    for (q, k, v, kl), w in dev_inputs:
+        o, lse = fd.decode(q, k, v, kl, scale=w.scale)
+        expected.append((o.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream(device=gpu)
+            with torch.cuda.stream(s):
+                for rep in range(5):
+                    i = (t + rep) % len(dev_inputs)
+                    (q, k, v, kl), w = dev_inputs[i]
+                    o, lse = fd.decode(q, k, v, kl, scale=w.scale)
+                    s.synchronize()
+                    if not (torch.equal(o, expected[i][0]) and torch.equal(lse, expected[i][1])):
+                        errors.append(f"thread {t} rep {rep} case {i}")
+        except Exception as e:  # reported below
+            errors.append(f"thread {t}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
