@@ -69,20 +69,21 @@ class Prepared:
             num_splits = w.num_splits
         # the library's automatic plan unless the workload or the caller fixes B
         self.auto = num_splits == 0
-        self.balanced = fd.uses_balanced_plan(hq, hkv, self.n_max, d, inp["q"].dtype,
-                                              lens is not None, num_splits)
-        if num_splits == 0:
+        # the library's own account of what fd_decode launches here
+        self.dplan = fd.decode_plan(batch, hq, hkv, self.n_max, d, inp["q"].dtype,
+                                    lens is not None, num_splits)
+        self.balanced = self.dplan["route"] == "balanced"
+        if self.balanced:  # B, L of fixed splits, for the split stage timed on its own
             self.B, self.L = fd.choose_splits(batch, hq, hkv, self.n_max, d, inp["q"].dtype,
-                                              ragged=lens is not None)
+                                              ragged=True)
         else:
-            self.B, self.L = num_splits, -(-self.n_max // num_splits)
+            self.B, self.L = self.dplan["num_splits"], self.dplan["split_len"]
         self.plan = "token-balanced" if self.balanced else "fixed-splits"
         self.o = torch.empty((batch, hq, d), dtype=workloads.TORCH_DTYPES[w.out_dtype],
                              device=dev)
         self.lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
         dec_b, dec_l = (0, 0) if self.auto else (self.B, self.L)
-        ws = fd.decode_workspace_bytes(batch, hq, hkv, self.n_max, d, inp["q"].dtype,
-                                       lens is not None, dec_b, dec_l)
+        ws = self.dplan["workspace_bytes"]
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
         # partial buffers of the split kernel when it is timed on its own
@@ -113,8 +114,7 @@ class Prepared:
         # partials written (fixed splits: B per row; balanced: at most one per
         # work-group piece, bounded by work-groups + units, counted in full)
         if self.balanced:
-            cus = torch.cuda.get_device_properties(dev).multi_processor_count
-            pieces = 2 * cus + batch * hkv
+            pieces = self.dplan["work_groups"] + batch * hkv
             self.part_bytes = pieces * (hq // hkv) * (d + 1) * 4
         else:
             self.part_bytes = batch * hq * self.B * (d + 1) * 4 if self.B > 1 else 0
@@ -535,7 +535,8 @@ def traffic_from_profile(name: str) -> dict | None:
 def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
     us = t["wall_us_per_step"]
     out = {"us_per_step": round(us, 2), "event_us_median": round(t["event_us_median"], 2),
-           "plan": p.plan, "kv_bytes": p.kv_bytes}
+           "plan": p.plan, "route": p.dplan["route"], "split_kernel": p.dplan["kernel"],
+           "kv_bytes": p.kv_bytes}
     if not p.balanced:
         out["num_splits"], out["split_len"] = p.B, p.L
     if p.copies > 1:
@@ -640,7 +641,8 @@ def main() -> int:
         "config": {"workload": head.name, "batch": head.batch, "heads_q": head.heads_q,
                    "heads_kv": head.heads_kv, "head_dim": head.head_dim,
                    "max_kv_len": p.n_max, "in_dtype": head.dtype, "out_dtype": head.out_dtype,
-                   "plan": p.plan, "num_splits": None if p.balanced else p.B,
+                   "plan": p.plan, "route": p.dplan["route"],
+                   "split_kernel": p.dplan["kernel"], "num_splits": None if p.balanced else p.B,
                    "split_len": None if p.balanced else p.L, "kv_bytes_per_step": p.kv_bytes,
                    "input_copies": p.copies, "parallelism": "single-gpu"},
         "inputs_sha256": workloads.digest(p.host),

@@ -183,39 +183,57 @@ int tiled_qt(int head_dim, long long nq) {
 // splits, 2..8 of them, on a grid whose split work-groups would not even fill
 // the GPU's wave slots once.  0 when not applicable.
 int fused_waves(int batch, int heads_q, int heads_kv, int head_dim, int in_dtype,
-                int num_splits) {
+                int num_splits, int cus) {
     if (num_splits < 2 || num_splits > 8 ||
         fd::split_mfma_supported(in_dtype, head_dim, heads_q / heads_kv) ||
         large_group(in_dtype, head_dim, heads_q / heads_kv))
-        return 0;
-    int cus = 0;
-    if (device_cus(&cus) != FD_OK)
         return 0;
     if ((long long)batch * heads_q * num_splits >= (long long)cus * fd::kWavesPerCU)
         return 0;
     return num_splits <= 2 ? 2 : (num_splits <= 4 ? 4 : 8);
 }
 
-int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
+// Which split kernel a launch described by a runs (FD_KERNEL_*).
+int split_kernel(const fd::SplitArgs &a, int in_dtype) {
     const int group = a.heads_q / a.heads_kv;
+    if (a.balanced)
+        return FD_KERNEL_BALANCED;
+    if (a.tile_qt > 0 || large_group(in_dtype, a.head_dim, group))
+        return FD_KERNEL_TILED;
+    if (fd::split_mfma_supported(in_dtype, a.head_dim, group))
+        return FD_KERNEL_GROUPED;
+    return FD_KERNEL_VECTOR;
+}
+
+// Waves per vector-kernel work-group: the fused small-grid count, else two
+// when one-wave work-groups would leave wave slots of the GPU empty, else one.
+int vector_waves(const fd::SplitArgs &a, int cus) {
+    if (a.fused_waves > 0)
+        return a.fused_waves;
+    const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
+    return wgs < (long long)cus * fd::kWavesPerCU ? fd::kWavesPerCU : 1;
+}
+
+int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     hipError_t e;
-    if (a.balanced || a.tile_qt > 0 || fd::split_mfma_supported(in_dtype, a.head_dim, group)) {
+    switch (split_kernel(a, in_dtype)) {
+    case FD_KERNEL_TILED:
+        if (a.tile_qt == 0)
+            a.tile_qt = tiled_qt(a.head_dim, a.heads_q / a.heads_kv);
         e = fd::launch_split_mfma(a, in_dtype, stream);
-    } else if (large_group(in_dtype, a.head_dim, group)) {
-        a.tile_qt = tiled_qt(a.head_dim, group);
+        break;
+    case FD_KERNEL_GROUPED:
+    case FD_KERNEL_BALANCED:
         e = fd::launch_split_mfma(a, in_dtype, stream);
-    } else {
-        // two waves per work-group when one-wave work-groups would leave wave
-        // slots of the GPU empty
+        break;
+    default: {
         int cus = 0;
         int rc = device_cus(&cus);
         if (rc != FD_OK)
             return rc;
-        const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
-        a.valu_waves = a.fused_waves > 0
-                           ? 0
-                           : (wgs < (long long)cus * fd::kWavesPerCU ? fd::kWavesPerCU : 1);
+        a.valu_waves = a.fused_waves > 0 ? 0 : vector_waves(a, cus);
         e = fd::launch_split_valu(a, in_dtype, stream);
+    }
     }
     if (e != hipSuccess)
         return fail(FD_ERR_HIP, "split kernel launch: %s", hipGetErrorString(e));
@@ -240,12 +258,8 @@ bool balanced_applies(int heads_q, int heads_kv, int max_kv_len, int head_dim, i
              group <= fd::split_mfma_balanced_max_group(head_dim)));
 }
 
-int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim, int cus,
                   BalancedPlan *p) {
-    int cus = 0;
-    int rc = device_cus(&cus);
-    if (rc != FD_OK)
-        return rc;
     p->num_wgs = cus * fd::kMfmaWgPerCU * kBalancedRounds;
     p->units = batch * heads_kv;
     p->gsz = heads_q / heads_kv;
@@ -256,6 +270,115 @@ int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head
     p->o_bytes = round256(slots * p->gsz * head_dim * sizeof(float));
     p->lse_bytes = round256(slots * p->gsz * sizeof(float));
     p->desc_bytes = round256((size_t)p->units * 2 * sizeof(int));
+    return FD_OK;
+}
+
+// The plan of one decode step (fd_decode / fd_decode_paged): the single place
+// where the route, the split kernel, B and L and the workspace are decided.
+// fd_decode_plan reports it, fd_decode_workspace_bytes its workspace, and
+// decode_impl carries it out.
+struct Plan {
+    fd_plan pub{};
+    int fused = 0;  // vector-kernel waves per row on FD_ROUTE_FUSED
+    BalancedPlan bal;
+};
+
+int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
+              bool has_lens, bool paged, int num_splits, int split_len, int cus, Plan *p) {
+    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0 || heads_q % heads_kv)
+        return fail(FD_ERR_INVALID, "bad sizes (batch=%d heads_q=%d heads_kv=%d max_kv_len=%d)",
+                    batch, heads_q, heads_kv, max_kv_len);
+    if (!head_dim_ok(head_dim) || !dtype_ok(in_dtype))
+        return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
+                    in_dtype);
+    if (num_splits < 0 || split_len < 0)
+        return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
+                    num_splits, split_len);
+    // explicit splits: checked before the device is asked for anything
+    if (num_splits > 0) {
+        if (split_len == 0) {
+            long long len = max_kv_len > 0 ? ((long long)max_kv_len + num_splits - 1) / num_splits
+                                           : 1;
+            if (paged)  // whole 16-token tiles
+                len = (len + 15) / 16 * 16;
+            split_len = (int)(len < 0x7fffffffLL ? len : 0x7ffffff0LL);
+        }
+        int rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
+        if (rc != FD_OK)
+            return rc;
+        if (paged && split_len % 16 != 0)
+            return fail(FD_ERR_INVALID, "paged K/V needs split_len (%d) to be a multiple of 16",
+                        split_len);
+    }
+    // the device's compute units, asked for only where a decision needs them
+    auto need_cus = [&cus]() { return cus > 0 ? FD_OK : device_cus(&cus); };
+    *p = Plan{};
+    fd_plan &r = p->pub;
+    fd::SplitArgs a{};
+    a.batch = batch;
+    a.heads_q = heads_q;
+    a.heads_kv = heads_kv;
+    a.max_kv_len = max_kv_len;
+    a.head_dim = head_dim;
+    const int group = heads_q / heads_kv;
+    int rc;
+    if (balanced_applies(heads_q, heads_kv, max_kv_len, head_dim, in_dtype, has_lens,
+                         num_splits)) {
+        if ((rc = need_cus()) != FD_OK ||
+            (rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, cus, &p->bal)) !=
+                FD_OK)
+            return rc;
+        r.route = FD_ROUTE_BALANCED;
+        r.kernel = FD_KERNEL_BALANCED;
+        r.work_groups = p->bal.num_wgs;
+        r.waves_per_group = 1;
+        r.query_tiles = (group + 15) / 16;
+        r.launches = 2;
+        r.workspace_bytes = p->bal.total();
+        return FD_OK;
+    }
+    if (num_splits == 0) {  // the automatic plan: whole 16-token tiles, B * L >= max_kv_len
+        if ((rc = need_cus()) != FD_OK ||
+            (rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                                   has_lens, cus, &num_splits, &split_len)) != FD_OK ||
+            (rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len)) != FD_OK)
+            return rc;
+    }
+    a.num_splits = num_splits;
+    a.split_len = split_len;
+    r.num_splits = num_splits;
+    r.split_len = split_len;
+    r.kernel = split_kernel(a, in_dtype);
+    switch (r.kernel) {
+    case FD_KERNEL_VECTOR:
+        if ((rc = need_cus()) != FD_OK)
+            return rc;
+        p->fused = num_splits > 1 ? fused_waves(batch, heads_q, heads_kv, head_dim, in_dtype,
+                                                num_splits, cus)
+                                  : 0;
+        a.fused_waves = p->fused;
+        r.waves_per_group = vector_waves(a, cus);
+        r.query_tiles = 0;
+        r.work_groups = (int64_t)batch * heads_q * (p->fused > 0 ? 1 : num_splits);
+        break;
+    case FD_KERNEL_GROUPED:
+        r.waves_per_group = 1;
+        r.query_tiles = 1;
+        r.work_groups = (int64_t)batch * heads_kv * num_splits;
+        break;
+    default: {  // FD_KERNEL_TILED: units padded to multiples of 8, times tile groups
+        const int qt = tiled_qt(head_dim, group);
+        const long long groups = ((group + 15) / 16 + qt - 1) / qt;
+        const long long units = (long long)batch * heads_kv * num_splits;
+        r.waves_per_group = 1;
+        r.query_tiles = qt;
+        r.work_groups = (units + 7) / 8 * 8 * groups;
+    }
+    }
+    r.route = num_splits == 1 ? FD_ROUTE_DIRECT : (p->fused > 0 ? FD_ROUTE_FUSED : FD_ROUTE_SPLITS);
+    r.launches = r.route == FD_ROUTE_SPLITS ? 2 : 1;
+    r.workspace_bytes =
+        r.route == FD_ROUTE_SPLITS ? fd_workspace_bytes(batch, heads_q, num_splits, head_dim) : 0;
     return FD_OK;
 }
 
@@ -355,33 +478,26 @@ int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_l
     if (!bytes)
         return fail(FD_ERR_INVALID, "null output pointer");
     *bytes = 0;
-    if (batch < 1 || heads_q < 1 || heads_kv < 1 || max_kv_len < 0 || heads_q % heads_kv)
-        return fail(FD_ERR_INVALID, "bad sizes (batch=%d heads_q=%d heads_kv=%d max_kv_len=%d)",
-                    batch, heads_q, heads_kv, max_kv_len);
-    if (!head_dim_ok(head_dim) || !dtype_ok(in_dtype))
-        return fail(FD_ERR_UNSUPPORTED, "head_dim %d / dtype %d not supported", head_dim,
-                    in_dtype);
-    if (num_splits < 0 || split_len < 0)
-        return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
-                    num_splits, split_len);
-    if (balanced_applies(heads_q, heads_kv, max_kv_len, head_dim, in_dtype, has_kv_lens != 0,
-                         num_splits)) {
-        BalancedPlan p;
-        int rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, &p);
-        if (rc != FD_OK)
-            return rc;
-        *bytes = p.total();
-        return FD_OK;
-    }
-    if (num_splits == 0) {
-        int rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
-                                  has_kv_lens != 0, 0, &num_splits, &split_len);
-        if (rc != FD_OK)
-            return rc;
-    }
-    *bytes = fused_waves(batch, heads_q, heads_kv, head_dim, in_dtype, num_splits) > 0
-                 ? 0
-                 : fd_workspace_bytes(batch, heads_q, num_splits, head_dim);
+    Plan p;
+    int rc = make_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                       has_kv_lens != 0, false, num_splits, split_len, 0, &p);
+    if (rc != FD_OK)
+        return rc;
+    *bytes = p.pub.workspace_bytes;
+    return FD_OK;
+}
+
+int fd_decode_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                   int in_dtype, int has_kv_lens, int paged, int num_splits, int split_len,
+                   int num_cus, fd_plan *plan) {
+    if (!plan)
+        return fail(FD_ERR_INVALID, "null output pointer");
+    Plan p;
+    int rc = make_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                       has_kv_lens != 0, paged != 0, num_splits, split_len, num_cus, &p);
+    if (rc != FD_OK)
+        return rc;
+    *plan = p.pub;
     return FD_OK;
 }
 
@@ -518,7 +634,11 @@ int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_s
     p->balanced = balanced_applies(heads_q, heads_kv, max_suffix_len, head_dim, in_dtype, has_lens,
                                    0);
     if (p->balanced) {
-        rc = balanced_plan(batch, heads_q, heads_kv, max_suffix_len, head_dim, &p->bal);
+        int cus = 0;
+        rc = device_cus(&cus);
+        if (rc != FD_OK)
+            return rc;
+        rc = balanced_plan(batch, heads_q, heads_kv, max_suffix_len, head_dim, cus, &p->bal);
         if (rc != FD_OK)
             return rc;
         p->bs = 0;
@@ -728,7 +848,8 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
 
 namespace {
 
-// The whole decode step, contiguous (pg null) or paged K/V.
+// The whole decode step, contiguous (pg null) or paged K/V, as make_plan
+// decides it.
 int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
                 int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
                 int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
@@ -744,81 +865,21 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
                     out_dtype, in_dtype);
     if (!aligned4(o) || (lse && !aligned4(lse)))
         return fail(FD_ERR_UNSUPPORTED, "o and lse must be 4-byte aligned");
-    if (num_splits < 0 || split_len < 0)
-        return fail(FD_ERR_INVALID, "num_splits (%d) and split_len (%d) must be >= 0",
-                    num_splits, split_len);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (balanced_applies(heads_q, heads_kv, max_kv_len, head_dim, in_dtype, kv_lens != nullptr,
-                         num_splits)) {
-        BalancedPlan p;
-        rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, &p);
-        if (rc != FD_OK)
-            return rc;
-        if (!workspace || workspace_bytes < p.total())
-            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total(),
-                        workspace ? workspace_bytes : (size_t)0);
-        if (!aligned16(workspace))
-            return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-        char *ws = static_cast<char *>(workspace);
-        fd::SplitArgs a{};
-        a.q = q;
-        a.k = k;
-        a.v = v;
-        a.kv_lens = kv_lens;
-        a.batch = batch;
-        a.heads_q = heads_q;
-        a.heads_kv = heads_kv;
-        a.max_kv_len = max_kv_len;
-        a.head_dim = head_dim;
-        a.num_splits = 0;
-        a.split_len = 0;
-        a.scale_log2 = scale * 1.4426950408889634f;
-        a.o_part = reinterpret_cast<float *>(ws);
-        a.lse_part = reinterpret_cast<float *>(ws + p.o_bytes);
-        a.out_dtype = out_dtype;
-        a.balanced = 1;
-        a.num_wgs = p.num_wgs;
-        a.unit_desc = reinterpret_cast<int *>(ws + p.o_bytes + p.lse_bytes);
-        set_paging(a, pg);
-        rc = launch_split(a, in_dtype, st);
-        if (rc != FD_OK)
-            return rc;
-        fd::SlotCombineArgs c{};
-        c.o_slots = a.o_part;
-        c.lse_slots = a.lse_part;
-        c.unit_desc = a.unit_desc;
-        c.kv_lens = kv_lens;
-        c.batch = batch;
-        c.heads_q = heads_q;
-        c.gsz = p.gsz;
-        c.max_kv_len = max_kv_len;
-        c.head_dim = head_dim;
-        c.max_count = p.num_wgs;
-        c.o = o;
-        c.out_dtype = out_dtype;
-        c.lse = lse;
-        hipError_t e = fd::launch_combine_slots(c, st);
-        if (e != hipSuccess)
-            return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
-        return FD_OK;
-    }
-    if (num_splits == 0) {
-        rc = fd_choose_splits(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
-                              kv_lens != nullptr, 0, &num_splits, &split_len);
-        if (rc != FD_OK)
-            return rc;
-    } else if (split_len == 0) {
-        split_len = max_kv_len > 0 ? (max_kv_len + num_splits - 1) / num_splits : 1;
-        if (pg)  // whole 16-token tiles
-            split_len = (split_len + 15) / 16 * 16;
-    }
-    rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
+    Plan p;
+    rc = make_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype, kv_lens != nullptr,
+                   pg != nullptr, num_splits, split_len, 0, &p);
     if (rc != FD_OK)
         return rc;
-    if (pg && split_len % 16 != 0)
-        return fail(FD_ERR_INVALID, "paged K/V needs split_len (%d) to be a multiple of 16",
-                    split_len);
-
+    const fd_plan &r = p.pub;
+    if (r.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < r.workspace_bytes)
+            return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                        r.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace))
+            return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
     fd::SplitArgs a{};
     a.q = q;
     a.k = k;
@@ -829,38 +890,56 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
     a.heads_kv = heads_kv;
     a.max_kv_len = max_kv_len;
     a.head_dim = head_dim;
-    a.num_splits = num_splits;
-    a.split_len = split_len;
+    a.num_splits = r.num_splits;
+    a.split_len = r.split_len;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_dtype = out_dtype;
     set_paging(a, pg);
-
-    if (num_splits == 1) {  // one split per row: the split stage writes o and lse itself
+    hipError_t e = hipSuccess;
+    switch (r.route) {
+    case FD_ROUTE_BALANCED: {
+        a.o_part = reinterpret_cast<float *>(ws);
+        a.lse_part = reinterpret_cast<float *>(ws + p.bal.o_bytes);
+        a.balanced = 1;
+        a.num_wgs = p.bal.num_wgs;
+        a.unit_desc = reinterpret_cast<int *>(ws + p.bal.o_bytes + p.bal.lse_bytes);
+        rc = launch_split(a, in_dtype, st);
+        if (rc != FD_OK)
+            return rc;
+        fd::SlotCombineArgs c{};
+        c.o_slots = a.o_part;
+        c.lse_slots = a.lse_part;
+        c.unit_desc = a.unit_desc;
+        c.kv_lens = kv_lens;
+        c.batch = batch;
+        c.heads_q = heads_q;
+        c.gsz = p.bal.gsz;
+        c.max_kv_len = max_kv_len;
+        c.head_dim = head_dim;
+        c.max_count = p.bal.num_wgs;
+        c.o = o;
+        c.out_dtype = out_dtype;
+        c.lse = lse;
+        e = fd::launch_combine_slots(c, st);
+        break;
+    }
+    case FD_ROUTE_DIRECT:  // one split per row: the split stage writes o and lse itself
+    case FD_ROUTE_FUSED:   // small grid: splits merged in LDS, final output directly
         a.o = o;
         a.lse = lse;
+        a.fused_waves = p.fused;
         return launch_split(a, in_dtype, st);
+    default: {  // FD_ROUTE_SPLITS
+        const size_t rows = (size_t)batch * heads_q * r.num_splits;
+        a.o_part = reinterpret_cast<float *>(ws);
+        a.lse_part = reinterpret_cast<float *>(ws + round256(rows * head_dim * sizeof(float)));
+        rc = launch_split(a, in_dtype, st);
+        if (rc != FD_OK)
+            return rc;
+        e = fd::launch_combine(a.o_part, a.lse_part, batch * heads_q, r.num_splits, head_dim, o,
+                               out_dtype, lse, st);
     }
-    a.fused_waves = fused_waves(batch, heads_q, heads_kv, head_dim, in_dtype, num_splits);
-    if (a.fused_waves > 0) {  // small grid: splits merged in LDS, final output directly
-        a.o = o;
-        a.lse = lse;
-        return launch_split(a, in_dtype, st);
     }
-    const size_t need = fd_workspace_bytes(batch, heads_q, num_splits, head_dim);
-    if (!workspace || workspace_bytes < need)
-        return fail(FD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace))
-        return fail(FD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-    const size_t rows = (size_t)batch * heads_q * num_splits;
-    a.o_part = static_cast<float *>(workspace);
-    a.lse_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                           round256(rows * head_dim * sizeof(float)));
-    rc = launch_split(a, in_dtype, st);
-    if (rc != FD_OK)
-        return rc;
-    hipError_t e = fd::launch_combine(a.o_part, a.lse_part, batch * heads_q, num_splits,
-                                      head_dim, o, out_dtype, lse, st);
     if (e != hipSuccess)
         return fail(FD_ERR_HIP, "combine kernel launch: %s", hipGetErrorString(e));
     return FD_OK;

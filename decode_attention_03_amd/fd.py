@@ -30,12 +30,24 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 
 #: every symbol include/fd.h declares
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
-           "fd_decode_workspace_bytes", "fd_decode_split", "fd_decode_split_mlo", "fd_combine",
+           "fd_decode_workspace_bytes", "fd_decode_plan", "fd_decode_split", "fd_decode_split_mlo", "fd_combine",
            "fd_combine_mlo", "fd_decode", "fd_decode_split_paged", "fd_decode_paged",
            "fd_cascade_workspace_bytes", "fd_decode_cascade")
 
+#: fd_plan.route and fd_plan.kernel codes, by name
+ROUTES = ("direct", "fused", "splits", "balanced")
+KERNELS = ("vector", "grouped", "tiled", "balanced")
+
 _lock = threading.Lock()
 _lib = None
+
+
+class _Plan(ctypes.Structure):
+    """struct fd_plan of include/fd.h."""
+    _fields_ = [("route", ctypes.c_int), ("kernel", ctypes.c_int), ("num_splits", ctypes.c_int),
+                ("split_len", ctypes.c_int), ("waves_per_group", ctypes.c_int),
+                ("query_tiles", ctypes.c_int), ("launches", ctypes.c_int),
+                ("work_groups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class FDError(RuntimeError):
@@ -63,6 +75,8 @@ def library() -> ctypes.CDLL:
         lib.fd_workspace_bytes.argtypes, lib.fd_workspace_bytes.restype = [I, I, I, I], S
         lib.fd_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(S)]
         lib.fd_decode_workspace_bytes.restype = I
+        lib.fd_decode_plan.argtypes = [I, I, I, I, I, I, I, I, I, I, I, ctypes.POINTER(_Plan)]
+        lib.fd_decode_plan.restype = I
         lib.fd_decode_split.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P]
         lib.fd_decode_split.restype = I
         lib.fd_decode_split_mlo.argtypes = [P, P, P, P, I, I, I, I, I, I, F, I, I, P, P, P, P]
@@ -169,16 +183,21 @@ def decode_workspace_bytes(batch: int, heads_q: int, heads_kv: int, max_kv_len: 
     return out.value
 
 
-def uses_balanced_plan(heads_q: int, heads_kv: int, max_kv_len: int, head_dim: int,
-                       dtype: torch.dtype, has_kv_lens: bool, num_splits: int = 0) -> bool:
-    """Whether fd_decode takes the token-balanced partition for these arguments
-    (the rule include/fd.h states: automatic plan, kv_lens given, a 16-bit
-    input type, a supported head_dim, and 2 to 32 / 32 / 16 query heads per
-    KV head at d = 64 / 128 / 256)."""
-    group = heads_q // heads_kv
-    max_group = {64: 32, 128: 32, 256: 16}.get(head_dim, 0)
-    return (num_splits == 0 and has_kv_lens and max_kv_len > 0 and 2 <= group <= max_group
-            and dtype in (torch.bfloat16, torch.float16))
+def decode_plan(batch: int, heads_q: int, heads_kv: int, max_kv_len: int, head_dim: int,
+                dtype: torch.dtype, has_kv_lens: bool, num_splits: int = 0, split_len: int = 0,
+                paged: bool = False, num_cus: int = 0) -> dict:
+    """What fd_decode (paged: fd_decode_paged) launches for these arguments:
+    route and kernel by name, B and L, waves and query tiles per work-group,
+    launches, split-kernel work-groups and workspace bytes.  num_cus 0: the
+    current device's compute units; > 0: plan for that many without a GPU."""
+    p = _Plan()
+    _check(library().fd_decode_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, _code(dtype),
+                                     int(bool(has_kv_lens)), int(bool(paged)), num_splits,
+                                     split_len, num_cus, ctypes.byref(p)))
+    return {"route": ROUTES[p.route], "kernel": KERNELS[p.kernel], "num_splits": p.num_splits,
+            "split_len": p.split_len, "waves_per_group": p.waves_per_group,
+            "query_tiles": p.query_tiles, "launches": p.launches, "work_groups": p.work_groups,
+            "workspace_bytes": p.workspace_bytes}
 
 
 def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, scale=None,

@@ -104,12 +104,51 @@ size_t fd_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim);
 /* Bytes of workspace fd_decode needs when called with exactly these
  * arguments (has_kv_lens: nonzero when kv_lens will be non-NULL), including
  * the automatic plan of num_splits == 0 described at fd_decode.  Writes 0 when
- * no workspace is needed.  May query the current HIP device (compute units).
+ * no workspace is needed; equals fd_decode_plan's workspace_bytes for the
+ * same arguments.  May query the current HIP device (compute units).
  * Returns FD_OK, FD_ERR_INVALID (bad sizes, null bytes), FD_ERR_UNSUPPORTED
  * (head_dim or dtype) or FD_ERR_HIP. */
 int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_len,
                               int head_dim, int in_dtype, int has_kv_lens, int num_splits,
                               int split_len, size_t *bytes);
+
+/* Routes of a decode step (fd_plan.route). */
+#define FD_ROUTE_DIRECT 0   /* one split per row: the split kernel writes o and lse */
+#define FD_ROUTE_FUSED 1    /* 2..8 splits of a row in one work-group, merged in LDS */
+#define FD_ROUTE_SPLITS 2   /* fixed splits into the workspace, then the combine */
+#define FD_ROUTE_BALANCED 3 /* token-balanced pieces into the workspace, then the combine */
+
+/* Split kernels (fd_plan.kernel). */
+#define FD_KERNEL_VECTOR 0   /* vector ALUs, one query head per wave (MHA, fp32) */
+#define FD_KERNEL_GROUPED 1  /* matrix cores, one 16-query tile of a KV head's group */
+#define FD_KERNEL_TILED 2    /* matrix cores, several 16-query tiles per K/V read */
+#define FD_KERNEL_BALANCED 3 /* matrix cores over the token-balanced partition */
+
+/* What fd_decode / fd_decode_paged launch for a set of arguments. */
+typedef struct fd_plan {
+    int route;           /* FD_ROUTE_* */
+    int kernel;          /* FD_KERNEL_* */
+    int num_splits;      /* B (0 on FD_ROUTE_BALANCED) */
+    int split_len;       /* L (0 on FD_ROUTE_BALANCED) */
+    int waves_per_group; /* wave64s per work-group of the split kernel */
+    int query_tiles;     /* 16-query tiles per matrix-core work-group (0: vector kernel) */
+    int launches;        /* kernel launches of the step: 1 or 2 */
+    int64_t work_groups; /* grid size of the split kernel */
+    size_t workspace_bytes; /* what fd_decode_workspace_bytes reports */
+} fd_plan;
+
+/* The plan fd_decode (paged == 0) or fd_decode_paged (paged != 0, max_kv_len
+ * = max_pages_per_seq * page_size) follows for these arguments: the route,
+ * the split kernel, B and L, and the workspace (the rules are at fd_decode).
+ * has_kv_lens: nonzero when kv_lens will be non-NULL.  num_cus <= 0 queries
+ * the current HIP device (cached); > 0 plans for that many compute units
+ * without touching a device.  Host-only and deterministic.  Returns FD_OK,
+ * FD_ERR_INVALID (bad sizes, B * L < max_kv_len, a paged split_len that is
+ * not a multiple of 16, null plan), FD_ERR_UNSUPPORTED (head_dim or dtype)
+ * or FD_ERR_HIP; the same arguments make fd_decode fail the same way. */
+int fd_decode_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                   int in_dtype, int has_kv_lens, int paged, int num_splits, int split_len,
+                   int num_cus, fd_plan *plan);
 
 /* Split stage ([P1] §2.5 stage 1; [P3] §3.2.1 stage 1): for every
  * (b, h, split i) with token range [i*L, min((i+1)*L, N_b)) write

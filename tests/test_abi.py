@@ -103,27 +103,104 @@ def test_workspace_bytes(lib):
     assert ws % 256 == 0 and ws >= 3 * 5 * 7 * 65 * 4
 
 
-def test_decode_workspace_bytes_explicit_splits(lib):
-    """With the split count given, fd_decode needs fd_workspace_bytes, or
-    nothing when a small grid merges its splits in one work-group (that case
-    needs the device's CU count, so without a GPU it is never taken); bad
-    arguments are rejected."""
-    out = ctypes.c_size_t(123)
-    for B, has_lens in ((4, 0), (4, 1), (1, 1), (37, 0)):
-        assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, has_lens, B, 0,
-                                             ctypes.byref(out)) == fd.OK
-        assert out.value in (0, lib.fd_workspace_bytes(3, 8, B, 128))
-        assert B <= 8 or out.value == lib.fd_workspace_bytes(3, 8, B, 128)
-    assert lib.fd_decode_workspace_bytes(3, 8, 3, 1000, 128, fd.BF16, 0, 4, 0,
-                                         ctypes.byref(out)) == fd.ERR_INVALID
-    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 96, fd.BF16, 0, 4, 0,
-                                         ctypes.byref(out)) == fd.ERR_UNSUPPORTED
-    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, 7, 0, 4, 0,
-                                         ctypes.byref(out)) == fd.ERR_UNSUPPORTED
-    assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, 0, -1, 0,
-                                         ctypes.byref(out)) == fd.ERR_INVALID
+def _plan(lib, batch, hq, hkv, n, d, dt, has_lens=0, B=0, L=0, paged=0, cus=256):
+    p = fd._Plan()
+    rc = lib.fd_decode_plan(batch, hq, hkv, n, d, dt, has_lens, paged, B, L, cus, ctypes.byref(p))
+    return rc, p
+
+
+def test_decode_plan_struct_layout():
+    """The binding's fd_plan mirrors the header: seven ints, then two 64-bit
+    fields on 8-byte boundaries."""
+    assert ctypes.sizeof(fd._Plan) == 7 * 4 + 4 + 8 + 8
+    assert fd._Plan.work_groups.offset == 32 and fd._Plan.workspace_bytes.offset == 40
+
+
+@pytest.mark.parametrize("case", [
+    # the five named workloads on 256 CUs
+    ((1, 1, 1, 1024, 64, fd.F32, 0, 4, 256), dict(route=fd.ROUTES.index("fused"), kernel=0,
+                                                  num_splits=4, split_len=256, waves_per_group=4,
+                                                  launches=1, work_groups=1, workspace_bytes=0)),
+    ((8, 32, 32, 4096, 128, fd.BF16, 0, 0, 0), dict(route=0, kernel=0, num_splits=1,
+                                                    split_len=4096, waves_per_group=2, launches=1,
+                                                    work_groups=256, workspace_bytes=0)),
+    ((1, 32, 32, 65536, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=0, num_splits=16,
+                                                     split_len=4096, waves_per_group=1,
+                                                     launches=2, work_groups=512)),
+    ((16, 64, 8, 32768, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, num_splits=0,
+                                                     split_len=0, query_tiles=1, launches=2,
+                                                     work_groups=512)),
+    ((4, 16, 16, 131072, 256, fd.F16, 0, 0, 0), dict(route=2, kernel=0, num_splits=8,
+                                                     split_len=16384, waves_per_group=1,
+                                                     work_groups=512)),
+    # grouped heads: one tile, fixed splits without lengths
+    ((16, 64, 8, 32768, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=1, query_tiles=1)),
+    # multi-query with 64 heads at d = 64: four tiles per work-group
+    ((4, 64, 1, 8192, 64, fd.F16, 0, 0, 0), dict(kernel=2, query_tiles=4)),
+    # 32 per KV head, ragged: balanced over two tiles; 40: past the balanced plan
+    ((16, 64, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=2)),
+    ((16, 80, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=2, kernel=2, query_tiles=2)),
+    # explicit splits: one split writes o itself; fp32 grouped heads stay on the vector kernel
+    ((2, 8, 2, 1000, 128, fd.BF16, 1, 1, 0), dict(route=0, kernel=1, num_splits=1,
+                                                  split_len=1000, launches=1, workspace_bytes=0)),
+    ((2, 8, 2, 1000, 64, fd.F32, 1, 3, 0), dict(route=1, kernel=0, num_splits=3, split_len=334,
+                                                waves_per_group=4, work_groups=16)),
+])
+def test_decode_plan_routes(lib, case):
+    args, want = case
+    rc, p = _plan(lib, *args[:7], B=args[7], L=args[8])
+    assert rc == fd.OK, fd.last_error()
+    for key, value in want.items():
+        assert getattr(p, key) == value, (key, getattr(p, key), value)
+    batch, hq, hkv, n, d, dt = args[:6]
+    if p.route == fd.ROUTES.index("splits"):
+        assert p.launches == 2
+        assert p.workspace_bytes == lib.fd_workspace_bytes(batch, hq, p.num_splits, d)
+        assert p.num_splits * p.split_len >= n
+    elif p.route == fd.ROUTES.index("balanced"):
+        # o and LSE slots for work-groups + units, and one descriptor per unit
+        slots = p.work_groups + batch * hkv
+        assert p.workspace_bytes >= slots * (hq // hkv) * (d + 1) * 4 + batch * hkv * 8
+    else:
+        assert p.launches == 1 and p.workspace_bytes == 0
+    # the plan does not change on a repeated call
+    rc2, p2 = _plan(lib, *args[:7], B=args[7], L=args[8])
+    assert rc2 == fd.OK and bytes(p2) == bytes(p)
+
+
+def test_decode_plan_paged_and_errors(lib):
+    # paged: an implicit split length is rounded up to whole 16-token tiles
+    rc, p = _plan(lib, 8, 32, 32, 4096, 128, fd.BF16, 0, 3, 0, paged=1)
+    assert rc == fd.OK and (p.num_splits, p.split_len) == (3, 1376)
+    rc, p = _plan(lib, 8, 32, 32, 4096, 128, fd.BF16, 0, 3, 0, paged=0)
+    assert rc == fd.OK and (p.num_splits, p.split_len) == (3, 1366)
+    assert _plan(lib, 8, 32, 32, 4096, 128, fd.BF16, 0, 41, 100, paged=1)[0] == fd.ERR_INVALID
+    assert _plan(lib, 8, 32, 32, 4096, 128, fd.BF16, 0, 4, 1000)[0] == fd.ERR_INVALID  # B*L < N
+    assert _plan(lib, 3, 8, 3, 1000, 128, fd.BF16)[0] == fd.ERR_INVALID
+    assert _plan(lib, 3, 8, 2, 1000, 96, fd.BF16)[0] == fd.ERR_UNSUPPORTED
+    assert _plan(lib, 3, 8, 2, 1000, 128, 7)[0] == fd.ERR_UNSUPPORTED
+    assert _plan(lib, 3, 8, 2, 1000, 128, fd.BF16, 0, -1)[0] == fd.ERR_INVALID
+    assert lib.fd_decode_plan(3, 8, 2, 1000, 128, fd.BF16, 0, 0, 4, 0, 256, None) == fd.ERR_INVALID
+    out = ctypes.c_size_t()
     assert lib.fd_decode_workspace_bytes(3, 8, 2, 1000, 128, fd.BF16, 0, 4, 0,
                                          None) == fd.ERR_INVALID
+    assert lib.fd_decode_workspace_bytes(3, 8, 3, 1000, 128, fd.BF16, 0, 4, 0,
+                                         ctypes.byref(out)) == fd.ERR_INVALID
+
+
+def test_decode_plan_small_grids_fuse(lib):
+    """The vector kernel merges 2..8 splits of a row in one work-group only
+    while the split work-groups would not fill two waves per CU."""
+    for B, waves in ((2, 2), (3, 4), (4, 4), (5, 8), (8, 8)):
+        rc, p = _plan(lib, 1, 4, 4, 4096, 128, fd.BF16, 0, B, 0)
+        assert rc == fd.OK and p.route == 1 and p.waves_per_group == waves
+        assert p.work_groups == 4
+    rc, p = _plan(lib, 1, 4, 4, 4096, 128, fd.BF16, 0, 9, 0)
+    assert p.route == 2
+    rc, p = _plan(lib, 64, 8, 8, 4096, 128, fd.BF16, 0, 2, 0)  # 1024 work-groups: not fused
+    assert p.route == 2 and p.waves_per_group == 1
+    rc, p = _plan(lib, 64, 8, 8, 4096, 128, fd.BF16, 0, 2, 0, cus=1024)  # a bigger GPU: fused
+    assert p.route == 1
 
 
 def _split(lib, **kw):

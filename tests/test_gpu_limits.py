@@ -57,7 +57,7 @@ def test_kv_tensors_past_4gib(gpu, case):
         # 2 x 2,228,224 tokens x 4 KV heads x 128 x 2 B = 4.56 GB per tensor
         n = (1 << 21) + (1 << 17)
         w, inp = workloads.custom(2, 32, 4, 128, n, dtype="bf16", seed=61, lens=[n, n - 12345])
-        assert fd.uses_balanced_plan(32, 4, n, 128, torch.bfloat16, True, 0)
+        assert fd.decode_plan(2, 32, 4, n, 128, torch.bfloat16, True)["route"] == "balanced"
     else:
         # 1 x 4,456,448 tokens x 4 heads x 64 x 4 B = 4.56 GB per tensor
         n = (1 << 22) + (1 << 18)

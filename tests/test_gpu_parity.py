@@ -350,3 +350,47 @@ def test_concurrent_host_threads(gpu):
     for th in threads:
         th.join()
     assert not errors, errors
+
+
+@pytest.mark.parametrize("route,shape", [
+    ("direct", dict(batch=4, hq=8, hkv=8, d=128, n=1000, dtype="bf16", B=1)),
+    ("fused", dict(batch=1, hq=4, hkv=4, d=64, n=1000, dtype="f32", B=3)),
+    ("splits", dict(batch=2, hq=8, hkv=2, d=128, n=1500, dtype="bf16", B=5)),
+    ("balanced", dict(batch=3, hq=16, hkv=2, d=128, n=2000, dtype="bf16", B=0,
+                      lens=[2000, 3, 1111])),
+    ("splits", dict(batch=2, hq=48, hkv=2, d=64, n=700, dtype="f16", B=0)),
+])
+def test_decode_plan_is_what_runs(gpu, route, shape):
+    """fd_decode_plan on the device names the route taken; the plan for the
+    device's CU count is the same; fd_decode given exactly the planned
+    workspace (none when the plan needs none) matches the oracle."""
+    import ctypes
+
+    s = shape
+    lens = s.get("lens")
+    w, inp = workloads.custom(s["batch"], s["hq"], s["hkv"], s["d"], s["n"], dtype=s["dtype"],
+                              seed=81 + s["hq"], lens=lens)
+    q, k, v, kl = _to(gpu, inp)
+    plan = fd.decode_plan(s["batch"], s["hq"], s["hkv"], s["n"], s["d"], q.dtype, kl is not None,
+                          s["B"])
+    cus = torch.cuda.get_device_properties(gpu).multi_processor_count
+    assert plan == fd.decode_plan(s["batch"], s["hq"], s["hkv"], s["n"], s["d"], q.dtype,
+                                  kl is not None, s["B"], num_cus=cus)
+    assert plan["route"] == route, plan
+    print(plan, flush=True)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=gpu)
+    ws = (torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=gpu)
+          if plan["workspace_bytes"] else None)
+    code = {torch.float32: fd.F32, torch.float16: fd.F16, torch.bfloat16: fd.BF16}[q.dtype]
+    P = ctypes.c_void_p
+    rc = fd.library().fd_decode(
+        P(q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
+        None if kl is None else P(kl.data_ptr()), s["batch"], s["hq"], s["hkv"], s["n"], s["d"],
+        code, code, ctypes.c_float(w.scale), s["B"], 0, P(o.data_ptr()), P(lse.data_ptr()),
+        None if ws is None else P(ws.data_ptr()), plan["workspace_bytes"],
+        P(torch.cuda.current_stream(gpu).cuda_stream))
+    assert rc == fd.OK, fd.last_error()
+    torch.cuda.synchronize()
+    ro, rl = _oracle(w, inp)
+    _assert_close(f"plan_{route}", o, lse, ro.reshape(-1, s["d"]), rl.reshape(-1), s["dtype"])
