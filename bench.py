@@ -519,6 +519,35 @@ def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     return out
 
 
+def cpu_baseline_workload(p: Prepared, one_thread: bool) -> dict:
+    """Part of the cpu_baseline leg: the fp64 oracle over one whole decode step
+    of p's workload, on the same host inputs, by wall clock, on the host cores
+    and, when asked, on one thread (a reported baseline beside the GPU's step,
+    never its target)."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    w, inp = p.w, p.host
+    lens = inp["kv_lens"]
+    args = (w.dtype, workloads.raw(inp["q"]), workloads.raw(inp["k"]), workloads.raw(inp["v"]),
+            None if lens is None else lens.numpy())
+    threads = oracle.threads()
+    t0 = time.perf_counter()
+    oracle.attention(*args, scale=w.scale)
+    wall = time.perf_counter() - t0
+    out = {"us_per_step": round(wall * 1e6, 1), "cores": threads, "kind": "oracle",
+           "kv_GBps": round(p.kv_bytes / wall / 1e9, 3)}
+    if one_thread:
+        oracle.set_threads(1)
+        try:
+            t1 = time.perf_counter()
+            oracle.attention(*args, scale=w.scale)
+            one = time.perf_counter() - t1
+        finally:
+            oracle.set_threads(threads)
+        out["one_thread_us_per_step"] = round(one * 1e6, 1)
+    return out
+
+
 def traffic_from_profile(name: str) -> dict | None:
     """HBM bytes per split-kernel launch from a committed rocprofv3 counter
     summary, when it was taken on the current kernel sources."""
@@ -664,6 +693,10 @@ def main() -> int:
             others[w.name] = summarize(q, tt, su)
             others[w.name]["inputs_sha256"] = workloads.digest(q.host)
             log(f"[bench] {w.name}: {others[w.name]}")
+            if cpu is not None:  # the oracle beside it: one step (one thread too up to 1 GiB)
+                cw = cpu_baseline_workload(q, one_thread=q.kv_bytes <= (1 << 30))
+                cpu.setdefault("workloads", {})[w.name] = cw
+                log(f"[bench] oracle {w.name}: {cw}")
             q.free()
             del q
             torch.cuda.empty_cache()
