@@ -168,14 +168,29 @@ bool large_group(int in_dtype, int head_dim, int group) {
            fd::split_mfma_tiled_supported(in_dtype, head_dim);
 }
 
-// Query tiles per work-group of the tiled kernel for nq queries per KV head:
-// the most that fit, but no more than there are tiles.
-int tiled_qt(int head_dim, long long nq) {
+// Shape of the tiled kernel's work-groups for nq queries per KV head: qt
+// query tiles per wave (the most a wave holds, but no more than there are
+// tiles) and, past what one wave holds, several waves per work-group sharing
+// each staged K/V step (up to the most the head size allows), so that the
+// work-groups of a unit read its rows as few times as possible; groups is
+// the number of work-groups per unit.
+struct TiledShape {
+    int qt = 1, waves = 1;
+    long long groups = 1;
+    int per_cu() const { return fd::split_mfma_tiled_wg_per_cu(waves); }
+};
+
+TiledShape tiled_shape(int head_dim, long long nq) {
+    TiledShape t;
     const long long tiles = (nq + 15) / 16;
-    int qt = fd::split_mfma_tile_max_qt(head_dim);
-    while (qt > 1 && qt / 2 >= tiles)
-        qt /= 2;
-    return qt;
+    t.qt = fd::split_mfma_tile_max_qt(head_dim);
+    while (t.qt > 1 && t.qt / 2 >= tiles)
+        t.qt /= 2;
+    const int wmax = fd::split_mfma_tile_max_waves(head_dim);
+    while (t.waves < wmax && (long long)t.qt * t.waves < tiles)
+        t.waves *= 2;
+    t.groups = (tiles + (long long)t.qt * t.waves - 1) / ((long long)t.qt * t.waves);
+    return t;
 }
 
 // Waves per work-group when the vector kernel runs every split of a row in one
@@ -218,8 +233,11 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
     hipError_t e;
     switch (split_kernel(a, in_dtype)) {
     case FD_KERNEL_TILED:
-        if (a.tile_qt == 0)
-            a.tile_qt = tiled_qt(a.head_dim, a.heads_q / a.heads_kv);
+        if (a.tile_qt == 0) {
+            const TiledShape t = tiled_shape(a.head_dim, a.heads_q / a.heads_kv);
+            a.tile_qt = t.qt;
+            a.tile_waves = t.waves;
+        }
         e = fd::launch_split_mfma(a, in_dtype, stream);
         break;
     case FD_KERNEL_GROUPED:
@@ -367,12 +385,11 @@ int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim
         r.work_groups = (int64_t)batch * heads_kv * num_splits;
         break;
     default: {  // FD_KERNEL_TILED: units padded to multiples of 8, times tile groups
-        const int qt = tiled_qt(head_dim, group);
-        const long long groups = ((group + 15) / 16 + qt - 1) / qt;
+        const TiledShape t = tiled_shape(head_dim, group);
         const long long units = (long long)batch * heads_kv * num_splits;
-        r.waves_per_group = 1;
-        r.query_tiles = qt;
-        r.work_groups = (units + 7) / 8 * 8 * groups;
+        r.waves_per_group = t.waves;
+        r.query_tiles = t.qt * t.waves;
+        r.work_groups = (units + 7) / 8 * 8 * t.groups;
     }
     }
     r.route = num_splits == 1 ? FD_ROUTE_DIRECT : (p->fused > 0 ? FD_ROUTE_FUSED : FD_ROUTE_SPLITS);
@@ -433,10 +450,9 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     long long units = (long long)batch * (grouped ? heads_kv : heads_q);
     int per_cu = grouped ? fd::kMfmaWgPerCU : kWorkGroupsPerCU;
     if (tiled) {
-        const long long tiles = (group + 15) / 16;
-        const int qt = tiled_qt(head_dim, group);
-        units = (long long)batch * heads_kv * ((tiles + qt - 1) / qt);
-        per_cu = fd::kPrefixWgPerCU;
+        const TiledShape t = tiled_shape(head_dim, group);
+        units = (long long)batch * heads_kv * t.groups;
+        per_cu = t.per_cu();
     }
     const long long target = (long long)num_cus * per_cu * (ragged ? kRaggedRounds : 1);
     long long b = (target + units - 1) / units;
@@ -574,6 +590,7 @@ int check_combine(const float *o_part, int batch, int heads_q, int num_splits, i
 struct CascadePlan {
     int bp = 0, lp = 0, bs = 1, ls = 1;
     int tile_qt = 0;  // > 0: the prefix runs on the tiled matrix-core kernel
+    int tile_waves = 1;
     // ragged grouped suffixes: token-balanced partition (bal), its slots merged
     // with the prefix partials by the slot combine; bs/ls unused then
     bool balanced = false;
@@ -595,10 +612,9 @@ int prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int head_d
     if (rc != FD_OK)
         return rc;
     const long long nq = (long long)batch * (heads_q / heads_kv);
-    const long long tiles = (nq + 15) / 16;
-    const int qt = tiled_qt(head_dim, nq);
-    const long long per_split = (long long)heads_kv * ((tiles + qt - 1) / qt);
-    long long b = ((long long)cus * fd::kPrefixWgPerCU + per_split - 1) / per_split;
+    const TiledShape t = tiled_shape(head_dim, nq);
+    const long long per_split = (long long)heads_kv * t.groups;
+    long long b = ((long long)cus * t.per_cu() + per_split - 1) / per_split;
     const long long bmax = (prefix_len + kMinPrefixSplitLen - 1) / kMinPrefixSplitLen;
     b = b > bmax ? bmax : b;
     b = b > kMaxAutoSplits ? kMaxAutoSplits : (b < 1 ? 1 : b);
@@ -606,7 +622,8 @@ int prefix_plan(int batch, int heads_q, int heads_kv, int prefix_len, int head_d
     len = (len + 15) / 16 * 16;
     p->bp = (int)((prefix_len + len - 1) / len);
     p->lp = (int)len;
-    p->tile_qt = qt;
+    p->tile_qt = t.qt;
+    p->tile_waves = t.waves;
     return FD_OK;
 }
 
@@ -730,6 +747,7 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
         pa.num_splits = p.bp;
         pa.split_len = p.lp;
         pa.tile_qt = p.tile_qt;
+        pa.tile_waves = p.tile_waves;
         rc = launch_split(pa, in_dtype, st);
         if (rc != FD_OK)
             return rc;

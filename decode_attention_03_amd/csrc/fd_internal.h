@@ -32,6 +32,9 @@ constexpr int kMfmaWgPerCU = FD_MFMA_WG_PER_CU;
 #define FD_PREFIX_WG_PER_CU 4
 #endif
 constexpr int kPrefixWgPerCU = FD_PREFIX_WG_PER_CU;
+// With several waves per work-group (tile_waves) the same number of waves
+// per CU: kPrefixWgPerCU / tile_waves work-groups (each wave needs over half
+// of a SIMD's registers, so one wave per SIMD is what fits anyway).
 
 // Everything one split-stage launch needs.  Shapes follow the public layouts:
 // q [batch, heads_q, d], K/V [batch, max_kv_len, heads_kv, d].
@@ -78,6 +81,10 @@ struct SplitArgs {
     // the KV head; otherwise the G queries of one sequence (groups larger
     // than one tile).  0 selects the one-tile kernels.
     int tile_qt;
+    // Tiled kernel: waves per work-group (1, 2 or 4; 0 means 1).  The waves
+    // take tile_qt tiles each and share every K/V step staged in LDS, so a
+    // work-group serves tile_qt * tile_waves tiles from one read of the rows.
+    int tile_waves;
     // Fixed-split partial slots: split i of row r is slot r * part_stride +
     // part_offset + i (part_stride 0 means num_splits), so two launches can
     // fill one partial buffer.
@@ -107,7 +114,12 @@ bool split_mfma_supported(int in_dtype, int head_dim, int group);
 // The tiled kernel: any group size (per sequence: groups larger than one
 // tile; shared prefix: any).
 bool split_mfma_tiled_supported(int in_dtype, int head_dim);
-int split_mfma_tile_max_qt(int head_dim);  // query tiles per work-group, 1..4
+int split_mfma_tile_max_qt(int head_dim);  // query tiles per wave, 1..4
+// Most waves a tiled work-group can have at this head size (each loads an
+// equal share of every staged row group): 2 at d = 64, 4 at d = 128 and 256.
+int split_mfma_tile_max_waves(int head_dim);
+// Resident tiled work-groups per CU with this many waves each.
+int split_mfma_tiled_wg_per_cu(int waves);
 // Largest group the token-balanced kernel takes (all of a unit's query tiles
 // in one work-group).
 int split_mfma_balanced_max_group(int head_dim);

@@ -160,6 +160,22 @@ typedef __attribute__((address_space(3))) char lds_char;
 #define FD_PREFIX_QT128 2
 #endif
 constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the tiled kernel
+// Tiled work-groups of several waves: K/V bytes per step (shared by the
+// waves), non-temporal loads or not, and waves per SIMD aimed at.
+#ifndef FD_WIDE_STEP_KB
+#define FD_WIDE_STEP_KB 0
+#endif
+#ifndef FD_WIDE_NT
+#define FD_WIDE_NT 0
+#endif
+#ifndef FD_WIDE_WPE
+#define FD_WIDE_WPE 1
+#endif
+// 0: 8 KB per wave (16 KB for two waves, 32 KB for four)
+template <int W>
+constexpr int wide_step_kb() {
+    return FD_WIDE_STEP_KB > 0 ? FD_WIDE_STEP_KB : 8 * W;
+}
 
 // Where a piece's results go.  Partial i of query row `row` (slot h of a
 // tile when `local`) is at index (row or h) * stride + off: o at o + index * D
@@ -204,15 +220,22 @@ struct QMap {
 // (NTLOAD) unless other work-groups will read the same rows.  Called by the whole wave; t0 >= t1
 // writes (0, -inf).  (Device pass only: the body uses LDS address-space
 // pointers and gfx950-only builtins that the host pass cannot type.)
-template <int DT, int D, bool PAGED, int QT, int NTLOAD = 1, int STEP_KB = FD_MFMA_STEP_KB>
+template <int DT, int D, bool PAGED, int QT, int NTLOAD = 1, int STEP_KB = FD_MFMA_STEP_KB,
+          int W = 1>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
                                            long t0, long t1, const QMap &qm,
                                            const PieceOut &out) {
     using T = Tiles<D, STEP_KB>;
     constexpr int NC = T::NC, NT = T::NT, U = T::U;
     using M = Mma<DT>;
+    // W waves share each step: wave wv loads row groups wv, wv + W, ... of
+    // every tile, and all of them compute on all rows (two LDS buffers, one
+    // barrier per step).  W == 1: one wave, one buffer, no barrier.
+    static_assert(T::IPT % W == 0, "row groups per tile must divide among the waves");
+    constexpr int JW = T::IPT / W;  // row groups per tile a wave loads
 
-    const int lane = threadIdx.x;
+    const int lane = W > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int col = lane & 15;  // tile token (K reads) / query slot (S) / d column (O)
     const int grp = lane >> 4;  // 0..3
 
@@ -262,8 +285,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         // first + 16u + r, clamped to the last valid token; a step past the
         // last one re-reads the last step, so prefetches need no condition).
         struct Stage {
-            u32x4 k[U][T::IPT];
-            u32x4 v[U][T::IPT];
+            u32x4 k[U][JW];
+            u32x4 v[U][JW];
         };
         const int lrow = lane / T::CPR;  // row within a row group
         const int lq = lane % T::CPR;    // logical chunk this lane carries
@@ -324,32 +347,43 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 const char *kb = static_cast<const char *>(a.k) + base + lane_off64;
                 const char *vb = static_cast<const char *>(a.v) + base + lane_off64;
 #pragma unroll
-                for (int j = 0; j < T::IPT; ++j) {
-                    int rel = 16 * u + j * T::RPI + lrow;
+                for (int jj = 0; jj < JW; ++jj) {
+                    int rel = 16 * u + (jj * W + wv) * T::RPI + lrow;
                     rel = rel < last_rel ? rel : last_rel;
                     // row within the base: the step-relative token, or the
                     // token's row within its page
                     const uint32_t row =
                         PAGED ? ((uint32_t)((int)t0 + first + rel) & pmask) : (uint32_t)rel;
                     const uint32_t off = row * stride32 + lane_off32;
-                    g.k[u][j] = ld128<NTLOAD>(kb + off);
-                    g.v[u][j] = ld128<NTLOAD>(vb + off);
+                    g.k[u][jj] = ld128<NTLOAD>(kb + off);
+                    g.v[u][jj] = ld128<NTLOAD>(vb + off);
                 }
             }
         };
 
-        // Write a step's rows into the LDS tiles, chunks swizzled per row.
-        auto stage = [&](const Stage &g) {
+        // Write a step's rows into LDS tiles at buf, chunks swizzled per row.
+        auto stage = [&](const Stage &g, lds_char *buf) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int j = 0; j < T::IPT; ++j) {
-                    const int r = j * T::RPI + lrow;
+                for (int jj = 0; jj < JW; ++jj) {
+                    const int r = (jj * W + wv) * T::RPI + lrow;
                     *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
-                        tb + u * T::TILE + r * T::ROW + (lq ^ T::swz_k(r)) * 16) = g.k[u][j];
+                        buf + u * T::TILE + r * T::ROW + (lq ^ T::swz_k(r)) * 16) = g.k[u][jj];
                     *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
-                        tb + (U + u) * T::TILE + r * T::ROW + (lq ^ T::swz_v(r)) * 16) = g.v[u][j];
+                        buf + (U + u) * T::TILE + r * T::ROW + (lq ^ T::swz_v(r)) * 16) =
+                        g.v[u][jj];
                 }
+        };
+        // Several waves: even steps in buffer 0, odd steps in buffer 1.  A
+        // wave stages step s + 1 only after the barrier that follows every
+        // wave's staging of step s, which each wave reaches after computing
+        // step s - 1: the buffer it overwrites has been read by all.
+        lds_char *const b0 = tb;
+        lds_char *const b1 = W > 1 ? tb + T::BUF : tb;
+        auto wg_sync = [] {
+            if constexpr (W > 1)
+                __syncthreads();
         };
 
         // All LDS fragments of one step: K for the S product, V (read
@@ -468,20 +502,22 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             lookup(2, pa);
             for (int pr = 0; pr < npairs; ++pr) {
                 const int st = 2 * pr;
-                stage(ga);
+                stage(ga, b0);
                 __builtin_amdgcn_sched_barrier(0);
                 load_step(st + 2, pa, ga);
                 __builtin_amdgcn_sched_barrier(0);
-                fetch(tb, f);
+                wg_sync();
+                fetch(b0, f);
                 compute_step(st, f);
                 if constexpr (PAGED)
                     __builtin_amdgcn_sched_barrier(0);
                 lookup(st + 3, pb);
-                stage(gb);
+                stage(gb, b1);
                 __builtin_amdgcn_sched_barrier(0);
                 load_step(st + 3, pb, gb);
                 __builtin_amdgcn_sched_barrier(0);
-                fetch(tb, f);
+                wg_sync();
+                fetch(b1, f);
                 compute_step(st + 1, f);
                 if constexpr (PAGED)
                     __builtin_amdgcn_sched_barrier(0);
@@ -493,20 +529,23 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 load_step(st + 1, pb, gb);
                 lookup(st + 2, pa);
                 __builtin_amdgcn_sched_barrier(0);
-                stage(ga);
-                fetch(tb, f);
+                stage(ga, b0);
+                wg_sync();
+                fetch(b0, f);
                 compute_step(st, f);
                 load_step(st + 2, pa, ga);
                 lookup(st + 3, pb);
                 __builtin_amdgcn_sched_barrier(0);
-                stage(gb);
-                fetch(tb, f);
+                stage(gb, b1);
+                wg_sync();
+                fetch(b1, f);
                 compute_step(st + 1, f);
             }
         }
         if (nsteps & 1) {
-            stage(ga);
-            fetch(tb, f);
+            stage(ga, b0);
+            wg_sync();
+            fetch(b0, f);
             compute_step(nsteps - 1, f);
         }
     }
@@ -594,8 +633,9 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 }
 
 // Query tiles: all queries of a KV head that read the same K/V, in tiles of
-// 16, QT tiles per work-group; a (KV head, split) unit with more tiles gets
-// several work-groups.  Two uses: a shared prefix (cascade), whose batch * G
+// 16, QT tiles per wave and W waves per work-group (the waves share every K/V
+// step staged in LDS, each loading a 1/W share of its rows); a (KV head,
+// split) unit with more tiles gets several work-groups.  Two uses: a shared prefix (cascade), whose batch * G
 // queries all read the prefix, and groups of more than 16 query heads per KV
 // head (up to multi-query attention), whose G queries read their sequence's
 // K/V.  Each work-group serves its QT tiles from every K/V tile it stages,
@@ -606,13 +646,15 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 // unit = (sequence, split, KV head), KV head fastest (one sequence for a
 // shared prefix).  The K/V loads are ordinary (temporal) loads, as other
 // work-groups may read the same rows.
-template <int DT, int D, int QT, bool PAGED>
-__global__ __launch_bounds__(64) void split_mfma_tiled_kernel(SplitArgs a) {
+template <int DT, int D, int QT, bool PAGED, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 1 ? FD_WIDE_WPE : 1)))
+void split_mfma_tiled_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D, kPrefixStepKB>::BUF];
+    constexpr int SKB = W > 1 ? wide_step_kb<W>() : kPrefixStepKB;
+    __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
     const int G = a.heads_q / a.heads_kv;
     const int nq = a.shared_kv ? a.batch * G : G;
-    const int groups = ((nq + 15) / 16 + QT - 1) / QT;  // tile groups per unit
+    const int groups = ((nq + 15) / 16 + QT * W - 1) / (QT * W);  // tile groups per unit
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
     const int unit = (slot / groups) * 8 + xcd;
@@ -627,7 +669,9 @@ __global__ __launch_bounds__(64) void split_mfma_tiled_kernel(SplitArgs a) {
     const int n = a.shared_kv ? a.max_kv_len : clamp_len(a.kv_lens, b, a.max_kv_len);
     const long t0 = (long)split * a.split_len;
     const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
-    const QMap qm{a.shared_kv ? 0 : b * a.heads_q, G, nq, j * QT, a.heads_q, kvh};
+    // wave wv of the work-group takes tiles (j * W + wv) * QT ...
+    const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+    const QMap qm{a.shared_kv ? 0 : b * a.heads_q, G, nq, (j * W + wv) * QT, a.heads_q, kvh};
     PieceOut out{nullptr, nullptr, nullptr, 0, 0, false};
     if (a.o_part) {
         out.o = a.o_part;
@@ -636,8 +680,8 @@ __global__ __launch_bounds__(64) void split_mfma_tiled_kernel(SplitArgs a) {
         out.lse = a.m_part ? a.m_part : a.lse_part;
         out.l = a.m_part ? a.l_part : nullptr;
     }
-    mfma_piece<DT, D, PAGED, QT, 0, kPrefixStepKB>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm,
-                                                   out);
+    constexpr int NTL = W > 1 ? FD_WIDE_NT : 0;
+    mfma_piece<DT, D, PAGED, QT, NTL, SKB, W>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -728,13 +772,27 @@ constexpr int tile_max_qt() {
     return D == 64 ? 4 : (D == 128 ? FD_PREFIX_QT128 : 1);
 }
 
+// Waves of a tiled work-group: each loads an equal share of the row groups
+// of every staged tile (2 at d = 64, 4 at d = 128 and 256), capped by
+// FD_TILE_MAX_WAVES.
+#ifndef FD_TILE_MAX_WAVES
+#define FD_TILE_MAX_WAVES 4
+#endif
+template <int D>
+constexpr int tile_max_waves() {
+    constexpr int ipt = Tiles<D, kPrefixStepKB>::IPT;
+    constexpr int w = ipt >= 4 ? 4 : ipt;
+    return w < FD_TILE_MAX_WAVES ? w : FD_TILE_MAX_WAVES;
+}
+
 // The tiled kernel for QT query tiles per work-group, paged or contiguous.
-template <int DT, int D, int QT>
-void launch_tiled(const SplitArgs &a, dim3 g, dim3 blk, size_t pad, hipStream_t stream) {
+template <int DT, int D, int QT, int W = 1>
+void launch_tiled(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
+    const dim3 blk(64 * W);
     if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, true>), g, blk, pad, stream, a);
+        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, true, W>), g, blk, pad, stream, a);
     else
-        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false>), g, blk, pad, stream, a);
+        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false, W>), g, blk, pad, stream, a);
 }
 
 // The token-balanced kernel for QT query tiles per unit, paged or contiguous.
@@ -749,12 +807,17 @@ void launch_balanced(const SplitArgs &a, dim3 g, dim3 blk, size_t pad, hipStream
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
-    const size_t kStatic = a.tile_qt > 0 ? (size_t)Tiles<D, kPrefixStepKB>::BUF : (size_t)T::BUF;
+    const int tw = a.tile_waves > 1 ? a.tile_waves : 1;
+    const size_t kStatic =
+        a.tile_qt == 0 ? (size_t)T::BUF
+        : tw == 4      ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
+        : tw == 2      ? (size_t)2 * Tiles<D, wide_step_kb<2>()>::BUF
+                       : (size_t)Tiles<D, kPrefixStepKB>::BUF;
     long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
     if (a.tile_qt > 0) {  // query tiles: (8-aligned units) x tile groups
         const long nq = (long)(a.shared_kv ? a.batch : 1) * (a.heads_q / a.heads_kv);
         const long tiles = (nq + 15) / 16;
-        const long groups = (tiles + a.tile_qt - 1) / a.tile_qt;
+        const long groups = (tiles + (long)a.tile_qt * tw - 1) / ((long)a.tile_qt * tw);
         const long units = (long)(a.shared_kv ? 1 : a.batch) * a.heads_kv * a.num_splits;
         grid = (units + 7) / 8 * 8 * groups;
         if (grid > 0x7fffffffL)
@@ -762,21 +825,37 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
-    const int per_cu = a.tile_qt > 0 ? kPrefixWgPerCU : kMfmaWgPerCU;
+    const int per_cu = a.tile_qt == 0 ? kMfmaWgPerCU
+                       : tw == 1      ? kPrefixWgPerCU
+                                      : (kPrefixWgPerCU * FD_WIDE_WPE / tw > 1
+                                             ? kPrefixWgPerCU * FD_WIDE_WPE / tw
+                                             : 1);
     if (per_cu > 0 && lds > 0) {
         const size_t want = (size_t)lds / (per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
     }
     const dim3 g((unsigned)grid), blk(64);
-    if (a.tile_qt > 0) {
+    if (a.tile_qt > 0 && tw > 1) {
+        // several waves per work-group, each with the most tiles it holds
+        constexpr int Q = tile_max_qt<D>();
+        if (a.tile_qt != Q || tw > tile_max_waves<D>())
+            return hipErrorInvalidValue;
+        if (tw == 2)
+            launch_tiled<DT, D, Q, 2>(a, g, pad, stream);
+        else if (tw == 4) {
+            if constexpr (tile_max_waves<D>() >= 4)
+                launch_tiled<DT, D, Q, 4>(a, g, pad, stream);
+        } else
+            return hipErrorInvalidValue;
+    } else if (a.tile_qt > 0) {
         if (a.tile_qt == 1) {
-            launch_tiled<DT, D, 1>(a, g, blk, pad, stream);
+            launch_tiled<DT, D, 1>(a, g, pad, stream);
         } else if (a.tile_qt == 2 && tile_max_qt<D>() >= 2) {
             if constexpr (tile_max_qt<D>() >= 2)
-                launch_tiled<DT, D, 2>(a, g, blk, pad, stream);
+                launch_tiled<DT, D, 2>(a, g, pad, stream);
         } else if (a.tile_qt == 4 && tile_max_qt<D>() >= 4) {
             if constexpr (tile_max_qt<D>() >= 4)
-                launch_tiled<DT, D, 4>(a, g, blk, pad, stream);
+                launch_tiled<DT, D, 4>(a, g, pad, stream);
         } else {
             return hipErrorInvalidValue;
         }
@@ -817,6 +896,22 @@ int split_mfma_tile_max_qt(int head_dim) {
     case 128: return tile_max_qt<128>();
     case 256: return tile_max_qt<256>();
     default: return 0;
+    }
+}
+
+int split_mfma_tiled_wg_per_cu(int waves) {
+    if (waves <= 1)
+        return kPrefixWgPerCU;
+    const int n = kPrefixWgPerCU * FD_WIDE_WPE / waves;
+    return n > 1 ? n : 1;
+}
+
+int split_mfma_tile_max_waves(int head_dim) {
+    switch (head_dim) {
+    case 64: return tile_max_waves<64>();
+    case 128: return tile_max_waves<128>();
+    case 256: return tile_max_waves<256>();
+    default: return 1;
     }
 }
 
