@@ -263,6 +263,7 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
 // applies.  Workspace: o slots, LSE slots, unit descriptors, each 256-aligned.
 struct BalancedPlan {
     int num_wgs = 0, units = 0, gsz = 0;
+    int waves = 1;  // per work-group (fd::split_mfma_balanced_waves)
     size_t o_bytes = 0, lse_bytes = 0, desc_bytes = 0;
     size_t total() const { return o_bytes + lse_bytes + desc_bytes; }
 };
@@ -278,9 +279,12 @@ bool balanced_applies(int heads_q, int heads_kv, int max_kv_len, int head_dim, i
 
 int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim, int cus,
                   BalancedPlan *p) {
-    p->num_wgs = cus * fd::kMfmaWgPerCU * kBalancedRounds;
     p->units = batch * heads_kv;
     p->gsz = heads_q / heads_kv;
+    p->waves = fd::split_mfma_balanced_waves(head_dim, p->gsz);
+    if (p->waves < 1)
+        return fail(FD_ERR_INVALID, "group of %d too large for the balanced plan", p->gsz);
+    p->num_wgs = cus * fd::split_mfma_balanced_wg_per_cu(p->waves) * kBalancedRounds;
     // positions (units * max_kv_len) times work-groups must stay within int64
     if ((double)p->units * max_kv_len * p->num_wgs > 4.0e18)
         return fail(FD_ERR_INVALID, "batch * heads_kv * max_kv_len too large for the balanced plan");
@@ -349,7 +353,7 @@ int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim
         r.route = FD_ROUTE_BALANCED;
         r.kernel = FD_KERNEL_BALANCED;
         r.work_groups = p->bal.num_wgs;
-        r.waves_per_group = 1;
+        r.waves_per_group = p->bal.waves;
         r.query_tiles = (group + 15) / 16;
         r.launches = 2;
         r.workspace_bytes = p->bal.total();
@@ -764,6 +768,7 @@ int fd_decode_cascade(const void *q, const void *k_prefix, const void *v_prefix,
         sa.lse_part = reinterpret_cast<float *>(bws + p.bal.o_bytes);
         sa.balanced = 1;
         sa.num_wgs = p.bal.num_wgs;
+        sa.tile_waves = p.bal.waves;
         sa.unit_desc = reinterpret_cast<int *>(bws + p.bal.o_bytes + p.bal.lse_bytes);
         rc = launch_split(sa, in_dtype, st);
         if (rc != FD_OK)
@@ -920,6 +925,7 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
         a.lse_part = reinterpret_cast<float *>(ws + p.bal.o_bytes);
         a.balanced = 1;
         a.num_wgs = p.bal.num_wgs;
+        a.tile_waves = p.bal.waves;
         a.unit_desc = reinterpret_cast<int *>(ws + p.bal.o_bytes + p.bal.lse_bytes);
         rc = launch_split(a, in_dtype, st);
         if (rc != FD_OK)

@@ -81,9 +81,10 @@ struct SplitArgs {
     // the KV head; otherwise the G queries of one sequence (groups larger
     // than one tile).  0 selects the one-tile kernels.
     int tile_qt;
-    // Tiled kernel: waves per work-group (1, 2 or 4; 0 means 1).  The waves
-    // take tile_qt tiles each and share every K/V step staged in LDS, so a
-    // work-group serves tile_qt * tile_waves tiles from one read of the rows.
+    // Tiled and token-balanced kernels: waves per work-group (1, 2 or 4; 0
+    // means 1).  The waves take their own query tiles and share every K/V
+    // step staged in LDS, so a work-group serves all of its tiles from one
+    // read of the rows.
     int tile_waves;
     // Fixed-split partial slots: split i of row r is slot r * part_stride +
     // part_offset + i (part_stride 0 means num_splits), so two launches can
@@ -121,8 +122,11 @@ int split_mfma_tile_max_waves(int head_dim);
 // Resident tiled work-groups per CU with this many waves each.
 int split_mfma_tiled_wg_per_cu(int waves);
 // Largest group the token-balanced kernel takes (all of a unit's query tiles
-// in one work-group).
+// in one work-group), the waves of its work-groups for a group size (0: too
+// large), and its resident work-groups per CU with that many waves.
 int split_mfma_balanced_max_group(int head_dim);
+int split_mfma_balanced_waves(int head_dim, int group);
+int split_mfma_balanced_wg_per_cu(int waves);
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.

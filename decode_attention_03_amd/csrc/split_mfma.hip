@@ -160,16 +160,17 @@ typedef __attribute__((address_space(3))) char lds_char;
 #define FD_PREFIX_QT128 2
 #endif
 constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the tiled kernel
-// Tiled work-groups of several waves: K/V bytes per step (shared by the
-// waves), non-temporal loads or not, and waves per SIMD aimed at.
+// Work-groups of several waves (tiled and token-balanced kernels): K/V bytes
+// per step, shared by the waves (0: 8 KB per wave); non-temporal loads or not
+// (measured: ordinary loads 4-6 % faster on both kernels).
 #ifndef FD_WIDE_STEP_KB
 #define FD_WIDE_STEP_KB 0
 #endif
 #ifndef FD_WIDE_NT
 #define FD_WIDE_NT 0
 #endif
-#ifndef FD_WIDE_WPE
-#define FD_WIDE_WPE 1
+#ifndef FD_BAL_WIDE_NT
+#define FD_BAL_WIDE_NT 0
 #endif
 // 0: 8 KB per wave (16 KB for two waves, 32 KB for four)
 template <int W>
@@ -647,8 +648,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 // shared prefix).  The K/V loads are ordinary (temporal) loads, as other
 // work-groups may read the same rows.
 template <int DT, int D, int QT, bool PAGED, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 1 ? FD_WIDE_WPE : 1)))
-void split_mfma_tiled_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64 * W) void split_mfma_tiled_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int SKB = W > 1 ? wide_step_kb<W>() : kPrefixStepKB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
@@ -688,11 +688,15 @@ void split_mfma_tiled_kernel(SplitArgs a) {
 // Token-balanced partition (partition.h): work-group w walks its share of the
 // flattened (sequence, KV head, token) space piece by piece; the piece of unit
 // u goes to slot w + rank(u) of the slot arrays (o [slot][G][d], LSE [slot][G]).
-// The G query heads of a unit take QT = ceil(G / 16) tiles.
-template <int DT, int D, bool PAGED, int QT>
-__global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
+// The G query heads of a unit take ceil(G / 16) tiles: QT per wave, W waves
+// per work-group (W > 1: the waves share each K/V step staged in LDS, as in
+// the tiled kernel).
+template <int DT, int D, bool PAGED, int QT, int W = 1>
+__global__ __launch_bounds__(64 * W) void split_mfma_balanced_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __shared__ __attribute__((aligned(1024))) char tile_buf[Tiles<D>::BUF];
+    constexpr int SKB = W > 1 ? wide_step_kb<W>() : FD_MFMA_STEP_KB;
+    __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
+    const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int w = blockIdx.x;
     const int G = a.heads_q / a.heads_kv;
     PieceCursor c;
@@ -710,12 +714,13 @@ __global__ __launch_bounds__(64) void split_mfma_balanced_kernel(SplitArgs a) {
         const int hi = c.t + avail - kPieceCost < ng ? c.t + avail - kPieceCost : ng;
         if (hi > lo) {
             const int slot = w + c.rank;
-            const QMap qm{c.b * a.heads_q + c.x * G, G, 0, 0, a.heads_q, c.x};
+            const QMap qm{c.b * a.heads_q + c.x * G, G, 0, wv * QT, a.heads_q, c.x};
             const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G,
                                nullptr, 1, 0, true};
             const long t0 = (long)lo * kGranule;
             const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
-            mfma_piece<DT, D, PAGED, QT>(a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
+            mfma_piece<DT, D, PAGED, QT, (W > 1 ? FD_BAL_WIDE_NT : 1), SKB, W>(
+                a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
             if (lo == 0 && threadIdx.x == 0) {
                 const long long ustart = c.pos - c.t;  // the unit's first position
                 const int first = balanced_owner(ustart + kPieceCost, c.total, c.w_eff);
@@ -772,6 +777,13 @@ constexpr int tile_max_qt() {
     return D == 64 ? 4 : (D == 128 ? FD_PREFIX_QT128 : 1);
 }
 
+// Query tiles per wave of the token-balanced kernel: at most two (four, at
+// d = 64, measured slower than the tiled kernel's fixed splits).
+template <int D>
+constexpr int balanced_qt() {
+    return tile_max_qt<D>() < 2 ? tile_max_qt<D>() : 2;
+}
+
 // Waves of a tiled work-group: each loads an equal share of the row groups
 // of every staged tile (2 at d = 64, 4 at d = 128 and 256), capped by
 // FD_TILE_MAX_WAVES.
@@ -796,12 +808,15 @@ void launch_tiled(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
 }
 
 // The token-balanced kernel for QT query tiles per unit, paged or contiguous.
-template <int DT, int D, int QT>
-void launch_balanced(const SplitArgs &a, dim3 g, dim3 blk, size_t pad, hipStream_t stream) {
+template <int DT, int D, int QT, int W = 1>
+void launch_balanced(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
+    const dim3 blk(64 * W);
     if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, true, QT>), g, blk, pad, stream, a);
+        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, true, QT, W>), g, blk, pad, stream,
+                           a);
     else
-        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, false, QT>), g, blk, pad, stream, a);
+        hipLaunchKernelGGL((split_mfma_balanced_kernel<DT, D, false, QT, W>), g, blk, pad, stream,
+                           a);
 }
 
 template <int DT, int D>
@@ -809,10 +824,10 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     const int tw = a.tile_waves > 1 ? a.tile_waves : 1;
     const size_t kStatic =
-        a.tile_qt == 0 ? (size_t)T::BUF
-        : tw == 4      ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
-        : tw == 2      ? (size_t)2 * Tiles<D, wide_step_kb<2>()>::BUF
-                       : (size_t)Tiles<D, kPrefixStepKB>::BUF;
+        tw == 4                        ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
+        : tw == 2                      ? (size_t)2 * Tiles<D, wide_step_kb<2>()>::BUF
+        : a.tile_qt > 0 && !a.balanced ? (size_t)Tiles<D, kPrefixStepKB>::BUF
+                                       : (size_t)T::BUF;
     long grid = a.balanced ? (long)a.num_wgs : (long)a.batch * a.heads_kv * a.num_splits;
     if (a.tile_qt > 0) {  // query tiles: (8-aligned units) x tile groups
         const long nq = (long)(a.shared_kv ? a.batch : 1) * (a.heads_q / a.heads_kv);
@@ -825,11 +840,9 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
-    const int per_cu = a.tile_qt == 0 ? kMfmaWgPerCU
-                       : tw == 1      ? kPrefixWgPerCU
-                                      : (kPrefixWgPerCU * FD_WIDE_WPE / tw > 1
-                                             ? kPrefixWgPerCU * FD_WIDE_WPE / tw
-                                             : 1);
+    const int per_cu = a.balanced ? split_mfma_balanced_wg_per_cu(tw)
+                       : a.tile_qt == 0 ? kMfmaWgPerCU
+                                        : split_mfma_tiled_wg_per_cu(tw);
     if (per_cu > 0 && lds > 0) {
         const size_t want = (size_t)lds / (per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
@@ -860,12 +873,25 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
             return hipErrorInvalidValue;
         }
     } else if (a.balanced) {
-        const int qt = (a.heads_q / a.heads_kv + 15) / 16;
-        if (qt == 1) {
-            launch_balanced<DT, D, 1>(a, g, blk, pad, stream);
-        } else if (qt == 2 && tile_max_qt<D>() >= 2) {
-            if constexpr (tile_max_qt<D>() >= 2)
-                launch_balanced<DT, D, 2>(a, g, blk, pad, stream);
+        // QT = ceil(G / 16) tiles on one wave (up to two), or two (one at
+        // d = 256) per wave on tw waves
+        const int tiles = (a.heads_q / a.heads_kv + 15) / 16;
+        constexpr int QB = balanced_qt<D>();
+        if (tw > 1) {
+            if (tiles > QB * tw || tw > tile_max_waves<D>())
+                return hipErrorInvalidValue;
+            if (tw == 2)
+                launch_balanced<DT, D, QB, 2>(a, g, pad, stream);
+            else if (tw == 4) {
+                if constexpr (tile_max_waves<D>() >= 4)
+                    launch_balanced<DT, D, QB, 4>(a, g, pad, stream);
+            } else
+                return hipErrorInvalidValue;
+        } else if (tiles == 1) {
+            launch_balanced<DT, D, 1>(a, g, pad, stream);
+        } else if (tiles == 2 && QB >= 2) {
+            if constexpr (QB >= 2)
+                launch_balanced<DT, D, 2>(a, g, pad, stream);
         } else {
             return hipErrorInvalidValue;
         }
@@ -902,7 +928,7 @@ int split_mfma_tile_max_qt(int head_dim) {
 int split_mfma_tiled_wg_per_cu(int waves) {
     if (waves <= 1)
         return kPrefixWgPerCU;
-    const int n = kPrefixWgPerCU * FD_WIDE_WPE / waves;
+    const int n = kPrefixWgPerCU / waves;  // one wave per SIMD
     return n > 1 ? n : 1;
 }
 
@@ -915,13 +941,40 @@ int split_mfma_tile_max_waves(int head_dim) {
     }
 }
 
-// Up to two tiles: with four (64 heads at d = 64, multi-query) the pieces are
-// bound by their arithmetic, and the tiled kernel's fixed splits at four
-// work-groups per CU measured 5 % faster on a ragged batch than the balanced
-// plan's two.
+int split_mfma_balanced_wg_per_cu(int waves) {
+    if (waves <= 1)
+        return kMfmaWgPerCU;
+    const int n = kPrefixWgPerCU / waves;  // one wave per SIMD
+    return n > 1 ? n : 1;
+}
+
+// Up to two tiles per wave (with four, 64 heads at d = 64, one wave's pieces
+// were bound by their arithmetic: the tiled kernel's fixed splits measured
+// 5 % faster on a ragged batch), on up to the most waves the head size allows.
 int split_mfma_balanced_max_group(int head_dim) {
-    const int qt = split_mfma_tile_max_qt(head_dim);
-    return 16 * (qt < 2 ? qt : 2);
+    switch (head_dim) {
+    case 64: return 16 * balanced_qt<64>() * tile_max_waves<64>();
+    case 128: return 16 * balanced_qt<128>() * tile_max_waves<128>();
+    case 256: return 16 * balanced_qt<256>() * tile_max_waves<256>();
+    default: return 0;
+    }
+}
+
+int split_mfma_balanced_waves(int head_dim, int group) {
+    const int tiles = (group + 15) / 16;
+    int qt = 0, wmax = 1;
+    switch (head_dim) {
+    case 64: qt = balanced_qt<64>(); wmax = tile_max_waves<64>(); break;
+    case 128: qt = balanced_qt<128>(); wmax = tile_max_waves<128>(); break;
+    case 256: qt = balanced_qt<256>(); wmax = tile_max_waves<256>(); break;
+    default: return 0;
+    }
+    if (tiles <= qt)
+        return 1;
+    int w = 2;
+    while (w < wmax && qt * w < tiles)
+        w *= 2;
+    return qt * w >= tiles ? w : 0;
 }
 
 bool split_mfma_tiled_supported(int in_dtype, int head_dim) {

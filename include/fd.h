@@ -195,10 +195,12 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
 /* Whole decode step: split + combine.
  *   num_splits == 0 (automatic plan, split_len ignored):
  *     - kv_lens given and grouped heads on the matrix cores (bf16/f16,
- *       2 <= heads_q/heads_kv <= 32, 32, 16 at head_dim 64, 128, 256): a
+ *       2 <= heads_q/heads_kv <= 64, 128, 64 at head_dim 64, 128, 256): a
  *       token-balanced partition.  The
  *       (sequence, KV head, token) space of the actual lengths is cut into
- *       equal shares, one per work-group (CUs x 2), so every work-group
+ *       equal shares, one per work-group (CUs x 2 for up to 32 query heads
+ *       per KV head, fewer for larger groups, whose work-groups have several
+ *       waves), so every work-group
  *       streams the same number of K/V rows whatever the length mix; a share
  *       may end inside one (sequence, head) row and continue in the next, and
  *       each such piece yields one (o, LSE) pair that the combine merges with

@@ -139,10 +139,17 @@ def test_decode_plan_struct_layout():
     ((4, 64, 1, 8192, 64, fd.F16, 0, 0, 0), dict(kernel=2, query_tiles=4)),
     # 128 per KV head at d = 128: four waves of two tiles share each staged step
     ((4, 128, 1, 8192, 128, fd.BF16, 0, 0, 0), dict(kernel=2, query_tiles=8, waves_per_group=4)),
-    # 32 per KV head, ragged: balanced over two tiles; 40: past the balanced plan
-    ((16, 64, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=2)),
-    ((16, 80, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=2, kernel=2, query_tiles=4,
-                                                     waves_per_group=2)),
+    # ragged: 32 per KV head balanced on one wave of two tiles, 40 on two waves
+    # (two work-groups per CU), 128 on four (one per CU); 136: past the
+    # balanced plan, tiled work-groups of four waves (two per unit)
+    ((16, 64, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=2,
+                                                     waves_per_group=1, work_groups=512)),
+    ((16, 80, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=3,
+                                                     waves_per_group=2, work_groups=512)),
+    ((16, 256, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=8,
+                                                      waves_per_group=4, work_groups=256)),
+    ((16, 272, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=2, kernel=2, query_tiles=8,
+                                                      waves_per_group=4)),
     # explicit splits: one split writes o itself; fp32 grouped heads stay on the vector kernel
     ((2, 8, 2, 1000, 128, fd.BF16, 1, 1, 0), dict(route=0, kernel=1, num_splits=1,
                                                   split_len=1000, launches=1, workspace_bytes=0)),

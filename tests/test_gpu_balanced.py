@@ -5,8 +5,9 @@ The partition cuts the flattened (sequence, KV head, token) space into equal
 shares; these cases aim at its corners: empty sequences between full ones,
 every sequence empty, fewer positions than work-groups, more than 64
 sequences (the in-kernel prefix scan runs over several 64-lane chunks), one
-sequence spread over hundreds of pieces, clamped lengths, and groups of 17 to
-32 query heads per KV head (two query tiles per piece).  K/V rows past each
+sequence spread over hundreds of pieces, clamped lengths, groups of 17 to
+32 query heads per KV head (two query tiles per piece), and larger groups on
+work-groups of two or four waves.  K/V rows past each
 length are NaN and the workspace starts NaN-filled, so a read past a length or
 of an unwritten slot shows up as a wrong or non-finite result.
 """
@@ -35,6 +36,13 @@ CASES = [
     ("group32_d64_mqa", 9, 1, 32, 64, "f16", 3000, [3000, 2, 0, 1777, 3000, 64, 500, 0, 2999]),
     ("group24_d64", 5, 2, 24, 64, "bf16", 2000, [1999, 0, 300, 2000, 33]),
     ("group17_d128", 4, 3, 17, 128, "f16", 2500, [2500, 1, 1024, 0]),
+    # more tiles than one wave holds: two or four waves per work-group share
+    # each staged K/V step (the last wave's last tile partial or empty)
+    ("group48_d64_2waves", 5, 2, 48, 64, "f16", 2200, [2200, 0, 15, 1999, 640]),
+    ("group64_d128_2waves", 4, 2, 64, 128, "bf16", 3000, [3000, 1, 0, 2047]),
+    ("group128_d128_4waves", 6, 1, 128, 128, "bf16", 2500, [2500, 17, 0, 1300, 2499, 64]),
+    ("group40_d256_4waves", 3, 2, 40, 256, "f16", 1800, [1800, 900, 0]),
+    ("group24_d256_2waves", 5, 1, 24, 256, "bf16", 1500, [0, 1500, 3, 777, 1499]),
 ]
 
 
@@ -76,6 +84,10 @@ def test_balanced_partition_cases(gpu, case):
     kl = inp["kv_lens"].to(gpu)
     need = fd.decode_workspace_bytes(batch, hkv * group, hkv, n_max, d, q.dtype, True)
     assert need > 0
+    plan = fd.decode_plan(batch, hkv * group, hkv, n_max, d, q.dtype, True)
+    assert plan["route"] == "balanced" and plan["workspace_bytes"] == need
+    if name.endswith("waves"):
+        assert plan["waves_per_group"] == int(name[-6]), plan
     ws = torch.full((need // 4 + 1,), float("nan"), device=gpu)
     o, lse = fd.decode(q, k, v, kl, scale=w.scale, workspace=ws)
     torch.cuda.synchronize()
