@@ -482,6 +482,43 @@ def time_shard(steps: int, warmup: int, dev: torch.device) -> dict:
     return out
 
 
+# Group sizes past one 16-query tile, up to multi-query attention (bf16/fp16
+# on the matrix cores): the tiled kernel's fixed splits without lengths, the
+# token-balanced plan with ragged lengths.
+GROUPS = [
+    workloads.Workload("mqa_bf16_b32_hq64_hkv1_d128_n8192", batch=32, heads_q=64, heads_kv=1,
+                       head_dim=128, max_kv_len=8192, dtype="bf16", out_dtype="bf16", seed=8),
+    workloads.Workload("gqa32_bf16_b16_hq64_hkv2_d128_n16384", batch=16, heads_q=64, heads_kv=2,
+                       head_dim=128, max_kv_len=16384, dtype="bf16", out_dtype="bf16", seed=9),
+    workloads.Workload("mqa_bf16_b32_hq128_hkv1_d128_ragged512_16384", batch=32, heads_q=128,
+                       heads_kv=1, head_dim=128, max_kv_len=16384, dtype="bf16", out_dtype="bf16",
+                       seed=10, ragged=(512, 16384)),
+    workloads.Workload("gqa32_bf16_b16_hq64_hkv2_d128_ragged512_32768", batch=16, heads_q=64,
+                       heads_kv=2, head_dim=128, max_kv_len=32768, dtype="bf16", out_dtype="bf16",
+                       seed=11, ragged=(512, 32768)),
+    workloads.Workload("mqa_f16_b32_hq64_hkv1_d64_ragged512_16384", batch=32, heads_q=64,
+                       heads_kv=1, head_dim=64, max_kv_len=16384, dtype="f16", out_dtype="f16",
+                       seed=12, ragged=(512, 16384)),
+]
+
+
+def time_groups(steps: int, warmup: int, dev: torch.device) -> dict:
+    """Decode steps of the large-group workloads, with the plan each takes."""
+    out = {}
+    for w in GROUPS:
+        p = Prepared(w, dev)
+        t = time_steps(p, steps, warmup)
+        su = time_split_kernel(p, steps, warmup)
+        r = summarize(p, t, su)
+        r["waves_per_group"] = p.dplan["waves_per_group"]
+        r["query_tiles_per_group"] = p.dplan["query_tiles"]
+        out[w.name] = r
+        p.free()
+        del p
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     """The fp64 oracle on the host cores, on whole decode steps of the same
     workload, repeated until about budget_s seconds of wall time."""
@@ -597,7 +634,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="oracle seconds (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
-    ap.add_argument("--section", choices=("cascade", "paged", "shard"), default=None,
+    ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups"), default=None,
                     help="time only this section of the full run and print its JSON (profiling)")
     args = ap.parse_args()
 
@@ -628,6 +665,8 @@ def main() -> int:
             sec = time_cascade(args.steps, args.warmup, dev, materialised=False)
         elif args.section == "shard":
             sec = time_shard(args.steps, args.warmup, dev)
+        elif args.section == "groups":
+            sec = time_groups(args.steps, args.warmup, dev)
         else:  # the paged step of the ragged grouped workload, 16-token pages
             w = workloads.WORKLOADS[4]
             sec = {"workload": w.name, **time_paged(w, dev, 16, args.steps, args.warmup)}
@@ -737,6 +776,10 @@ def main() -> int:
         shard = time_shard(args.steps, args.warmup, dev)
         log(f"[bench] shard: {shard}")
         result["shard"] = shard
+        # groups past one matrix-core tile, up to multi-query attention
+        groups = time_groups(args.steps, args.warmup, dev)
+        log(f"[bench] groups: {groups}")
+        result["groups"] = groups
         for c in late:
             run_workload(c)
     print(json.dumps(result), flush=True)
