@@ -45,7 +45,8 @@ def _check(name, o, lse, ro, rl, dtype):
 
 
 @pytest.mark.parametrize("dtype,group,d", [("bf16", 8, 128), ("bf16", 1, 128), ("f32", 1, 64),
-                                           ("f16", 4, 256), ("f16", 2, 64), ("bf16", 32, 128)])
+                                           ("f16", 4, 256), ("f16", 2, 64), ("bf16", 32, 128),
+                                           ("bf16", 64, 128), ("f16", 40, 256)])
 @pytest.mark.parametrize("prefix_len", [0, 1, 777, 5000])
 def test_cascade_matches_concatenated_attention(gpu, dtype, group, d, prefix_len):
     w = workloads.Workload("cascade_test", batch=5, heads_q=2 * group, heads_kv=2, head_dim=d,
