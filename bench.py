@@ -505,6 +505,7 @@ GROUPS = [
 def time_groups(steps: int, warmup: int, dev: torch.device) -> dict:
     """Decode steps of the large-group workloads, with the plan each takes."""
     out = {}
+    res = {"workload": "query_groups_32_to_128", "cases": out}
     for w in GROUPS:
         p = Prepared(w, dev)
         t = time_steps(p, steps, warmup)
@@ -516,7 +517,7 @@ def time_groups(steps: int, warmup: int, dev: torch.device) -> dict:
         p.free()
         del p
         torch.cuda.empty_cache()
-    return out
+    return res
 
 
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:

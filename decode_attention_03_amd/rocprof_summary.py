@@ -131,7 +131,7 @@ def main() -> int:
     ap.add_argument("--pmc-steps", type=int, default=3)
     ap.add_argument("--skip-copy", action="store_true",
                     help="reuse the copy calibration already in RAW")
-    ap.add_argument("--section", choices=("cascade", "paged", "shard"), default=None,
+    ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups"), default=None,
                     help="profile one section of bench.py instead of a named workload")
     args = ap.parse_args()
     if args.section:
@@ -338,7 +338,8 @@ def section_main(args) -> int:
     """Kernel trace and HBM bytes per dispatch of every kernel that one bench.py
     section launches (cascade: the shared-prefix kernel, the suffix kernel and
     the combine; paged: the ragged grouped workload over 16-token pages;
-    shard: one GPU's share of the long-context workload and the merge)."""
+    shard: one GPU's share of the long-context workload and the merge;
+    groups: five shapes with 32 to 128 query heads per KV head)."""
     raw = os.path.abspath(args.raw)
     out = os.path.abspath(args.out)
     os.makedirs(raw, exist_ok=True)
