@@ -169,6 +169,9 @@ constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the t
 #ifndef FD_WIDE_NT
 #define FD_WIDE_NT 0
 #endif
+#ifndef FD_MFMA_NT
+#define FD_MFMA_NT 1  // one-wave grouped kernels: non-temporal K/V loads
+#endif
 #ifndef FD_BAL_WIDE_NT
 #define FD_BAL_WIDE_NT 0
 #endif
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
         out.lse = a.m_part ? a.m_part : a.lse_part;
         out.l = a.m_part ? a.l_part : nullptr;
     }
-    mfma_piece<DT, D, PAGED, 1>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
+    mfma_piece<DT, D, PAGED, 1, FD_MFMA_NT>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -719,7 +722,7 @@ __global__ __launch_bounds__(64 * W) void split_mfma_balanced_kernel(SplitArgs a
                                nullptr, 1, 0, true};
             const long t0 = (long)lo * kGranule;
             const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
-            mfma_piece<DT, D, PAGED, QT, (W > 1 ? FD_BAL_WIDE_NT : 1), SKB, W>(
+            mfma_piece<DT, D, PAGED, QT, (W > 1 ? FD_BAL_WIDE_NT : FD_MFMA_NT), SKB, W>(
                 a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
             if (lo == 0 && threadIdx.x == 0) {
                 const long long ustart = c.pos - c.t;  // the unit's first position
