@@ -183,10 +183,16 @@ struct TiledShape {
 TiledShape tiled_shape(int head_dim, long long nq) {
     TiledShape t;
     const long long tiles = (nq + 15) / 16;
+    const int wmax = fd::split_mfma_tile_max_waves(head_dim);
+    if (fd::split_mfma_tile_spread() && tiles > 1 && tiles <= wmax) {
+        t.qt = 1;  // one tile on each of the waves
+        while (t.waves < tiles)
+            t.waves *= 2;
+        return t;
+    }
     t.qt = fd::split_mfma_tile_max_qt(head_dim);
     while (t.qt > 1 && t.qt / 2 >= tiles)
         t.qt /= 2;
-    const int wmax = fd::split_mfma_tile_max_waves(head_dim);
     while (t.waves < wmax && (long long)t.qt * t.waves < tiles)
         t.waves *= 2;
     t.groups = (tiles + (long long)t.qt * t.waves - 1) / ((long long)t.qt * t.waves);

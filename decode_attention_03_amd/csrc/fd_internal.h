@@ -119,6 +119,9 @@ int split_mfma_tile_max_qt(int head_dim);  // query tiles per wave, 1..4
 // Most waves a tiled work-group can have at this head size (each loads an
 // equal share of every staged row group): 2 at d = 64, 4 at d = 128 and 256.
 int split_mfma_tile_max_waves(int head_dim);
+// Whether the tiled kernel spreads a group's tiles one per wave while the
+// waves cover it (else each wave takes as many tiles as it holds).
+bool split_mfma_tile_spread();
 // Resident tiled work-groups per CU with this many waves each.
 int split_mfma_tiled_wg_per_cu(int waves);
 // Largest group the token-balanced kernel takes (all of a unit's query tiles

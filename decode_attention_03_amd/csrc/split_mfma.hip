@@ -169,6 +169,12 @@ constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the t
 #ifndef FD_WIDE_NT
 #define FD_WIDE_NT 0
 #endif
+#ifndef FD_BAL_SPREAD
+#define FD_BAL_SPREAD 1  // balanced plan: one query tile per wave while the waves cover the group
+#endif
+#ifndef FD_TILE_SPREAD
+#define FD_TILE_SPREAD 1  // tiled kernel: one query tile per wave while the waves cover the group
+#endif
 #ifndef FD_MFMA_NT
 #define FD_MFMA_NT 1  // one-wave grouped kernels: non-temporal K/V loads
 #endif
@@ -852,15 +858,23 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     const dim3 g((unsigned)grid), blk(64);
     if (a.tile_qt > 0 && tw > 1) {
-        // several waves per work-group, each with the most tiles it holds
+        // several waves per work-group, each with one tile or the most it holds
         constexpr int Q = tile_max_qt<D>();
-        if (a.tile_qt != Q || tw > tile_max_waves<D>())
+        if ((a.tile_qt != Q && a.tile_qt != 1) || tw > tile_max_waves<D>())
             return hipErrorInvalidValue;
-        if (tw == 2)
-            launch_tiled<DT, D, Q, 2>(a, g, pad, stream);
-        else if (tw == 4) {
-            if constexpr (tile_max_waves<D>() >= 4)
-                launch_tiled<DT, D, Q, 4>(a, g, pad, stream);
+        const bool one = a.tile_qt == 1;
+        if (tw == 2) {
+            if (one)
+                launch_tiled<DT, D, 1, 2>(a, g, pad, stream);
+            else
+                launch_tiled<DT, D, Q, 2>(a, g, pad, stream);
+        } else if (tw == 4) {
+            if constexpr (tile_max_waves<D>() >= 4) {
+                if (one)
+                    launch_tiled<DT, D, 1, 4>(a, g, pad, stream);
+                else
+                    launch_tiled<DT, D, Q, 4>(a, g, pad, stream);
+            }
         } else
             return hipErrorInvalidValue;
     } else if (a.tile_qt > 0) {
@@ -881,13 +895,22 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         const int tiles = (a.heads_q / a.heads_kv + 15) / 16;
         constexpr int QB = balanced_qt<D>();
         if (tw > 1) {
+            // one tile per wave when the waves cover the group, else QB
             if (tiles > QB * tw || tw > tile_max_waves<D>())
                 return hipErrorInvalidValue;
-            if (tw == 2)
-                launch_balanced<DT, D, QB, 2>(a, g, pad, stream);
-            else if (tw == 4) {
-                if constexpr (tile_max_waves<D>() >= 4)
-                    launch_balanced<DT, D, QB, 4>(a, g, pad, stream);
+            const bool one = tiles <= tw;
+            if (tw == 2) {
+                if (one)
+                    launch_balanced<DT, D, 1, 2>(a, g, pad, stream);
+                else
+                    launch_balanced<DT, D, QB, 2>(a, g, pad, stream);
+            } else if (tw == 4) {
+                if constexpr (tile_max_waves<D>() >= 4) {
+                    if (one)
+                        launch_balanced<DT, D, 1, 4>(a, g, pad, stream);
+                    else
+                        launch_balanced<DT, D, QB, 4>(a, g, pad, stream);
+                }
             } else
                 return hipErrorInvalidValue;
         } else if (tiles == 1) {
@@ -935,6 +958,8 @@ int split_mfma_tiled_wg_per_cu(int waves) {
     return n > 1 ? n : 1;
 }
 
+bool split_mfma_tile_spread() { return FD_TILE_SPREAD != 0; }
+
 int split_mfma_tile_max_waves(int head_dim) {
     switch (head_dim) {
     case 64: return tile_max_waves<64>();
@@ -972,9 +997,16 @@ int split_mfma_balanced_waves(int head_dim, int group) {
     case 256: qt = balanced_qt<256>(); wmax = tile_max_waves<256>(); break;
     default: return 0;
     }
-    if (tiles <= qt)
+    if (tiles <= 1)
         return 1;
     int w = 2;
+    if (FD_BAL_SPREAD && tiles <= wmax) {  // one tile on each of w waves
+        while (w < tiles)
+            w *= 2;
+        return w;
+    }
+    if (tiles <= qt)
+        return 1;
     while (w < wmax && qt * w < tiles)
         w *= 2;
     return qt * w >= tiles ? w : 0;

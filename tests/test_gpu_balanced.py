@@ -32,14 +32,14 @@ CASES = [
     ("clamped", 4, 4, 8, 128, "bf16", 300, [0, 300, 5000, -3]),
     ("group2_d256", 6, 3, 2, 256, "bf16", 3000, [2999, 1, 1500, 0, 3000, 64]),
     # groups past one 16-query tile: every tile of a unit in the one work-group
-    ("group32_d128", 6, 2, 32, 128, "bf16", 6000, [6000, 0, 17, 4099, 1, 2500]),
+    ("group32_d128_2waves", 6, 2, 32, 128, "bf16", 6000, [6000, 0, 17, 4099, 1, 2500]),
     ("group32_d64_mqa", 9, 1, 32, 64, "f16", 3000, [3000, 2, 0, 1777, 3000, 64, 500, 0, 2999]),
     ("group24_d64", 5, 2, 24, 64, "bf16", 2000, [1999, 0, 300, 2000, 33]),
     ("group17_d128", 4, 3, 17, 128, "f16", 2500, [2500, 1, 1024, 0]),
     # more tiles than one wave holds: two or four waves per work-group share
     # each staged K/V step (the last wave's last tile partial or empty)
     ("group48_d64_2waves", 5, 2, 48, 64, "f16", 2200, [2200, 0, 15, 1999, 640]),
-    ("group64_d128_2waves", 4, 2, 64, 128, "bf16", 3000, [3000, 1, 0, 2047]),
+    ("group64_d128_4waves", 4, 2, 64, 128, "bf16", 3000, [3000, 1, 0, 2047]),
     ("group128_d128_4waves", 6, 1, 128, 128, "bf16", 2500, [2500, 17, 0, 1300, 2499, 64]),
     ("group40_d256_4waves", 3, 2, 40, 256, "f16", 1800, [1800, 900, 0]),
     ("group24_d256_2waves", 5, 1, 24, 256, "bf16", 1500, [0, 1500, 3, 777, 1499]),
