@@ -161,13 +161,15 @@ typedef __attribute__((address_space(3))) char lds_char;
 #endif
 constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the tiled kernel
 // Work-groups of several waves (tiled and token-balanced kernels): K/V bytes
-// per step, shared by the waves (0: 8 KB per wave); non-temporal loads or not
-// (measured: ordinary loads 4-6 % faster on both kernels).
+// per step, shared by the waves (0: 8 KB per wave); non-temporal loads (1),
+// ordinary loads (0), or (-1) non-temporal when each wave holds one query
+// tile and ordinary when it holds more (measured: with one tile per wave the
+// non-temporal hint is 3-9 % faster, with two it is 4 % slower).
 #ifndef FD_WIDE_STEP_KB
 #define FD_WIDE_STEP_KB 0
 #endif
 #ifndef FD_WIDE_NT
-#define FD_WIDE_NT 0
+#define FD_WIDE_NT -1
 #endif
 #ifndef FD_BAL_SPREAD
 #define FD_BAL_SPREAD 1  // balanced plan: one query tile per wave while the waves cover the group
@@ -178,13 +180,14 @@ constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the t
 #ifndef FD_MFMA_NT
 #define FD_MFMA_NT 1  // one-wave grouped kernels: non-temporal K/V loads
 #endif
-#ifndef FD_BAL_WIDE_NT
-#define FD_BAL_WIDE_NT 0
-#endif
 // 0: 8 KB per wave (16 KB for two waves, 32 KB for four)
 template <int W>
 constexpr int wide_step_kb() {
     return FD_WIDE_STEP_KB > 0 ? FD_WIDE_STEP_KB : 8 * W;
+}
+template <int QT>
+constexpr int wide_nt() {
+    return FD_WIDE_NT < 0 ? (QT == 1 ? 1 : 0) : FD_WIDE_NT;
 }
 
 // Where a piece's results go.  Partial i of query row `row` (slot h of a
@@ -689,7 +692,7 @@ __global__ __launch_bounds__(64 * W) void split_mfma_tiled_kernel(SplitArgs a) {
         out.lse = a.m_part ? a.m_part : a.lse_part;
         out.l = a.m_part ? a.l_part : nullptr;
     }
-    constexpr int NTL = W > 1 ? FD_WIDE_NT : 0;
+    constexpr int NTL = W > 1 ? wide_nt<QT>() : 0;
     mfma_piece<DT, D, PAGED, QT, NTL, SKB, W>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(64 * W) void split_mfma_balanced_kernel(SplitArgs a
                                nullptr, 1, 0, true};
             const long t0 = (long)lo * kGranule;
             const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
-            mfma_piece<DT, D, PAGED, QT, (W > 1 ? FD_BAL_WIDE_NT : FD_MFMA_NT), SKB, W>(
+            mfma_piece<DT, D, PAGED, QT, (W > 1 ? wide_nt<QT>() : FD_MFMA_NT), SKB, W>(
                 a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
             if (lo == 0 && threadIdx.x == 0) {
                 const long long ustart = c.pos - c.t;  // the unit's first position
