@@ -57,7 +57,8 @@ def _decode_case(gpu, w, inp, num_splits=0):
 
 
 @pytest.mark.parametrize("case", ["fused_small_f32", "mha_one_split", "mha_splits_combine",
-                                  "gqa_ragged_balanced"])
+                                  "gqa_ragged_balanced", "mqa_ragged_four_waves",
+                                  "mqa_two_wave_tiles"])
 def test_decode_graph_replay(gpu, case):
     if case == "fused_small_f32":
         w = workloads.WORKLOADS[1]
@@ -69,9 +70,16 @@ def test_decode_graph_replay(gpu, case):
     elif case == "mha_splits_combine":
         w, inp = workloads.custom(1, 32, 32, 128, 20000, dtype="bf16", seed=42)
         B = 0
-    else:
+    elif case == "gqa_ragged_balanced":
         w, inp = workloads.custom(6, 32, 4, 128, 9000, dtype="bf16", seed=43,
                                   lens=[9000, 17, 0, 4096, 8191, 300])
+        B = 0
+    elif case == "mqa_ragged_four_waves":  # balanced plan, four waves per work-group
+        w, inp = workloads.custom(4, 64, 1, 128, 5000, dtype="bf16", seed=45,
+                                  lens=[5000, 0, 1234, 4097])
+        B = 0
+    else:  # tiled kernel, two waves of one tile each, fixed splits
+        w, inp = workloads.custom(3, 32, 1, 128, 3000, dtype="f16", seed=46)
         B = 0
     step, outs = _decode_case(gpu, w, inp, B)
     o, lse = _capture_and_replay(gpu, step, outs)
