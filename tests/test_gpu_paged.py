@@ -66,7 +66,8 @@ def test_paged_named_workloads(gpu, cfg, page_size):
 
 
 @pytest.mark.parametrize("dtype,group,d", [("f32", 1, 64), ("bf16", 1, 128), ("bf16", 8, 128),
-                                           ("f16", 4, 256), ("f16", 2, 64), ("bf16", 32, 128)])
+                                           ("f16", 4, 256), ("f16", 2, 64), ("bf16", 32, 128),
+                                           ("bf16", 128, 128), ("f16", 40, 256)])
 @pytest.mark.parametrize("page_size", [16, 32, 1024])
 def test_paged_split_bitwise_equal_contiguous(gpu, dtype, group, d, page_size):
     """Same split count and length: paged partials equal contiguous partials
