@@ -499,6 +499,8 @@ GROUPS = [
     workloads.Workload("mqa_f16_b32_hq64_hkv1_d64_ragged512_16384", batch=32, heads_q=64,
                        heads_kv=1, head_dim=64, max_kv_len=16384, dtype="f16", out_dtype="f16",
                        seed=12, ragged=(512, 16384)),
+    workloads.Workload("mqa_f16_b32_hq64_hkv1_d64_n8192", batch=32, heads_q=64, heads_kv=1,
+                       head_dim=64, max_kv_len=8192, dtype="f16", out_dtype="f16", seed=14),
 ]
 
 

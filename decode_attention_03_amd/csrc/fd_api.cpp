@@ -193,6 +193,10 @@ TiledShape tiled_shape(int head_dim, long long nq) {
     t.qt = fd::split_mfma_tile_max_qt(head_dim);
     while (t.qt > 1 && t.qt / 2 >= tiles)
         t.qt /= 2;
+    if (tiles > t.qt) {  // several waves, each with at most wide_qt tiles
+        const int wq = fd::split_mfma_wide_qt(head_dim);
+        t.qt = t.qt < wq ? t.qt : wq;
+    }
     while (t.waves < wmax && (long long)t.qt * t.waves < tiles)
         t.waves *= 2;
     t.groups = (tiles + (long long)t.qt * t.waves - 1) / ((long long)t.qt * t.waves);

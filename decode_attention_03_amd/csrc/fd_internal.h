@@ -117,8 +117,10 @@ bool split_mfma_supported(int in_dtype, int head_dim, int group);
 bool split_mfma_tiled_supported(int in_dtype, int head_dim);
 int split_mfma_tile_max_qt(int head_dim);  // query tiles per wave, 1..4
 // Most waves a tiled work-group can have at this head size (each loads an
-// equal share of every staged row group): 2 at d = 64, 4 at d = 128 and 256.
+// equal share of every staged step's row groups): 4 at every head size.
 int split_mfma_tile_max_waves(int head_dim);
+// Query tiles per wave when a work-group has several waves (1 or 2).
+int split_mfma_wide_qt(int head_dim);
 // Whether the tiled kernel spreads a group's tiles one per wave while the
 // waves cover it (else each wave takes as many tiles as it holds).
 bool split_mfma_tile_spread();

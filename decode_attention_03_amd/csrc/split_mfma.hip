@@ -241,11 +241,17 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
     using T = Tiles<D, STEP_KB>;
     constexpr int NC = T::NC, NT = T::NT, U = T::U;
     using M = Mma<DT>;
-    // W waves share each step: wave wv loads row groups wv, wv + W, ... of
-    // every tile, and all of them compute on all rows (two LDS buffers, one
-    // barrier per step).  W == 1: one wave, one buffer, no barrier.
-    static_assert(T::IPT % W == 0, "row groups per tile must divide among the waves");
-    constexpr int JW = T::IPT / W;  // row groups per tile a wave loads
+    // W waves share each step, and all of them compute on all of its rows
+    // (two LDS buffers, one barrier per step; W == 1: one wave, one buffer,
+    // no barrier).  The loads are shared out by 1 KB row group: with no more
+    // waves than a tile has row groups (IPT), wave wv loads row groups wv,
+    // wv + W, ... of every tile; with more, the R = W / IPT waves with the
+    // same wv % IPT take every R-th tile, starting at tile wv / IPT.
+    constexpr int R = W > T::IPT ? W / T::IPT : 1;
+    static_assert(W <= T::IPT ? T::IPT % W == 0 : (W % T::IPT == 0 && U % R == 0),
+                  "a step's row groups must divide evenly among the waves");
+    constexpr int TU = U / R;                        // tiles a wave loads rows of
+    constexpr int JW = W > T::IPT ? 1 : T::IPT / W;  // row groups per tile a wave loads
 
     const int lane = W > 1 ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
     const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
@@ -298,9 +304,13 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         // first + 16u + r, clamped to the last valid token; a step past the
         // last one re-reads the last step, so prefetches need no condition).
         struct Stage {
-            u32x4 k[U][JW];
-            u32x4 v[U][JW];
+            u32x4 k[TU][JW];
+            u32x4 v[TU][JW];
         };
+        // the tile and row group of this wave's uu-th tile and jj-th row group
+        const int u_first = W > T::IPT ? wv / T::IPT : 0;
+        auto tile_of = [&](int uu) { return uu * R + u_first; };
+        auto group_of = [&](int jj) { return W > T::IPT ? wv % T::IPT : jj * W + wv; };
         const int lrow = lane / T::CPR;  // row within a row group
         const int lq = lane % T::CPR;    // logical chunk this lane carries
         const size_t lane_off = (size_t)kvh * T::ROW + lq * 16;
@@ -309,7 +319,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         // (so are t0 and the step start), so it lies in one page, also after
         // its rows are clamped to the last valid token.
         struct Pages {
-            int pg[U];
+            int pg[TU];  // of the tiles this wave loads
         };
         auto lookup = [&](int st, Pages &P) {
             if constexpr (PAGED) {
@@ -323,9 +333,10 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                     (const __attribute__((address_space(4))) int32_t *)a.block_table +
                     (size_t)b * a.max_pages;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int uu = 0; uu < TU; ++uu) {
+                    const int u = tile_of(uu);
                     const int rel = 16 * u < last_rel ? 16 * u : last_rel;
-                    P.pg[u] = bt[((int)t0 + first + rel) >> a.page_shift];  // clamped at use
+                    P.pg[uu] = bt[((int)t0 + first + rel) >> a.page_shift];  // clamped at use
                 }
             }
         };
@@ -344,7 +355,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             const int first = sa * kStepTok;
             const int last_rel = ntok - 1 - first;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int uu = 0; uu < TU; ++uu) {
+                const int u = tile_of(uu);
                 // base of tile u: contiguous K/V, or the tile's page
                 size_t base;
                 uint32_t pmask = 0xffffffffu;
@@ -352,7 +364,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                     const size_t seq = a.shared_kv ? 0 : (size_t)b * a.max_kv_len;
                     base = (seq + (size_t)t0 + first) * tok_stride;
                 } else {
-                    int pg = P.pg[u];
+                    int pg = P.pg[uu];
                     pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
                     base = ((size_t)pg << a.page_shift) * tok_stride;
                     pmask = (1u << a.page_shift) - 1u;
@@ -361,15 +373,15 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 const char *vb = static_cast<const char *>(a.v) + base + lane_off64;
 #pragma unroll
                 for (int jj = 0; jj < JW; ++jj) {
-                    int rel = 16 * u + (jj * W + wv) * T::RPI + lrow;
+                    int rel = 16 * u + group_of(jj) * T::RPI + lrow;
                     rel = rel < last_rel ? rel : last_rel;
                     // row within the base: the step-relative token, or the
                     // token's row within its page
                     const uint32_t row =
                         PAGED ? ((uint32_t)((int)t0 + first + rel) & pmask) : (uint32_t)rel;
                     const uint32_t off = row * stride32 + lane_off32;
-                    g.k[u][jj] = ld128<NTLOAD>(kb + off);
-                    g.v[u][jj] = ld128<NTLOAD>(vb + off);
+                    g.k[uu][jj] = ld128<NTLOAD>(kb + off);
+                    g.v[uu][jj] = ld128<NTLOAD>(vb + off);
                 }
             }
         };
@@ -377,15 +389,16 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         // Write a step's rows into LDS tiles at buf, chunks swizzled per row.
         auto stage = [&](const Stage &g, lds_char *buf) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int uu = 0; uu < TU; ++uu)
 #pragma unroll
                 for (int jj = 0; jj < JW; ++jj) {
-                    const int r = (jj * W + wv) * T::RPI + lrow;
+                    const int u = tile_of(uu);
+                    const int r = group_of(jj) * T::RPI + lrow;
                     *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
-                        buf + u * T::TILE + r * T::ROW + (lq ^ T::swz_k(r)) * 16) = g.k[u][jj];
+                        buf + u * T::TILE + r * T::ROW + (lq ^ T::swz_k(r)) * 16) = g.k[uu][jj];
                     *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(
                         buf + (U + u) * T::TILE + r * T::ROW + (lq ^ T::swz_v(r)) * 16) =
-                        g.v[u][jj];
+                        g.v[uu][jj];
                 }
         };
         // Several waves: even steps in buffer 0, odd steps in buffer 1.  A
@@ -789,24 +802,24 @@ constexpr int tile_max_qt() {
     return D == 64 ? 4 : (D == 128 ? FD_PREFIX_QT128 : 1);
 }
 
-// Query tiles per wave of the token-balanced kernel: at most two (four, at
-// d = 64, measured slower than the tiled kernel's fixed splits).
+// Query tiles per wave in multi-wave work-groups and in the token-balanced
+// kernel: at most two (four tiles on one wave, at d = 64, measured slower in
+// the balanced kernel than the tiled kernel's fixed splits, and with four
+// waves they spill).
 template <int D>
-constexpr int balanced_qt() {
+constexpr int wide_qt() {
     return tile_max_qt<D>() < 2 ? tile_max_qt<D>() : 2;
 }
 
-// Waves of a tiled work-group: each loads an equal share of the row groups
-// of every staged tile (2 at d = 64, 4 at d = 128 and 256), capped by
+// Waves of a multi-wave work-group: up to 4 at every head size (each loads
+// an equal share of every staged step's row groups), capped by
 // FD_TILE_MAX_WAVES.
 #ifndef FD_TILE_MAX_WAVES
 #define FD_TILE_MAX_WAVES 4
 #endif
 template <int D>
 constexpr int tile_max_waves() {
-    constexpr int ipt = Tiles<D, kPrefixStepKB>::IPT;
-    constexpr int w = ipt >= 4 ? 4 : ipt;
-    return w < FD_TILE_MAX_WAVES ? w : FD_TILE_MAX_WAVES;
+    return 4 < FD_TILE_MAX_WAVES ? 4 : FD_TILE_MAX_WAVES;
 }
 
 // The tiled kernel for QT query tiles per work-group, paged or contiguous.
@@ -861,8 +874,8 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     const dim3 g((unsigned)grid), blk(64);
     if (a.tile_qt > 0 && tw > 1) {
-        // several waves per work-group, each with one tile or the most it holds
-        constexpr int Q = tile_max_qt<D>();
+        // several waves per work-group, each with one tile or wide_qt
+        constexpr int Q = wide_qt<D>();
         if ((a.tile_qt != Q && a.tile_qt != 1) || tw > tile_max_waves<D>())
             return hipErrorInvalidValue;
         const bool one = a.tile_qt == 1;
@@ -896,7 +909,7 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         // QT = ceil(G / 16) tiles on one wave (up to two), or two (one at
         // d = 256) per wave on tw waves
         const int tiles = (a.heads_q / a.heads_kv + 15) / 16;
-        constexpr int QB = balanced_qt<D>();
+        constexpr int QB = wide_qt<D>();
         if (tw > 1) {
             // one tile per wave when the waves cover the group, else QB
             if (tiles > QB * tw || tw > tile_max_waves<D>())
@@ -954,6 +967,15 @@ int split_mfma_tile_max_qt(int head_dim) {
     }
 }
 
+int split_mfma_wide_qt(int head_dim) {
+    switch (head_dim) {
+    case 64: return wide_qt<64>();
+    case 128: return wide_qt<128>();
+    case 256: return wide_qt<256>();
+    default: return 1;
+    }
+}
+
 int split_mfma_tiled_wg_per_cu(int waves) {
     if (waves <= 1)
         return kPrefixWgPerCU;
@@ -984,9 +1006,9 @@ int split_mfma_balanced_wg_per_cu(int waves) {
 // 5 % faster on a ragged batch), on up to the most waves the head size allows.
 int split_mfma_balanced_max_group(int head_dim) {
     switch (head_dim) {
-    case 64: return 16 * balanced_qt<64>() * tile_max_waves<64>();
-    case 128: return 16 * balanced_qt<128>() * tile_max_waves<128>();
-    case 256: return 16 * balanced_qt<256>() * tile_max_waves<256>();
+    case 64: return 16 * wide_qt<64>() * tile_max_waves<64>();
+    case 128: return 16 * wide_qt<128>() * tile_max_waves<128>();
+    case 256: return 16 * wide_qt<256>() * tile_max_waves<256>();
     default: return 0;
     }
 }
@@ -995,9 +1017,9 @@ int split_mfma_balanced_waves(int head_dim, int group) {
     const int tiles = (group + 15) / 16;
     int qt = 0, wmax = 1;
     switch (head_dim) {
-    case 64: qt = balanced_qt<64>(); wmax = tile_max_waves<64>(); break;
-    case 128: qt = balanced_qt<128>(); wmax = tile_max_waves<128>(); break;
-    case 256: qt = balanced_qt<256>(); wmax = tile_max_waves<256>(); break;
+    case 64: qt = wide_qt<64>(); wmax = tile_max_waves<64>(); break;
+    case 128: qt = wide_qt<128>(); wmax = tile_max_waves<128>(); break;
+    case 256: qt = wide_qt<256>(); wmax = tile_max_waves<256>(); break;
     default: return 0;
     }
     if (tiles <= 1)

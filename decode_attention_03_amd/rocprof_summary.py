@@ -339,7 +339,7 @@ def section_main(args) -> int:
     section launches (cascade: the shared-prefix kernel, the suffix kernel and
     the combine; paged: the ragged grouped workload over 16-token pages;
     shard: one GPU's share of the long-context workload and the merge;
-    groups: five shapes with 32 to 128 query heads per KV head)."""
+    groups: six shapes with 32 to 128 query heads per KV head)."""
     raw = os.path.abspath(args.raw)
     out = os.path.abspath(args.out)
     os.makedirs(raw, exist_ok=True)
