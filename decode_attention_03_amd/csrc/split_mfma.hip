@@ -14,7 +14,8 @@
 // one wave (one work-group) owns one (sequence b, KV head, split i) and the
 // tokens [i*L, min((i+1)*L, N_b)) ([P1] §2.5 stage 1), in tiles of 16
 // tokens (larger groups, and a prefix shared by the whole batch, use the
-// tiled kernel further down: 16-query tiles, several per work-group):
+// tiled kernel further down: 16-query tiles, several per work-group, on up to
+// four waves that share each K/V step staged in LDS):
 //
 //   S^T (16 tokens x 16 heads) = K_tile (16 x d) . Q_g^T (d x 16):
 //     v_mfma_f32_16x16x32 over d.  A 128-bit load of 8 contiguous d-elements
@@ -791,8 +792,8 @@ int lds_per_cu_mfma() {
     return v > 0 ? v : 0;
 }
 
-// Query tiles per work-group of the tiled kernel that fit in the register
-// file without spilling next to 16 KB steps (every tile keeps its
+// Query tiles per wave of a one-wave tiled work-group that fit in the
+// register file without spilling next to 16 KB steps (every tile keeps its
 // own Q fragments, O accumulators and softmax state).  Four tiles fit at
 // d = 128 with 8 KB steps, but measured slower: the smaller steps and the
 // shorter splits that the fewer work-groups need cost more than the halved
@@ -822,7 +823,8 @@ constexpr int tile_max_waves() {
     return 4 < FD_TILE_MAX_WAVES ? 4 : FD_TILE_MAX_WAVES;
 }
 
-// The tiled kernel for QT query tiles per work-group, paged or contiguous.
+// The tiled kernel for QT query tiles per wave and W waves, paged or
+// contiguous.
 template <int DT, int D, int QT, int W = 1>
 void launch_tiled(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
     const dim3 blk(64 * W);
@@ -832,7 +834,8 @@ void launch_tiled(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
         hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false, W>), g, blk, pad, stream, a);
 }
 
-// The token-balanced kernel for QT query tiles per unit, paged or contiguous.
+// The token-balanced kernel for QT query tiles per wave and W waves, paged or
+// contiguous.
 template <int DT, int D, int QT, int W = 1>
 void launch_balanced(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
     const dim3 blk(64 * W);
