@@ -197,7 +197,8 @@ TiledShape tiled_shape(int head_dim, long long nq) {
         const int wq = fd::split_mfma_wide_qt(head_dim);
         t.qt = t.qt < wq ? t.qt : wq;
     }
-    while (t.waves < wmax && (long long)t.qt * t.waves < tiles)
+    const int wcap = wmax < 4 ? wmax : 4;  // more than four waves hold one tile each
+    while (t.waves < wcap && (long long)t.qt * t.waves < tiles)
         t.waves *= 2;
     t.groups = (tiles + (long long)t.qt * t.waves - 1) / ((long long)t.qt * t.waves);
     return t;

@@ -184,7 +184,9 @@ constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the t
 // 0: 8 KB per wave (16 KB for two waves, 32 KB for four)
 template <int W>
 constexpr int wide_step_kb() {
-    return FD_WIDE_STEP_KB > 0 ? FD_WIDE_STEP_KB : 8 * W;
+    // eight waves (two per SIMD, 256 registers each): 16 KB, so that a step's
+    // fragments fit
+    return FD_WIDE_STEP_KB > 0 ? FD_WIDE_STEP_KB : (W > 4 ? 16 : 8 * W);
 }
 template <int QT>
 constexpr int wide_nt() {
@@ -674,7 +676,8 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 // shared prefix).  The K/V loads are ordinary (temporal) loads, as other
 // work-groups may read the same rows.
 template <int DT, int D, int QT, bool PAGED, int W>
-__global__ __launch_bounds__(64 * W) void split_mfma_tiled_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 4 ? 2 : 1)))
+void split_mfma_tiled_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int SKB = W > 1 ? wide_step_kb<W>() : kPrefixStepKB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
@@ -718,7 +721,8 @@ __global__ __launch_bounds__(64 * W) void split_mfma_tiled_kernel(SplitArgs a) {
 // per work-group (W > 1: the waves share each K/V step staged in LDS, as in
 // the tiled kernel).
 template <int DT, int D, bool PAGED, int QT, int W = 1>
-__global__ __launch_bounds__(64 * W) void split_mfma_balanced_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 4 ? 2 : 1)))
+void split_mfma_balanced_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int SKB = W > 1 ? wide_step_kb<W>() : FD_MFMA_STEP_KB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
@@ -816,11 +820,12 @@ constexpr int wide_qt() {
 // an equal share of every staged step's row groups), capped by
 // FD_TILE_MAX_WAVES.
 #ifndef FD_TILE_MAX_WAVES
-#define FD_TILE_MAX_WAVES 4
+#define FD_TILE_MAX_WAVES 8
 #endif
 template <int D>
 constexpr int tile_max_waves() {
-    return 4 < FD_TILE_MAX_WAVES ? 4 : FD_TILE_MAX_WAVES;
+    constexpr int w = D <= 128 ? 8 : 4;  // eight: one tile per wave, two waves per SIMD
+    return w < FD_TILE_MAX_WAVES ? w : FD_TILE_MAX_WAVES;
 }
 
 // The tiled kernel for QT query tiles per wave and W waves, paged or
@@ -852,7 +857,8 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     const int tw = a.tile_waves > 1 ? a.tile_waves : 1;
     const size_t kStatic =
-        tw == 4                        ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
+        tw == 8                        ? (size_t)2 * Tiles<D, wide_step_kb<8>()>::BUF
+        : tw == 4                      ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
         : tw == 2                      ? (size_t)2 * Tiles<D, wide_step_kb<2>()>::BUF
         : a.tile_qt > 0 && !a.balanced ? (size_t)Tiles<D, kPrefixStepKB>::BUF
                                        : (size_t)T::BUF;
@@ -894,6 +900,12 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
                 else
                     launch_tiled<DT, D, Q, 4>(a, g, pad, stream);
             }
+        } else if (tw == 8) {
+            if constexpr (tile_max_waves<D>() >= 8) {
+                if (!one)
+                    return hipErrorInvalidValue;
+                launch_tiled<DT, D, 1, 8>(a, g, pad, stream);
+            }
         } else
             return hipErrorInvalidValue;
     } else if (a.tile_qt > 0) {
@@ -929,6 +941,12 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
                         launch_balanced<DT, D, 1, 4>(a, g, pad, stream);
                     else
                         launch_balanced<DT, D, QB, 4>(a, g, pad, stream);
+                }
+            } else if (tw == 8) {
+                if constexpr (tile_max_waves<D>() >= 8) {
+                    if (!one)
+                        return hipErrorInvalidValue;
+                    launch_balanced<DT, D, 1, 8>(a, g, pad, stream);
                 }
             } else
                 return hipErrorInvalidValue;
@@ -1007,11 +1025,17 @@ int split_mfma_balanced_wg_per_cu(int waves) {
 // Up to two tiles per wave (with four, 64 heads at d = 64, one wave's pieces
 // were bound by their arithmetic: the tiled kernel's fixed splits measured
 // 5 % faster on a ragged batch), on up to the most waves the head size allows.
+// Most tiles a multi-wave work-group holds: qt per wave on up to four waves,
+// or one per wave on more.
+constexpr int max_tiles_per_wg(int qt, int wmax) {
+    return qt * (wmax < 4 ? wmax : 4) > wmax ? qt * (wmax < 4 ? wmax : 4) : wmax;
+}
+
 int split_mfma_balanced_max_group(int head_dim) {
     switch (head_dim) {
-    case 64: return 16 * wide_qt<64>() * tile_max_waves<64>();
-    case 128: return 16 * wide_qt<128>() * tile_max_waves<128>();
-    case 256: return 16 * wide_qt<256>() * tile_max_waves<256>();
+    case 64: return 16 * max_tiles_per_wg(wide_qt<64>(), tile_max_waves<64>());
+    case 128: return 16 * max_tiles_per_wg(wide_qt<128>(), tile_max_waves<128>());
+    case 256: return 16 * max_tiles_per_wg(wide_qt<256>(), tile_max_waves<256>());
     default: return 0;
     }
 }
@@ -1035,7 +1059,8 @@ int split_mfma_balanced_waves(int head_dim, int group) {
     }
     if (tiles <= qt)
         return 1;
-    while (w < wmax && qt * w < tiles)
+    const int wq = wmax < 4 ? wmax : 4;  // more than four waves hold one tile each
+    while (w < wq && qt * w < tiles)
         w *= 2;
     return qt * w >= tiles ? w : 0;
 }

@@ -39,9 +39,9 @@ CASES = [
     # more tiles than one wave holds: two or four waves per work-group share
     # each staged K/V step (the last wave's last tile partial or empty)
     ("group48_d64_4waves", 5, 2, 48, 64, "f16", 2200, [2200, 0, 15, 1999, 640]),
-    ("group96_d64_4waves", 3, 1, 96, 64, "bf16", 2100, [2100, 5, 1600]),
+    ("group96_d64_8waves", 3, 1, 96, 64, "bf16", 2100, [2100, 5, 1600]),
     ("group64_d128_4waves", 4, 2, 64, 128, "bf16", 3000, [3000, 1, 0, 2047]),
-    ("group128_d128_4waves", 6, 1, 128, 128, "bf16", 2500, [2500, 17, 0, 1300, 2499, 64]),
+    ("group128_d128_8waves", 6, 1, 128, 128, "bf16", 2500, [2500, 17, 0, 1300, 2499, 64]),
     ("group40_d256_4waves", 3, 2, 40, 256, "f16", 1800, [1800, 900, 0]),
     ("group24_d256_2waves", 5, 1, 24, 256, "bf16", 1500, [0, 1500, 3, 777, 1499]),
 ]
