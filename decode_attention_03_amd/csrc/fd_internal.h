@@ -81,8 +81,8 @@ struct SplitArgs {
     // the KV head; otherwise the G queries of one sequence (groups larger
     // than one tile).  0 selects the one-tile kernels.
     int tile_qt;
-    // Tiled and token-balanced kernels: waves per work-group (1, 2 or 4; 0
-    // means 1).  The waves take their own query tiles and share every K/V
+    // Tiled and token-balanced kernels: waves per work-group (1, 2, 4 or 8;
+    // 0 means 1).  The waves take their own query tiles and share every K/V
     // step staged in LDS, so a work-group serves all of its tiles from one
     // read of the rows.
     int tile_waves;
@@ -117,7 +117,8 @@ bool split_mfma_supported(int in_dtype, int head_dim, int group);
 bool split_mfma_tiled_supported(int in_dtype, int head_dim);
 int split_mfma_tile_max_qt(int head_dim);  // query tiles per wave, 1..4
 // Most waves a tiled work-group can have at this head size (each loads an
-// equal share of every staged step's row groups): 4 at every head size.
+// equal share of every staged step's row groups): 8 at d <= 128 (one tile
+// per wave, two waves per SIMD), 4 at d = 256.
 int split_mfma_tile_max_waves(int head_dim);
 // Query tiles per wave when a work-group has several waves (1 or 2).
 int split_mfma_wide_qt(int head_dim);

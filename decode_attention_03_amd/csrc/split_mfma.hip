@@ -15,7 +15,7 @@
 // tokens [i*L, min((i+1)*L, N_b)) ([P1] §2.5 stage 1), in tiles of 16
 // tokens (larger groups, and a prefix shared by the whole batch, use the
 // tiled kernel further down: 16-query tiles, several per work-group, on up to
-// four waves that share each K/V step staged in LDS):
+// eight waves that share each K/V step staged in LDS):
 //
 //   S^T (16 tokens x 16 heads) = K_tile (16 x d) . Q_g^T (d x 16):
 //     v_mfma_f32_16x16x32 over d.  A 128-bit load of 8 contiguous d-elements
