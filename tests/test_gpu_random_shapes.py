@@ -1,7 +1,8 @@
 """GPU parity over seeded random shapes, through the C ABI, against the oracle.
 
 Each case draws (from one fixed seed) a batch size, head counts and group
-size (1 to 40 query heads per KV head), head size, input type, ragged
+size (1 to 128 query heads per KV head, so every work-group shape from one
+to eight waves appears), head size, input type, ragged
 lengths (some empty), a split plan (automatic, one split, or an explicit
 count and length) and the entry point: contiguous decode, paged decode, or
 the split stage in either partial format followed by its combine.  The
@@ -26,7 +27,7 @@ N_CASES = 120
 
 def _draw(i):
     g = np.random.default_rng(1000 + i)
-    group = int(g.choice([1, 1, 2, 4, 8, 16, 17, 32, 40]))
+    group = int(g.choice([1, 1, 2, 4, 8, 16, 17, 32, 40, 80, 128]))
     hkv = int(g.integers(1, 4))
     d = int(g.choice([64, 128, 256]))
     dtype = str(g.choice(["f32", "bf16", "f16"]))
