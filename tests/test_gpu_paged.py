@@ -8,7 +8,6 @@ original contiguous K/V, and with the same split count and length the paged
 kernels must reproduce the contiguous kernels bit for bit: the page lookup
 changes addresses, not arithmetic.
 """
-import dataclasses
 
 import numpy as np
 import pytest
