@@ -295,7 +295,7 @@ int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head
     p->waves = fd::split_mfma_balanced_waves(head_dim, p->gsz);
     if (p->waves < 1)
         return fail(FD_ERR_INVALID, "group of %d too large for the balanced plan", p->gsz);
-    p->num_wgs = cus * fd::split_mfma_balanced_wg_per_cu(p->waves) * kBalancedRounds;
+    p->num_wgs = cus * fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz) * kBalancedRounds;
     // positions (units * max_kv_len) times work-groups must stay within int64
     if ((double)p->units * max_kv_len * p->num_wgs > 4.0e18)
         return fail(FD_ERR_INVALID, "batch * heads_kv * max_kv_len too large for the balanced plan");

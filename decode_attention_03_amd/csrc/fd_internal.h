@@ -132,7 +132,7 @@ int split_mfma_tiled_wg_per_cu(int waves);
 // large), and its resident work-groups per CU with that many waves.
 int split_mfma_balanced_max_group(int head_dim);
 int split_mfma_balanced_waves(int head_dim, int group);
-int split_mfma_balanced_wg_per_cu(int waves);
+int split_mfma_balanced_wg_per_cu(int head_dim, int group);
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.

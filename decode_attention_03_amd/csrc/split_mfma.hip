@@ -188,6 +188,14 @@ constexpr int wide_step_kb() {
     // fragments fit
     return FD_WIDE_STEP_KB > 0 ? FD_WIDE_STEP_KB : (W > 4 ? 16 : 8 * W);
 }
+// Token-balanced work-groups of four one-tile waves at d <= 128: 16 KB steps
+// and two waves per SIMD (two work-groups per CU), which measured 1.5-5 %
+// faster there than 32 KB steps at one wave per SIMD (on the tiled kernel's
+// fixed splits the same change was slower).
+template <int D, int QT, int W>
+constexpr bool bal_two_per_simd() {
+    return W == 4 && QT == 1 && D <= 128;
+}
 template <int QT>
 constexpr int wide_nt() {
     return FD_WIDE_NT < 0 ? (QT == 1 ? 1 : 0) : FD_WIDE_NT;
@@ -721,10 +729,13 @@ void split_mfma_tiled_kernel(SplitArgs a) {
 // per work-group (W > 1: the waves share each K/V step staged in LDS, as in
 // the tiled kernel).
 template <int DT, int D, bool PAGED, int QT, int W = 1>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 4 ? 2 : 1)))
+__global__ __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu(W > 4 || bal_two_per_simd<D, QT, W>() ? 2 : 1)))
 void split_mfma_balanced_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int SKB = W > 1 ? wide_step_kb<W>() : FD_MFMA_STEP_KB;
+    constexpr int SKB = bal_two_per_simd<D, QT, W>() ? 16
+                        : W > 1                     ? wide_step_kb<W>()
+                                                    : FD_MFMA_STEP_KB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
     const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int w = blockIdx.x;
@@ -856,8 +867,12 @@ template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     const int tw = a.tile_waves > 1 ? a.tile_waves : 1;
+    // balanced four-wave work-groups with one tile per wave (bal_two_per_simd)
+    const bool bal_two = a.balanced && tw == 4 && D <= 128 &&
+                         (a.heads_q / a.heads_kv + 15) / 16 <= tw;
     const size_t kStatic =
-        tw == 8                        ? (size_t)2 * Tiles<D, wide_step_kb<8>()>::BUF
+        bal_two                        ? (size_t)2 * Tiles<D, 16>::BUF
+        : tw == 8                      ? (size_t)2 * Tiles<D, wide_step_kb<8>()>::BUF
         : tw == 4                      ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
         : tw == 2                      ? (size_t)2 * Tiles<D, wide_step_kb<2>()>::BUF
         : a.tile_qt > 0 && !a.balanced ? (size_t)Tiles<D, kPrefixStepKB>::BUF
@@ -874,7 +889,7 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     }
     size_t pad = 0;
     const int lds = lds_per_cu_mfma();
-    const int per_cu = a.balanced ? split_mfma_balanced_wg_per_cu(tw)
+    const int per_cu = a.balanced ? split_mfma_balanced_wg_per_cu(D, a.heads_q / a.heads_kv)
                        : a.tile_qt == 0 ? kMfmaWgPerCU
                                         : split_mfma_tiled_wg_per_cu(tw);
     if (per_cu > 0 && lds > 0) {
@@ -1015,9 +1030,12 @@ int split_mfma_tile_max_waves(int head_dim) {
     }
 }
 
-int split_mfma_balanced_wg_per_cu(int waves) {
+int split_mfma_balanced_wg_per_cu(int head_dim, int group) {
+    const int waves = split_mfma_balanced_waves(head_dim, group);
     if (waves <= 1)
         return kMfmaWgPerCU;
+    if (waves == 4 && head_dim <= 128 && (group + 15) / 16 <= waves)
+        return 2;  // bal_two_per_simd
     const int n = kPrefixWgPerCU / waves;  // one wave per SIMD
     return n > 1 ? n : 1;
 }

@@ -140,13 +140,14 @@ def test_decode_plan_struct_layout():
     # 128 per KV head at d = 128: eight waves of one tile share each staged step
     ((4, 128, 1, 8192, 128, fd.BF16, 0, 0, 0), dict(kernel=2, query_tiles=8, waves_per_group=8)),
     # ragged: 32 per KV head balanced on two waves of one tile (two work-groups
-    # per CU), 40 on four waves of one tile, 128 on eight of one (one per CU);
+    # per CU), 40 on four waves of one tile (two per CU, two waves per SIMD),
+    # 128 on eight of one (one per CU);
     # 136: past the balanced plan, tiled work-groups of four waves of two tiles
     # (two per unit)
     ((16, 64, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=2,
                                                      waves_per_group=2, work_groups=512)),
     ((16, 80, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=3,
-                                                     waves_per_group=4, work_groups=256)),
+                                                     waves_per_group=4, work_groups=512)),
     ((16, 256, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=3, query_tiles=8,
                                                       waves_per_group=8, work_groups=256)),
     ((16, 272, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=2, kernel=2, query_tiles=8,
