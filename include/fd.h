@@ -198,9 +198,9 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
  *       2 <= heads_q/heads_kv <= 128, 128, 64 at head_dim 64, 128, 256): a
  *       token-balanced partition.  The
  *       (sequence, KV head, token) space of the actual lengths is cut into
- *       equal shares, one per work-group (CUs x 2 for up to 16 query heads
- *       per KV head, fewer for larger groups, whose work-groups have several
- *       waves), so every work-group
+ *       equal shares, one per work-group (CUs x 2, or CUs x 1 for the
+ *       larger groups whose work-groups have four or eight waves), so every
+ *       work-group
  *       streams the same number of K/V rows whatever the length mix; a share
  *       may end inside one (sequence, head) row and continue in the next, and
  *       each such piece yields one (o, LSE) pair that the combine merges with
