@@ -16,8 +16,7 @@
 //
 // Definitions (all positions 64-bit; a position is one granule of
 // kGranule = 16 tokens, so every piece starts on a 16-token tile boundary):
-//   unit u = b * hx + x: one (sequence b, head x) pair reading one KV head
-//            (hx = heads_kv for the grouped kernel, heads_q for the vector one);
+//   unit (b, x): one (sequence b, KV head x) pair; hx = heads_kv;
 //   N_b    = kv_lens[b] clamped to [0, max_kv_len], g_b = ceil(N_b / 16);
 //   a unit of a non-empty sequence costs g_b + kPieceCost positions: the
 //            first kPieceCost stand for the fixed cost of starting a piece
@@ -25,15 +24,20 @@
 //            so that shares balance time rather than bytes; its granule j
 //            (tokens [16 j, min(16 j + 16, N_b))) is position kPieceCost + j
 //            of the unit; empty sequences cost nothing;
-//   the flattened space lists units in order, unit u covering positions
-//            [S_u, S_u + g_b + kPieceCost);
-//   T      = sum of all unit costs, W_eff = min(num_wgs, T);
+//   the flattened space lists units head-major, (0, 0), (1, 0), ...,
+//            (batch - 1, 0), (0, 1), ..., each unit covering its cost in
+//            positions; head x therefore holds [x P, (x + 1) P), P being the
+//            summed cost of the sequences, and when hx divides num_wgs the
+//            work-groups of different heads get the same token ranges and
+//            stream the same K/V rows (one row of every head) side by side,
+//            as fixed splits do;
+//   T      = hx P, W_eff = min(num_wgs, T);
 //   work-group w < W_eff covers [floor(w T / W_eff), floor((w+1) T / W_eff)),
 //            never empty; work-groups w >= W_eff do nothing; a work-group's
 //            piece of unit u is the unit's granules inside its range (none
 //            when the range only touches the unit's leading cost positions);
 //   the piece of unit u handled by work-group w writes slot w + rank(u),
-//            rank(u) = number of non-empty units before u; a unit's pieces
+//            rank(u) = number of non-empty units before u in that order; a unit's pieces
 //            therefore fill consecutive slots, and slots < num_wgs + units;
 //   the work-group that handles a unit's granule 0 writes the unit's
 //            descriptor {first slot, slot count}; units of empty sequences
@@ -108,39 +112,43 @@ struct PieceCursor {
 __device__ __forceinline__ bool balanced_start(const int32_t *kv_lens, int batch, int max_kv_len,
                                                int hx, int w, int num_wgs, PieceCursor &c) {
     const int lane = threadIdx.x & 63;
-    long long gsum = 0;
+    long long gsum = 0;  // positions of one head: the sum of the unit costs
+    int ne_all = 0;      // non-empty sequences
     for (int base = 0; base < batch; base += 64) {
         const int i = base + lane;
-        gsum += i < batch ? unit_cost(kv_lens, i, max_kv_len) : 0;
+        const int n = i < batch ? unit_cost(kv_lens, i, max_kv_len) : 0;
+        gsum += n;
+        ne_all += __popcll(__ballot(n > 0));
     }
-    c.total = uniform(wave_sum_ll(gsum) * hx);
+    const long long per_head = uniform(wave_sum_ll(gsum));
+    c.total = per_head * hx;
     c.w_eff = c.total < num_wgs ? (int)c.total : num_wgs;
     if (w >= c.w_eff)
         return false;
     c.pos = c.total * w / c.w_eff;
     c.end = c.total * (w + 1) / c.w_eff;
-    // the sequence whose units contain `pos`
+    // head-major order: head x holds positions [x * per_head, (x + 1) * per_head)
+    c.x = uniform((int)(c.pos / per_head));
+    const long long off = c.pos - (long long)c.x * per_head;
+    // the sequence whose unit of head x contains `pos`
     long long before = 0;  // positions of the sequences before this chunk
     int nonempty = 0;      // non-empty sequences before this chunk
     for (int base = 0; base < batch; base += 64) {
         const int i = base + lane;
         const long long n = i < batch ? unit_cost(kv_lens, i, max_kv_len) : 0;
         const long long incl = wave_scan_ll(n, lane);
-        const unsigned long long hit = __ballot(i < batch && before + hx * incl > c.pos);
+        const unsigned long long hit = __ballot(i < batch && before + incl > off);
         const unsigned long long ne = __ballot(n > 0);
         if (hit) {
             const int l = __ffsll((long long)hit) - 1;
             const long long nb = __shfl(n, l, 64);
-            const long long start = before + hx * (__shfl(incl, l, 64) - nb);
-            const long long off = c.pos - start;
             c.b = uniform(base + l);
-            c.x = uniform((int)(off / nb));
-            c.t = uniform((int)(off % nb));
+            c.t = uniform((int)(off - (before + __shfl(incl, l, 64) - nb)));
             const int ne_before = nonempty + __popcll(ne & ((1ull << l) - 1ull));
-            c.rank = uniform(ne_before * hx + c.x);
+            c.rank = uniform(c.x * ne_all + ne_before);
             return true;
         }
-        before += hx * __shfl(incl, 63, 64);
+        before += __shfl(incl, 63, 64);
         nonempty += __popcll(ne);
     }
     return false;  // not reached: pos < T lies in some non-empty sequence

@@ -723,7 +723,7 @@ void split_mfma_tiled_kernel(SplitArgs a) {
 }
 
 // Token-balanced partition (partition.h): work-group w walks its share of the
-// flattened (sequence, KV head, token) space piece by piece; the piece of unit
+// flattened (KV head, sequence, token) space piece by piece; the piece of unit
 // u goes to slot w + rank(u) of the slot arrays (o [slot][G][d], LSE [slot][G]).
 // The G query heads of a unit take ceil(G / 16) tiles: QT per wave, W waves
 // per work-group (W > 1: the waves share each K/V step staged in LDS, as in
@@ -774,19 +774,21 @@ void split_mfma_balanced_kernel(SplitArgs a) {
         c.pos += avail;
         if (c.pos >= c.end)
             break;
-        // next unit: the next KV head, else the next non-empty sequence
+        // next unit: the next non-empty sequence of this KV head, else the
+        // first one of the next KV head
         c.t = 0;
         ++c.rank;
-        if (++c.x == a.heads_kv) {
-            c.x = 0;
-            do {
-                ++c.b;
-                n = c.b < a.batch ? clamp_len(a.kv_lens, c.b, a.max_kv_len) : 0;
-            } while (n == 0 && c.b < a.batch);
-            if (n == 0)
-                break;  // not reached: positions remain, so a non-empty sequence follows
-            ng = (n + kGranule - 1) / kGranule;
-        }
+        do {
+            if (++c.b == a.batch) {
+                c.b = 0;
+                if (++c.x == a.heads_kv)
+                    break;
+            }
+            n = clamp_len(a.kv_lens, c.b, a.max_kv_len);
+        } while (n == 0);
+        if (c.x == a.heads_kv)
+            break;  // not reached: positions remain, so a non-empty unit follows
+        ng = (n + kGranule - 1) / kGranule;
     }
 #endif  // __HIP_DEVICE_COMPILE__
 }

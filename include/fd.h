@@ -197,7 +197,7 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
  *     - kv_lens given and grouped heads on the matrix cores (bf16/f16,
  *       2 <= heads_q/heads_kv <= 128, 128, 64 at head_dim 64, 128, 256): a
  *       token-balanced partition.  The
- *       (sequence, KV head, token) space of the actual lengths is cut into
+ *       (KV head, sequence, token) space of the actual lengths is cut into
  *       equal shares, one per work-group (CUs x 2, or CUs x 1 for the
  *       larger groups whose work-groups have four or eight waves), so every
  *       work-group

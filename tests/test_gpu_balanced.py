@@ -1,7 +1,7 @@
 """GPU parity of the token-balanced partition (fd_decode's automatic plan for
 ragged grouped-head batches) against the fp64 oracle, through the C ABI.
 
-The partition cuts the flattened (sequence, KV head, token) space into equal
+The partition cuts the flattened (KV head, sequence, token) space into equal
 shares; these cases aim at its corners: empty sequences between full ones,
 every sequence empty, fewer positions than work-groups, more than 64
 sequences (the in-kernel prefix scan runs over several 64-lane chunks), one
