@@ -738,7 +738,15 @@ void split_mfma_balanced_kernel(SplitArgs a) {
                                                     : FD_MFMA_STEP_KB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
     const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
-    const int w = blockIdx.x;
+    // Share index.  When the KV heads come in multiples of the 8 XCDs (which
+    // take work-groups round-robin), neighbouring work-groups take the same
+    // token range of consecutive heads, so each XCD streams whole heads, as
+    // it does under fixed splits; measured 1.2 us faster per step on 8 KV heads
+    // and 0.7 us slower on 2, where the plain order stays.
+    const int w = a.heads_kv % 8 == 0 && a.num_wgs % a.heads_kv == 0
+                      ? (int)(blockIdx.x % a.heads_kv) * (a.num_wgs / a.heads_kv) +
+                            (int)(blockIdx.x / a.heads_kv)
+                      : (int)blockIdx.x;
     const int G = a.heads_q / a.heads_kv;
     PieceCursor c;
     if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c))

@@ -5,7 +5,8 @@ The partition cuts the flattened (KV head, sequence, token) space into equal
 shares; these cases aim at its corners: empty sequences between full ones,
 every sequence empty, fewer positions than work-groups, more than 64
 sequences (the in-kernel prefix scan runs over several 64-lane chunks), one
-sequence spread over hundreds of pieces, clamped lengths, groups of 17 to
+sequence spread over hundreds of pieces, clamped lengths, KV heads in
+multiples of eight (the permuted share order) and not, groups of 17 to
 32 query heads per KV head (two query tiles per piece), and larger groups on
 work-groups of two or four waves.  K/V rows past each
 length are NaN and the workspace starts NaN-filled, so a read past a length or
@@ -31,6 +32,13 @@ CASES = [
     ("one_long_row", 3, 1, 16, 256, "f16", 40000, [1, 40000, 2]),
     ("clamped", 4, 4, 8, 128, "bf16", 300, [0, 300, 5000, -3]),
     ("group2_d256", 6, 3, 2, 256, "bf16", 3000, [2999, 1, 1500, 0, 3000, 64]),
+    # KV heads in multiples of 8: neighbouring work-groups take consecutive
+    # heads of one share (the share index is permuted); 24 heads do not
+    # divide the work-group count and keep the plain order
+    ("hkv8_group8", 6, 8, 8, 128, "bf16", 3000, [3000, 0, 17, 2500, 1, 1999]),
+    ("hkv16_group4_d64", 9, 16, 4, 64, "f16", 1200, [0, 1200, 5, 0, 777, 1199, 0, 64, 300]),
+    ("hkv8_group32", 3, 8, 32, 128, "bf16", 2000, [2000, 1, 1500]),
+    ("hkv24_group2", 2, 24, 2, 64, "bf16", 500, [500, 250]),
     # groups past one 16-query tile: every tile of a unit in the one work-group
     ("group32_d128_2waves", 6, 2, 32, 128, "bf16", 6000, [6000, 0, 17, 4099, 1, 2500]),
     ("group32_d64_mqa", 9, 1, 32, 64, "f16", 3000, [3000, 2, 0, 1777, 3000, 64, 500, 0, 2999]),
