@@ -7,8 +7,10 @@ KV bandwidth (bytes of K and V a step must read / step time) against the
 
 One "step" is one fd_decode call (split kernel + combine kernel) over one
 batch of the workload, inputs already resident in HBM.  The headline
-workload is the bf16 multi-head batch (--config 2); the other named workloads
-are timed in the same run and reported under "workloads".  Each workload keeps
+workload is the ragged grouped-query bf16 batch (--config 4: 16 sequences of
+512-32768 tokens, 64 query heads on 8 KV heads, d = 128), one of the two
+long-context bf16 workloads; the other named workloads are timed in the same
+run and reported under "workloads".  Each workload keeps
 enough copies of its K/V in HBM that consecutive steps read different copies,
 so a step cannot be served from the 256 MB Infinity Cache (the 0.5 MiB fp32
 workload is cache-resident by nature and reports µs only).
@@ -83,6 +85,7 @@ class Prepared:
                              device=dev)
         self.lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
         dec_b, dec_l = (0, 0) if self.auto else (self.B, self.L)
+        self.dec_b, self.dec_l = dec_b, dec_l
         ws = self.dplan["workspace_bytes"]
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.ws_bytes = ws
@@ -100,6 +103,7 @@ class Prepared:
         lens_p = None if self.lens is None else P(self.lens.data_ptr())
         self.decode_args = []
         self.split_args = []
+        self.stage_args = []  # fd_decode_stages with the split stage only
         for k, v in self.kv:
             self.decode_args.append((P(self.q.data_ptr()), P(k.data_ptr()), P(v.data_ptr()),
                                      lens_p, batch, hq, hkv, self.n_max, d, self.in_code,
@@ -110,6 +114,7 @@ class Prepared:
                                     lens_p, batch, hq, hkv, self.n_max, d, self.in_code,
                                     ctypes.c_float(w.scale), self.B, self.L,
                                     P(self.o_part.data_ptr()), P(self.lse_part.data_ptr()), sp))
+            self.stage_args.append(self.decode_args[-1][:-1] + (fd.STAGE_SPLIT, sp))
         # algorithmic bytes of the timed split launch: K/V rows, q, and the
         # partials written (fixed splits: B per row; balanced: at most one per
         # work-group piece, bounded by work-groups + units, counted in full)
@@ -129,6 +134,12 @@ class Prepared:
 
     def split(self, i: int) -> None:
         rc = self.lib.fd_decode_split(*self.split_args[i % self.copies])
+        if rc != fd.OK:
+            raise fd.FDError(rc, fd.last_error())
+
+    def split_stage(self, i: int) -> None:
+        """The split launch of fd_decode alone (fd_decode_stages)."""
+        rc = self.lib.fd_decode_stages(*self.stage_args[i % self.copies])
         if rc != fd.OK:
             raise fd.FDError(rc, fd.last_error())
 
@@ -210,11 +221,11 @@ def time_graph_steps(p: Prepared, steps: int, per_graph: int = 20) -> float:
 
 
 def time_split_kernel(p: Prepared, steps: int, warmup: int) -> float:
-    """Average duration (µs) of the split kernel alone: HIP events on its stream
-    around `steps` back-to-back launches, divided by `steps`.  The balanced
-    plan's split stage has no entry point of its own; for it the whole decode
-    (split + combine) is timed, which bounds the split kernel from above."""
-    run = p.decode if p.balanced else p.split
+    """Average duration (µs) of fd_decode's split kernel alone (its split
+    stage through fd_decode_stages: the same kernel and plan as inside the
+    step): HIP events on its stream around `steps` back-to-back launches,
+    divided by `steps`."""
+    run = p.split_stage
     settle(run)
     for i in range(warmup):
         run(i)
@@ -309,9 +320,7 @@ def time_paged(w: workloads.Workload, dev: torch.device, page_size: int, steps: 
     pages = [(pg["k_pages"].to(dev), pg["v_pages"].to(dev)) for _ in range(copies)]
     batch, hq, hkv, d = w.batch, w.heads_q, w.heads_kv, w.head_dim
     ps, max_pages, num_pages = page_size, pg["max_pages"], pg["num_pages"]
-    B, L = (w.num_splits, 0) if w.num_splits else (0, 0)
-    if B:
-        L = fd._tile_split_len(max_pages * ps, B)
+    B, L = (w.num_splits, 0) if w.num_splits else (0, 0)  # L 0: the library's chunking
     out_dt = workloads.TORCH_DTYPES[w.out_dtype]
     o = torch.empty((batch, hq, d), dtype=out_dt, device=dev)
     lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
@@ -545,17 +554,28 @@ def cpu_baseline(p: Prepared, budget_s: float) -> dict:
            "kind": "oracle", "us_per_step": round(us, 1),
            "sample": f"{reps} whole decode step(s) of {w.name} (every row, fp64, OpenMP over "
                      f"(sequence, head)), {wall:.1f} s wall"}
-    # the same oracle on one thread, one step, for reference
+    # the same oracle on one thread, for reference, over the first sequences
+    # of the batch up to >= 256 MiB of K/V (the whole step when smaller)
+    nb, sample_bytes = 0, 0
+    row = w.heads_kv * w.head_dim * 2 * inp["k"].element_size()
+    while nb < w.batch and sample_bytes < (256 << 20):
+        sample_bytes += row * (p.n_max if lens is None else int(lens[nb]))
+        nb += 1
+    sub = (w.dtype, workloads.raw(inp["q"][:nb]), workloads.raw(inp["k"][:nb]),
+           workloads.raw(inp["v"][:nb]), None if lens is None else lens[:nb].numpy())
     oracle.set_threads(1)
     try:
         t1 = time.perf_counter()
-        oracle.attention(*args, scale=w.scale)
+        oracle.attention(*sub, scale=w.scale)
         one = time.perf_counter() - t1
     finally:
         oracle.set_threads(threads)
-    out["one_thread"] = {"value": round(p.kv_bytes / one / 1e9, 3), "unit": "GB/s",
-                         "us_per_step": round(one * 1e6, 1),
-                         "sample": f"1 whole decode step of {w.name} on 1 thread"}
+    what = (f"1 whole decode step of {w.name}" if nb == w.batch else
+            f"sequences 0..{nb - 1} of one decode step of {w.name} ({sample_bytes} bytes of K/V)")
+    out["one_thread"] = {"value": round(sample_bytes / one / 1e9, 3), "unit": "GB/s",
+                         "us_per_step": round(one * 1e6 * p.kv_bytes / sample_bytes, 1),
+                         "sample": f"{what} on 1 thread; us_per_step scaled to the whole step "
+                                   "by K/V bytes"}
     return out
 
 
@@ -618,7 +638,8 @@ def summarize(p: Prepared, t: dict, split_us: float | None) -> dict:
         # taken out by graph replay
         out["graph_us_per_step"] = round(time_graph_steps(p, 200), 2)
     if split_us is not None:
-        out["split_kernel_us" if not p.balanced else "split_and_combine_us"] = round(split_us, 2)
+        out["split_kernel_us"] = round(split_us, 2)
+        out["split_kernel_GBps"] = round(p.split_bytes / (split_us * 1e-6) / 1e9, 1)
     prof = traffic_from_profile(p.w.name)
     if prof is not None:
         out["split_traffic_bytes_per_launch"] = prof["hbm_bytes_per_launch"]
@@ -631,7 +652,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="headline workload (1-5)")
+    ap.add_argument("--config", type=int, default=4, help="headline workload (1-5)")
     ap.add_argument("--num-splits", type=int, default=0, help="override the split count")
     ap.add_argument("--only", action="store_true", help="time the headline workload only")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="oracle seconds (0: skip)")
@@ -650,6 +671,11 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    # bring up the HIP runtime and this device's context before any threaded
+    # CPU work (the input generator runs a thread pool)
+    torch.cuda.init()
+    torch.empty(1, device=dev)
+    torch.cuda.synchronize(dev)
 
     if args.copy_probe:
         # a streaming elementwise kernel (out = -in) that reads and writes
@@ -686,8 +712,7 @@ def main() -> int:
     achieved = p.split_bytes / (split_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "split" if not p.balanced else "split+combine (token-balanced)",
-                "kernel_us": round(split_us, 2),
+                "kernel": f"split ({p.dplan['kernel']})", "kernel_us": round(split_us, 2),
                 "algorithmic_bytes_per_launch": p.split_bytes}
     prof = traffic_from_profile(head.name)
     if prof is not None:
@@ -707,7 +732,9 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # storage and matrix-core operand type; every sum accumulates in fp32
+        "dtype": head.dtype,
+        "accumulate_dtype": "f32",
         "data": "synthetic",
         "config": {"workload": head.name, "batch": head.batch, "heads_q": head.heads_q,
                    "heads_kv": head.heads_kv, "head_dim": head.head_dim,
@@ -758,10 +785,10 @@ def main() -> int:
         log(f"[bench] partial formats: {pf}")
         result["partial_formats"] = pf
         torch.cuda.empty_cache()
-        # the paged K/V cache (block-table indirection) on the headline and
+        # the paged K/V cache (block-table indirection) on the multi-head and
         # the ragged grouped workloads, 16-token pages
         paged = {}
-        for c in (args.config, 4):
+        for c in (2, 4):
             w = workloads.WORKLOADS[c]
             r = time_paged(w, dev, 16, args.steps, args.warmup)
             contiguous = (result if c == args.config else others[w.name])["us_per_step"]

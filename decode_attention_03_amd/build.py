@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -39,6 +40,24 @@ def source_hash(kernel: str) -> str:
             h.update(f.read())
     return h.hexdigest()[:16]
 
+
+#: written beside the library: the hash of the sources it was built from
+RECORD = os.path.join(PKG, "libfd.build.json")
+
+
+def library_source_hash() -> str:
+    """Short SHA-256 over every file the library is built from (csrc/ and
+    include/), names included, so a build can be matched to its sources."""
+    h = hashlib.sha256()
+    for folder in (CSRC, os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(folder)):
+            path = os.path.join(folder, name)
+            if os.path.isfile(path):
+                h.update(name.encode() + b"\0")
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
+
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -60,8 +79,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libfd)")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra: list[str], objdir: str) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, *lang, "-c", path, "-o", obj]
@@ -76,12 +95,20 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra_flags: list[str] | None = None, verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str = LIB) -> str:
+    """Compile and link the library to `out`.  Only the plain build (no
+    extra flags, at LIB) records its sources' hash beside it, which is what
+    fd.library() checks before loading; a build with extra flags (a tuning
+    or instrumented variant) goes to its own object folder and, at LIB,
+    leaves a record that no source hash matches."""
     extra = list(extra_flags or [])
+    tag = hashlib.sha256(" ".join(extra).encode()).hexdigest()[:8] if extra else ""
+    objdir = os.path.join(BUILD, tag) if tag else BUILD
+    os.makedirs(objdir, exist_ok=True)
+    sources = library_source_hash()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, objdir), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -91,10 +118,15 @@ def build(extra_flags: list[str] | None = None, verbose: bool = True) -> str:
     import ctypes
 
     ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    if os.path.abspath(out) == os.path.abspath(LIB):
+        record = {"sources_sha256": None if extra else sources, "flags": extra}
+        with open(RECORD + ".tmp", "w", encoding="utf-8") as f:
+            json.dump(record, f)
+        os.replace(RECORD + ".tmp", RECORD)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

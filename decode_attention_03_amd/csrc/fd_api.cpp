@@ -22,7 +22,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;          // 0.1.0
+constexpr int kVersion = 200;          // 0.2.0
 constexpr int kMaxSplits = 8192;       // combine keeps one weight per split in LDS
 constexpr int kWorkGroupsPerCU = fd::kWavesPerCU;  // resident one-wave work-groups per CU
 constexpr int kRaggedRounds = 4;       // work-group rounds aimed at for ragged batches
@@ -37,6 +37,13 @@ constexpr int kMaxAutoSplits = 512;
 constexpr int kBalancedRounds = 1;     // token-balanced work-groups: CUs * per-CU * rounds
 
 thread_local std::string g_error;
+
+#if FD_WG_CLOCKS
+// Instrumented builds: the stamp buffer the token-balanced kernel writes
+// (fd_debug_wg_clocks); used while it holds four words per work-group.
+unsigned long long *g_wg_clock = nullptr;
+size_t g_wg_clock_bytes = 0;
+#endif
 
 int fail(int code, const char *fmt, ...) {
     char buf[512];
@@ -106,6 +113,18 @@ int check_split_inputs(const void *q, const void *k, const void *v, const int32_
     if ((size_t)heads_kv * head_dim * elem_bytes(in_dtype) > ((size_t)1 << 24))
         return fail(FD_ERR_UNSUPPORTED, "one token's K row over all heads exceeds 16 MiB");
     return FD_OK;
+}
+
+// split_len 0 with num_splits > 0: ceil(max_kv_len / num_splits) tokens per
+// split ("adv04: Flash-Decoding" §4 chunking), in whole 16-token tiles for a
+// paged cache (a tile must not straddle two pages).
+int resolve_split_len(int max_kv_len, int num_splits, int split_len, bool paged) {
+    if (num_splits < 1 || split_len != 0)
+        return split_len;
+    long long len = max_kv_len > 0 ? ((long long)max_kv_len + num_splits - 1) / num_splits : 1;
+    if (paged)
+        len = (len + 15) / 16 * 16;
+    return (int)(len < 0x7fffffffLL ? len : 0x7ffffff0LL);
 }
 
 int check_partition(int batch, int heads_q, int max_kv_len, int num_splits, int split_len) {
@@ -290,12 +309,19 @@ bool balanced_applies(int heads_q, int heads_kv, int max_kv_len, int head_dim, i
 
 int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim, int cus,
                   BalancedPlan *p) {
-    p->units = batch * heads_kv;
+    // slot indices (work-group + unit rank) and the combine's row grid
+    // (batch * heads_q) are 32-bit in the kernels
+    const long long units = (long long)batch * heads_kv;
     p->gsz = heads_q / heads_kv;
     p->waves = fd::split_mfma_balanced_waves(head_dim, p->gsz);
     if (p->waves < 1)
         return fail(FD_ERR_INVALID, "group of %d too large for the balanced plan", p->gsz);
-    p->num_wgs = cus * fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz) * kBalancedRounds;
+    const long long wgs =
+        (long long)cus * fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz) * kBalancedRounds;
+    if (units + wgs > 0x7fffffffLL || (long long)batch * heads_q > 0x7fffffffLL)
+        return fail(FD_ERR_INVALID, "batch * heads exceeds the launch limit of the balanced plan");
+    p->units = (int)units;
+    p->num_wgs = (int)wgs;
     // positions (units * max_kv_len) times work-groups must stay within int64
     if ((double)p->units * max_kv_len * p->num_wgs > 4.0e18)
         return fail(FD_ERR_INVALID, "batch * heads_kv * max_kv_len too large for the balanced plan");
@@ -329,13 +355,7 @@ int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim
                     num_splits, split_len);
     // explicit splits: checked before the device is asked for anything
     if (num_splits > 0) {
-        if (split_len == 0) {
-            long long len = max_kv_len > 0 ? ((long long)max_kv_len + num_splits - 1) / num_splits
-                                           : 1;
-            if (paged)  // whole 16-token tiles
-                len = (len + 15) / 16 * 16;
-            split_len = (int)(len < 0x7fffffffLL ? len : 0x7ffffff0LL);
-        }
+        split_len = resolve_split_len(max_kv_len, num_splits, split_len, paged);
         int rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
         if (rc != FD_OK)
             return rc;
@@ -546,6 +566,7 @@ int split_stage(const void *q, const void *k, const void *v, const int32_t *kv_l
                                 in_dtype, scale);
     if (rc != FD_OK)
         return rc;
+    split_len = resolve_split_len(max_kv_len, num_splits, split_len, pg != nullptr);
     rc = check_partition(batch, heads_q, max_kv_len, num_splits, split_len);
     if (rc != FD_OK)
         return rc;
@@ -883,11 +904,18 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
 namespace {
 
 // The whole decode step, contiguous (pg null) or paged K/V, as make_plan
-// decides it.
+// decides it; stages (FD_STAGE_*) selects the split launch, the combine
+// launch or both.
 int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_lens, int batch,
                 int heads_q, int heads_kv, int max_kv_len, int head_dim, int in_dtype,
                 int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
-                void *workspace, size_t workspace_bytes, void *stream, const Paging *pg) {
+                void *workspace, size_t workspace_bytes, void *stream, const Paging *pg,
+                int stages = FD_STAGE_SPLIT | FD_STAGE_COMBINE) {
+    if (stages < 1 || stages > (FD_STAGE_SPLIT | FD_STAGE_COMBINE))
+        return fail(FD_ERR_INVALID, "stages %d is not FD_STAGE_SPLIT, FD_STAGE_COMBINE or both",
+                    stages);
+    const bool run_split = (stages & FD_STAGE_SPLIT) != 0;
+    const bool run_combine = (stages & FD_STAGE_COMBINE) != 0;
     int rc = check_split_inputs(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim,
                                 in_dtype, scale);
     if (rc != FD_OK)
@@ -938,9 +966,15 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
         a.num_wgs = p.bal.num_wgs;
         a.tile_waves = p.bal.waves;
         a.unit_desc = reinterpret_cast<int *>(ws + p.bal.o_bytes + p.bal.lse_bytes);
-        rc = launch_split(a, in_dtype, st);
-        if (rc != FD_OK)
+#if FD_WG_CLOCKS
+        a.wg_clock = g_wg_clock_bytes >= (size_t)p.bal.num_wgs * 4 * sizeof(unsigned long long)
+                         ? g_wg_clock
+                         : nullptr;
+#endif
+        if (run_split && (rc = launch_split(a, in_dtype, st)) != FD_OK)
             return rc;
+        if (!run_combine)
+            return FD_OK;
         fd::SlotCombineArgs c{};
         c.o_slots = a.o_part;
         c.lse_slots = a.lse_part;
@@ -963,14 +997,15 @@ int decode_impl(const void *q, const void *k, const void *v, const int32_t *kv_l
         a.o = o;
         a.lse = lse;
         a.fused_waves = p.fused;
-        return launch_split(a, in_dtype, st);
+        return run_split ? launch_split(a, in_dtype, st) : FD_OK;
     default: {  // FD_ROUTE_SPLITS
         const size_t rows = (size_t)batch * heads_q * r.num_splits;
         a.o_part = reinterpret_cast<float *>(ws);
         a.lse_part = reinterpret_cast<float *>(ws + round256(rows * head_dim * sizeof(float)));
-        rc = launch_split(a, in_dtype, st);
-        if (rc != FD_OK)
+        if (run_split && (rc = launch_split(a, in_dtype, st)) != FD_OK)
             return rc;
+        if (!run_combine)
+            return FD_OK;
         e = fd::launch_combine(a.o_part, a.lse_part, batch * heads_q, r.num_splits, head_dim, o,
                                out_dtype, lse, st);
     }
@@ -991,6 +1026,28 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
     return decode_impl(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
                        out_dtype, scale, num_splits, split_len, o, lse, workspace,
                        workspace_bytes, stream, nullptr);
+}
+
+#if FD_WG_CLOCKS
+// Instrumented builds only (not part of fd.h): from now on the token-balanced
+// split kernel of fd_decode writes per-work-group stamps into buf (device
+// memory, 4 x 8 bytes per work-group, see SplitArgs::wg_clock) when it holds
+// that many bytes; buf NULL turns the stamps off.
+int fd_debug_wg_clocks(void *buf, size_t bytes) {
+    g_wg_clock = static_cast<unsigned long long *>(buf);
+    g_wg_clock_bytes = buf ? bytes : 0;
+    return FD_OK;
+}
+#endif
+
+int fd_decode_stages(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                     int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                     int in_dtype, int out_dtype, float scale, int num_splits, int split_len,
+                     void *o, float *lse, void *workspace, size_t workspace_bytes, int stages,
+                     void *stream) {
+    return decode_impl(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                       out_dtype, scale, num_splits, split_len, o, lse, workspace,
+                       workspace_bytes, stream, nullptr, stages);
 }
 
 int fd_decode_split_paged(const void *q, const void *k_pages, const void *v_pages,

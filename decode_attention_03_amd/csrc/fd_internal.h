@@ -6,6 +6,10 @@
 
 #include <cstdint>
 
+#ifndef FD_WG_CLOCKS
+#define FD_WG_CLOCKS 0
+#endif
+
 namespace fd {
 
 // Element type codes (same values as the FD_* codes of the public header).
@@ -99,6 +103,14 @@ struct SplitArgs {
     // split (and merge in LDS) when the grid has fewer work-groups than the
     // GPU has wave slots, e.g. one split per row.
     int valu_waves;
+#if FD_WG_CLOCKS
+    // Instrumented builds only (-DFD_WG_CLOCKS=1): the token-balanced kernel
+    // writes four 64-bit words per share w at wg_clock[4 w ..]: the constant
+    // 100 MHz clock at its start and at its end, (pieces << 32) | tokens
+    // (the K/V rows its pieces read, per KV head), and its block index.
+    // Null: no stamps.
+    unsigned long long *wg_clock;
+#endif
 };
 
 // VALU split kernel: one work-group (a.valu_waves waves) per (sequence, query

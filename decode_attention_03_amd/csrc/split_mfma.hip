@@ -733,6 +733,10 @@ __global__ __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(W > 4 || bal_two_per_simd<D, QT, W>() ? 2 : 1)))
 void split_mfma_balanced_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
+#if FD_WG_CLOCKS
+    const unsigned long long clk0 = (unsigned long long)wall_clock64();
+    unsigned long long clk_work = 0;  // (pieces << 32) | tokens
+#endif
     constexpr int SKB = bal_two_per_simd<D, QT, W>() ? 16
                         : W > 1                     ? wide_step_kb<W>()
                                                     : FD_MFMA_STEP_KB;
@@ -749,8 +753,26 @@ void split_mfma_balanced_kernel(SplitArgs a) {
                       : (int)blockIdx.x;
     const int G = a.heads_q / a.heads_kv;
     PieceCursor c;
+#if FD_WG_CLOCKS
+    // stamps of share w: start and end clocks, work, block index (thread 0,
+    // ordinary vector stores; w < num_wgs and the host sized the buffer)
+    auto stamp = [&] {
+        if (a.wg_clock && threadIdx.x == 0) {
+            const unsigned long long clk1 = (unsigned long long)wall_clock64();
+            a.wg_clock[4 * (size_t)w + 0] = clk0;
+            a.wg_clock[4 * (size_t)w + 1] = clk1;
+            a.wg_clock[4 * (size_t)w + 2] = clk_work;
+            a.wg_clock[4 * (size_t)w + 3] = blockIdx.x;
+        }
+    };
+    if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c)) {
+        stamp();
+        return;
+    }
+#else
     if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c))
         return;
+#endif
     int n = clamp_len(a.kv_lens, c.b, a.max_kv_len);  // tokens of the current sequence
     int ng = (n + kGranule - 1) / kGranule;            // and its granules
     while (true) {
@@ -770,6 +792,9 @@ void split_mfma_balanced_kernel(SplitArgs a) {
             const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
             mfma_piece<DT, D, PAGED, QT, (W > 1 ? wide_nt<QT>() : FD_MFMA_NT), SKB, W>(
                 a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
+#if FD_WG_CLOCKS
+            clk_work += (1ull << 32) + (unsigned long long)(t1 - t0);
+#endif
             if (lo == 0 && threadIdx.x == 0) {
                 const long long ustart = c.pos - c.t;  // the unit's first position
                 const int first = balanced_owner(ustart + kPieceCost, c.total, c.w_eff);
@@ -798,6 +823,9 @@ void split_mfma_balanced_kernel(SplitArgs a) {
             break;  // not reached: positions remain, so a non-empty unit follows
         ng = (n + kGranule - 1) / kGranule;
     }
+#if FD_WG_CLOCKS
+    stamp();
+#endif
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

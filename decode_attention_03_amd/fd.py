@@ -13,6 +13,7 @@ o [batch, heads_q, d]; lse float32 [batch, heads_q].
 from __future__ import annotations
 
 import ctypes
+import json
 import math
 import os
 import threading
@@ -21,6 +22,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfd.so")
+#: written beside libfd.so by the build: the hash of the sources it came from
+BUILD_RECORD = os.path.join(_PKG, "libfd.build.json")
 
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
@@ -30,9 +33,13 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 
 #: every symbol include/fd.h declares
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
-           "fd_decode_workspace_bytes", "fd_decode_plan", "fd_decode_split", "fd_decode_split_mlo", "fd_combine",
-           "fd_combine_mlo", "fd_decode", "fd_decode_split_paged", "fd_decode_paged",
-           "fd_cascade_workspace_bytes", "fd_decode_cascade")
+           "fd_decode_workspace_bytes", "fd_decode_plan", "fd_decode_split",
+           "fd_decode_split_mlo", "fd_combine", "fd_combine_mlo", "fd_decode", "fd_decode_stages",
+           "fd_decode_split_paged", "fd_decode_paged", "fd_cascade_workspace_bytes",
+           "fd_decode_cascade")
+
+#: fd_decode_stages' stage bits
+STAGE_SPLIT, STAGE_COMBINE = 1, 2
 
 #: fd_plan.route and fd_plan.kernel codes, by name
 ROUTES = ("direct", "fused", "splits", "balanced")
@@ -56,15 +63,37 @@ class FDError(RuntimeError):
         self.code = code
 
 
+def check_fresh(path: str | None = None, record: str | None = None) -> None:
+    """Raise unless the library at path (default LIB_PATH) was built from the
+    sources now in csrc/ and include/ (the build records their hash beside
+    it, at BUILD_RECORD)."""
+    from decode_attention_03_amd import build
+
+    path = LIB_PATH if path is None else path
+    record = BUILD_RECORD if record is None else record
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    try:
+        with open(record, encoding="utf-8") as f:
+            built = json.load(f).get("sources_sha256")
+    except (OSError, ValueError):
+        built = None
+    now = build.library_source_hash()
+    if built != now:
+        raise RuntimeError(f"{path} was not built from the current sources (built from "
+                           f"{built}, sources now {now}): rebuild it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+
+
 def library() -> ctypes.CDLL:
-    """Open libfd.so (once).  Raises if it has not been built."""
+    """Open libfd.so (once).  Raises if it has not been built, or was built
+    from other sources than the ones in the tree."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        check_fresh()
         lib = ctypes.CDLL(LIB_PATH)
         P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         IP = ctypes.POINTER(ctypes.c_int)
@@ -87,6 +116,9 @@ def library() -> ctypes.CDLL:
         lib.fd_combine_mlo.restype = I
         lib.fd_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, P]
         lib.fd_decode.restype = I
+        lib.fd_decode_stages.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, I,
+                                         P]
+        lib.fd_decode_stages.restype = I
         lib.fd_decode_split_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P,
                                               P, P]
         lib.fd_decode_split_paged.restype = I
@@ -130,10 +162,49 @@ def _stream(device: torch.device):
 
 
 def _on_device(name: str, t: torch.Tensor, device: torch.device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _buffer(name: str, t: torch.Tensor, device: torch.device, shape: tuple,
+            dtype: torch.dtype) -> None:
+    """A caller-supplied output buffer: on the device, contiguous, exactly
+    this shape and dtype (the kernels write all of it by raw pointer)."""
+    _on_device(name, t, device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)}")
+
+
+def _outputs(o, lse, return_lse: bool, shape: tuple, out_dtype, dev):
+    """o [batch, heads_q, d] in out_dtype and lse [batch, heads_q] float32:
+    allocated when not given, else checked."""
+    if out_dtype not in _CODES:
+        raise TypeError(f"unsupported output dtype {out_dtype}")
+    if o is None:
+        o = torch.empty(shape, dtype=out_dtype, device=dev)
+    else:
+        _buffer("o", o, dev, shape, out_dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(shape[:2], dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _buffer("lse", lse, dev, shape[:2], torch.float32)
+    return o, lse
+
+
+def _workspace(workspace, need: int, dev):
+    """The caller's workspace (any dtype; on the device and contiguous), or a
+    new one of `need` bytes; returns (tensor or None, its size in bytes)."""
+    if workspace is None:
+        if not need:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _on_device("workspace", workspace, dev)
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 def _shapes(q, k, v, kv_lens):
@@ -200,26 +271,40 @@ def decode_plan(batch: int, heads_q: int, heads_kv: int, max_kv_len: int, head_d
             "workspace_bytes": p.workspace_bytes}
 
 
+def _parts(names_shapes, given: dict, dev) -> list:
+    """Partial buffers (float32): allocated when not given, else checked."""
+    out = []
+    for name, shape in names_shapes:
+        t = given.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+        else:
+            _buffer(name, t, dev, shape, torch.float32)
+        out.append(t)
+    return out
+
+
+def _splits(num_splits: int) -> int:
+    num_splits = int(num_splits)
+    if num_splits < 1:
+        raise ValueError(f"num_splits must be >= 1, got {num_splits}")
+    return num_splits
+
+
 def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, scale=None,
                  o_part=None, lse_part=None):
-    """Split stage: returns (o_part [batch, Hq, B, d] f32, lse_part [batch, Hq, B] f32)."""
+    """Split stage: returns (o_part [batch, Hq, B, d] f32, lse_part [batch, Hq, B] f32).
+    split_len 0: the library's ceil(N / num_splits)."""
     batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
-    if split_len == 0:
-        split_len = max(1, -(-n_max // num_splits))
+    B = _splits(num_splits)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if o_part is None:
-        o_part = torch.empty((batch, heads_q, num_splits, d), dtype=torch.float32, device=q.device)
-    if lse_part is None:
-        lse_part = torch.empty((batch, heads_q, num_splits), dtype=torch.float32, device=q.device)
-    _on_device("o_part", o_part, q.device)
-    _on_device("lse_part", lse_part, q.device)
-    if (o_part.shape != (batch, heads_q, num_splits, d) or o_part.dtype != torch.float32
-            or lse_part.shape != (batch, heads_q, num_splits) or lse_part.dtype != torch.float32):
-        raise ValueError("o_part / lse_part have the wrong shape or dtype")
+    o_part, lse_part = _parts((("o_part", (batch, heads_q, B, d)),
+                               ("lse_part", (batch, heads_q, B))),
+                              {"o_part": o_part, "lse_part": lse_part}, q.device)
     with torch.cuda.device(q.device):  # launches go to the current device
         _check(library().fd_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
                                          heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
-                                         num_splits, split_len, _ptr(o_part), _ptr(lse_part),
+                                         B, int(split_len), _ptr(o_part), _ptr(lse_part),
                                          _stream(q.device)))
     return o_part, lse_part
 
@@ -229,50 +314,41 @@ def decode_split_mlo(q, k, v, kv_lens=None, *, num_splits: int, split_len: int =
     """Split stage, m/l/o format: returns (o_part [batch, Hq, B, d], m_part
     [batch, Hq, B], l_part [batch, Hq, B]), all float32."""
     batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
-    if split_len == 0:
-        split_len = max(1, -(-n_max // num_splits))
+    B = _splits(num_splits)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    shape = (batch, heads_q, num_splits)
-    if o_part is None:
-        o_part = torch.empty((*shape, d), dtype=torch.float32, device=q.device)
-    if m_part is None:
-        m_part = torch.empty(shape, dtype=torch.float32, device=q.device)
-    if l_part is None:
-        l_part = torch.empty(shape, dtype=torch.float32, device=q.device)
-    for name, t, want in (("o_part", o_part, (*shape, d)), ("m_part", m_part, shape),
-                          ("l_part", l_part, shape)):
-        _on_device(name, t, q.device)
-        if t.shape != want or t.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32 {want}")
+    shape = (batch, heads_q, B)
+    o_part, m_part, l_part = _parts((("o_part", (*shape, d)), ("m_part", shape),
+                                     ("l_part", shape)),
+                                    {"o_part": o_part, "m_part": m_part, "l_part": l_part},
+                                    q.device)
     with torch.cuda.device(q.device):  # launches go to the current device
         _check(library().fd_decode_split_mlo(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
                                              heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
-                                             num_splits, split_len, _ptr(o_part), _ptr(m_part),
+                                             B, int(split_len), _ptr(o_part), _ptr(m_part),
                                              _ptr(l_part), _stream(q.device)))
     return o_part, m_part, l_part
 
 
-def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return_lse=True):
-    """Combine stage, m/l/o format -> (o, lse)."""
-    if o_part.dim() != 4 or any(t.dtype != torch.float32 for t in (o_part, m_part, l_part)):
-        raise ValueError("o_part must be float32 [batch, Hq, B, d]; m_part, l_part float32 "
-                         "[batch, Hq, B]")
+def _partials_in(o_part, scalars: dict):
+    """Checks the inputs of a combine: o_part float32 [batch, Hq, B, d] and
+    each per-split scalar float32 [batch, Hq, B], all on one HIP device."""
+    if not isinstance(o_part, torch.Tensor) or o_part.dim() != 4 or o_part.dtype != torch.float32:
+        raise ValueError("o_part must be float32 [batch, Hq, B, d]")
     batch, heads_q, nb, d = o_part.shape
-    if m_part.shape != (batch, heads_q, nb) or l_part.shape != (batch, heads_q, nb):
-        raise ValueError("m_part / l_part shape does not match o_part")
     dev = o_part.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a HIP device")
-    for name, t in (("o_part", o_part), ("m_part", m_part), ("l_part", l_part)):
-        _on_device(name, t, dev)
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
-    _on_device("o", o, dev)
-    if lse is not None:
-        _on_device("lse", lse, dev)
+    _on_device("o_part", o_part, dev)
+    for name, t in scalars.items():
+        _buffer(name, t, dev, (batch, heads_q, nb), torch.float32)
+    return batch, heads_q, nb, d, dev
+
+
+def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return_lse=True):
+    """Combine stage, m/l/o format -> (o, lse)."""
+    batch, heads_q, nb, d, dev = _partials_in(o_part, {"m_part": m_part, "l_part": l_part})
+    o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
+                      out_dtype or (o.dtype if o is not None else torch.float32), dev)
     with torch.cuda.device(dev):  # launches go to the current device
         _check(library().fd_combine_mlo(_ptr(o_part), _ptr(m_part), _ptr(l_part), batch,
                                         heads_q, nb, d, _ptr(o), _code(o.dtype), _ptr(lse),
@@ -282,25 +358,9 @@ def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return
 
 def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True):
     """Combine stage: LSE merge over the split axis -> (o, lse)."""
-    if o_part.dim() != 4 or o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
-        raise ValueError("o_part must be float32 [batch, Hq, B, d], "
-                         "lse_part float32 [batch, Hq, B]")
-    batch, heads_q, nb, d = o_part.shape
-    if lse_part.shape != (batch, heads_q, nb):
-        raise ValueError("lse_part shape does not match o_part")
-    dev = o_part.device
-    if dev.type != "cuda":
-        raise ValueError("tensors must live on a HIP device")
-    _on_device("o_part", o_part, dev)
-    _on_device("lse_part", lse_part, dev)
-    out_dtype = out_dtype or torch.float32
-    if o is None:
-        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
-    _on_device("o", o, dev)
-    if lse is not None:
-        _on_device("lse", lse, dev)
+    batch, heads_q, nb, d, dev = _partials_in(o_part, {"lse_part": lse_part})
+    o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
+                      out_dtype or (o.dtype if o is not None else torch.float32), dev)
     with torch.cuda.device(dev):  # launches go to the current device
         _check(library().fd_combine(_ptr(o_part), _ptr(lse_part), batch, heads_q, nb, d, _ptr(o),
                                     _code(o.dtype), _ptr(lse), _stream(dev)))
@@ -308,41 +368,36 @@ def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True)
 
 
 def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len: int = 0,
-           out_dtype=None, return_lse: bool = True, workspace=None, o=None, lse=None):
+           out_dtype=None, return_lse: bool = True, workspace=None, o=None, lse=None,
+           stages: int = STAGE_SPLIT | STAGE_COMBINE):
     """Whole decode step (split + combine) -> (o, lse or None).
 
     num_splits 0 lets the library plan the partition (fixed splits from
     fd_choose_splits, or the token-balanced partition for ragged grouped-head
     batches).  workspace (any dtype, on the device) is allocated here when not
-    given and the plan needs one.
+    given and the plan needs one.  stages other than both bits calls
+    fd_decode_stages: the split launch alone (STAGE_SPLIT) or the combine
+    launch alone (STAGE_COMBINE, after a split call with the same arguments
+    and workspace).
     """
     batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out_dtype = out_dtype or q.dtype
     dev = q.device
-    if o is None:
-        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
+                      out_dtype or (o.dtype if o is not None else q.dtype), dev)
     with torch.cuda.device(dev):  # the plan depends on this device's compute units
         need = decode_workspace_bytes(batch, heads_q, heads_kv, n_max, d, q.dtype,
                                       kv_lens is not None, num_splits, split_len)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _on_device("o", o, dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q, heads_kv, n_max, d,
+            _code(q.dtype), _code(o.dtype), scale, num_splits, split_len, _ptr(o), _ptr(lse),
+            _ptr(workspace), ws_bytes)
     with torch.cuda.device(dev):  # launches go to the current device
-        _check(library().fd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q,
-                                   heads_kv, n_max, d, _code(q.dtype), _code(o.dtype), scale,
-                                   num_splits, split_len, _ptr(o), _ptr(lse), _ptr(workspace),
-                                   ws_bytes, _stream(dev)))
+        if stages == STAGE_SPLIT | STAGE_COMBINE:
+            _check(library().fd_decode(*args, _stream(dev)))
+        else:
+            _check(library().fd_decode_stages(*args, int(stages), _stream(dev)))
     return o, lse
-
-
-def _tile_split_len(n: int, num_splits: int) -> int:
-    """ceil(n / num_splits) rounded up to whole 16-token tiles (paged K/V needs it)."""
-    per = -(-n // num_splits)
-    return max(16, -(-per // 16) * 16)
 
 
 def _paged_shapes(q, k_pages, v_pages, block_table, kv_lens):
@@ -372,22 +427,19 @@ def _paged_shapes(q, k_pages, v_pages, block_table, kv_lens):
 
 def decode_split_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, num_splits: int,
                        split_len: int = 0, scale=None, o_part=None, lse_part=None):
-    """Split stage over a paged K/V cache -> (o_part, lse_part), as decode_split."""
+    """Split stage over a paged K/V cache -> (o_part, lse_part), as decode_split
+    (split_len 0: the library's ceil(N / num_splits) in whole 16-token tiles)."""
     batch, heads_q, heads_kv, ps, max_pages, num_pages, d = _paged_shapes(
         q, k_pages, v_pages, block_table, kv_lens)
-    if split_len == 0:
-        split_len = _tile_split_len(max_pages * ps, num_splits)
+    B = _splits(num_splits)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if o_part is None:
-        o_part = torch.empty((batch, heads_q, num_splits, d), dtype=torch.float32, device=q.device)
-    if lse_part is None:
-        lse_part = torch.empty((batch, heads_q, num_splits), dtype=torch.float32, device=q.device)
-    _on_device("o_part", o_part, q.device)
-    _on_device("lse_part", lse_part, q.device)
+    o_part, lse_part = _parts((("o_part", (batch, heads_q, B, d)),
+                               ("lse_part", (batch, heads_q, B))),
+                              {"o_part": o_part, "lse_part": lse_part}, q.device)
     with torch.cuda.device(q.device):  # launches go to the current device
         _check(library().fd_decode_split_paged(
             _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
-            heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), scale, num_splits, split_len,
+            heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), scale, B, int(split_len),
             _ptr(o_part), _ptr(lse_part), _stream(q.device)))
     return o_part, lse_part
 
@@ -399,19 +451,13 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, scale=None,
     batch, heads_q, heads_kv, ps, max_pages, num_pages, d = _paged_shapes(
         q, k_pages, v_pages, block_table, kv_lens)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out_dtype = out_dtype or q.dtype
     dev = q.device
-    if o is None:
-        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
+                      out_dtype or (o.dtype if o is not None else q.dtype), dev)
     with torch.cuda.device(dev):  # the plan depends on this device's compute units
         need = decode_workspace_bytes(batch, heads_q, heads_kv, max_pages * ps, d, q.dtype,
                                       kv_lens is not None, num_splits, split_len)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _on_device("o", o, dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     with torch.cuda.device(dev):  # launches go to the current device
         _check(library().fd_decode_paged(
             _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch,
@@ -460,18 +506,12 @@ def decode_cascade(q, k_prefix, v_prefix, k_suffix, v_suffix, suffix_lens=None, 
         if suffix_lens.dtype != torch.int32 or suffix_lens.shape != (batch,):
             raise ValueError("suffix_lens must be int32 [batch]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out_dtype = out_dtype or q.dtype
-    if o is None:
-        o = torch.empty((batch, heads_q, d), dtype=out_dtype, device=dev)
-    if lse is None and return_lse:
-        lse = torch.empty((batch, heads_q), dtype=torch.float32, device=dev)
+    o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
+                      out_dtype or (o.dtype if o is not None else q.dtype), dev)
     with torch.cuda.device(dev):  # the plan depends on this device's compute units
         need = cascade_workspace_bytes(batch, heads_q, heads_kv, prefix_len, max_suffix_len, d,
                                        q.dtype, suffix_lens is not None)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    _on_device("o", o, dev)
+    workspace, ws_bytes = _workspace(workspace, max(need, 16), dev)
     with torch.cuda.device(dev):  # launches go to the current device
         _check(library().fd_decode_cascade(
             _ptr(q), _ptr(k_prefix), _ptr(v_prefix), prefix_len, _ptr(k_suffix), _ptr(v_suffix),

@@ -267,12 +267,8 @@ def main() -> int:
                      f"{r['max_us']:.2f} | {100 * r['share']:.1f} % |")
     if split_rows:
         s = split_rows[0]
-        if roof["kernel"] == "split":
-            timed, what = s["avg_us"], "split kernel"
-        else:  # the plan's split stage has no entry point of its own: split + combine
-            comb = [r for r in stats if family_of(r["kernel"]) == "combine"]
-            timed = s["avg_us"] + (comb[0]["avg_us"] if comb else 0.0)
-            what = "split + combine kernels"
+        # bench.py times fd_decode's split stage alone (fd_decode_stages)
+        timed, what = s["avg_us"], "split kernel"
         lines += [
             "",
             f"bench.py (same command, not under the profiler): {what} {roof['kernel_us']} µs "

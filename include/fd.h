@@ -155,7 +155,9 @@ int fd_decode_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int hea
  *   o_part[b,h,i,:] = sum_j exp(s_j - m) V_j / l,
  *   lse_part[b,h,i] = m + log l      (m = max s_j, l = sum_j exp(s_j - m)),
  * and (0, -inf) for an empty range ([P3] §3.2.1 merge identity).
- * num_splits >= 1, split_len >= 1, num_splits * split_len >= max_kv_len. */
+ * num_splits >= 1; split_len == 0 means L = ceil(max_kv_len / num_splits)
+ * ([P2] §4 chunking), else split_len >= 1 with
+ * num_splits * split_len >= max_kv_len. */
 int fd_decode_split(const void *q, const void *k, const void *v, const int32_t *kv_lens,
                     int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
                     int in_dtype, float scale, int num_splits, int split_len, float *o_part,
@@ -227,6 +229,26 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
               int out_dtype, float scale, int num_splits, int split_len, void *o, float *lse,
               void *workspace, size_t workspace_bytes, void *stream);
 
+/* The two launches of fd_decode, one call each ([P1] §2.5: stage 1 writes
+ * the splits' partial results to a temporary buffer, stage 2 reduces them;
+ * [P2] §5 names the same split -> temporary buffer -> reduce structure).
+ * stages = FD_STAGE_SPLIT queues only the split launch, FD_STAGE_COMBINE only
+ * the combine launch, both bits the whole step (= fd_decode).  A combine
+ * call must follow a split call with the same arguments and workspace on the
+ * same stream (or after it has completed); in between the workspace holds
+ * the partial results in the plan's internal layout.  On the single-launch
+ * routes (FD_ROUTE_DIRECT, FD_ROUTE_FUSED) the split call writes o and lse
+ * and the combine call queues nothing.  Arguments and errors as fd_decode,
+ * plus FD_ERR_INVALID for stages outside {1, 2, 3}.  Lets a caller time or
+ * schedule the two kernels separately. */
+#define FD_STAGE_SPLIT 1
+#define FD_STAGE_COMBINE 2
+int fd_decode_stages(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                     int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                     int in_dtype, int out_dtype, float scale, int num_splits, int split_len,
+                     void *o, float *lse, void *workspace, size_t workspace_bytes, int stages,
+                     void *stream);
+
 /* Paged K/V cache ([P2] §5: the kernel follows a block table over
  * non-contiguous pages instead of gathering them first; [P4] §7.1: the page
  * offsets cost an index lookup).  Same operation as fd_decode_split /
@@ -242,8 +264,8 @@ int fd_decode(const void *q, const void *k, const void *v, const int32_t *kv_len
  * page_size) entries of a table row are read; an entry outside
  * [0, num_pages) is clamped into it (memory stays in bounds, that sequence's
  * result is then meaningless).  split_len must be a multiple of 16 (the
- * automatic plan's is; fd_decode_paged given num_splits > 0 and split_len ==
- * 0 rounds ceil(N / num_splits) up to one).  Workspace: fd_decode_workspace_bytes with max_kv_len
+ * automatic plan's is; given num_splits > 0 and split_len == 0, both paged
+ * calls round ceil(N / num_splits) up to one).  Workspace: fd_decode_workspace_bytes with max_kv_len
  * = max_pages_per_seq * page_size.  Extra errors: FD_ERR_INVALID for a null
  * block_table, max_pages_per_seq or num_pages < 1, or split_len % 16 != 0;
  * FD_ERR_UNSUPPORTED for page_size or page bytes out of range. */

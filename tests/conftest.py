@@ -28,5 +28,11 @@ def gpu():
         pytest.fail("GPU test selected but torch sees no GPU")
     from decode_attention_03_amd import fd
 
-    fd.library()  # raises if libfd.so is missing or fails to load
-    return torch.device("cuda:0")
+    dev = torch.device("cuda:0")
+    # the HIP runtime and the device context come up before any test draws
+    # inputs (the input generator runs a thread pool)
+    torch.cuda.init()
+    torch.empty(1, device=dev)
+    torch.cuda.synchronize(dev)
+    fd.library()  # raises if libfd.so is missing, stale or fails to load
+    return dev

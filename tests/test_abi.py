@@ -232,7 +232,11 @@ def test_decode_split_validation(lib):
     assert _split(lib, n=-1) == fd.ERR_INVALID
     assert _split(lib, hq=3) == fd.ERR_INVALID
     assert _split(lib, B=3) == fd.ERR_INVALID            # 3 * 16 < 64
-    assert _split(lib, L=0) == fd.ERR_INVALID
+    assert _split(lib, L=-1) == fd.ERR_INVALID
+    # L = 0: the library's ceil(64 / 3) = 22 passes the partition checks and
+    # the call stops at the next check
+    assert _split(lib, B=3, L=0, o_part=FAKE + 4) == fd.ERR_UNSUPPORTED
+    assert "aligned" in fd.last_error()
     assert _split(lib, B=0) == fd.ERR_INVALID
     assert _split(lib, B=9000, L=1) == fd.ERR_INVALID
     assert _split(lib, scale=float("nan")) == fd.ERR_INVALID
@@ -378,6 +382,24 @@ def test_decode_validation(lib):
     assert "workspace" in fd.last_error() or "aligned" in fd.last_error()
 
 
+def _stages(lib, stages, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kv_lens=None, batch=1, hq=4, hkv=2, n=64, d=64, dt=fd.BF16,
+             out=fd.BF16, scale=0.125, B=4, L=0, o=FAKE, lse=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.fd_decode_stages(a["q"], a["k"], a["v"], a["kv_lens"], a["batch"], a["hq"],
+                                a["hkv"], a["n"], a["d"], a["dt"], a["out"], a["scale"], a["B"],
+                                a["L"], a["o"], a["lse"], a["ws"], a["ws_bytes"], stages, None)
+
+
+def test_decode_stages_validation(lib):
+    for bad in (0, 4, -1):
+        assert _stages(lib, bad) == fd.ERR_INVALID
+        assert "stages" in fd.last_error()
+    for ok in (fd.STAGE_SPLIT, fd.STAGE_COMBINE, fd.STAGE_SPLIT | fd.STAGE_COMBINE):
+        assert _stages(lib, ok) == fd.ERR_WORKSPACE  # the same checks as fd_decode
+        assert _stages(lib, ok, o=None) == fd.ERR_INVALID
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     """No fallback: with libfd.so missing, the binding raises instead of
     computing anything some other way."""
@@ -407,3 +429,71 @@ def test_binding_rejects_host_tensors():
         fd.combine(torch.zeros(1, 4, 2, 64), torch.zeros(1, 4, 2))
     with pytest.raises(ValueError, match="HIP device"):
         fd.combine_mlo(torch.zeros(1, 4, 2, 64), torch.zeros(1, 4, 2), torch.zeros(1, 4, 2))
+
+
+def test_binding_checks_caller_buffers():
+    """Caller-supplied outputs, partials and workspaces are checked for
+    device, contiguity, exact shape and dtype before their pointers reach
+    the library (the checks run on whatever device the inputs are on, so the
+    CPU device stands in for the GPU here)."""
+    import torch
+
+    cpu, meta = torch.device("cpu"), torch.device("meta")
+    shape = (2, 4, 64)
+    o, lse = fd._outputs(None, None, True, shape, torch.bfloat16, cpu)
+    assert o.shape == shape and o.dtype == torch.bfloat16 and lse.shape == (2, 4)
+    assert fd._outputs(None, None, False, shape, torch.float32, cpu)[1] is None
+    bad_o = [torch.zeros(2, 4, 32, dtype=torch.bfloat16),            # shape
+             torch.zeros(shape, dtype=torch.float16),                # dtype
+             torch.zeros(shape, dtype=torch.bfloat16, device=meta),  # device
+             torch.zeros(2, 64, 4, dtype=torch.bfloat16).transpose(1, 2)]  # layout
+    for t in bad_o:
+        with pytest.raises(ValueError):
+            fd._outputs(t, None, True, shape, torch.bfloat16, cpu)
+    for t in (torch.zeros(2, 5), torch.zeros(2, 4, dtype=torch.float64),
+              torch.zeros(2, 4, device=meta), torch.zeros(4, 2).t()):
+        with pytest.raises(ValueError):
+            fd._outputs(None, t, True, shape, torch.bfloat16, cpu)
+    with pytest.raises(TypeError):
+        fd._outputs(None, None, True, shape, torch.int32, cpu)
+    # workspace: any dtype, on the device and contiguous
+    ws, n = fd._workspace(torch.zeros(10, dtype=torch.int32), 40, cpu)
+    assert n == 40
+    assert fd._workspace(None, 0, cpu) == (None, 0)
+    for t in (torch.zeros(64, device=meta), torch.zeros(8, 8)[:, 0]):
+        with pytest.raises(ValueError):
+            fd._workspace(t, 16, cpu)
+    # partial buffers of the split stage and the inputs of the combine
+    parts = fd._parts((("o_part", (2, 4, 3, 64)), ("lse_part", (2, 4, 3))), {}, cpu)
+    assert [tuple(t.shape) for t in parts] == [(2, 4, 3, 64), (2, 4, 3)]
+    with pytest.raises(ValueError):
+        fd._parts((("lse_part", (2, 4, 3)),), {"lse_part": torch.zeros(2, 4, 2)}, cpu)
+    with pytest.raises(ValueError):
+        fd._parts((("lse_part", (2, 4, 3)),), {"lse_part": torch.zeros(2, 4, 3).half()}, cpu)
+    with pytest.raises(ValueError):
+        fd.combine(torch.zeros(1, 4, 2, 64), torch.zeros(1, 4, 3))
+    with pytest.raises(ValueError):
+        fd.combine(torch.zeros(1, 4, 2, 64), torch.zeros(1, 4, 2, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        fd.decode_split(torch.zeros(1, 4, 64), torch.zeros(1, 16, 2, 64),
+                        torch.zeros(1, 16, 2, 64), num_splits=0)
+
+
+def test_stale_library_is_refused(monkeypatch, tmp_path):
+    """A library whose build record names other sources (or none) is not
+    loaded: every GPU run uses what the build compiled from these sources."""
+    import json
+
+    lib = tmp_path / "libfd.so"
+    lib.write_bytes(b"")
+    rec = tmp_path / "libfd.build.json"
+    rec.write_text(json.dumps({"sources_sha256": "0" * 16}))
+    with pytest.raises(RuntimeError, match="current sources"):
+        fd.check_fresh(str(lib), str(rec))
+    rec.write_text(json.dumps({"sources_sha256": None, "flags": ["-DX=1"]}))
+    with pytest.raises(RuntimeError, match="current sources"):
+        fd.check_fresh(str(lib), str(rec))
+    from decode_attention_03_amd import build
+
+    rec.write_text(json.dumps({"sources_sha256": build.library_source_hash()}))
+    fd.check_fresh(str(lib), str(rec))
