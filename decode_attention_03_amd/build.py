@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfd.so")
-SOURCES = ["fd_api.cpp", "split_valu.hip", "split_mfma.hip", "combine.hip"]
+SOURCES = ["fd_api.cpp", "split_valu.hip", "split_mfma.hip", "combine.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 #: the source files each kernel family is compiled from; a measurement taken

@@ -1050,6 +1050,30 @@ int fd_decode_stages(const void *q, const void *k, const void *v, const int32_t 
                        workspace_bytes, stream, nullptr, stages);
 }
 
+int fd_decode_noalloc(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                      int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                      int in_dtype, int out_dtype, float scale, int num_splits, int split_len,
+                      void *o, float *lse, void *stream) {
+    size_t need = 0;
+    int rc = fd_decode_workspace_bytes(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                                       kv_lens != nullptr, num_splits, split_len, &need);
+    if (rc != FD_OK)
+        return rc;
+    if (need > fd::kScratchBytes)
+        return fail(FD_ERR_WORKSPACE,
+                    "fd_decode_noalloc: this step needs %zu bytes of scratch, more than the "
+                    "library's %zu; call fd_decode with a workspace of that size instead",
+                    need, fd::kScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        hipError_t e = fd::scratch_buffer(&ws);
+        if (e != hipSuccess)
+            return fail(FD_ERR_HIP, "scratch buffer address: %s", hipGetErrorString(e));
+    }
+    return decode_impl(q, k, v, kv_lens, batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype,
+                       out_dtype, scale, num_splits, split_len, o, lse, ws, need, stream, nullptr);
+}
+
 int fd_decode_split_paged(const void *q, const void *k_pages, const void *v_pages,
                           const int32_t *block_table, const int32_t *kv_lens, int batch,
                           int heads_q, int heads_kv, int page_size, int max_pages_per_seq,

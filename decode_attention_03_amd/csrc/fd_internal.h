@@ -177,4 +177,12 @@ struct SlotCombineArgs {
 };
 hipError_t launch_combine_slots(const SlotCombineArgs &c, hipStream_t stream);
 
+// The library-owned scratch of fd_decode_noalloc (noalloc.hip): kScratchBytes
+// of device memory per device, 256-byte aligned, held until the process ends.
+// scratch_buffer returns its device address on the current device (looked up
+// once per device with hipGetSymbolAddress).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_buffer(void **ptr);
+
 }  // namespace fd

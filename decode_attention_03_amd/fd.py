@@ -35,8 +35,8 @@ _ERR_NAMES = {ERR_INVALID: "FD_ERR_INVALID", ERR_UNSUPPORTED: "FD_ERR_UNSUPPORTE
 EXPORTS = ("fd_version", "fd_last_error", "fd_choose_splits", "fd_workspace_bytes",
            "fd_decode_workspace_bytes", "fd_decode_plan", "fd_decode_split",
            "fd_decode_split_mlo", "fd_combine", "fd_combine_mlo", "fd_decode", "fd_decode_stages",
-           "fd_decode_split_paged", "fd_decode_paged", "fd_cascade_workspace_bytes",
-           "fd_decode_cascade")
+           "fd_decode_noalloc", "fd_decode_split_paged", "fd_decode_paged",
+           "fd_cascade_workspace_bytes", "fd_decode_cascade")
 
 #: fd_decode_stages' stage bits
 STAGE_SPLIT, STAGE_COMBINE = 1, 2
@@ -119,6 +119,8 @@ def library() -> ctypes.CDLL:
         lib.fd_decode_stages.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, I,
                                          P]
         lib.fd_decode_stages.restype = I
+        lib.fd_decode_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P]
+        lib.fd_decode_noalloc.restype = I
         lib.fd_decode_split_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P,
                                               P, P]
         lib.fd_decode_split_paged.restype = I
@@ -397,6 +399,26 @@ def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len:
             _check(library().fd_decode(*args, _stream(dev)))
         else:
             _check(library().fd_decode_stages(*args, int(stages), _stream(dev)))
+    return o, lse
+
+
+def decode_noalloc(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0,
+                   split_len: int = 0, out_dtype=None, return_lse: bool = True, o=None,
+                   lse=None):
+    """decode() through fd_decode_noalloc: the partials go to the library's own
+    32 MiB scratch per GPU instead of a workspace (nothing is allocated by the
+    library; o and lse are allocated here unless given).  Calls that overlap
+    on one GPU race on that scratch."""
+    batch, heads_q, heads_kv, n_max, d = _shapes(q, k, v, kv_lens)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dev = q.device
+    o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
+                      out_dtype or (o.dtype if o is not None else q.dtype), dev)
+    with torch.cuda.device(dev):  # launches go to the current device
+        _check(library().fd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
+                                           heads_q, heads_kv, n_max, d, _code(q.dtype),
+                                           _code(o.dtype), scale, num_splits, split_len, _ptr(o),
+                                           _ptr(lse), _stream(dev)))
     return o, lse
 
 

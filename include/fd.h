@@ -249,6 +249,23 @@ int fd_decode_stages(const void *q, const void *k, const void *v, const int32_t 
                      void *o, float *lse, void *workspace, size_t workspace_bytes, int stages,
                      void *stream);
 
+/* fd_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, plan, kernels and results as fd_decode, without the
+ * workspace arguments.  The partial results go to a scratch buffer the
+ * library owns: 32 MiB of device memory per GPU, a file-scope device array
+ * each GPU holds from the first such call until the process ends.  Steps
+ * whose plan needs more (fd_decode_workspace_bytes > 32 MiB) are refused
+ * with FD_ERR_WORKSPACE before anything is launched.  No call allocates or
+ * frees memory.  Every call on one GPU shares that GPU's buffer: calls that
+ * overlap on one GPU (other host threads, other streams) race, so callers
+ * serialise them (one stream, or their own ordering).  Nothing in the buffer
+ * needs clearing between calls. */
+int fd_decode_noalloc(const void *q, const void *k, const void *v, const int32_t *kv_lens,
+                      int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                      int in_dtype, int out_dtype, float scale, int num_splits, int split_len,
+                      void *o, float *lse, void *stream);
+
 /* Paged K/V cache ([P2] §5: the kernel follows a block table over
  * non-contiguous pages instead of gathering them first; [P4] §7.1: the page
  * offsets cost an index lookup).  Same operation as fd_decode_split /

@@ -391,6 +391,21 @@ def _stages(lib, stages, **kw):
                                 a["L"], a["o"], a["lse"], a["ws"], a["ws_bytes"], stages, None)
 
 
+def test_decode_noalloc_refuses_large_steps(lib):
+    """fd_decode_noalloc refuses a step whose plan needs more than the
+    library's 32 MiB scratch before any device call (here: 8192 one-token
+    splits of multi-query attention, 545 MB of partials)."""
+    rc = lib.fd_decode_noalloc(FAKE, FAKE, FAKE, None, 4, 64, 1, 8192, 64, fd.F16, fd.F16,
+                               0.125, 8192, 1, FAKE, None, None)
+    assert rc == fd.ERR_WORKSPACE
+    assert "scratch" in fd.last_error() and str(32 << 20) in fd.last_error()
+    # invalid arguments are reported as by fd_decode
+    assert lib.fd_decode_noalloc(FAKE, FAKE, FAKE, None, 1, 3, 2, 64, 64, fd.F16, fd.F16, 0.125,
+                                 0, 0, FAKE, None, None) == fd.ERR_INVALID
+    assert lib.fd_decode_noalloc(FAKE, FAKE, FAKE, None, 1, 4, 2, 64, 96, fd.F16, fd.F16, 0.125,
+                                 4, 0, FAKE, None, None) == fd.ERR_UNSUPPORTED
+
+
 def test_decode_stages_validation(lib):
     for bad in (0, 4, -1):
         assert _stages(lib, bad) == fd.ERR_INVALID

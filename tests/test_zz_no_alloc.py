@@ -1,0 +1,91 @@
+"""fd_decode_noalloc: fd_decode with the library's own scratch buffer in
+place of a caller workspace, for callers that cannot allocate.
+
+Each call is checked through the C ABI against fd_decode on the same inputs
+(the same plan and kernels, so the outputs must be bit-identical) and
+against the fp64 oracle at the usual bounds; calls follow each other with
+different shapes and routes, the later ones smaller, so a call must not
+depend on what the one before left in the shared scratch.  A step whose plan
+needs more scratch than the library holds is refused before any launch."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_03_amd import fd, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (1.5e-2, 1e-3), "bf16": (1.5e-2, 1e-3)}
+SCRATCH_BYTES = 32 << 20
+
+
+def _run_pair(dev, w, num_splits=0, check_oracle=True):
+    inp = workloads.generate(w)
+    lens = inp["kv_lens"]
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    kl = None if lens is None else lens.to(dev)
+    need = fd.decode_workspace_bytes(w.batch, w.heads_q, w.heads_kv, inp["max_kv_len"],
+                                     w.head_dim, q.dtype, kl is not None, num_splits)
+    assert need <= SCRATCH_BYTES
+    o_ref, lse_ref = fd.decode(q, k, v, kl, num_splits=num_splits, scale=w.scale)
+    o = torch.full_like(o_ref, float("nan"))
+    lse = torch.full_like(lse_ref, float("nan"))
+    fd.decode_noalloc(q, k, v, kl, num_splits=num_splits, scale=w.scale, o=o, lse=lse)
+    torch.cuda.synchronize()
+    bits = torch.int32 if o.dtype == torch.float32 else torch.int16
+    assert torch.equal(o.view(bits), o_ref.view(bits)), w.name
+    assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), w.name
+    if check_oracle:
+        ro, rl = oracle.attention(w.dtype, workloads.raw(inp["q"]), workloads.raw(inp["k"]),
+                                  workloads.raw(inp["v"]), None if lens is None else lens.numpy(),
+                                  scale=w.scale)
+        go = o.float().cpu().double().numpy().reshape(ro.shape)
+        gl = lse.cpu().double().numpy().reshape(rl.shape)
+        tol_o, tol_l = TOL[w.dtype]
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+        assert np.abs(go - ro).max() <= tol_o
+        assert (np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0) <= tol_l
+    return need
+
+
+def test_noalloc_matches_decode_on_successive_calls(gpu):
+    # 1: the ragged grouped-query workload at full size (token-balanced plan,
+    # the largest scratch use of the named workloads)
+    n1 = _run_pair(gpu, workloads.WORKLOADS[4], check_oracle=False)
+    # 2: a smaller ragged grouped batch (same route, fewer slots), oracle-checked
+    w2 = workloads.Workload("na_bal", 5, 32, 4, 128, 6000, "bf16", "bf16", 41, ragged=(0, 6000))
+    n2 = _run_pair(gpu, w2)
+    # 3: smaller still: fixed splits of the vector kernel plus the plain combine
+    w3 = workloads.Workload("na_splits", 1, 8, 8, 64, 9000, "f16", "f16", 42)
+    n3 = _run_pair(gpu, w3)
+    assert n1 > n2 > n3 > 0
+    # 4: no scratch at all (one split per row), then a scratch user again
+    w4 = workloads.Workload("na_direct", 4, 64, 64, 128, 1024, "bf16", "bf16", 43)
+    assert _run_pair(gpu, w4) == 0
+    w5 = workloads.Workload("na_grouped", 2, 16, 2, 256, 3000, "f16", "f16", 44)
+    assert _run_pair(gpu, w5) > 0
+
+
+def test_noalloc_refuses_steps_beyond_the_scratch(gpu):
+    """Multi-query attention with 64 query heads, 4 sequences of 8192 tokens
+    and 8192 fixed splits of one token needs 545 MB of partials: refused with
+    FD_ERR_WORKSPACE before anything is launched (the buffers below are the
+    step's true sizes, so nothing could be read out of bounds either way)."""
+    lib = fd.library()
+    batch, hq, hkv, n, d, B = 4, 64, 1, 8192, 64, 8192
+    need = lib.fd_workspace_bytes(batch, hq, B, d)
+    assert need > SCRATCH_BYTES
+    q = torch.zeros(batch, hq, d, dtype=torch.float16, device=gpu)
+    k = torch.zeros(batch, n, hkv, d, dtype=torch.float16, device=gpu)
+    o = torch.empty(batch, hq, d, dtype=torch.float16, device=gpu)
+    P = ctypes.c_void_p
+    rc = lib.fd_decode_noalloc(P(q.data_ptr()), P(k.data_ptr()), P(k.data_ptr()), None, batch,
+                               hq, hkv, n, d, fd.F16, fd.F16, 0.125, B, 1, P(o.data_ptr()),
+                               None, None)
+    assert rc == fd.ERR_WORKSPACE
+    assert "scratch" in fd.last_error()
+    torch.cuda.synchronize()
