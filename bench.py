@@ -660,7 +660,16 @@ def main() -> int:
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups"), default=None,
                     help="time only this section of the full run and print its JSON (profiling)")
+    ap.add_argument("--library", default=None,
+                    help="time a tuning variant (decode_attention_03_amd/variants/NAME.so, built "
+                         "with python -m decode_attention_03_amd.build NAME -DKNOB=value) "
+                         "instead of libfd.so; the JSON line names it")
     args = ap.parse_args()
+    variant = None
+    if args.library:
+        rec = fd.use_variant(os.path.abspath(args.library))
+        variant = {"path": os.path.relpath(os.path.abspath(args.library), ROOT),
+                   "flags": rec.get("flags")}
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -699,7 +708,8 @@ def main() -> int:
         else:  # the paged step of the ragged grouped workload, 16-token pages
             w = workloads.WORKLOADS[4]
             sec = {"workload": w.name, **time_paged(w, dev, 16, args.steps, args.warmup)}
-        print(json.dumps({"section": args.section, **sec}), flush=True)
+        print(json.dumps({"section": args.section, "library_variant": variant, **sec}),
+              flush=True)
         return 0
 
     head = workloads.WORKLOADS[args.config]
@@ -748,6 +758,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if variant is not None:  # never the product library: say which build was timed
+        result["library_variant"] = variant
     p.free()
     del p
     torch.cuda.empty_cache()

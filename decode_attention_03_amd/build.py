@@ -26,9 +26,11 @@ ARCH = "gfx950"
 #: the source files each kernel family is compiled from; a measurement taken
 #: on a kernel stays valid while these files are unchanged
 KERNEL_SOURCES = {
-    "split_valu": ["split_valu.hip", "dev_common.h", "fd_internal.h"],
-    "split_mfma": ["split_mfma.hip", "partition.h", "dev_common.h", "fd_internal.h"],
-    "combine": ["combine.hip", "partition.h", "dev_common.h", "fd_internal.h"],
+    "split_valu": ["split_valu.hip", "dev_common.h", "fd_internal.h", "mfma_policy.h"],
+    "split_mfma": ["split_mfma.hip", "partition.h", "partition_plan.h", "dev_common.h",
+                   "fd_internal.h", "mfma_policy.h"],
+    "combine": ["combine.hip", "partition.h", "partition_plan.h", "dev_common.h",
+                "fd_internal.h", "mfma_policy.h"],
 }
 
 
@@ -95,12 +97,22 @@ def _compile(src: str, extra: list[str], objdir: str) -> str:
     return obj
 
 
+def record_path(lib_path: str) -> str:
+    """The build record beside a library: libX.so -> libX.build.json."""
+    base = lib_path[:-3] if lib_path.endswith(".so") else lib_path
+    return base + ".build.json"
+
+
+#: tuning variants (built with extra -D flags) live here, one .so each
+VARIANTS = os.path.join(PKG, "variants")
+
+
 def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str = LIB) -> str:
-    """Compile and link the library to `out`.  Only the plain build (no
-    extra flags, at LIB) records its sources' hash beside it, which is what
-    fd.library() checks before loading; a build with extra flags (a tuning
-    or instrumented variant) goes to its own object folder and, at LIB,
-    leaves a record that no source hash matches."""
+    """Compile and link the library to `out` and record beside it the hash of
+    the sources and the extra flags it was built with (fd.library() loads
+    the product library only if it was built from the current sources with
+    no extra flags).  A build with extra flags (a tuning or instrumented
+    variant) compiles into its own object folder."""
     extra = list(extra_flags or [])
     tag = hashlib.sha256(" ".join(extra).encode()).hexdigest()[:8] if extra else ""
     objdir = os.path.join(BUILD, tag) if tag else BUILD
@@ -119,15 +131,25 @@ def build(extra_flags: list[str] | None = None, verbose: bool = True, out: str =
 
     ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
     os.replace(tmp, out)
-    if os.path.abspath(out) == os.path.abspath(LIB):
-        record = {"sources_sha256": None if extra else sources, "flags": extra}
-        with open(RECORD + ".tmp", "w", encoding="utf-8") as f:
-            json.dump(record, f)
-        os.replace(RECORD + ".tmp", RECORD)
+    rec_path = record_path(out)
+    with open(rec_path + ".tmp", "w", encoding="utf-8") as f:
+        json.dump({"sources_sha256": sources, "flags": extra}, f)
+    os.replace(rec_path + ".tmp", rec_path)
     if verbose:
         print(f"built {out}")
     return out
 
 
+def build_variant(name: str, flags: list[str]) -> str:
+    """A tuning variant: the library built with `flags` (build-time knobs,
+    -DNAME=value) at variants/<name>.so, for bench.py --library."""
+    os.makedirs(VARIANTS, exist_ok=True)
+    return build(extra_flags=flags, out=os.path.join(VARIANTS, f"{name}.so"))
+
+
 if __name__ == "__main__":
-    build()
+    # python -m decode_attention_03_amd.build [NAME -DKNOB=value ...]
+    if len(sys.argv) > 2:
+        build_variant(sys.argv[1], sys.argv[2:])
+    else:
+        build()

@@ -8,7 +8,7 @@
 //        (mini-vllm-tutorial.vercel.app)
 //   [P3] "FlashDecoding 数学推导：传统 m/l/o 方法与 LSE 方法"
 //        (my-webpage-adu.pages.dev, 2026-07-16)
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdarg>

@@ -2,7 +2,7 @@
 // of libfd (not installed, not part of the C ABI).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstdint>
 
@@ -122,29 +122,9 @@ hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t strea
 // MFMA split kernels for grouped heads (bf16/f16): one work-group per
 // (sequence, KV head, split) computing all G <= 16 query rows of the group in
 // one tile; with tile_qt set, the tiled kernel (16-query tiles, several
-// work-groups per unit).
-bool split_mfma_supported(int in_dtype, int head_dim, int group);
-// The tiled kernel: any group size (per sequence: groups larger than one
-// tile; shared prefix: any).
-bool split_mfma_tiled_supported(int in_dtype, int head_dim);
-int split_mfma_tile_max_qt(int head_dim);  // query tiles per wave, 1..4
-// Most waves a tiled work-group can have at this head size (each loads an
-// equal share of every staged step's row groups): 8 at d <= 128 (one tile
-// per wave, two waves per SIMD), 4 at d = 256.
-int split_mfma_tile_max_waves(int head_dim);
-// Query tiles per wave when a work-group has several waves (1 or 2).
-int split_mfma_wide_qt(int head_dim);
-// Whether the tiled kernel spreads a group's tiles one per wave while the
-// waves cover it (else each wave takes as many tiles as it holds).
-bool split_mfma_tile_spread();
-// Resident tiled work-groups per CU with this many waves each.
-int split_mfma_tiled_wg_per_cu(int waves);
-// Largest group the token-balanced kernel takes (all of a unit's query tiles
-// in one work-group), the waves of its work-groups for a group size (0: too
-// large), and its resident work-groups per CU with that many waves.
-int split_mfma_balanced_max_group(int head_dim);
-int split_mfma_balanced_waves(int head_dim, int group);
-int split_mfma_balanced_wg_per_cu(int head_dim, int group);
+// work-groups per unit); with balanced set, the token-balanced kernel.  Which
+// one serves a group, and in what shape, is decided by the functions of
+// mfma_policy.h (included below).
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream);
 
 // LSE merge of num_splits partials for `rows` = batch * heads_q rows.
@@ -186,3 +166,5 @@ constexpr int kMaxDevices = 64;
 hipError_t scratch_buffer(void **ptr);
 
 }  // namespace fd
+
+#include "mfma_policy.h"

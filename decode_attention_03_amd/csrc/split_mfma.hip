@@ -73,7 +73,6 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxGroup = 16;    // query heads per KV head one wave can hold
 [[maybe_unused]] constexpr float kRescaleGap = 8.f;  // log2 units the running max may lag
 
 template <int DT>
@@ -157,9 +156,6 @@ typedef __attribute__((address_space(3))) char lds_char;
 #ifndef FD_PREFIX_STEP_KB
 #define FD_PREFIX_STEP_KB 16
 #endif
-#ifndef FD_PREFIX_QT128
-#define FD_PREFIX_QT128 2
-#endif
 constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the tiled kernel
 // Work-groups of several waves (tiled and token-balanced kernels): K/V bytes
 // per step, shared by the waves (0: 8 KB per wave); non-temporal loads (1),
@@ -172,12 +168,17 @@ constexpr int kPrefixStepKB = FD_PREFIX_STEP_KB;  // K/V bytes per step of the t
 #ifndef FD_WIDE_NT
 #define FD_WIDE_NT -1
 #endif
-#ifndef FD_BAL_SPREAD
-#define FD_BAL_SPREAD 1  // balanced plan: one query tile per wave while the waves cover the group
+// Work-groups of several waves: register sets of K/V loads in flight per wave
+// (2: the next two steps; more keeps deeper pipelines of loads going while
+// the waves wait for each other at every step's barrier).  Contiguous K/V at
+// d <= 128 only; paged K/V and d = 256 keep two.
+#ifndef FD_WIDE_SETS
+#define FD_WIDE_SETS 2
 #endif
-#ifndef FD_TILE_SPREAD
-#define FD_TILE_SPREAD 1  // tiled kernel: one query tile per wave while the waves cover the group
-#endif
+template <int D, bool PAGED, int W>
+constexpr int wide_sets() {
+    return (W > 1 && !PAGED && D <= 128) ? FD_WIDE_SETS : 2;
+}
 #ifndef FD_MFMA_NT
 #define FD_MFMA_NT 1  // one-wave grouped kernels: non-temporal K/V loads
 #endif
@@ -194,7 +195,7 @@ constexpr int wide_step_kb() {
 // fixed splits the same change was slower).
 template <int D, int QT, int W>
 constexpr bool bal_two_per_simd() {
-    return W == 4 && QT == 1 && D <= 128;
+    return fd::bal_two_per_simd(D, QT, W);
 }
 template <int QT>
 constexpr int wide_nt() {
@@ -245,7 +246,7 @@ struct QMap {
 // writes (0, -inf).  (Device pass only: the body uses LDS address-space
 // pointers and gfx950-only builtins that the host pass cannot type.)
 template <int DT, int D, bool PAGED, int QT, int NTLOAD = 1, int STEP_KB = FD_MFMA_STEP_KB,
-          int W = 1>
+          int W = 1, int NS = 2>
 __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const tb, int b, int kvh,
                                            long t0, long t1, const QMap &qm,
                                            const PieceOut &out) {
@@ -528,6 +529,37 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
         // one wave's LDS operations execute in order, so a step's writes
         // follow the previous step's reads.
         Frags f;
+        if constexpr (NS > 2) {
+            // NS register sets (contiguous K/V, d <= 128): steps 0 .. NS - 1
+            // go out first; step st is staged from set st % NS, which is then
+            // refilled with step st + NS, so NS - 1 to NS steps of loads stay
+            // in flight while a step is computed.  LDS still alternates two
+            // buffers by step parity, with the same barrier rule as below.
+            static_assert(!PAGED && D <= 128, "deeper load pipelines: contiguous K/V, d <= 128");
+            Stage g[NS];
+            Pages none;
+#pragma unroll
+            for (int i = 0; i < NS; ++i)
+                if (i < nsteps)
+                    load_step(i, none, g[i]);
+            for (int base = 0; base < nsteps; base += NS) {
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    const int st = base + j;
+                    if (st >= nsteps)
+                        break;
+                    lds_char *const buf = (st & 1) ? b1 : b0;
+                    stage(g[j], buf);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (st + NS < nsteps)
+                        load_step(st + NS, none, g[j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    wg_sync();
+                    fetch(buf, f);
+                    compute_step(st, f);
+                }
+            }
+        } else {
         Stage ga, gb;
         Pages pa, pb;
         const int npairs = nsteps >> 1;
@@ -585,6 +617,7 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             fetch(b0, f);
             compute_step(nsteps - 1, f);
         }
+        }  // NS == 2
     }
 
 #pragma unroll
@@ -718,7 +751,8 @@ void split_mfma_tiled_kernel(SplitArgs a) {
         out.l = a.m_part ? a.l_part : nullptr;
     }
     constexpr int NTL = W > 1 ? wide_nt<QT>() : 0;
-    mfma_piece<DT, D, PAGED, QT, NTL, SKB, W>(a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
+    mfma_piece<DT, D, PAGED, QT, NTL, SKB, W, wide_sets<D, PAGED, W>()>(
+        a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -742,15 +776,9 @@ void split_mfma_balanced_kernel(SplitArgs a) {
                                                     : FD_MFMA_STEP_KB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
     const int wv = W > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
-    // Share index.  When the KV heads come in multiples of the 8 XCDs (which
-    // take work-groups round-robin), neighbouring work-groups take the same
-    // token range of consecutive heads, so each XCD streams whole heads, as
-    // it does under fixed splits; measured 1.2 us faster per step on 8 KV heads
-    // and 0.7 us slower on 2, where the plain order stays.
-    const int w = a.heads_kv % 8 == 0 && a.num_wgs % a.heads_kv == 0
-                      ? (int)(blockIdx.x % a.heads_kv) * (a.num_wgs / a.heads_kv) +
-                            (int)(blockIdx.x / a.heads_kv)
-                      : (int)blockIdx.x;
+    // share index (partition_plan.h: neighbouring work-groups take consecutive
+    // heads of one token range when the KV heads come in multiples of 8)
+    const int w = share_index((int)blockIdx.x, a.heads_kv, a.num_wgs);
     const int G = a.heads_q / a.heads_kv;
     PieceCursor c;
 #if FD_WG_CLOCKS
@@ -773,56 +801,22 @@ void split_mfma_balanced_kernel(SplitArgs a) {
     if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c))
         return;
 #endif
-    int n = clamp_len(a.kv_lens, c.b, a.max_kv_len);  // tokens of the current sequence
-    int ng = (n + kGranule - 1) / kGranule;            // and its granules
-    while (true) {
-        // this work-group covers positions [c.t, c.t + avail) of unit (c.b, c.x),
-        // whose granule j is position kPieceCost + j
-        const long long left = c.end - c.pos;
-        const int ucost = ng + kPieceCost;
-        const int avail = left < (long long)(ucost - c.t) ? (int)left : ucost - c.t;
-        const int lo = c.t > kPieceCost ? c.t - kPieceCost : 0;                     // granules
-        const int hi = c.t + avail - kPieceCost < ng ? c.t + avail - kPieceCost : ng;
-        if (hi > lo) {
-            const int slot = w + c.rank;
-            const QMap qm{c.b * a.heads_q + c.x * G, G, 0, wv * QT, a.heads_q, c.x};
-            const PieceOut out{a.o_part + (size_t)slot * G * D, a.lse_part + (size_t)slot * G,
-                               nullptr, 1, 0, true};
-            const long t0 = (long)lo * kGranule;
-            const long t1 = (long)hi * kGranule < n ? (long)hi * kGranule : n;
-            mfma_piece<DT, D, PAGED, QT, (W > 1 ? wide_nt<QT>() : FD_MFMA_NT), SKB, W>(
-                a, (lds_char *)tile_buf, c.b, c.x, t0, t1, qm, out);
-#if FD_WG_CLOCKS
-            clk_work += (1ull << 32) + (unsigned long long)(t1 - t0);
-#endif
-            if (lo == 0 && threadIdx.x == 0) {
-                const long long ustart = c.pos - c.t;  // the unit's first position
-                const int first = balanced_owner(ustart + kPieceCost, c.total, c.w_eff);
-                const int last = balanced_owner(ustart + kPieceCost + ng - 1, c.total, c.w_eff);
-                const size_t u = (size_t)c.b * a.heads_kv + c.x;
-                a.unit_desc[2 * u] = slot;  // this work-group owns granule 0: first == w
-                a.unit_desc[2 * u + 1] = last - first + 1;
-            }
+    walk_share(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, c, [&](const Piece &p) {
+        const QMap qm{p.b * a.heads_q + p.x * G, G, 0, wv * QT, a.heads_q, p.x};
+        const PieceOut out{a.o_part + (size_t)p.slot * G * D, a.lse_part + (size_t)p.slot * G,
+                           nullptr, 1, 0, true};
+        mfma_piece<DT, D, PAGED, QT, (W > 1 ? wide_nt<QT>() : FD_MFMA_NT), SKB, W,
+                   wide_sets<D, PAGED, W>()>(a, (lds_char *)tile_buf, p.b, p.x, p.t0, p.t1, qm,
+                                             out);
+        if (p.first && threadIdx.x == 0) {  // the unit's descriptor {first slot, count}
+            const size_t u = (size_t)p.b * a.heads_kv + p.x;
+            a.unit_desc[2 * u] = p.slot;
+            a.unit_desc[2 * u + 1] = p.desc_count;
         }
-        c.pos += avail;
-        if (c.pos >= c.end)
-            break;
-        // next unit: the next non-empty sequence of this KV head, else the
-        // first one of the next KV head
-        c.t = 0;
-        ++c.rank;
-        do {
-            if (++c.b == a.batch) {
-                c.b = 0;
-                if (++c.x == a.heads_kv)
-                    break;
-            }
-            n = clamp_len(a.kv_lens, c.b, a.max_kv_len);
-        } while (n == 0);
-        if (c.x == a.heads_kv)
-            break;  // not reached: positions remain, so a non-empty unit follows
-        ng = (n + kGranule - 1) / kGranule;
-    }
+#if FD_WG_CLOCKS
+        clk_work += (1ull << 32) + (unsigned long long)(p.t1 - p.t0);
+#endif
+    });
 #if FD_WG_CLOCKS
     stamp();
 #endif
@@ -843,38 +837,6 @@ int lds_per_cu_mfma() {
         cached[dev].store(v, std::memory_order_relaxed);
     }
     return v > 0 ? v : 0;
-}
-
-// Query tiles per wave of a one-wave tiled work-group that fit in the
-// register file without spilling next to 16 KB steps (every tile keeps its
-// own Q fragments, O accumulators and softmax state).  Four tiles fit at
-// d = 128 with 8 KB steps, but measured slower: the smaller steps and the
-// shorter splits that the fewer work-groups need cost more than the halved
-// re-reads save.
-template <int D>
-constexpr int tile_max_qt() {
-    return D == 64 ? 4 : (D == 128 ? FD_PREFIX_QT128 : 1);
-}
-
-// Query tiles per wave in multi-wave work-groups and in the token-balanced
-// kernel: at most two (four tiles on one wave, at d = 64, measured slower in
-// the balanced kernel than the tiled kernel's fixed splits, and with four
-// waves they spill).
-template <int D>
-constexpr int wide_qt() {
-    return tile_max_qt<D>() < 2 ? tile_max_qt<D>() : 2;
-}
-
-// Waves of a multi-wave work-group: up to 4 at every head size (each loads
-// an equal share of every staged step's row groups), capped by
-// FD_TILE_MAX_WAVES.
-#ifndef FD_TILE_MAX_WAVES
-#define FD_TILE_MAX_WAVES 8
-#endif
-template <int D>
-constexpr int tile_max_waves() {
-    constexpr int w = D <= 128 ? 8 : 4;  // eight: one tile per wave, two waves per SIMD
-    return w < FD_TILE_MAX_WAVES ? w : FD_TILE_MAX_WAVES;
 }
 
 // The tiled kernel for QT query tiles per wave and W waves, paged or
@@ -1031,105 +993,6 @@ hipError_t launch_dt(const SplitArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
-
-int split_mfma_tile_max_qt(int head_dim) {
-    switch (head_dim) {
-    case 64: return tile_max_qt<64>();
-    case 128: return tile_max_qt<128>();
-    case 256: return tile_max_qt<256>();
-    default: return 0;
-    }
-}
-
-int split_mfma_wide_qt(int head_dim) {
-    switch (head_dim) {
-    case 64: return wide_qt<64>();
-    case 128: return wide_qt<128>();
-    case 256: return wide_qt<256>();
-    default: return 1;
-    }
-}
-
-int split_mfma_tiled_wg_per_cu(int waves) {
-    if (waves <= 1)
-        return kPrefixWgPerCU;
-    const int n = kPrefixWgPerCU / waves;  // one wave per SIMD
-    return n > 1 ? n : 1;
-}
-
-bool split_mfma_tile_spread() { return FD_TILE_SPREAD != 0; }
-
-int split_mfma_tile_max_waves(int head_dim) {
-    switch (head_dim) {
-    case 64: return tile_max_waves<64>();
-    case 128: return tile_max_waves<128>();
-    case 256: return tile_max_waves<256>();
-    default: return 1;
-    }
-}
-
-int split_mfma_balanced_wg_per_cu(int head_dim, int group) {
-    const int waves = split_mfma_balanced_waves(head_dim, group);
-    if (waves <= 1)
-        return kMfmaWgPerCU;
-    if (waves == 4 && head_dim <= 128 && (group + 15) / 16 <= waves)
-        return 2;  // bal_two_per_simd
-    const int n = kPrefixWgPerCU / waves;  // one wave per SIMD
-    return n > 1 ? n : 1;
-}
-
-// Up to two tiles per wave (with four, 64 heads at d = 64, one wave's pieces
-// were bound by their arithmetic: the tiled kernel's fixed splits measured
-// 5 % faster on a ragged batch), on up to the most waves the head size allows.
-// Most tiles a multi-wave work-group holds: qt per wave on up to four waves,
-// or one per wave on more.
-constexpr int max_tiles_per_wg(int qt, int wmax) {
-    return qt * (wmax < 4 ? wmax : 4) > wmax ? qt * (wmax < 4 ? wmax : 4) : wmax;
-}
-
-int split_mfma_balanced_max_group(int head_dim) {
-    switch (head_dim) {
-    case 64: return 16 * max_tiles_per_wg(wide_qt<64>(), tile_max_waves<64>());
-    case 128: return 16 * max_tiles_per_wg(wide_qt<128>(), tile_max_waves<128>());
-    case 256: return 16 * max_tiles_per_wg(wide_qt<256>(), tile_max_waves<256>());
-    default: return 0;
-    }
-}
-
-int split_mfma_balanced_waves(int head_dim, int group) {
-    const int tiles = (group + 15) / 16;
-    int qt = 0, wmax = 1;
-    switch (head_dim) {
-    case 64: qt = wide_qt<64>(); wmax = tile_max_waves<64>(); break;
-    case 128: qt = wide_qt<128>(); wmax = tile_max_waves<128>(); break;
-    case 256: qt = wide_qt<256>(); wmax = tile_max_waves<256>(); break;
-    default: return 0;
-    }
-    if (tiles <= 1)
-        return 1;
-    int w = 2;
-    if (FD_BAL_SPREAD && tiles <= wmax) {  // one tile on each of w waves
-        while (w < tiles)
-            w *= 2;
-        return w;
-    }
-    if (tiles <= qt)
-        return 1;
-    const int wq = wmax < 4 ? wmax : 4;  // more than four waves hold one tile each
-    while (w < wq && qt * w < tiles)
-        w *= 2;
-    return qt * w >= tiles ? w : 0;
-}
-
-bool split_mfma_tiled_supported(int in_dtype, int head_dim) {
-    return (in_dtype == kBF16 || in_dtype == kF16) &&
-           (head_dim == 64 || head_dim == 128 || head_dim == 256);
-}
-
-bool split_mfma_supported(int in_dtype, int head_dim, int group) {
-    return (in_dtype == kBF16 || in_dtype == kF16) && group >= 2 && group <= kMaxGroup &&
-           (head_dim == 64 || head_dim == 128 || head_dim == 256);
-}
 
 hipError_t launch_split_mfma(const SplitArgs &a, int in_dtype, hipStream_t stream) {
     switch (in_dtype) {

@@ -63,10 +63,12 @@ class FDError(RuntimeError):
         self.code = code
 
 
-def check_fresh(path: str | None = None, record: str | None = None) -> None:
+def check_fresh(path: str | None = None, record: str | None = None,
+                allow_flags: bool = False) -> dict:
     """Raise unless the library at path (default LIB_PATH) was built from the
-    sources now in csrc/ and include/ (the build records their hash beside
-    it, at BUILD_RECORD)."""
+    sources now in csrc/ and include/ (the build records their hash and its
+    extra compiler flags beside it, at BUILD_RECORD), and, unless
+    allow_flags, without extra flags.  Returns the record."""
     from decode_attention_03_amd import build
 
     path = LIB_PATH if path is None else path
@@ -76,14 +78,34 @@ def check_fresh(path: str | None = None, record: str | None = None) -> None:
                            "`python -c 'import __graft_entry__ as g; g.build()'`")
     try:
         with open(record, encoding="utf-8") as f:
-            built = json.load(f).get("sources_sha256")
+            rec = json.load(f)
     except (OSError, ValueError):
-        built = None
+        rec = {}
+    built = rec.get("sources_sha256")
     now = build.library_source_hash()
-    if built != now:
+    if built != now or (rec.get("flags") and not allow_flags):
         raise RuntimeError(f"{path} was not built from the current sources (built from "
-                           f"{built}, sources now {now}): rebuild it with "
+                           f"{built} with flags {rec.get('flags')}, sources now {now}): "
+                           "rebuild it with "
                            "`python -c 'import __graft_entry__ as g; g.build()'`")
+    return rec
+
+
+_variant = None
+
+
+def use_variant(path: str) -> dict:
+    """Load a tuning variant (decode_attention_03_amd/build.py build_variant:
+    the library built with extra -D knobs) instead of libfd.so; must come
+    before the first library() call.  Returns its build record."""
+    global _variant
+    if _lib is not None:
+        raise RuntimeError("the library is already loaded")
+    from decode_attention_03_amd import build
+
+    rec = check_fresh(path, build.record_path(path), allow_flags=True)
+    _variant = path
+    return rec
 
 
 def library() -> ctypes.CDLL:
@@ -93,8 +115,9 @@ def library() -> ctypes.CDLL:
     with _lock:
         if _lib is not None:
             return _lib
-        check_fresh()
-        lib = ctypes.CDLL(LIB_PATH)
+        if _variant is None:
+            check_fresh()
+        lib = ctypes.CDLL(LIB_PATH if _variant is None else _variant)
         P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         IP = ctypes.POINTER(ctypes.c_int)
         lib.fd_version.argtypes, lib.fd_version.restype = [], I

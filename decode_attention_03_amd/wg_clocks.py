@@ -95,8 +95,11 @@ def run(config: int, launches: int, out_dir: str | None) -> dict:
     torch.cuda.init()
     torch.empty(1, device=dev)
     torch.cuda.synchronize(dev)
+    from decode_attention_03_amd import build, fd
+
     if not os.path.exists(VARIANT):
         raise RuntimeError(f"{VARIANT} is missing: run with --build first (on the CPU)")
+    fd.check_fresh(VARIANT, build.record_path(VARIANT), allow_flags=True)
     lib = ctypes.CDLL(VARIANT)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fd_decode_stages.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, I, P]

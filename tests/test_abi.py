@@ -18,7 +18,12 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call below fails v
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(fd.LIB_PATH):
+    # FD_TEST_LIBRARY: another build of the same sources (the sanitized
+    # host-only build of tests/test_host_sanitized.py)
+    other = os.environ.get("FD_TEST_LIBRARY")
+    if other and fd._variant is None and fd._lib is None:
+        fd.use_variant(other)
+    if not other and not os.path.exists(fd.LIB_PATH):
         import __graft_entry__
 
         __graft_entry__.build()
@@ -420,6 +425,7 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     computing anything some other way."""
     monkeypatch.setattr(fd, "LIB_PATH", str(tmp_path / "missing" / "libfd.so"))
     monkeypatch.setattr(fd, "_lib", None)
+    monkeypatch.setattr(fd, "_variant", None)
     with pytest.raises(RuntimeError, match="missing"):
         fd.library()
 
@@ -512,3 +518,10 @@ def test_stale_library_is_refused(monkeypatch, tmp_path):
 
     rec.write_text(json.dumps({"sources_sha256": build.library_source_hash()}))
     fd.check_fresh(str(lib), str(rec))
+    # a tuning variant (extra -D flags) is the product library only when asked for
+    rec.write_text(json.dumps({"sources_sha256": build.library_source_hash(),
+                               "flags": ["-DFD_WIDE_SETS=3"]}))
+    with pytest.raises(RuntimeError, match="current sources"):
+        fd.check_fresh(str(lib), str(rec))
+    assert fd.check_fresh(str(lib), str(rec), allow_flags=True)["flags"] == ["-DFD_WIDE_SETS=3"]
+    assert build.record_path("/x/libfd.so") == "/x/libfd.build.json"

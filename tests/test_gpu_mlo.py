@@ -12,6 +12,7 @@ import torch
 
 import oracle
 from decode_attention_03_amd import fd, workloads
+from tests.test_gpu_parity import combine_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -62,10 +63,11 @@ def test_split_mlo_partials(gpu, dtype, group, d):
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_combine_mlo_synthetic(gpu, out, d):
     """m/l/o merge alone on triples with empty splits, an all-empty row, a single
-    finite split and spreads over 200 in m."""
+    finite split and spreads over 200 in m; o values ~ N(0, 0.5^2), held to
+    the absolute bounds of the LSE combine's test (combine_bounds there)."""
     rng = np.random.default_rng(100 + d)
     batch, hq, B = 3, 5, 29
-    op = rng.standard_normal((batch, hq, B, d))
+    op = 0.5 * rng.standard_normal((batch, hq, B, d))
     mp = rng.uniform(-40, 40, (batch, hq, B))
     lp = rng.uniform(1.0, 500.0, (batch, hq, B))
     mp[0, 0, :] = -np.inf
@@ -84,11 +86,12 @@ def test_combine_mlo_synthetic(gpu, out, d):
     o, lse = fd.combine_mlo(o_part.to(gpu), m_part.to(gpu), l_part.to(gpu),
                             out_dtype=workloads.TORCH_DTYPES[out])
     go, gl = _np(o), _np(lse)
-    tol = 1e-5 if out == "f32" else 8e-3
-    assert np.abs(go - ro).max() <= tol * max(1.0, np.abs(ro).max())
+    assert np.abs(op).max() < 4.0
     assert np.array_equal(np.isneginf(gl), np.isneginf(rlse))
     fin = np.isfinite(rlse)
-    assert np.abs(gl[fin] - rlse[fin]).max() <= 1e-5 * max(1.0, np.abs(rlse[fin]).max())
+    tol_o, tol_l = combine_bounds(out, rlse[fin])
+    assert np.abs(go - ro).max() <= tol_o
+    assert np.all(np.abs(gl[fin] - rlse[fin]) <= tol_l)
     assert np.all(go[0, 0] == 0)
 
 

@@ -108,3 +108,24 @@ def test_digest_names_the_inputs():
     r = workloads.digest(workloads.generate(
         dataclasses.replace(workloads.WORKLOADS[4], batch=2, ragged=(3, 40))))
     assert "kv_lens" in r
+
+
+def test_named_workload_inputs_match_pinned_digests():
+    """Every input tensor of the five named workloads hashes to the digest
+    stored in tests/golden/workload_digests.json (written by
+    tests/golden/make_workload_digests.py from the generator alone): a change
+    of the generator, of torch's random streams or of the rounding into the
+    storage types fails here instead of silently changing the benchmark."""
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "workload_digests.json")
+    with open(path, encoding="utf-8") as f:
+        pinned = json.load(f)["workloads"]
+    assert sorted(v["config"] for v in pinned.values()) == sorted(workloads.WORKLOADS)
+    for c, w in sorted(workloads.WORKLOADS.items()):
+        inp = workloads.generate(w)
+        got = {"config": c, "max_kv_len": inp["max_kv_len"], **workloads.digest(inp)}
+        del inp
+        assert got == pinned[w.name], w.name
