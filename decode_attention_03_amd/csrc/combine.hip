@@ -186,6 +186,93 @@ __device__ __forceinline__ void combine_row(const RowSource src, size_t rowid, v
     }
 }
 
+// One pass over a row's partials, the merge folded in as it goes ("FlashDecoding
+// 数学推导：传统 m/l/o 方法与 LSE 方法" §2.3.5: merging (o, S) pairs one at a time
+// in any order gives the global pair).  The running pair is kept as (m, l, acc):
+// the largest S so far, l = sum_i exp(S_i - m) and acc = sum_i exp(S_i - m) o_i;
+// a partial with a larger S rescales both by exp(m_old - m_new).  At the end
+// o = acc / l and S = m + log l.  The V4 threads of a row each own one float4
+// column slice and read every partial's S (the same address for the row's
+// threads) and their slice of its o; sixteen partials are loaded before any
+// is merged, so a thread has up to 32 loads in flight, and nothing crosses
+// threads: no LDS, no barrier.  -inf partials (empty splits) are skipped, so
+// whatever their o slot holds contributes nothing.  The order is fixed, so the
+// result is reproducible.
+template <int D>
+__device__ __forceinline__ void combine_row_online(const RowSource &src, int c, size_t rowid,
+                                                   void *o, int out_dtype, float *lse) {
+    const int n = src.count + src.count2;
+    float m = -INFINITY, l = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto merge = [&](float s, float4 x) {
+        if (s == -INFINITY)
+            return;
+        if (s > m) {  // the new term sets the reference: rescale what is held
+            const float alpha = m == -INFINITY ? 0.f : fast_exp2((m - s) * kLog2e);
+            l = l * alpha + 1.f;
+            acc.x = acc.x * alpha + x.x;
+            acc.y = acc.y * alpha + x.y;
+            acc.z = acc.z * alpha + x.z;
+            acc.w = acc.w * alpha + x.w;
+            m = s;
+        } else {
+            const float e = fast_exp2((s - m) * kLog2e);
+            l += e;
+            acc.x += e * x.x;
+            acc.y += e * x.y;
+            acc.z += e * x.z;
+            acc.w += e * x.w;
+        }
+    };
+    // up to kChunk partials' loads in flight before they are merged (all of a
+    // row's partials at once for rows of up to kChunk, e.g. 16 splits)
+    constexpr int kChunk = 16;
+    for (int i = 0; i < n; i += kChunk) {
+        float s[kChunk];
+        float4 x[kChunk];
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+            s[k] = -INFINITY;
+            x[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i + k < n) {
+                s[k] = row_s(src, i + k);
+                x[k] = row_o(src, i + k, c);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k)
+            merge(s[k], x[k]);
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t base = rowid * D + 4 * c;
+    store_out(o, base + 0, acc.x * inv, out_dtype);
+    store_out(o, base + 1, acc.y * inv, out_dtype);
+    store_out(o, base + 2, acc.z * inv, out_dtype);
+    store_out(o, base + 3, acc.w * inv, out_dtype);
+    if (c == 0 && lse)
+        lse[rowid] = l > 0.f ? m + fast_log2(l) * kLn2 : -INFINITY;
+}
+
+// Rows per one-pass combine work-group: 256 threads, D / 4 per row.
+template <int D>
+constexpr int online_rows() {
+    return kCombineThreads / (D / 4);
+}
+
+// Fixed splits, one pass: rows_per_block rows of B contiguous partials each.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_online_kernel(
+    const float *__restrict__ o_part, const float *__restrict__ lse_part, int num_splits,
+    int rows, void *o, int out_dtype, float *lse) {
+    constexpr int V4 = D / 4;
+    const size_t rowid = (size_t)blockIdx.x * online_rows<D>() + threadIdx.x / V4;
+    if (rowid >= (size_t)rows)
+        return;
+    const RowSource src{lse_part + rowid * num_splits, o_part + rowid * num_splits * D,
+                        num_splits, 1, D, nullptr};
+    combine_row_online<D>(src, (int)(threadIdx.x % V4), rowid, o, out_dtype, lse);
+}
+
 // Fixed splits: row r's partials are contiguous, B of them.
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
@@ -238,10 +325,72 @@ __global__ __launch_bounds__(kCombineThreads) void combine_slots_kernel(SlotComb
     combine_row<D>(src, rowid, a.o, a.out_dtype, a.lse, weights);
 }
 
+// Token-balanced slots (and a cascade's prefix partials), one pass:
+// rows_per_block rows per work-group, each row as in combine_slots_kernel.
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void combine_slots_online_kernel(SlotCombineArgs a) {
+    constexpr int V4 = D / 4;
+    const size_t rowid = (size_t)blockIdx.x * online_rows<D>() + threadIdx.x / V4;
+    if (rowid >= (size_t)a.batch * a.heads_q)
+        return;
+    const int b = (int)(rowid / a.heads_q);
+    const int h = (int)(rowid % a.heads_q);
+    const int g = h % a.gsz;
+    const size_t u = (size_t)b * (a.heads_q / a.gsz) + h / a.gsz;
+    // the descriptor is read whether or not the sequence has tokens (units of
+    // empty sequences have none written; their entries are read, then ignored),
+    // so its load and the length's go out together
+    const int first = a.unit_desc[2 * u];
+    const int count = a.unit_desc[2 * u + 1];
+    const bool any = clamp_len(a.kv_lens, b, a.max_kv_len) > 0;
+    RowSource src{a.pre_lse + rowid * a.pre_count, a.pre_o + rowid * a.pre_count * D,
+                  a.pre_count, 1, D, nullptr};
+    src.s_stride2 = a.gsz;
+    src.o_stride2 = a.gsz * D;
+    src.count2 = any ? count : 0;
+    src.S2 = a.lse_slots + (any ? (size_t)first * a.gsz + g : 0);
+    src.O2 = a.o_slots + (any ? ((size_t)first * a.gsz + g) * D : 0);
+    combine_row_online<D>(src, (int)(threadIdx.x % V4), rowid, a.o, a.out_dtype, a.lse);
+}
+
 }  // namespace
+
+// One-pass combine kernels (1) or the work-group-per-row kernels with LDS
+// reductions (0).
+#ifndef FD_COMBINE_ONLINE
+#define FD_COMBINE_ONLINE 1
+#endif
+
+template <int D>
+void launch_online(const float *o_part, const float *lse_part, int rows, int num_splits, void *o,
+                   int out_dtype, float *lse, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((rows + online_rows<D>() - 1) / online_rows<D>());
+    hipLaunchKernelGGL(combine_online_kernel<D>, dim3(blocks), dim3(kCombineThreads), 0, stream,
+                       o_part, lse_part, num_splits, rows, o, out_dtype, lse);
+}
+
+template <int D>
+void launch_slots_online(const SlotCombineArgs &c, hipStream_t stream) {
+    const size_t rows = (size_t)c.batch * c.heads_q;
+    const unsigned blocks = (unsigned)((rows + online_rows<D>() - 1) / online_rows<D>());
+    hipLaunchKernelGGL(combine_slots_online_kernel<D>, dim3(blocks), dim3(kCombineThreads), 0,
+                       stream, c);
+}
 
 hipError_t launch_combine(const float *o_part, const float *lse_part, int rows, int num_splits,
                           int head_dim, void *o, int out_dtype, float *lse, hipStream_t stream) {
+    if (FD_COMBINE_ONLINE) {
+        switch (head_dim) {
+        case 64: launch_online<64>(o_part, lse_part, rows, num_splits, o, out_dtype, lse, stream);
+            break;
+        case 128: launch_online<128>(o_part, lse_part, rows, num_splits, o, out_dtype, lse, stream);
+            break;
+        case 256: launch_online<256>(o_part, lse_part, rows, num_splits, o, out_dtype, lse, stream);
+            break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     const size_t shmem = sizeof(float) * (size_t)num_splits;
     switch (head_dim) {
     case 64:
@@ -286,6 +435,15 @@ hipError_t launch_combine_mlo(const float *o_part, const float *m_part, const fl
 }
 
 hipError_t launch_combine_slots(const SlotCombineArgs &c, hipStream_t stream) {
+    if (FD_COMBINE_ONLINE) {
+        switch (c.head_dim) {
+        case 64: launch_slots_online<64>(c, stream); break;
+        case 128: launch_slots_online<128>(c, stream); break;
+        case 256: launch_slots_online<256>(c, stream); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     const size_t shmem = sizeof(float) * (size_t)(c.max_count + c.pre_count);
     const dim3 grid((unsigned)((size_t)c.batch * c.heads_q));
     switch (c.head_dim) {

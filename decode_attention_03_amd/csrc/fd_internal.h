@@ -107,8 +107,9 @@ struct SplitArgs {
     // Instrumented builds only (-DFD_WG_CLOCKS=1): the token-balanced kernel
     // writes four 64-bit words per share w at wg_clock[4 w ..]: the constant
     // 100 MHz clock at its start and at its end, (pieces << 32) | tokens
-    // (the K/V rows its pieces read, per KV head), and its block index.
-    // Null: no stamps.
+    // (the K/V rows its pieces read, per KV head), and where it ran: the
+    // HW_ID register << 32 | the XCD << 24 | its block index.  Null: no
+    // stamps.
     unsigned long long *wg_clock;
 #endif
 };

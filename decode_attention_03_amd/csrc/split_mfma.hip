@@ -202,6 +202,13 @@ constexpr int wide_nt() {
     return FD_WIDE_NT < 0 ? (QT == 1 ? 1 : 0) : FD_WIDE_NT;
 }
 
+// Whether a step of a piece is full (every token before the piece's end), as
+// a type, so that both kinds of step are compiled without a per-score branch.
+template <bool FULL>
+struct StepKind {
+    static constexpr bool value = FULL;
+};
+
 // Where a piece's results go.  Partial i of query row `row` (slot h of a
 // tile when `local`) is at index (row or h) * stride + off: o at o + index * D
 // (fp32, normalised), its LSE at lse[index] (m/l/o format: m there and l at
@@ -275,7 +282,9 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
     // This lane's share of l for slot `col`, twice: over the weights as
     // rounded for the matrix core (o is normalised by it, so the weights
     // applied to V sum to exactly 1) and over the fp32 weights (the LSE uses
-    // it, free of the rounding).
+    // it, free of the rounding).  (Summing the rounded weights on the matrix
+    // cores instead, as P . ones, measured 4 us slower per step on the ragged
+    // grouped-query batch: one more dependent product per token tile.)
     float lsum[QT], lexact[QT];
     float mtrue[QT];  // max of this lane's scores (the m/l/o format's m)
 #pragma unroll
@@ -453,10 +462,19 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             }
         };
 
-        auto compute_step = [&](int st, const Frags &f) {
+        // One step's arithmetic.  FULL (every token of the step lies before
+        // the piece's end, and the scale is positive, as it is for 1/sqrt(d)):
+        // no per-score end mask, the lane's max is taken over the unscaled
+        // scores (a positive scale keeps the order) and scaled once, and the
+        // scale enters each weight through one fused multiply-add,
+        // p = 2^(s * scale log2(e) - m).  Otherwise (the last step of a
+        // piece) scores past the end are masked to -inf and scaled one by one.
+        auto compute_step_impl = [&](int st, const Frags &f, auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                // S^T tiles on the matrix cores, scaled into the log2 domain.
+                // S^T tiles on the matrix cores: raw scores (FULL) or scores
+                // scaled into the log2 domain
                 float x[U][4];
                 float mx = -INFINITY;  // max of this lane's tokens
 #pragma unroll
@@ -467,11 +485,17 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                         s = M::s_tile(f.k[u][c], qf[qt][c], s);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int rel = st * kStepTok + 16 * u + 4 * grp + r;
-                        x[u][r] = rel < ntok ? s[r] * a.scale_log2 : -INFINITY;
+                        if constexpr (FULL) {
+                            x[u][r] = s[r];
+                        } else {
+                            const int rel = st * kStepTok + 16 * u + 4 * grp + r;
+                            x[u][r] = rel < ntok ? s[r] * a.scale_log2 : -INFINITY;
+                        }
                         mx = fmaxf(mx, x[u][r]);
                     }
                 }
+                if constexpr (FULL)
+                    mx *= a.scale_log2;
                 mtrue[qt] = fmaxf(mtrue[qt], mx);
                 // The reference max of a slot only has to bound its scores
                 // within 2^kRescaleGap, so the four lanes of a slot synchronise
@@ -500,8 +524,12 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 for (int u = 0; u < U; ++u) {
                     float p[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        p[r] = fast_exp2(x[u][r] - mref);
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (FULL)
+                            p[r] = fast_exp2(fmaf(x[u][r], a.scale_log2, -mref));
+                        else
+                            p[r] = fast_exp2(x[u][r] - mref);
+                    }
                     lexact[qt] += (p[0] + p[1]) + (p[2] + p[3]);
                     const u32x2 pa = M::pack(p, &lsum[qt]);
 #pragma unroll
@@ -509,6 +537,12 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                         oacc[qt][t] = M::pv_tile(pa, f.v[u][t], oacc[qt][t]);
                 }
             }
+        };
+        auto compute_step = [&](int st, const Frags &f) {
+            if ((st + 1) * kStepTok <= ntok && a.scale_log2 > 0.f)
+                compute_step_impl(st, f, StepKind<true>{});
+            else
+                compute_step_impl(st, f, StepKind<false>{});
         };
 
         // Pipeline over two register sets.  A step's rows leave their
@@ -533,27 +567,40 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             // NS register sets (contiguous K/V, d <= 128): steps 0 .. NS - 1
             // go out first; step st is staged from set st % NS, which is then
             // refilled with step st + NS, so NS - 1 to NS steps of loads stay
-            // in flight while a step is computed.  LDS still alternates two
-            // buffers by step parity, with the same barrier rule as below.
+            // in flight while a step is computed.  Every refill is issued,
+            // past the last step too (load_step re-reads the last step then):
+            // with no conditional loads the compiler's wait for a set counts
+            // exactly the 2 (NS - 1) younger loads.  LDS still alternates
+            // two buffers by step parity, with the same barrier rule as below.
             static_assert(!PAGED && D <= 128, "deeper load pipelines: contiguous K/V, d <= 128");
             Stage g[NS];
             Pages none;
 #pragma unroll
             for (int i = 0; i < NS; ++i)
-                if (i < nsteps)
-                    load_step(i, none, g[i]);
-            for (int base = 0; base < nsteps; base += NS) {
+                load_step(i, none, g[i]);
+            const int ngroups = nsteps / NS;
+            for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
                 for (int j = 0; j < NS; ++j) {
-                    const int st = base + j;
-                    if (st >= nsteps)
-                        break;
+                    const int st = gi * NS + j;
                     lds_char *const buf = (st & 1) ? b1 : b0;
                     stage(g[j], buf);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (st + NS < nsteps)
-                        load_step(st + NS, none, g[j]);
+                    load_step(st + NS, none, g[j]);
                     __builtin_amdgcn_sched_barrier(0);
+                    wg_sync();
+                    fetch(buf, f);
+                    compute_step(st, f);
+                }
+            }
+            // the last nsteps % NS steps: already in flight, no more loads
+            const int rem = nsteps - ngroups * NS;
+#pragma unroll
+            for (int j = 0; j < NS - 1; ++j) {
+                if (j < rem) {
+                    const int st = ngroups * NS + j;
+                    lds_char *const buf = (st & 1) ? b1 : b0;
+                    stage(g[j], buf);
                     wg_sync();
                     fetch(buf, f);
                     compute_step(st, f);
@@ -790,7 +837,12 @@ void split_mfma_balanced_kernel(SplitArgs a) {
             a.wg_clock[4 * (size_t)w + 0] = clk0;
             a.wg_clock[4 * (size_t)w + 1] = clk1;
             a.wg_clock[4 * (size_t)w + 2] = clk_work;
-            a.wg_clock[4 * (size_t)w + 3] = blockIdx.x;
+            // where it ran: the HW_ID register (CU, SIMD, shader engine) in the
+            // high word, the XCD (XCC_ID register) above the block index
+            const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+            const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xff;
+            a.wg_clock[4 * (size_t)w + 3] =
+                ((unsigned long long)hw << 32) | ((unsigned long long)xcc << 24) | blockIdx.x;
         }
     };
     if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_kv, w, a.num_wgs, c)) {

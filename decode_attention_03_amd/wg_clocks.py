@@ -13,7 +13,7 @@ launches of the named workload's fd_decode (after a settle period, each into
 its own stamp buffer) and summarises, per launch and over all of them: when
 work-groups start and finish relative to the first start, how long each
 runs, the rate each one streams K/V at, and how these differ between the
-eight XCDs (block index mod 8).  Whether a slow step comes from a few
+eight XCDs (the XCC_ID register).  Whether a slow step comes from a few
 work-groups finishing late (a tail) or from every work-group streaming
 slower shows up as the spread of finish times against the spread of rates.
 """
@@ -70,7 +70,7 @@ def analyse(stamps: list[list[tuple]], row_bytes: int) -> dict:
             durs.append(d)
             r = tokens * row_bytes / (d * 1e-6) / 1e9 if d > 0 else 0.0
             rates.append(r)
-            by_xcd.setdefault(blk % 8, []).append(r)
+            by_xcd.setdefault((blk >> 24) & 0xff, []).append(r)
     spans = [x["span_us"] for x in per_launch]
     return {
         "launches": len(stamps), "work_groups": len(stamps[0]) if stamps else 0,
@@ -84,7 +84,8 @@ def analyse(stamps: list[list[tuple]], row_bytes: int) -> dict:
     }
 
 
-def run(config: int, launches: int, out_dir: str | None) -> dict:
+def run(config: int, launches: int, out_dir: str | None, raw_path: str | None = None,
+        library: str | None = None) -> dict:
     import torch
 
     from decode_attention_03_amd import workloads
@@ -97,10 +98,13 @@ def run(config: int, launches: int, out_dir: str | None) -> dict:
     torch.cuda.synchronize(dev)
     from decode_attention_03_amd import build, fd
 
-    if not os.path.exists(VARIANT):
-        raise RuntimeError(f"{VARIANT} is missing: run with --build first (on the CPU)")
-    fd.check_fresh(VARIANT, build.record_path(VARIANT), allow_flags=True)
-    lib = ctypes.CDLL(VARIANT)
+    path = library or VARIANT  # another instrumented build (its flags include FD_WG_CLOCKS=1)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run with --build first (on the CPU)")
+    rec = fd.check_fresh(path, build.record_path(path), allow_flags=True)
+    if "-DFD_WG_CLOCKS=1" not in (rec.get("flags") or []):
+        raise RuntimeError(f"{path} is not an instrumented build (-DFD_WG_CLOCKS=1)")
+    lib = ctypes.CDLL(path)
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fd_decode_stages.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P, P, P, S, I, P]
     lib.fd_decode_stages.restype = I
@@ -161,6 +165,9 @@ def run(config: int, launches: int, out_dir: str | None) -> dict:
         a = b.view(-1, 4).cpu().tolist()
         stamps.append([(s, e, wk >> 32, wk & 0xffffffff, blk) for s, e, wk, blk in a
                        if wk >> 32 > 0])
+    if raw_path:  # every stamp, per launch: [start, end, pieces, tokens, where] per share
+        with open(raw_path, "w", encoding="utf-8") as f:
+            json.dump({"workload": w.name, "launches": [[list(x) for x in L] for L in stamps]}, f)
     row_bytes = w.head_dim * 2 * inp["k"].element_size()  # K + V of one token of one KV head
     res = {"workload": w.name, "plan_work_groups": nwg, **analyse(stamps, row_bytes)}
     if out_dir:
@@ -195,7 +202,7 @@ def write_summary(res: dict, config: int, out_dir: str) -> str:
         f"| finish after the first start (µs) | {fmt(res['finish_us'])} |",
         f"| work-group duration (µs) | {fmt(res['duration_us'])} |",
         f"| work-group K/V rate (GB/s) | {fmt(res['rate_GBps'])} |",
-        "| mean rate by XCD (block index mod 8, GB/s) | " +
+        "| mean rate by XCD (XCC_ID register, GB/s) | " +
         ", ".join(f"{x}: {r:.2f}" for x, r in res["rate_by_xcd_GBps"].items()) + " |",
         "",
     ]
@@ -211,11 +218,14 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--out", default=None, help="write the summary here")
+    ap.add_argument("--raw", default=None, help="write every stamp here (JSON)")
+    ap.add_argument("--library", default=None,
+                    help="an instrumented tuning variant instead of libfd_wgclocks.so")
     args = ap.parse_args()
     if args.build:
         print(build_variant())
         return 0
-    res = run(args.config, args.launches, args.out)
+    res = run(args.config, args.launches, args.out, args.raw, args.library)
     print(json.dumps(res), flush=True)
     return 0
 
