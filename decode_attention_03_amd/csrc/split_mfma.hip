@@ -462,19 +462,27 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
             }
         };
 
-        // One step's arithmetic.  FULL (every token of the step lies before
-        // the piece's end, and the scale is positive, as it is for 1/sqrt(d)):
-        // no per-score end mask, the lane's max is taken over the unscaled
-        // scores (a positive scale keeps the order) and scaled once, and the
-        // scale enters each weight through one fused multiply-add,
-        // p = 2^(s * scale log2(e) - m).  Otherwise (the last step of a
-        // piece) scores past the end are masked to -inf and scaled one by one.
+        // One step's arithmetic.  Every weight is p = 2^(x - m) with x the
+        // score scaled into the log2 domain (one product, rounded), and the
+        // lane's max is the max of the x, so both kinds of step give
+        // bit-identical weights for the same tokens (and paged K/V, which
+        // takes only the masked kind, bit-identical results).  FULL (every
+        // token of the step lies before the piece's end, and the scale is
+        // positive, as it is for 1/sqrt(d)): no per-score end mask, and the
+        // max is taken over the unscaled scores and scaled once (a positive
+        // scale keeps the order, and rounding keeps it too, so it is the
+        // same float).  Otherwise (the last step of a piece, or a scale
+        // <= 0) scores past the end are masked to -inf.
         auto compute_step_impl = [&](int st, const Frags &f, auto full_tag) {
+            // each product and difference rounded on its own: on a full step
+            // the compiler would otherwise fuse x = s * scale and x - m into
+            // one operation, which the masked step cannot, and the two kinds
+            // of step would round differently
+#pragma clang fp contract(off)
             constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                // S^T tiles on the matrix cores: raw scores (FULL) or scores
-                // scaled into the log2 domain
+                // S^T tiles on the matrix cores, scaled into the log2 domain
                 float x[U][4];
                 float mx = -INFINITY;  // max of this lane's tokens
 #pragma unroll
@@ -486,12 +494,13 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         if constexpr (FULL) {
-                            x[u][r] = s[r];
+                            x[u][r] = s[r] * a.scale_log2;
+                            mx = fmaxf(mx, s[r]);
                         } else {
                             const int rel = st * kStepTok + 16 * u + 4 * grp + r;
                             x[u][r] = rel < ntok ? s[r] * a.scale_log2 : -INFINITY;
+                            mx = fmaxf(mx, x[u][r]);
                         }
-                        mx = fmaxf(mx, x[u][r]);
                     }
                 }
                 if constexpr (FULL)
@@ -524,12 +533,8 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 for (int u = 0; u < U; ++u) {
                     float p[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if constexpr (FULL)
-                            p[r] = fast_exp2(fmaf(x[u][r], a.scale_log2, -mref));
-                        else
-                            p[r] = fast_exp2(x[u][r] - mref);
-                    }
+                    for (int r = 0; r < 4; ++r)
+                        p[r] = fast_exp2(x[u][r] - mref);
                     lexact[qt] += (p[0] + p[1]) + (p[2] + p[3]);
                     const u32x2 pa = M::pack(p, &lsum[qt]);
 #pragma unroll
@@ -538,11 +543,24 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 }
             }
         };
+        // The full-step body pays where the arithmetic bounds the step:
+        // work-groups of several waves or several query tiles per wave
+        // (cascade -1.5 us, large groups 2-10 %).  One-wave one-tile kernels
+        // are bound by their load stream, and a branch between two step
+        // bodies slowed them (ragged grouped-query workload 162.3 -> 164.2
+        // us per split stage; through 16-token pages 175 -> 181 us per step:
+        // the block-table reads are scalar loads waited on with the LDS
+        // counter, and the compiler then waited for them too early), so they,
+        // and every paged kernel, keep the one masked body.
         auto compute_step = [&](int st, const Frags &f) {
-            if ((st + 1) * kStepTok <= ntok && a.scale_log2 > 0.f)
-                compute_step_impl(st, f, StepKind<true>{});
-            else
+            if constexpr (PAGED || (W == 1 && QT == 1)) {
                 compute_step_impl(st, f, StepKind<false>{});
+            } else {
+                if ((st + 1) * kStepTok <= ntok && a.scale_log2 > 0.f)
+                    compute_step_impl(st, f, StepKind<true>{});
+                else
+                    compute_step_impl(st, f, StepKind<false>{});
+            }
         };
 
         // Pipeline over two register sets.  A step's rows leave their

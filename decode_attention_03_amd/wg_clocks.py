@@ -167,7 +167,8 @@ def run(config: int, launches: int, out_dir: str | None, raw_path: str | None = 
                        if wk >> 32 > 0])
     if raw_path:  # every stamp, per launch: [start, end, pieces, tokens, where] per share
         with open(raw_path, "w", encoding="utf-8") as f:
-            json.dump({"workload": w.name, "launches": [[list(x) for x in L] for L in stamps]}, f)
+            json.dump({"workload": w.name, "plan_work_groups": nwg,
+                       "launches": [[list(x) for x in L] for L in stamps]}, f)
     row_bytes = w.head_dim * 2 * inp["k"].element_size()  # K + V of one token of one KV head
     res = {"workload": w.name, "plan_work_groups": nwg, **analyse(stamps, row_bytes)}
     if out_dir:
@@ -188,7 +189,7 @@ def write_summary(res: dict, config: int, out_dir: str) -> str:
         f"    python3 -m decode_attention_03_amd.wg_clocks --config {config} --out profiles",
         "",
         "Instrumented build (-DFD_WG_CLOCKS=1): each work-group stores its start and end "
-        "times (the constant 100 MHz clock), its pieces and K/V tokens, and its block index. "
+        "times (the constant 100 MHz clock), its pieces and K/V tokens, and where it ran (block index, XCD, CU and SIMD from the hardware-ID registers). "
         f"{res['launches']} split-stage launches of fd_decode's plan after a 0.2 s settle; "
         f"{res['work_groups']} of {res['plan_work_groups']} work-groups had work.",
         "",
@@ -206,6 +207,7 @@ def write_summary(res: dict, config: int, out_dir: str) -> str:
         ", ".join(f"{x}: {r:.2f}" for x, r in res["rate_by_xcd_GBps"].items()) + " |",
         "",
     ]
+    os.makedirs(out_dir, exist_ok=True)
     path = os.path.join(out_dir, f"wg_clocks_{res['workload']}.md")
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines))
@@ -219,11 +221,29 @@ def main() -> int:
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--out", default=None, help="write the summary here")
     ap.add_argument("--raw", default=None, help="write every stamp here (JSON)")
+    ap.add_argument("--from-raw", default=None,
+                    help="summarise stamps saved with --raw instead of running (no GPU)")
     ap.add_argument("--library", default=None,
                     help="an instrumented tuning variant instead of libfd_wgclocks.so")
     args = ap.parse_args()
     if args.build:
         print(build_variant())
+        return 0
+    if args.from_raw:  # summarise stamps written earlier by --raw (no GPU)
+        with open(args.from_raw, encoding="utf-8") as f:
+            raw = json.load(f)
+        from decode_attention_03_amd import workloads
+
+        w = workloads.WORKLOADS[args.config]
+        if raw["workload"] != w.name:
+            raise SystemExit(f"{args.from_raw} holds {raw['workload']}, not {w.name}")
+        stamps = [[tuple(x) for x in launch] for launch in raw["launches"]]
+        elem = 4 if w.dtype == "f32" else 2
+        res = {"workload": w.name, "plan_work_groups": raw.get("plan_work_groups", len(stamps[0])),
+               **analyse(stamps, w.head_dim * 2 * elem)}
+        if args.out:
+            write_summary(res, args.config, args.out)
+        print(json.dumps(res), flush=True)
         return 0
     res = run(args.config, args.launches, args.out, args.raw, args.library)
     print(json.dumps(res), flush=True)
