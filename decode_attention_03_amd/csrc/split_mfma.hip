@@ -118,6 +118,13 @@ struct Mma<kF16> {
 #ifndef FD_MFMA_STEP_KB
 #define FD_MFMA_STEP_KB 8
 #endif
+// Weights computed after the rescale check (0) or speculatively before it,
+// against the reference max as it stands, and redone in the rare rescale
+// branch (1): the check's ballot then no longer sits between the scores and
+// the exponentials.
+#ifndef FD_SPEC_WEIGHTS
+#define FD_SPEC_WEIGHTS 1
+#endif
 
 template <int D, int STEP_KB = FD_MFMA_STEP_KB>
 struct Tiles {
@@ -510,6 +517,18 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                 // within 2^kRescaleGap, so the four lanes of a slot synchronise
                 // (and O, l are rescaled) only when some lane's tokens outgrow
                 // it; in steady state this is a single ballot.
+                float p[U][4];
+                if constexpr (FD_SPEC_WEIGHTS) {
+                    // the weights against the reference max as it stands,
+                    // computed while the check below resolves; redone in the
+                    // (rare) rescale branch
+                    const float mref0 = m_used[qt] == -INFINITY ? 0.f : m_used[qt];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            p[u][r] = fast_exp2(x[u][r] - mref0);
+                }
                 if (__ballot(mx > m_used[qt] + kRescaleGap)) {
                     float hm = fmaxf(mx, __shfl_xor(mx, 16, 64));
                     hm = fmaxf(hm, __shfl_xor(hm, 32, 64));
@@ -527,16 +546,27 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                         for (int t = 0; t < NT; ++t)
                             oacc[qt][t][r] *= ar;
                     }
+                    if constexpr (FD_SPEC_WEIGHTS) {
+                        const float mref1 = m_used[qt] == -INFINITY ? 0.f : m_used[qt];
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                p[u][r] = fast_exp2(x[u][r] - mref1);
+                    }
                 }
-                const float mref = m_used[qt] == -INFINITY ? 0.f : m_used[qt];
+                if constexpr (!FD_SPEC_WEIGHTS) {
+                    const float mref = m_used[qt] == -INFINITY ? 0.f : m_used[qt];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            p[u][r] = fast_exp2(x[u][r] - mref);
+                }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    float p[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        p[r] = fast_exp2(x[u][r] - mref);
-                    lexact[qt] += (p[0] + p[1]) + (p[2] + p[3]);
-                    const u32x2 pa = M::pack(p, &lsum[qt]);
+                    lexact[qt] += (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
+                    const u32x2 pa = M::pack(p[u], &lsum[qt]);
 #pragma unroll
                     for (int t = 0; t < NT; ++t)
                         oacc[qt][t] = M::pv_tile(pa, f.v[u][t], oacc[qt][t]);
