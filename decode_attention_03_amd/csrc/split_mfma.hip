@@ -72,6 +72,9 @@ typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 [[maybe_unused]] constexpr float kRescaleGap = 8.f;  // log2 units the running max may lag
 
@@ -89,12 +92,13 @@ struct Mma<kBF16> {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), b, c, 0,
                                                          0, 0);
     }
-    // Round four weights to bf16 (nearest even); returns the packed pair and
-    // adds the rounded values to *sum.
+    // Round four weights to bf16 (nearest even), two per conversion; returns
+    // the packed pair and adds the rounded values to *sum.
     static __device__ __forceinline__ u32x2 pack(const float *p, float *sum) {
-        const bf16x4_t v = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-        *sum += ((float)v[0] + (float)v[1]) + ((float)v[2] + (float)v[3]);
-        return __builtin_bit_cast(u32x2, v);
+        const bf16x2_t lo = __builtin_convertvector((f32x2_t){p[0], p[1]}, bf16x2_t);
+        const bf16x2_t hi = __builtin_convertvector((f32x2_t){p[2], p[3]}, bf16x2_t);
+        *sum += ((float)lo[0] + (float)lo[1]) + ((float)hi[0] + (float)hi[1]);
+        return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
     }
 };
 
@@ -109,9 +113,10 @@ struct Mma<kF16> {
                                                      __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ u32x2 pack(const float *p, float *sum) {
-        const f16x4_t v = {(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-        *sum += ((float)v[0] + (float)v[1]) + ((float)v[2] + (float)v[3]);
-        return __builtin_bit_cast(u32x2, v);
+        const f16x2_t lo = __builtin_convertvector((f32x2_t){p[0], p[1]}, f16x2_t);
+        const f16x2_t hi = __builtin_convertvector((f32x2_t){p[2], p[3]}, f16x2_t);
+        *sum += ((float)lo[0] + (float)lo[1]) + ((float)hi[0] + (float)hi[1]);
+        return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
     }
 };
 
