@@ -71,6 +71,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -92,6 +93,15 @@ struct Mma<kBF16> {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), b, c, 0,
                                                          0, 0);
     }
+    // P . V over two token tiles in one product: a holds the weights of
+    // tiles u and u + 1, b0 / b1 their V fragments (see the step body).
+    static __device__ __forceinline__ f32x4_t pv_tile2(u32x4 a, s16x4_t b0, s16x4_t b1,
+                                                       f32x4_t c) {
+        const s16x8_t b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0,
+                                                       0);
+    }
     // Round four weights to bf16 (nearest even), two per conversion; returns
     // the packed pair and adds the rounded values to *sum.
     static __device__ __forceinline__ u32x2 pack(const float *p, float *sum) {
@@ -112,6 +122,12 @@ struct Mma<kF16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
                                                      __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4_t pv_tile2(u32x4 a, s16x4_t b0, s16x4_t b1,
+                                                       f32x4_t c) {
+        const s16x8_t b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
     static __device__ __forceinline__ u32x2 pack(const float *p, float *sum) {
         const f16x2_t lo = __builtin_convertvector((f32x2_t){p[0], p[1]}, f16x2_t);
         const f16x2_t hi = __builtin_convertvector((f32x2_t){p[2], p[3]}, f16x2_t);
@@ -129,6 +145,11 @@ struct Mma<kF16> {
 // the exponentials.
 #ifndef FD_SPEC_WEIGHTS
 #define FD_SPEC_WEIGHTS 1
+#endif
+// P . V of a step with an even number of token tiles: one 16x16x32 product
+// per pair of tiles and d tile (1) or one 16x16x16 product per tile (0).
+#ifndef FD_PV32
+#define FD_PV32 1
 #endif
 
 template <int D, int STEP_KB = FD_MFMA_STEP_KB>
@@ -568,13 +589,34 @@ __device__ __forceinline__ void mfma_piece(const SplitArgs &a, lds_char *const t
                         for (int r = 0; r < 4; ++r)
                             p[u][r] = fast_exp2(x[u][r] - mref);
                 }
+                if constexpr (FD_PV32 && U % 2 == 0) {
+                    // Two token tiles per product.  The contraction runs over
+                    // 32 tokens in the order k = 8 * grp + 4 * j + r for token
+                    // 16 * (u + j) + 4 * grp + r: the lane holding slot `col`
+                    // in group grp has exactly those eight weights (S^T
+                    // element r of tiles u and u + 1), and the transposed V
+                    // reads of the two tiles give the same eight tokens of
+                    // its d column.
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    lexact[qt] += (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
-                    const u32x2 pa = M::pack(p[u], &lsum[qt]);
+                    for (int u = 0; u < U; u += 2) {
+                        lexact[qt] += (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
+                        const u32x2 pa0 = M::pack(p[u], &lsum[qt]);
+                        lexact[qt] += (p[u + 1][0] + p[u + 1][1]) + (p[u + 1][2] + p[u + 1][3]);
+                        const u32x2 pa1 = M::pack(p[u + 1], &lsum[qt]);
+                        const u32x4 pa = {pa0[0], pa0[1], pa1[0], pa1[1]};
 #pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        oacc[qt][t] = M::pv_tile(pa, f.v[u][t], oacc[qt][t]);
+                        for (int t = 0; t < NT; ++t)
+                            oacc[qt][t] = M::pv_tile2(pa, f.v[u][t], f.v[u + 1][t], oacc[qt][t]);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        lexact[qt] += (p[u][0] + p[u][1]) + (p[u][2] + p[u][3]);
+                        const u32x2 pa = M::pack(p[u], &lsum[qt]);
+#pragma unroll
+                        for (int t = 0; t < NT; ++t)
+                            oacc[qt][t] = M::pv_tile(pa, f.v[u][t], oacc[qt][t]);
+                    }
                 }
             }
         };
