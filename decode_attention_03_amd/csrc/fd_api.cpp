@@ -196,7 +196,8 @@ bool large_group(int in_dtype, int head_dim, int group) {
 struct TiledShape {
     int qt = 1, waves = 1;
     long long groups = 1;
-    int per_cu() const { return fd::split_mfma_tiled_wg_per_cu(waves); }
+    bool pair = false;  // two four-wave work-groups of one tile per wave for 5..8 tiles
+    int per_cu() const { return fd::split_mfma_tiled_wg_per_cu(waves, pair); }
 };
 
 TiledShape tiled_shape(int head_dim, long long nq) {
@@ -207,6 +208,11 @@ TiledShape tiled_shape(int head_dim, long long nq) {
         t.qt = 1;  // one tile on each of the waves
         while (t.waves < tiles)
             t.waves *= 2;
+        if (t.waves == 8 && fd::tiled_pair(head_dim, 1, 4, 2)) {
+            t.waves = 4;  // two four-wave work-groups per unit
+            t.groups = (tiles + 3) / 4;
+            t.pair = true;
+        }
         return t;
     }
     t.qt = fd::split_mfma_tile_max_qt(head_dim);

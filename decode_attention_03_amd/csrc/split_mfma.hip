@@ -858,11 +858,11 @@ __global__ __launch_bounds__(64) void split_mfma_kernel(SplitArgs a) {
 // unit = (sequence, split, KV head), KV head fastest (one sequence for a
 // shared prefix).  The K/V loads are ordinary (temporal) loads, as other
 // work-groups may read the same rows.
-template <int DT, int D, int QT, bool PAGED, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 4 ? 2 : 1)))
+template <int DT, int D, int QT, bool PAGED, int W, bool PAIR = false>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W > 4 || PAIR ? 2 : 1)))
 void split_mfma_tiled_kernel(SplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    constexpr int SKB = W > 1 ? wide_step_kb<W>() : kPrefixStepKB;
+    constexpr int SKB = PAIR ? 16 : W > 1 ? wide_step_kb<W>() : kPrefixStepKB;
     __shared__ __attribute__((aligned(1024))) char tile_buf[(W > 1 ? 2 : 1) * Tiles<D, SKB>::BUF];
     const int G = a.heads_q / a.heads_kv;
     const int nq = a.shared_kv ? a.batch * G : G;
@@ -892,7 +892,8 @@ void split_mfma_tiled_kernel(SplitArgs a) {
         out.lse = a.m_part ? a.m_part : a.lse_part;
         out.l = a.m_part ? a.l_part : nullptr;
     }
-    constexpr int NTL = W > 1 ? wide_nt<QT>() : 0;
+    // (paired work-groups read the unit's rows through L2: ordinary loads)
+    constexpr int NTL = PAIR ? 0 : W > 1 ? wide_nt<QT>() : 0;
     mfma_piece<DT, D, PAGED, QT, NTL, SKB, W, wide_sets<D, PAGED, W>()>(
         a, (lds_char *)tile_buf, b, kvh, t0, t1, qm, out);
 #endif  // __HIP_DEVICE_COMPILE__
@@ -988,13 +989,15 @@ int lds_per_cu_mfma() {
 
 // The tiled kernel for QT query tiles per wave and W waves, paged or
 // contiguous.
-template <int DT, int D, int QT, int W = 1>
+template <int DT, int D, int QT, int W = 1, bool PAIR = false>
 void launch_tiled(const SplitArgs &a, dim3 g, size_t pad, hipStream_t stream) {
     const dim3 blk(64 * W);
     if (a.block_table)
-        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, true, W>), g, blk, pad, stream, a);
+        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, true, W, PAIR>), g, blk, pad,
+                           stream, a);
     else
-        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false, W>), g, blk, pad, stream, a);
+        hipLaunchKernelGGL((split_mfma_tiled_kernel<DT, D, QT, false, W, PAIR>), g, blk, pad,
+                           stream, a);
 }
 
 // The token-balanced kernel for QT query tiles per wave and W waves, paged or
@@ -1014,11 +1017,20 @@ template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     const int tw = a.tile_waves > 1 ? a.tile_waves : 1;
+    // paired four-wave tiled work-groups (mfma_policy.h tiled_pair)
+    long tile_groups = 1;
+    if (a.tile_qt > 0) {
+        const long nq = (long)(a.shared_kv ? a.batch : 1) * (a.heads_q / a.heads_kv);
+        const long tiles = (nq + 15) / 16;
+        tile_groups = (tiles + (long)a.tile_qt * tw - 1) / ((long)a.tile_qt * tw);
+    }
+    const bool pair = a.tile_qt > 0 && !a.balanced && tiled_pair(D, a.tile_qt, tw, tile_groups);
     // balanced four-wave work-groups with one tile per wave (bal_two_per_simd)
     const bool bal_two = a.balanced && tw == 4 && D <= 128 &&
                          (a.heads_q / a.heads_kv + 15) / 16 <= tw;
     const size_t kStatic =
         bal_two                        ? (size_t)2 * Tiles<D, 16>::BUF
+        : pair                         ? (size_t)2 * Tiles<D, 16>::BUF
         : tw == 8                      ? (size_t)2 * Tiles<D, wide_step_kb<8>()>::BUF
         : tw == 4                      ? (size_t)2 * Tiles<D, wide_step_kb<4>()>::BUF
         : tw == 2                      ? (size_t)2 * Tiles<D, wide_step_kb<2>()>::BUF
@@ -1038,7 +1050,7 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     const int lds = lds_per_cu_mfma();
     const int per_cu = a.balanced ? split_mfma_balanced_wg_per_cu(D, a.heads_q / a.heads_kv)
                        : a.tile_qt == 0 ? kMfmaWgPerCU
-                                        : split_mfma_tiled_wg_per_cu(tw);
+                                        : split_mfma_tiled_wg_per_cu(tw, pair);
     if (per_cu > 0 && lds > 0) {
         const size_t want = (size_t)lds / (per_cu + 1) + 256;
         pad = want > kStatic ? want - kStatic : 0;
@@ -1057,10 +1069,14 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
                 launch_tiled<DT, D, Q, 2>(a, g, pad, stream);
         } else if (tw == 4) {
             if constexpr (tile_max_waves<D>() >= 4) {
-                if (one)
+                if (pair) {
+                    if constexpr (D <= 128)
+                        launch_tiled<DT, D, 1, 4, true>(a, g, pad, stream);
+                } else if (one) {
                     launch_tiled<DT, D, 1, 4>(a, g, pad, stream);
-                else
+                } else {
                     launch_tiled<DT, D, Q, 4>(a, g, pad, stream);
+                }
             }
         } else if (tw == 8) {
             if constexpr (tile_max_waves<D>() >= 8) {

@@ -142,8 +142,9 @@ def test_decode_plan_struct_layout():
     ((16, 64, 8, 32768, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=1, query_tiles=1)),
     # multi-query with 64 heads at d = 64: four tiles per work-group
     ((4, 64, 1, 8192, 64, fd.F16, 0, 0, 0), dict(kernel=2, query_tiles=4)),
-    # 128 per KV head at d = 128: eight waves of one tile share each staged step
-    ((4, 128, 1, 8192, 128, fd.BF16, 0, 0, 0), dict(kernel=2, query_tiles=8, waves_per_group=8)),
+    # 128 per KV head at d = 128: two work-groups per unit, each of four waves of
+    # one tile sharing each staged step (the unit's rows shared through L2)
+    ((4, 128, 1, 8192, 128, fd.BF16, 0, 0, 0), dict(kernel=2, query_tiles=4, waves_per_group=4)),
     # ragged: 32 per KV head balanced on two waves of one tile (two work-groups
     # per CU), 40 on four waves of one tile (two per CU, two waves per SIMD),
     # 128 on eight of one (one per CU);
