@@ -196,7 +196,7 @@ bool large_group(int in_dtype, int head_dim, int group) {
 struct TiledShape {
     int qt = 1, waves = 1;
     long long groups = 1;
-    bool pair = false;  // two four-wave work-groups of one tile per wave for 5..8 tiles
+    bool pair = false;  // 5..8 tiles on several smaller work-groups of one tile per wave
     int per_cu() const { return fd::split_mfma_tiled_wg_per_cu(waves, pair); }
 };
 
@@ -208,9 +208,10 @@ TiledShape tiled_shape(int head_dim, long long nq) {
         t.qt = 1;  // one tile on each of the waves
         while (t.waves < tiles)
             t.waves *= 2;
-        if (t.waves == 8 && fd::tiled_pair(head_dim, 1, 4, 2)) {
-            t.waves = 4;  // two four-wave work-groups per unit
-            t.groups = (tiles + 3) / 4;
+        constexpr int pw = fd::tiled_pair_waves();
+        if (t.waves == 8 && pw > 0 && fd::tiled_pair(head_dim, 1, pw, 2)) {
+            t.waves = pw;  // several smaller work-groups per unit
+            t.groups = (tiles + pw - 1) / pw;
             t.pair = true;
         }
         return t;

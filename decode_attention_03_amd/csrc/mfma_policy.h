@@ -95,21 +95,23 @@ inline int split_mfma_tile_max_waves(int head_dim) {
 inline bool split_mfma_tile_spread() { return FD_TILE_SPREAD != 0; }
 
 // Five to eight query tiles at d <= 128 on the tiled kernel: one eight-wave
-// work-group per unit (0), or two four-wave work-groups (1: one tile per
-// wave, 16 KB steps, two waves per SIMD from different work-groups, the
-// unit's K/V shared through L2), whose barriers are independent of each other.
+// work-group per unit (FD_TILE_PAIR 0), or several work-groups of
+// FD_TILE_PAIR waves (4 or 2) with one tile per wave, 16 KB steps and eight
+// waves per CU in all (two per SIMD, from different work-groups), the unit's
+// K/V shared through L2; their barriers are independent of each other.
 #ifndef FD_TILE_PAIR
-#define FD_TILE_PAIR 1
+#define FD_TILE_PAIR 4
 #endif
+constexpr int tiled_pair_waves() { return FD_TILE_PAIR; }
 constexpr bool tiled_pair(int head_dim, int qt, int waves, long long groups) {
-    return FD_TILE_PAIR != 0 && head_dim <= 128 && qt == 1 && waves == 4 && groups > 1;
+    return FD_TILE_PAIR != 0 && head_dim <= 128 && qt == 1 && waves == FD_TILE_PAIR &&
+           groups > 1;
 }
-
 // Resident tiled work-groups per CU with this many waves each (pair: the
 // four-wave work-groups above, two per CU).
 inline int split_mfma_tiled_wg_per_cu(int waves, bool pair = false) {
     if (pair)
-        return 2;
+        return 8 / waves;
     if (waves <= 1)
         return kPrefixWgPerCU;
     const int n = kPrefixWgPerCU / waves;  // one wave per SIMD

@@ -1017,7 +1017,7 @@ template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     using T = Tiles<D>;
     const int tw = a.tile_waves > 1 ? a.tile_waves : 1;
-    // paired four-wave tiled work-groups (mfma_policy.h tiled_pair)
+    // several smaller tiled work-groups per unit (mfma_policy.h tiled_pair)
     long tile_groups = 1;
     if (a.tile_qt > 0) {
         const long nq = (long)(a.shared_kv ? a.batch : 1) * (a.heads_q / a.heads_kv);
@@ -1063,10 +1063,14 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
             return hipErrorInvalidValue;
         const bool one = a.tile_qt == 1;
         if (tw == 2) {
-            if (one)
+            if (pair) {
+                if constexpr (D <= 128)
+                    launch_tiled<DT, D, 1, 2, true>(a, g, pad, stream);
+            } else if (one) {
                 launch_tiled<DT, D, 1, 2>(a, g, pad, stream);
-            else
+            } else {
                 launch_tiled<DT, D, Q, 2>(a, g, pad, stream);
+            }
         } else if (tw == 4) {
             if constexpr (tile_max_waves<D>() >= 4) {
                 if (pair) {
