@@ -60,10 +60,14 @@ def test_cascade_matches_concatenated_attention(gpu, dtype, group, d, prefix_len
 
 
 @pytest.mark.parametrize("dtype,group,d,batch", [("f16", 4, 64, 40), ("bf16", 8, 128, 33),
-                                                 ("bf16", 1, 256, 19)])
+                                                 ("bf16", 1, 256, 19), ("bf16", 8, 128, 16),
+                                                 ("bf16", 8, 128, 12), ("f16", 4, 64, 20)])
 def test_cascade_many_requests(gpu, dtype, group, d, batch):
     """Many requests per shared prefix: the prefix kernel's queries span many
-    16-query tiles (partial last tile), several tiles per work-group."""
+    16-query tiles (partial last tile), several tiles per work-group; with
+    five to eight tiles (128, 96 and 80 queries) the prefix runs on two
+    four-wave work-groups per KV head and split, the second one partly empty
+    for 96 and 80."""
     w = workloads.Workload("cascade_many", batch=batch, heads_q=2 * group, heads_kv=2,
                            head_dim=d, max_kv_len=700, dtype=dtype, out_dtype=dtype,
                            seed=batch + d, ragged=(0, 700))
