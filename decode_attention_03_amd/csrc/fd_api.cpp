@@ -35,6 +35,16 @@ constexpr int kMinSplitLenPerHead = 64;  // grouped: tokens per query head of th
 constexpr int kMinSplitLenPerHeadTiled = 8;
 constexpr int kMaxAutoSplits = 512;
 constexpr int kBalancedRounds = 1;     // token-balanced work-groups: CUs * per-CU * rounds
+// When those floors would leave the GPU's work-group slots partly empty
+// (small batches), splits may shrink to this many tokens per query head of
+// the group (at least kMinSplitLenFill), up to one round of work-groups: more
+// partial traffic (a few percent of the K/V bytes) against idle CUs, which
+// cost far more (FD_SPLIT_FILL 0 keeps the floors).
+#ifndef FD_SPLIT_FILL
+#define FD_SPLIT_FILL 1
+#endif
+constexpr int kMinSplitLenPerHeadFill = 16;
+constexpr int kMinSplitLenFill = 64;
 
 thread_local std::string g_error;
 
@@ -504,6 +514,17 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     long long bmax = (max_kv_len + min_len - 1) / min_len;
     if (bmax < 1)
         bmax = 1;
+    if (FD_SPLIT_FILL && b > bmax && !tiled) {
+        // the floor would leave work-group slots empty: let the splits shrink
+        // towards the fill floor, up to what fills the slots once
+        long long fill_len = (long long)kMinSplitLenPerHeadFill * (grouped ? group : 1);
+        fill_len = fill_len > kMinSplitLenFill ? fill_len : kMinSplitLenFill;
+        fill_len = fill_len < min_len ? fill_len : min_len;
+        const long long once = ((long long)num_cus * per_cu + units - 1) / units;
+        long long bfill = (max_kv_len + fill_len - 1) / fill_len;
+        bfill = bfill < once ? bfill : once;
+        bmax = bfill > bmax ? bfill : bmax;
+    }
     if (b > bmax)
         b = bmax;
     if (b > kMaxAutoSplits)

@@ -140,6 +140,15 @@ def test_decode_plan_struct_layout():
                                                      work_groups=512)),
     # grouped heads: one tile, fixed splits without lengths
     ((16, 64, 8, 32768, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=1, query_tiles=1)),
+    # small batches: the splits shrink below the usual floor (64 tokens per
+    # query head of the group, 256 for one head) until the work-groups fill
+    # the GPU once: 16 tokens per query head, at least 64
+    ((1, 32, 4, 16384, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=1, num_splits=128,
+                                                    split_len=128, work_groups=512)),
+    ((4, 32, 4, 4096, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=1, num_splits=32,
+                                                   split_len=128, work_groups=512)),
+    ((1, 32, 32, 1024, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=0, num_splits=16,
+                                                    split_len=64, work_groups=512)),
     # multi-query with 64 heads at d = 64: four tiles per work-group
     ((4, 64, 1, 8192, 64, fd.F16, 0, 0, 0), dict(kernel=2, query_tiles=4)),
     # 128 per KV head at d = 128: two work-groups per unit, each of four waves of
