@@ -12,6 +12,7 @@ o [batch, heads_q, d]; lse float32 [batch, heads_q].
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import json
 import math
@@ -112,6 +113,8 @@ def library() -> ctypes.CDLL:
     """Open libfd.so (once).  Raises if it has not been built, or was built
     from other sources than the ones in the tree."""
     global _lib
+    if _lib is not None:  # loaded: no lock on the per-call path
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -179,11 +182,31 @@ def _code(dtype: torch.dtype) -> int:
 
 
 def _ptr(t: torch.Tensor | None):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # an int (or None) for a c_void_p parameter: ctypes converts it by argtypes
+    return None if t is None else t.data_ptr()
+
+
+# torch's current raw HIP stream of a device, without building a Stream object
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _raw_stream is not None and device.index is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _on(device: torch.device):
+    """Make device current for the launches (and the plan, which depends on its
+    compute units); no switch when it already is."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
+#: fd_decode_workspace_bytes results by (device, arguments): the plan depends
+#: only on them and on the device's compute-unit count
+_ws_cache: dict = {}
 
 
 def _on_device(name: str, t: torch.Tensor, device: torch.device) -> None:
@@ -326,7 +349,7 @@ def decode_split(q, k, v, kv_lens=None, *, num_splits: int, split_len: int = 0, 
     o_part, lse_part = _parts((("o_part", (batch, heads_q, B, d)),
                                ("lse_part", (batch, heads_q, B))),
                               {"o_part": o_part, "lse_part": lse_part}, q.device)
-    with torch.cuda.device(q.device):  # launches go to the current device
+    with _on(q.device):  # launches go to the current device
         _check(library().fd_decode_split(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
                                          heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
                                          B, int(split_len), _ptr(o_part), _ptr(lse_part),
@@ -346,7 +369,7 @@ def decode_split_mlo(q, k, v, kv_lens=None, *, num_splits: int, split_len: int =
                                      ("l_part", shape)),
                                     {"o_part": o_part, "m_part": m_part, "l_part": l_part},
                                     q.device)
-    with torch.cuda.device(q.device):  # launches go to the current device
+    with _on(q.device):  # launches go to the current device
         _check(library().fd_decode_split_mlo(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
                                              heads_q, heads_kv, n_max, d, _code(q.dtype), scale,
                                              B, int(split_len), _ptr(o_part), _ptr(m_part),
@@ -374,7 +397,7 @@ def combine_mlo(o_part, m_part, l_part, out_dtype=None, o=None, lse=None, return
     batch, heads_q, nb, d, dev = _partials_in(o_part, {"m_part": m_part, "l_part": l_part})
     o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
                       out_dtype or (o.dtype if o is not None else torch.float32), dev)
-    with torch.cuda.device(dev):  # launches go to the current device
+    with _on(dev):  # launches go to the current device
         _check(library().fd_combine_mlo(_ptr(o_part), _ptr(m_part), _ptr(l_part), batch,
                                         heads_q, nb, d, _ptr(o), _code(o.dtype), _ptr(lse),
                                         _stream(dev)))
@@ -386,7 +409,7 @@ def combine(o_part, lse_part, out_dtype=None, o=None, lse=None, return_lse=True)
     batch, heads_q, nb, d, dev = _partials_in(o_part, {"lse_part": lse_part})
     o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
                       out_dtype or (o.dtype if o is not None else torch.float32), dev)
-    with torch.cuda.device(dev):  # launches go to the current device
+    with _on(dev):  # launches go to the current device
         _check(library().fd_combine(_ptr(o_part), _ptr(lse_part), batch, heads_q, nb, d, _ptr(o),
                                     _code(o.dtype), _ptr(lse), _stream(dev)))
     return o, lse
@@ -410,14 +433,21 @@ def decode(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0, split_len:
     dev = q.device
     o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
                       out_dtype or (o.dtype if o is not None else q.dtype), dev)
-    with torch.cuda.device(dev):  # the plan depends on this device's compute units
-        need = decode_workspace_bytes(batch, heads_q, heads_kv, n_max, d, q.dtype,
-                                      kv_lens is not None, num_splits, split_len)
+    key = (dev.index, batch, heads_q, heads_kv, n_max, d, q.dtype, kv_lens is not None,
+           num_splits, split_len)
+    need = _ws_cache.get(key)
+    if need is None:
+        with _on(dev):  # the plan depends on this device's compute units
+            need = decode_workspace_bytes(batch, heads_q, heads_kv, n_max, d, q.dtype,
+                                          kv_lens is not None, num_splits, split_len)
+        if len(_ws_cache) > 4096:
+            _ws_cache.clear()
+        _ws_cache[key] = need
     workspace, ws_bytes = _workspace(workspace, need, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch, heads_q, heads_kv, n_max, d,
             _code(q.dtype), _code(o.dtype), scale, num_splits, split_len, _ptr(o), _ptr(lse),
             _ptr(workspace), ws_bytes)
-    with torch.cuda.device(dev):  # launches go to the current device
+    with _on(dev):  # launches go to the current device
         if stages == STAGE_SPLIT | STAGE_COMBINE:
             _check(library().fd_decode(*args, _stream(dev)))
         else:
@@ -437,7 +467,7 @@ def decode_noalloc(q, k, v, kv_lens=None, *, scale=None, num_splits: int = 0,
     dev = q.device
     o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
                       out_dtype or (o.dtype if o is not None else q.dtype), dev)
-    with torch.cuda.device(dev):  # launches go to the current device
+    with _on(dev):  # launches go to the current device
         _check(library().fd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_lens), batch,
                                            heads_q, heads_kv, n_max, d, _code(q.dtype),
                                            _code(o.dtype), scale, num_splits, split_len, _ptr(o),
@@ -481,7 +511,7 @@ def decode_split_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, num_sp
     o_part, lse_part = _parts((("o_part", (batch, heads_q, B, d)),
                                ("lse_part", (batch, heads_q, B))),
                               {"o_part": o_part, "lse_part": lse_part}, q.device)
-    with torch.cuda.device(q.device):  # launches go to the current device
+    with _on(q.device):  # launches go to the current device
         _check(library().fd_decode_split_paged(
             _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch, heads_q,
             heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), scale, B, int(split_len),
@@ -499,11 +529,11 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens=None, *, scale=None,
     dev = q.device
     o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
                       out_dtype or (o.dtype if o is not None else q.dtype), dev)
-    with torch.cuda.device(dev):  # the plan depends on this device's compute units
+    with _on(dev):  # the plan depends on this device's compute units
         need = decode_workspace_bytes(batch, heads_q, heads_kv, max_pages * ps, d, q.dtype,
                                       kv_lens is not None, num_splits, split_len)
     workspace, ws_bytes = _workspace(workspace, need, dev)
-    with torch.cuda.device(dev):  # launches go to the current device
+    with _on(dev):  # launches go to the current device
         _check(library().fd_decode_paged(
             _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens), batch,
             heads_q, heads_kv, ps, max_pages, num_pages, d, _code(q.dtype), _code(o.dtype), scale,
@@ -553,11 +583,11 @@ def decode_cascade(q, k_prefix, v_prefix, k_suffix, v_suffix, suffix_lens=None, 
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o, lse = _outputs(o, lse, return_lse, (batch, heads_q, d),
                       out_dtype or (o.dtype if o is not None else q.dtype), dev)
-    with torch.cuda.device(dev):  # the plan depends on this device's compute units
+    with _on(dev):  # the plan depends on this device's compute units
         need = cascade_workspace_bytes(batch, heads_q, heads_kv, prefix_len, max_suffix_len, d,
                                        q.dtype, suffix_lens is not None)
     workspace, ws_bytes = _workspace(workspace, max(need, 16), dev)
-    with torch.cuda.device(dev):  # launches go to the current device
+    with _on(dev):  # launches go to the current device
         _check(library().fd_decode_cascade(
             _ptr(q), _ptr(k_prefix), _ptr(v_prefix), prefix_len, _ptr(k_suffix), _ptr(v_suffix),
             _ptr(suffix_lens), batch, heads_q, heads_kv, max_suffix_len, d, _code(q.dtype),
