@@ -45,6 +45,14 @@ constexpr int kBalancedRounds = 1;     // token-balanced work-groups: CUs * per-
 #endif
 constexpr int kMinSplitLenPerHeadFill = 16;
 constexpr int kMinSplitLenFill = 64;
+// Split counts for equal lengths are chosen by rounds of work-groups
+// (FD_SPLIT_ROUNDS 0: the first count that fills the slots); a work-group's
+// fixed cost (first loads, partial write, the spread of a round's finish
+// times), as the K/V bytes it could have streamed meanwhile.
+#ifndef FD_SPLIT_ROUNDS
+#define FD_SPLIT_ROUNDS 1
+#endif
+constexpr long long kWgFixedBytes = 64 << 10;
 
 thread_local std::string g_error;
 
@@ -272,8 +280,9 @@ int split_kernel(const fd::SplitArgs &a, int in_dtype) {
 int vector_waves(const fd::SplitArgs &a, int cus) {
     if (a.fused_waves > 0)
         return a.fused_waves;
+    // two-wave work-groups only where they all fit in the wave slots at once
     const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
-    return wgs < (long long)cus * fd::kWavesPerCU ? fd::kWavesPerCU : 1;
+    return wgs <= cus ? fd::kWavesPerCU : 1;  // kWavesPerCU waves each on at most one per CU
 }
 
 int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
@@ -531,10 +540,35 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
         b = kMaxAutoSplits;
     if (b < 1)
         b = 1;
+    if (FD_SPLIT_ROUNDS && !ragged) {
+        // Equal lengths: every work-group streams the same rows, so the launch
+        // takes rounds(B) = ceil(units * B / slots) times one split's time.  A
+        // count just past a multiple of the slots leaves a mostly idle last
+        // round (16 sequences x 6 KV heads x 6 splits = 576 work-groups on 512
+        // slots ran twice as long as 480).  Take the count that minimises
+        // rounds x (split length + a work-group's fixed cost), and among counts
+        // within 1 % of that the fewest splits (fewer partials to merge).
+        const long long slots = (long long)num_cus * per_cu;
+        const long long hi = bmax < kMaxAutoSplits ? bmax : kMaxAutoSplits;
+        const long long row = 2LL * head_dim * (in_dtype == FD_F32 ? 4 : 2);  // K + V per token
+        const long long fixed = (kWgFixedBytes + row - 1) / row;
+        auto cost = [&](long long c) {
+            const long long len = ((max_kv_len + c - 1) / c + 15) / 16 * 16;
+            return (double)((units * c + slots - 1) / slots) * (double)(len + fixed);
+        };
+        double best = cost(b);
+        for (long long c = 1; c <= hi; ++c)
+            best = cost(c) < best ? cost(c) : best;
+        for (long long c = 1; c <= hi; ++c)
+            if (cost(c) <= best * 1.01) {
+                b = c;
+                break;
+            }
+    }
     // the vector kernel runs a lone split per row with one multi-wave
     // work-group per CU, which fills the same wave slots as up to kWavesPerCU
     // splits and needs no combine stage
-    if (!grouped && !tiled && !ragged && b >= 2 && b <= fd::kWavesPerCU)
+    if (!grouped && !tiled && !ragged && b >= 2 && b <= fd::kWavesPerCU && units <= num_cus)
         b = 1;
     long long len = (max_kv_len + b - 1) / b;
     len = (len + 15) / 16 * 16;  // whole 16-token tiles

@@ -149,6 +149,14 @@ def test_decode_plan_struct_layout():
                                                    split_len=128, work_groups=512)),
     ((1, 32, 32, 1024, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=0, num_splits=16,
                                                     split_len=64, work_groups=512)),
+    # equal lengths, work-group counts that do not divide the 512 slots: the
+    # count with the fewest rounds per token, not the first that fills them
+    # (16 x 6 KV heads: 5 splits, 480 work-groups in one round, not 6 and 576)
+    ((16, 48, 6, 16384, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=1, num_splits=5,
+                                                     split_len=3280, work_groups=480)),
+    # 8 x 40 heads (MHA): 8 splits, 2560 work-groups, five full rounds
+    ((8, 40, 40, 16384, 128, fd.BF16, 0, 0, 0), dict(route=2, kernel=0, num_splits=8,
+                                                     split_len=2048, work_groups=2560)),
     # multi-query with 64 heads at d = 64: four tiles per work-group
     ((4, 64, 1, 8192, 64, fd.F16, 0, 0, 0), dict(kernel=2, query_tiles=4)),
     # 128 per KV head at d = 128: two work-groups per unit, each of four waves of
