@@ -556,14 +556,47 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
             const long long len = ((max_kv_len + c - 1) / c + 15) / 16 * 16;
             return (double)((units * c + slots - 1) / slots) * (double)(len + fixed);
         };
-        double best = cost(b);
-        for (long long c = 1; c <= hi; ++c)
-            best = cost(c) < best ? cost(c) : best;
-        for (long long c = 1; c <= hi; ++c)
-            if (cost(c) <= best * 1.01) {
-                b = c;
-                break;
+        // Counts with the same number of rounds form bands [lo_r, top_r], top_r
+        // the largest count that takes r rounds; within a band the cost only
+        // falls as the count grows (shorter splits), so the least cost is at
+        // some band's top, and the fewest splits within 1 % of it is the first
+        // count of the first band whose top qualifies (binary search).  Only
+        // the 64 bands from one split's rounds up are searched: past them a
+        // partial last round costs little, and the fixed costs of more
+        // work-groups only add up.
+        const long long rounds_lo = (units + slots - 1) / slots;  // rounds of one split
+        long long rounds_hi = (units * hi + slots - 1) / slots;
+        rounds_hi = rounds_hi < rounds_lo + 63 ? rounds_hi : rounds_lo + 63;
+        if (hi >= 1) {
+            auto top = [&](long long r) {
+                const long long t = r * slots / units;
+                return t < hi ? t : hi;
+            };
+            double best = cost(b);
+            for (long long r = rounds_lo; r <= rounds_hi; ++r)
+                if (top(r) >= 1)
+                    best = cost(top(r)) < best ? cost(top(r)) : best;
+            const double thr = best * 1.01;
+            long long lo = 1;
+            for (long long r = rounds_lo; r <= rounds_hi && lo <= hi; ++r) {
+                const long long t = top(r);
+                if (t < lo)
+                    continue;
+                if (cost(t) <= thr) {
+                    long long a0 = lo, a1 = t;  // smallest count in [lo, t] within thr
+                    while (a0 < a1) {
+                        const long long mid = (a0 + a1) / 2;
+                        if (cost(mid) <= thr)
+                            a1 = mid;
+                        else
+                            a0 = mid + 1;
+                    }
+                    b = a0;
+                    break;
+                }
+                lo = t + 1;
             }
+        }
     }
     // the vector kernel runs a lone split per row with one multi-wave
     // work-group per CU, which fills the same wave slots as up to kWavesPerCU
