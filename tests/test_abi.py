@@ -6,6 +6,7 @@ the documented codes before any launch.
 """
 import ctypes
 import os
+import random
 import re
 
 import pytest
@@ -67,6 +68,30 @@ def test_choose_splits_contract(lib, batch, hq, hkv, d, dt, ragged):
         lib.fd_choose_splits(batch, hq, hkv, n, d, dt, ragged, 256, ctypes.byref(again[0]),
                              ctypes.byref(again[1]))
         assert (again[0].value, again[1].value) == (B, L)
+
+
+def test_choose_splits_contract_random_shapes(lib):
+    """The same contract over 3000 seeded random shapes, head counts that are
+    not powers of two and CU counts of other GPUs included (the count for equal
+    lengths is chosen by rounds of work-groups)."""
+    rng = random.Random(11)
+    for _ in range(3000):
+        hkv = rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16, 20, 24, 32, 40, 48, 64])
+        g = rng.choice([1, 1, 2, 4, 5, 6, 8, 12, 16, 24, 32, 64, 128])
+        batch = rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64, 100, 600])
+        n = rng.choice([0, 1, 15, 17, 100, 777, 1024, 3000, 4096, 10000, 65536, 131072,
+                        (1 << 20) + 5])
+        d = rng.choice([64, 128, 256])
+        dt = rng.choice([fd.F32, fd.F16, fd.BF16])
+        ragged = rng.choice([0, 1])
+        cus = rng.choice([256, 304, 80, 1])
+        b, length = ctypes.c_int(), ctypes.c_int()
+        args = (batch, hkv * g, hkv, n, d, dt, ragged, cus)
+        assert lib.fd_choose_splits(*args, ctypes.byref(b), ctypes.byref(length)) == fd.OK, args
+        B, L = b.value, length.value
+        assert 1 <= B <= 512 and L >= 1, args
+        assert B * L >= n and (n == 0 or (B - 1) * L < n), args
+        assert n == 0 or L % 16 == 0, args
 
 
 def test_choose_splits_fills_the_gpu(lib):
