@@ -205,6 +205,17 @@ bool large_group(int in_dtype, int head_dim, int group) {
            fd::split_mfma_tiled_supported(in_dtype, head_dim);
 }
 
+// Ragged batches whose heads the vector kernel serves (one query head per KV
+// head, or fp32) take the token-balanced partition on it, one unit per
+// (sequence, query head).
+#ifndef FD_VALU_BALANCED
+#define FD_VALU_BALANCED 1
+#endif
+bool balanced_vector(int in_dtype, int head_dim, int group) {
+    return FD_VALU_BALANCED && !fd::split_mfma_supported(in_dtype, head_dim, group) &&
+           !large_group(in_dtype, head_dim, group);
+}
+
 // Shape of the tiled kernel's work-groups for nq queries per KV head: qt
 // query tiles per wave (the most a wave holds, but no more than there are
 // tiles) and, past what one wave holds, several waves per work-group sharing
@@ -267,7 +278,8 @@ int fused_waves(int batch, int heads_q, int heads_kv, int head_dim, int in_dtype
 int split_kernel(const fd::SplitArgs &a, int in_dtype) {
     const int group = a.heads_q / a.heads_kv;
     if (a.balanced)
-        return FD_KERNEL_BALANCED;
+        return balanced_vector(in_dtype, a.head_dim, group) ? FD_KERNEL_VECTOR
+                                                            : FD_KERNEL_BALANCED;
     if (a.tile_qt > 0 || large_group(in_dtype, a.head_dim, group))
         return FD_KERNEL_TILED;
     if (fd::split_mfma_supported(in_dtype, a.head_dim, group))
@@ -305,7 +317,7 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
         int rc = device_cus(&cus);
         if (rc != FD_OK)
             return rc;
-        a.valu_waves = a.fused_waves > 0 ? 0 : vector_waves(a, cus);
+        a.valu_waves = a.fused_waves > 0 || a.balanced ? 0 : vector_waves(a, cus);
         e = fd::launch_split_valu(a, in_dtype, stream);
     }
     }
@@ -316,10 +328,12 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
 
 // Token-balanced partition of a ragged batch (partition.h): used by
 // fd_decode's automatic plan when kv_lens is given and the grouped kernel
-// applies.  Workspace: o slots, LSE slots, unit descriptors, each 256-aligned.
+// applies, or (FD_VALU_BALANCED) the vector kernel would run.  Workspace: o
+// slots, LSE slots, unit descriptors, each 256-aligned.
 struct BalancedPlan {
     int num_wgs = 0, units = 0, gsz = 0;
     int waves = 1;  // per work-group (fd::split_mfma_balanced_waves)
+    bool vector = false;  // vector kernel: units (b, query head), gsz 1
     size_t o_bytes = 0, lse_bytes = 0, desc_bytes = 0;
     size_t total() const { return o_bytes + lse_bytes + desc_bytes; }
 };
@@ -330,20 +344,26 @@ bool balanced_applies(int heads_q, int heads_kv, int max_kv_len, int head_dim, i
     return num_splits == 0 && has_lens && max_kv_len > 0 &&
            (fd::split_mfma_supported(in_dtype, head_dim, group) ||
             (large_group(in_dtype, head_dim, group) &&
-             group <= fd::split_mfma_balanced_max_group(head_dim)));
+             group <= fd::split_mfma_balanced_max_group(head_dim)) ||
+            balanced_vector(in_dtype, head_dim, group));
 }
 
-int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim, int cus,
-                  BalancedPlan *p) {
+int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim,
+                  int in_dtype, int cus, BalancedPlan *p) {
     // slot indices (work-group + unit rank) and the combine's row grid
     // (batch * heads_q) are 32-bit in the kernels
-    const long long units = (long long)batch * heads_kv;
-    p->gsz = heads_q / heads_kv;
-    p->waves = fd::split_mfma_balanced_waves(head_dim, p->gsz);
+    p->vector = balanced_vector(in_dtype, head_dim, heads_q / heads_kv);
+    // vector kernel: one unit per (sequence, query head), one-wave work-groups
+    // at kWavesPerCU per CU; matrix cores: one per (sequence, KV head)
+    const long long units = (long long)batch * (p->vector ? heads_q : heads_kv);
+    p->gsz = p->vector ? 1 : heads_q / heads_kv;
+    p->waves = p->vector ? 1 : fd::split_mfma_balanced_waves(head_dim, p->gsz);
     if (p->waves < 1)
         return fail(FD_ERR_INVALID, "group of %d too large for the balanced plan", p->gsz);
     const long long wgs =
-        (long long)cus * fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz) * kBalancedRounds;
+        (long long)cus *
+        (p->vector ? fd::kWavesPerCU : fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz)) *
+        kBalancedRounds;
     if (units + wgs > 0x7fffffffLL || (long long)batch * heads_q > 0x7fffffffLL)
         return fail(FD_ERR_INVALID, "batch * heads exceeds the launch limit of the balanced plan");
     p->units = (int)units;
@@ -404,14 +424,15 @@ int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim
     if (balanced_applies(heads_q, heads_kv, max_kv_len, head_dim, in_dtype, has_lens,
                          num_splits)) {
         if ((rc = need_cus()) != FD_OK ||
-            (rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, cus, &p->bal)) !=
+            (rc = balanced_plan(batch, heads_q, heads_kv, max_kv_len, head_dim, in_dtype, cus,
+                               &p->bal)) !=
                 FD_OK)
             return rc;
         r.route = FD_ROUTE_BALANCED;
-        r.kernel = FD_KERNEL_BALANCED;
+        r.kernel = p->bal.vector ? FD_KERNEL_VECTOR : FD_KERNEL_BALANCED;
         r.work_groups = p->bal.num_wgs;
         r.waves_per_group = p->bal.waves;
-        r.query_tiles = (group + 15) / 16;
+        r.query_tiles = p->bal.vector ? 0 : (group + 15) / 16;
         r.launches = 2;
         r.workspace_bytes = p->bal.total();
         return FD_OK;
@@ -786,7 +807,8 @@ int cascade_plan(int batch, int heads_q, int heads_kv, int prefix_len, int max_s
         rc = device_cus(&cus);
         if (rc != FD_OK)
             return rc;
-        rc = balanced_plan(batch, heads_q, heads_kv, max_suffix_len, head_dim, cus, &p->bal);
+        rc = balanced_plan(batch, heads_q, heads_kv, max_suffix_len, head_dim, in_dtype, cus,
+                           &p->bal);
         if (rc != FD_OK)
             return rc;
         p->bs = 0;

@@ -43,6 +43,7 @@
 #include <atomic>
 
 #include "dev_common.h"
+#include "partition.h"
 
 namespace fd {
 namespace {
@@ -109,7 +110,13 @@ __device__ __forceinline__ void unpack_row(const uint32_t *w, float *f) {
 // FUSED: one work-group per (sequence, head group) whose wave w computes split
 // w (num_splits <= THREADS / 64); the LDS merge then combines the splits and
 // the work-group writes the final output (a combine stage in LDS).
-template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false>
+// BAL: token-balanced partition (partition_plan.h) with one query head per
+// unit: a one-wave work-group walks its share piece by piece, each piece of
+// unit (b, h) writing its (o, LSE) to slot w + rank(unit) and the unit's
+// first piece its descriptor {first slot, count}, as the matrix-core
+// balanced kernel does for a group.
+template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false,
+          bool BAL = false>
 __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     using L = Layout<DT, D, LPR>;
     constexpr int EPL = L::EPL;
@@ -121,6 +128,8 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     // or (FUSED) each wave's rows share that wave's split
     constexpr int TPS = (FUSED ? RPW : kRows) / HPW;
     static_assert(kRows % HPW == 0 && RPW % HPW == 0, "HPW must divide the row counts");
+    static_assert(!BAL || (THREADS == 64 && HPW == 1 && !FUSED),
+                  "balanced pieces run on one-wave work-groups of one head");
 
     __shared__ float sm_acc[kRows][D];
     __shared__ float sm_m[kRows];
@@ -132,22 +141,11 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     const int hoff = row % HPW;                          // head of this row within the group
     const int tslot = (FUSED ? row % RPW : row) / HPW;  // token slot of this row
 
-    // Work-group -> (b, head group, split); the head group varies fastest so
-    // that neighbouring work-groups read neighbouring head rows of the same
-    // tokens.  FUSED: work-group -> (b, head group), split = wave.
-    const int ngroups = a.heads_q / HPW;
-    const int hg = blockIdx.x % ngroups;
-    const int rest = blockIdx.x / ngroups;
-    const int split = FUSED ? tid / 64 : rest % a.num_splits;
-    const int b = FUSED ? rest : rest / a.num_splits;
+    // One piece: tokens [t0, t1) of sequence b for head group hg, written as
+    // split `split` of its rows (fixed splits) or to slot `bslot` (BAL).
+    auto run = [&](int b, int hg, int split, long t0, long t1, long bslot) {
     const int hq = hg * HPW + hoff;
     const int kvh = hq / (a.heads_q / a.heads_kv);
-
-    int n = a.kv_lens ? a.kv_lens[b] : a.max_kv_len;
-    n = n < 0 ? 0 : (n > a.max_kv_len ? a.max_kv_len : n);
-    // (FUSED waves past num_splits get an empty range)
-    const long t0 = split < a.num_splits ? (long)split * a.split_len : (long)n;
-    const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
 
     float m = -INFINITY;  // running max of log2-domain scores in this row
     float l = 0.f;        // running sum of exp2(s - m)
@@ -337,7 +335,10 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
             compute_step(nsteps - 1, kw, vw);
     }
 
-    // Merge the TPS row states of each head.
+    // Merge the TPS row states of each head (BAL: after the previous piece's
+    // merge has read the LDS rows this one overwrites).
+    if constexpr (BAL)
+        __syncthreads();
     if (sub == 0) {
         sm_m[row] = m;
         sm_l[row] = l;
@@ -369,7 +370,11 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
             lse = (M + fast_log2(Ls)) * kLn2;
         }
         const size_t rowid = (size_t)b * a.heads_q + hg * HPW + hh;
-        if (a.o_part) {
+        if constexpr (BAL) {
+            a.o_part[(size_t)bslot * D + dd] = out;
+            if (dd == 0)
+                a.lse_part[bslot] = lse;
+        } else if (a.o_part) {
             const size_t slot =
                 rowid * (a.part_stride ? a.part_stride : a.num_splits) + a.part_offset + split;
             a.o_part[slot * D + dd] = out;
@@ -386,6 +391,40 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
             if (dd == 0 && a.lse)
                 a.lse[rowid] = lse;
         }
+    }
+    };
+
+    if constexpr (BAL) {
+        // share index (partition_plan.h: neighbouring work-groups take
+        // consecutive heads of one token range when the heads come in
+        // multiples of 8)
+        const int w = share_index((int)blockIdx.x, a.heads_q, a.num_wgs);
+        PieceCursor c;
+        if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_q, w, a.num_wgs, c))
+            return;
+        walk_share(a.kv_lens, a.batch, a.max_kv_len, a.heads_q, w, c, [&](const Piece &p) {
+            run(p.b, p.x, 0, p.t0, p.t1, p.slot);
+            if (p.first && threadIdx.x == 0) {  // the unit's descriptor {first slot, count}
+                const size_t u = (size_t)p.b * a.heads_q + p.x;
+                a.unit_desc[2 * u] = p.slot;
+                a.unit_desc[2 * u + 1] = p.desc_count;
+            }
+        });
+    } else {
+        // Work-group -> (b, head group, split); the head group varies fastest so
+        // that neighbouring work-groups read neighbouring head rows of the same
+        // tokens.  FUSED: work-group -> (b, head group), split = wave.
+        const int ngroups = a.heads_q / HPW;
+        const int hg = blockIdx.x % ngroups;
+        const int rest = blockIdx.x / ngroups;
+        const int split = FUSED ? tid / 64 : rest % a.num_splits;
+        const int b = FUSED ? rest : rest / a.num_splits;
+        int n = a.kv_lens ? a.kv_lens[b] : a.max_kv_len;
+        n = n < 0 ? 0 : (n > a.max_kv_len ? a.max_kv_len : n);
+        // (FUSED waves past num_splits get an empty range)
+        const long t0 = split < a.num_splits ? (long)split * a.split_len : (long)n;
+        const long t1 = t0 + a.split_len < n ? t0 + a.split_len : n;
+        run(b, hg, split, t0, t1, 0);
     }
 }
 
@@ -407,12 +446,14 @@ int lds_per_cu() {
     return v > 0 ? v : 0;
 }
 
-template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false>
+template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false,
+          bool BAL = false>
 hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
     constexpr int kRows = THREADS / LPR;
     constexpr size_t kStatic = sizeof(float) * (size_t)(kRows * D + 2 * kRows);
-    const long grid = (long)a.batch * (a.heads_q / HPW) * (FUSED ? 1 : a.num_splits);
-    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR, PAGED, FUSED>;
+    const long grid =
+        BAL ? (long)a.num_wgs : (long)a.batch * (a.heads_q / HPW) * (FUSED ? 1 : a.num_splits);
+    auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR, PAGED, FUSED, BAL>;
     size_t pad = 0;
     const int lds = lds_per_cu();
     if (wg_per_cu > 0 && lds > 0) {
@@ -467,6 +508,11 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         default:
             return hipErrorInvalidValue;
         }
+    }
+    if (a.balanced) {  // token-balanced shares, one-wave work-groups
+        return a.block_table
+                   ? launch_cfg<DT, D, 64, 1, LPR, true, false, true>(a, kWavesPerCU, stream)
+                   : launch_cfg<DT, D, 64, 1, LPR, false, false, true>(a, kWavesPerCU, stream);
     }
     if (a.block_table) {
         if (a.valu_waves > 1)

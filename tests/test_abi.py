@@ -200,6 +200,13 @@ def test_decode_plan_struct_layout():
                                                       waves_per_group=8, work_groups=256)),
     ((16, 272, 2, 16384, 128, fd.BF16, 1, 0, 0), dict(route=2, kernel=2, query_tiles=8,
                                                       waves_per_group=4)),
+    # ragged with one query head per KV head, or fp32: balanced on the vector
+    # kernel, one-wave work-groups at two per CU, one unit per (sequence, query head)
+    ((16, 32, 32, 32768, 128, fd.BF16, 1, 0, 0), dict(route=3, kernel=0, query_tiles=0,
+                                                      waves_per_group=1, launches=2,
+                                                      work_groups=512)),
+    ((6, 8, 2, 4096, 64, fd.F32, 1, 0, 0), dict(route=3, kernel=0, query_tiles=0,
+                                                waves_per_group=1, work_groups=512)),
     # explicit splits: one split writes o itself; fp32 grouped heads stay on the vector kernel
     ((2, 8, 2, 1000, 128, fd.BF16, 1, 1, 0), dict(route=0, kernel=1, num_splits=1,
                                                   split_len=1000, launches=1, workspace_bytes=0)),
@@ -218,9 +225,12 @@ def test_decode_plan_routes(lib, case):
         assert p.workspace_bytes == lib.fd_workspace_bytes(batch, hq, p.num_splits, d)
         assert p.num_splits * p.split_len >= n
     elif p.route == fd.ROUTES.index("balanced"):
-        # o and LSE slots for work-groups + units, and one descriptor per unit
-        slots = p.work_groups + batch * hkv
-        assert p.workspace_bytes >= slots * (hq // hkv) * (d + 1) * 4 + batch * hkv * 8
+        # o and LSE slots for work-groups + units, and one descriptor per unit;
+        # units are (sequence, KV head) of hq / hkv rows on the matrix cores,
+        # (sequence, query head) of one row on the vector kernel
+        units, gsz = (batch * hq, 1) if p.kernel == 0 else (batch * hkv, hq // hkv)
+        slots = p.work_groups + units
+        assert p.workspace_bytes >= slots * gsz * (d + 1) * 4 + units * 8
     else:
         assert p.launches == 1 and p.workspace_bytes == 0
     # the plan does not change on a repeated call

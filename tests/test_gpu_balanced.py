@@ -1,5 +1,6 @@
 """GPU parity of the token-balanced partition (fd_decode's automatic plan for
-ragged grouped-head batches) against the fp64 oracle, through the C ABI.
+ragged batches: grouped heads on the matrix-core kernel, one query head per
+KV head or fp32 on the vector kernel) against the fp64 oracle, through the C ABI.
 
 The partition cuts the flattened (KV head, sequence, token) space into equal
 shares; these cases aim at its corners: empty sequences between full ones,
@@ -21,7 +22,7 @@ from decode_attention_03_amd import fd, workloads
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f16": (1.5e-2, 1e-3), "bf16": (1.5e-2, 1e-3)}
+TOL = {"f32": (1e-5, 1e-5), "f16": (1.5e-2, 1e-3), "bf16": (1.5e-2, 1e-3)}
 
 # name, batch, heads_kv, group, d, dtype, max_kv_len, lens (None: drawn from seed)
 CASES = [
@@ -52,6 +53,20 @@ CASES = [
     ("group128_d128_8waves", 6, 1, 128, 128, "bf16", 2500, [2500, 17, 0, 1300, 2499, 64]),
     ("group40_d256_4waves", 3, 2, 40, 256, "f16", 1800, [1800, 900, 0]),
     ("group24_d256_2waves", 5, 1, 24, 256, "bf16", 1500, [0, 1500, 3, 777, 1499]),
+    # the vector kernel's pieces: one unit per (sequence, query head); query
+    # heads in multiples of 8 that divide the work-group count take the
+    # permuted share order (8, 32), 40 and 3 the plain one
+    ("vec_mha_zeros_between", 7, 4, 1, 128, "bf16", 5000, [0, 5000, 0, 0, 17, 3000, 0]),
+    ("vec_mha_all_empty", 5, 2, 1, 64, "f16", 64, [0, 0, 0, 0, 0]),
+    ("vec_mha_all_one_token", 40, 3, 1, 64, "bf16", 8, [1] * 40),
+    ("vec_mha_batch130", 130, 2, 1, 128, "f16", 700, None),
+    ("vec_mha_one_long_row", 3, 1, 1, 256, "f16", 40000, [1, 40000, 2]),
+    ("vec_mha_clamped_h8", 4, 8, 1, 128, "bf16", 300, [0, 300, 5000, -3]),
+    ("vec_mha_h32_d256", 5, 32, 1, 256, "bf16", 3000, [3000, 1, 0, 2047, 1500]),
+    ("vec_mha_h40_d64", 3, 40, 1, 64, "f16", 1000, [999, 0, 1000]),
+    ("vec_f32_mha_d64", 6, 4, 1, 64, "f32", 2000, [2000, 0, 17, 1999, 1, 640]),
+    ("vec_f32_gqa4_d128", 5, 2, 4, 128, "f32", 1500, [1500, 3, 0, 777, 1499]),
+    ("vec_f32_d256", 3, 2, 1, 256, "f32", 1000, [1000, 0, 999]),
 ]
 
 
@@ -95,6 +110,10 @@ def test_balanced_partition_cases(gpu, case):
     assert need > 0
     plan = fd.decode_plan(batch, hkv * group, hkv, n_max, d, q.dtype, True)
     assert plan["route"] == "balanced" and plan["workspace_bytes"] == need
+    vector = name.startswith("vec_")
+    assert (plan["kernel"] == "vector") == vector, plan
+    if vector:  # one unit per (sequence, query head), one-wave work-groups
+        assert plan["waves_per_group"] == 1 and plan["query_tiles"] == 0, plan
     if name.endswith("waves"):
         assert plan["waves_per_group"] == int(name[-6]), plan
     ws = torch.full((need // 4 + 1,), float("nan"), device=gpu)
@@ -106,10 +125,12 @@ def test_balanced_partition_cases(gpu, case):
     _check(name, o, lse, ro, rl, dtype)
 
 
-def test_balanced_matches_fixed_splits_and_repeats(gpu):
+@pytest.mark.parametrize("group", [8, 1])
+def test_balanced_matches_fixed_splits_and_repeats(gpu, group):
     """The balanced plan and a fixed-split plan of the same inputs agree to the
-    bf16 bounds; two balanced runs are bitwise equal."""
-    w, inp, eff = _case_inputs("zeros_between", 7, 2, 8, 128, "bf16", 5000,
+    bf16 bounds; two balanced runs are bitwise equal (matrix-core and vector
+    kernels)."""
+    w, inp, eff = _case_inputs("zeros_between", 7, 2, group, 128, "bf16", 5000,
                                [0, 5000, 0, 0, 17, 3000, 0])
     q, k, v = inp["q"].to(gpu), inp["k"].to(gpu), inp["v"].to(gpu)
     kl = inp["kv_lens"].to(gpu)
