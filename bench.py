@@ -46,10 +46,11 @@ def log(msg: str) -> None:
 class Prepared:
     """A workload resident on the GPU with pre-bound fd_decode arguments."""
 
-    def __init__(self, w: workloads.Workload, dev: torch.device, num_splits: int = 0):
+    def __init__(self, w: workloads.Workload, dev: torch.device, num_splits: int = 0,
+                 host: dict | None = None):
         self.w = w
         t0 = time.time()
-        inp = workloads.generate(w)
+        inp = workloads.generate(w) if host is None else host
         self.host = inp
         lens = inp["kv_lens"]
         self.kv_bytes = workloads.kv_bytes(w, lens)
@@ -119,8 +120,12 @@ class Prepared:
         # partials written (fixed splits: B per row; balanced: at most one per
         # work-group piece, bounded by work-groups + units, counted in full)
         if self.balanced:
-            pieces = self.dplan["work_groups"] + batch * hkv
-            self.part_bytes = pieces * (hq // hkv) * (d + 1) * 4
+            # units: (sequence, KV head) of hq / hkv rows on the matrix cores,
+            # (sequence, query head) of one row on the vector kernel
+            vec = self.dplan["kernel"] == "vector"
+            units, rows = (batch * hq, 1) if vec else (batch * hkv, hq // hkv)
+            pieces = self.dplan["work_groups"] + units
+            self.part_bytes = pieces * rows * (d + 1) * 4
         else:
             self.part_bytes = batch * hq * self.B * (d + 1) * 4 if self.B > 1 else 0
         self.split_bytes = self.kv_bytes + self.q.numel() * self.q.element_size() + self.part_bytes
@@ -531,6 +536,42 @@ def time_groups(steps: int, warmup: int, dev: torch.device) -> dict:
     return res
 
 
+RAGGED_MHA = [
+    workloads.Workload("mha_bf16_b8_h32_d128_ragged512_32768", batch=8, heads_q=32, heads_kv=32,
+                       head_dim=128, max_kv_len=32768, dtype="bf16", out_dtype="bf16", seed=15,
+                       ragged=(512, 32768)),
+    workloads.Workload("mha_f16_b4_h16_d256_ragged1024_32768", batch=4, heads_q=16, heads_kv=16,
+                       head_dim=256, max_kv_len=32768, dtype="f16", out_dtype="f16", seed=16,
+                       ragged=(1024, 32768)),
+]
+
+
+def time_ragged_mha(steps: int, warmup: int, dev: torch.device) -> dict:
+    """Decode steps of ragged multi-head batches: the library's plan (the
+    token-balanced partition on the vector kernel) and, on the same inputs,
+    the fixed splits the library picks for ragged lengths."""
+    out = {}
+    for w in RAGGED_MHA:
+        p = Prepared(w, dev)
+        t = time_steps(p, steps, warmup)
+        su = time_split_kernel(p, steps, warmup)
+        r = summarize(p, t, su)
+        host, B = p.host, p.B
+        p.free()
+        del p
+        torch.cuda.empty_cache()
+        f = Prepared(w, dev, B, host=host)
+        tf = time_steps(f, steps, warmup)
+        r["fixed_splits"] = {"num_splits": f.B, "split_len": f.L,
+                             "us_per_step": round(tf["wall_us_per_step"], 2)}
+        r["speedup_vs_fixed_splits"] = round(tf["wall_us_per_step"] / t["wall_us_per_step"], 3)
+        f.free()
+        del f, host
+        torch.cuda.empty_cache()
+        out[w.name] = r
+    return {"workload": "ragged_mha", "cases": out}
+
+
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
     """The fp64 oracle on the host cores, on whole decode steps of the same
     workload, repeated until about budget_s seconds of wall time."""
@@ -658,7 +699,7 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="oracle seconds (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
-    ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups"), default=None,
+    ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups", "ragged_mha"), default=None,
                     help="time only this section of the full run and print its JSON (profiling)")
     ap.add_argument("--library", default=None,
                     help="time a tuning variant (decode_attention_03_amd/variants/NAME.so, built "
@@ -705,6 +746,8 @@ def main() -> int:
             sec = time_shard(args.steps, args.warmup, dev)
         elif args.section == "groups":
             sec = time_groups(args.steps, args.warmup, dev)
+        elif args.section == "ragged_mha":
+            sec = time_ragged_mha(args.steps, args.warmup, dev)
         else:  # the paged step of the ragged grouped workload, 16-token pages
             w = workloads.WORKLOADS[4]
             sec = {"workload": w.name, **time_paged(w, dev, 16, args.steps, args.warmup)}
@@ -822,6 +865,10 @@ def main() -> int:
         groups = time_groups(args.steps, args.warmup, dev)
         log(f"[bench] groups: {groups}")
         result["groups"] = groups
+        # ragged multi-head batches: balanced pieces on the vector kernel
+        rm = time_ragged_mha(args.steps, args.warmup, dev)
+        log(f"[bench] ragged_mha: {rm}")
+        result["ragged_mha"] = rm
         for c in late:
             run_workload(c)
     print(json.dumps(result), flush=True)

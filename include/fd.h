@@ -119,7 +119,8 @@ int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_l
 #define FD_ROUTE_BALANCED 3 /* token-balanced pieces into the workspace, then the combine */
 
 /* Split kernels (fd_plan.kernel). */
-#define FD_KERNEL_VECTOR 0   /* vector ALUs, one query head per wave (MHA, fp32) */
+#define FD_KERNEL_VECTOR 0   /* vector ALUs, one query head per wave (MHA, fp32); on
+                                FD_ROUTE_BALANCED it walks the token-balanced shares */
 #define FD_KERNEL_GROUPED 1  /* matrix cores, one 16-query tile of a KV head's group */
 #define FD_KERNEL_TILED 2    /* matrix cores, several 16-query tiles per K/V read */
 #define FD_KERNEL_BALANCED 3 /* matrix cores over the token-balanced partition */
@@ -210,6 +211,10 @@ int fd_combine_mlo(const float *o_part, const float *m_part, const float *l_part
  *       [P3] §2.3.5).  The split points depend on the lengths, so results
  *       agree with a fixed-split run up to rounding, and are reproducible
  *       for fixed inputs.
+ *     - kv_lens given and heads the vector kernel serves (one query head per
+ *       KV head in bf16/f16, or fp32 with any group): the same partition
+ *       with one unit per (sequence, query head) instead of (sequence, KV
+ *       head), on one-wave work-groups (CUs x 2).
  *     - otherwise: B and L from fd_choose_splits (ragged = kv_lens != NULL).
  *   num_splits > 0, split_len == 0: L = ceil(max_kv_len / num_splits)
  *     ([P2] §4 chunking).  num_splits > 0, split_len > 0: used as given.
