@@ -88,8 +88,17 @@ FD_HD int balanced_owner(long long p, long long total, int w_eff) {
 // consecutive heads, so each XCD streams whole heads, as it does under fixed
 // splits (measured 1.2 us faster per step on 8 KV heads and 0.7 us slower on
 // 2, where the plain order stays).  A bijection of [0, num_wgs) either way.
+#ifndef FD_SHARE_ROTATE
+#define FD_SHARE_ROTATE 0
+#endif
 FD_HD int share_index(int block, int hx, int num_wgs) {
-    return hx % 8 == 0 && num_wgs % hx == 0 ? (block % hx) * (num_wgs / hx) + block / hx : block;
+    if (hx % 8 != 0 || num_wgs % hx != 0)
+        return block;
+    const int s = block / hx;  // token range (share within a head)
+    // FD_SHARE_ROTATE: head of position j within range s rotated by s, so that
+    // each XCD streams every head in turn rather than the same ones throughout
+    const int x = FD_SHARE_ROTATE ? (block % hx + s) % hx : block % hx;
+    return x * (num_wgs / hx) + s;
 }
 
 // Where one work-group's share of the flattened space starts.

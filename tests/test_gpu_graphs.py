@@ -58,7 +58,7 @@ def _decode_case(gpu, w, inp, num_splits=0):
 
 @pytest.mark.parametrize("case", ["fused_small_f32", "mha_one_split", "mha_splits_combine",
                                   "gqa_ragged_balanced", "mqa_ragged_four_waves",
-                                  "mqa_two_wave_tiles"])
+                                  "mqa_two_wave_tiles", "mha_ragged_balanced_vector"])
 def test_decode_graph_replay(gpu, case):
     if case == "fused_small_f32":
         w = workloads.WORKLOADS[1]
@@ -77,6 +77,10 @@ def test_decode_graph_replay(gpu, case):
     elif case == "mqa_ragged_four_waves":  # balanced plan, four waves per work-group
         w, inp = workloads.custom(4, 64, 1, 128, 5000, dtype="bf16", seed=45,
                                   lens=[5000, 0, 1234, 4097])
+        B = 0
+    elif case == "mha_ragged_balanced_vector":  # balanced plan on the vector kernel
+        w, inp = workloads.custom(5, 16, 16, 128, 7000, dtype="bf16", seed=47,
+                                  lens=[7000, 0, 33, 4096, 6999])
         B = 0
     else:  # tiled kernel, two waves of one tile each, fixed splits
         w, inp = workloads.custom(3, 32, 1, 128, 3000, dtype="f16", seed=46)

@@ -68,6 +68,12 @@ def test_noalloc_matches_decode_on_successive_calls(gpu):
     assert _run_pair(gpu, w4) == 0
     w5 = workloads.Workload("na_grouped", 2, 16, 2, 256, 3000, "f16", "f16", 44)
     assert _run_pair(gpu, w5) > 0
+    # 6: ragged multi-head (balanced plan on the vector kernel), then a smaller one
+    w6 = workloads.Workload("na_bal_vec", 6, 16, 16, 128, 5000, "bf16", "bf16", 45,
+                            ragged=(0, 5000))
+    w7 = workloads.Workload("na_bal_vec_f32", 3, 4, 2, 64, 2000, "f32", "f32", 46,
+                            ragged=(1, 2000))
+    assert _run_pair(gpu, w6) > _run_pair(gpu, w7) > 0
 
 
 def test_noalloc_refuses_steps_beyond_the_scratch(gpu):
