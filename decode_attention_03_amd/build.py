@@ -26,7 +26,8 @@ ARCH = "gfx950"
 #: the source files each kernel family is compiled from; a measurement taken
 #: on a kernel stays valid while these files are unchanged
 KERNEL_SOURCES = {
-    "split_valu": ["split_valu.hip", "dev_common.h", "fd_internal.h", "mfma_policy.h"],
+    "split_valu": ["split_valu.hip", "partition.h", "partition_plan.h", "dev_common.h",
+                   "fd_internal.h", "mfma_policy.h"],
     "split_mfma": ["split_mfma.hip", "partition.h", "partition_plan.h", "dev_common.h",
                    "fd_internal.h", "mfma_policy.h"],
     "combine": ["combine.hip", "partition.h", "partition_plan.h", "dev_common.h",
