@@ -131,8 +131,8 @@ def main() -> int:
     ap.add_argument("--pmc-steps", type=int, default=3)
     ap.add_argument("--skip-copy", action="store_true",
                     help="reuse the copy calibration already in RAW")
-    ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups"), default=None,
-                    help="profile one section of bench.py instead of a named workload")
+    ap.add_argument("--section", choices=("cascade", "paged", "shard", "groups", "ragged_mha"),
+                    default=None, help="profile one section of bench.py instead of a named workload")
     args = ap.parse_args()
     if args.section:
         return section_main(args)
@@ -335,7 +335,9 @@ def section_main(args) -> int:
     section launches (cascade: the shared-prefix kernel, the suffix kernel and
     the combine; paged: the ragged grouped workload over 16-token pages;
     shard: one GPU's share of the long-context workload and the merge;
-    groups: six shapes with 32 to 128 query heads per KV head)."""
+    groups: six shapes with 32 to 128 query heads per KV head; ragged_mha:
+    two ragged multi-head batches, balanced on the vector kernel and as
+    fixed splits)."""
     raw = os.path.abspath(args.raw)
     out = os.path.abspath(args.out)
     os.makedirs(raw, exist_ok=True)
