@@ -569,7 +569,7 @@ def time_ragged_mha(steps: int, warmup: int, dev: torch.device) -> dict:
         del f, host
         torch.cuda.empty_cache()
         out[w.name] = r
-    return {"workload": "ragged_mha", "cases": out}
+    return {"workload": "mha_ragged_bf16_d128_and_f16_d256", "cases": out}
 
 
 def cpu_baseline(p: Prepared, budget_s: float) -> dict:
