@@ -222,6 +222,38 @@ void check_decode_through_stubs() {
                           d, FD_BF16, FD_BF16, 0.0883883f, fake, (float *)fake, c0, bytes,
                           nullptr) != FD_OK)
         fail(fd_last_error());
+    // ragged multi-head and fp32 grouped batches: the balanced partition on the
+    // vector kernel, one unit per (sequence, query head); and a cascade whose
+    // ragged suffixes take it
+    struct V {
+        int hq, hkv, d, dt;
+    } vs[] = {{32, 32, 128, FD_BF16}, {16, 16, 256, FD_F16}, {8, 2, 64, FD_F32}};
+    for (const V &v : vs) {
+        if (fd_decode_workspace_bytes(batch, v.hq, v.hkv, n_max, v.d, v.dt, 1, 0, 0, &bytes) !=
+            FD_OK)
+            fail(fd_last_error());
+        std::vector<char> vws(bytes + 256);
+        char *v0 = vws.data() + (256 - ((uintptr_t)vws.data() & 255));
+        log.workspace_end = v0 + bytes;
+        const long long b0 = log.balanced, s0 = log.split_valu;
+        if (fd_decode(fake, fake, fake, lens.data(), batch, v.hq, v.hkv, n_max, v.d, v.dt, v.dt,
+                      0.1f, 0, 0, fake, (float *)fake, v0, bytes, nullptr) != FD_OK)
+            fail(fd_last_error());
+        if (log.balanced != b0 + 1 || log.split_valu != s0 + 1)
+            fail("fd_decode did not take the balanced vector route", v.hq, v.hkv);
+    }
+    if (fd_cascade_workspace_bytes(batch, 32, 32, 4096, s_max, 128, FD_BF16, 1, &bytes) != FD_OK)
+        fail(fd_last_error());
+    std::vector<char> mws(bytes + 256);
+    char *m0 = mws.data() + (256 - ((uintptr_t)mws.data() & 255));
+    log.workspace_end = m0 + bytes;
+    const long long vb0 = log.balanced;
+    if (fd_decode_cascade(fake, fake, fake, 4096, fake, fake, suf.data(), batch, 32, 32, s_max,
+                          128, FD_BF16, FD_BF16, 0.0883883f, fake, (float *)fake, m0, bytes,
+                          nullptr) != FD_OK)
+        fail(fd_last_error());
+    if (log.balanced != vb0 + 1)
+        fail("multi-head cascade suffix did not take the balanced route", log.balanced);
     log.workspace_end = nullptr;
     // an undersized workspace is refused before any launch
     const long long launched = log.split_mfma;

@@ -50,25 +50,13 @@ const char *hipGetErrorString(hipError_t) { return "stubbed HIP runtime"; }
 }
 
 namespace fd {
+namespace {
 
-hipError_t launch_split_valu(const SplitArgs &a, int, hipStream_t) {
-    ++g_log.split_valu;
-    if (a.num_splits < 1 || a.split_len < 1 ||
-        (long long)a.num_splits * a.split_len < a.max_kv_len)
-        die("vector split launch with a partition that does not cover the cache");
-    return hipSuccess;
-}
-
-hipError_t launch_split_mfma(const SplitArgs &a, int, hipStream_t) {
-    ++g_log.split_mfma;
-    if (!a.balanced) {
-        if (a.num_splits < 1 || a.split_len < 1 ||
-            (long long)a.num_splits * a.split_len < a.max_kv_len)
-            die("matrix-core split launch with a partition that does not cover the cache");
-        return hipSuccess;
-    }
+// The token-balanced split stage over units of hx heads each (the matrix-core
+// kernel: KV heads, gsz = heads_q / heads_kv query rows per slot; the vector
+// kernel: query heads, one row per slot): every share walked on the host.
+void check_balanced(const SplitArgs &a, int hx) {
     ++g_log.balanced;
-    const int hx = a.heads_kv;
     const long long units = (long long)a.batch * hx;
     const long long slots = (long long)a.num_wgs + units;
     // the layout the plan carved: o slots, LSE slots, descriptors
@@ -98,6 +86,31 @@ hipError_t launch_split_mfma(const SplitArgs &a, int, hipStream_t) {
             ++g_log.pieces;
         });
     }
+}
+
+}  // namespace
+
+hipError_t launch_split_valu(const SplitArgs &a, int, hipStream_t) {
+    ++g_log.split_valu;
+    if (a.balanced) {  // one unit per (sequence, query head)
+        check_balanced(a, a.heads_q);
+        return hipSuccess;
+    }
+    if (a.num_splits < 1 || a.split_len < 1 ||
+        (long long)a.num_splits * a.split_len < a.max_kv_len)
+        die("vector split launch with a partition that does not cover the cache");
+    return hipSuccess;
+}
+
+hipError_t launch_split_mfma(const SplitArgs &a, int, hipStream_t) {
+    ++g_log.split_mfma;
+    if (!a.balanced) {
+        if (a.num_splits < 1 || a.split_len < 1 ||
+            (long long)a.num_splits * a.split_len < a.max_kv_len)
+            die("matrix-core split launch with a partition that does not cover the cache");
+        return hipSuccess;
+    }
+    check_balanced(a, a.heads_kv);
     return hipSuccess;
 }
 
