@@ -40,6 +40,10 @@
 // makes the combine stage unnecessary).  When even the splits of all rows
 // leave wave slots empty, one work-group per row runs one wave per split and
 // merges the splits in LDS (FUSED), so a small decode is a single launch.
+// Ragged batches instead take the token-balanced partition (BAL,
+// partition_plan.h): 2 * CUs one-wave work-groups, each walking an equal
+// share of the (query head, sequence, token) space piece by piece, every
+// piece an ordinary split of one row written to its slot.
 #include <atomic>
 
 #include "dev_common.h"
