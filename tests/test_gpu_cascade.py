@@ -45,6 +45,7 @@ def _check(name, o, lse, ro, rl, dtype):
 
 
 @pytest.mark.parametrize("dtype,group,d", [("bf16", 8, 128), ("bf16", 1, 128), ("f32", 1, 64),
+                                           ("f32", 4, 128), ("f16", 1, 256),
                                            ("f16", 4, 256), ("f16", 2, 64), ("bf16", 32, 128),
                                            ("bf16", 64, 128), ("f16", 40, 256)])
 @pytest.mark.parametrize("prefix_len", [0, 1, 777, 5000])
