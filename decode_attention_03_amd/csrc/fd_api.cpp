@@ -289,11 +289,13 @@ int split_kernel(const fd::SplitArgs &a, int in_dtype) {
 
 // Waves per vector-kernel work-group: the fused small-grid count, else two
 // when one-wave work-groups would leave wave slots of the GPU empty, else one.
-int vector_waves(const fd::SplitArgs &a, int cus) {
+int vector_waves(const fd::SplitArgs &a, int in_dtype, int cus) {
     if (a.fused_waves > 0)
         return a.fused_waves;
     // two-wave work-groups only where they all fit in the wave slots at once
-    const long long wgs = (long long)a.batch * a.heads_q * a.num_splits;
+    // (a work-group takes valu_heads_per_wg query heads)
+    const long long wgs = (long long)a.batch * a.heads_q * a.num_splits /
+                          fd::valu_heads_per_wg(in_dtype, a.heads_q / a.heads_kv);
     return wgs <= cus ? fd::kWavesPerCU : 1;  // kWavesPerCU waves each on at most one per CU
 }
 
@@ -317,7 +319,7 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
         int rc = device_cus(&cus);
         if (rc != FD_OK)
             return rc;
-        a.valu_waves = a.fused_waves > 0 || a.balanced ? 0 : vector_waves(a, cus);
+        a.valu_waves = a.fused_waves > 0 || a.balanced ? 0 : vector_waves(a, in_dtype, cus);
         e = fd::launch_split_valu(a, in_dtype, stream);
     }
     }
@@ -333,7 +335,7 @@ int launch_split(fd::SplitArgs a, int in_dtype, hipStream_t stream) {
 struct BalancedPlan {
     int num_wgs = 0, units = 0, gsz = 0;
     int waves = 1;  // per work-group (fd::split_mfma_balanced_waves)
-    bool vector = false;  // vector kernel: units (b, query head), gsz 1
+    bool vector = false;  // vector kernel: units (b, query-head group), gsz heads each
     size_t o_bytes = 0, lse_bytes = 0, desc_bytes = 0;
     size_t total() const { return o_bytes + lse_bytes + desc_bytes; }
 };
@@ -353,10 +355,12 @@ int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head
     // slot indices (work-group + unit rank) and the combine's row grid
     // (batch * heads_q) are 32-bit in the kernels
     p->vector = balanced_vector(in_dtype, head_dim, heads_q / heads_kv);
-    // vector kernel: one unit per (sequence, query head), one-wave work-groups
-    // at kWavesPerCU per CU; matrix cores: one per (sequence, KV head)
-    const long long units = (long long)batch * (p->vector ? heads_q : heads_kv);
-    p->gsz = p->vector ? 1 : heads_q / heads_kv;
+    // vector kernel: one unit per (sequence, group of valu_heads_per_wg query
+    // heads), one-wave work-groups at kWavesPerCU per CU; matrix cores: one
+    // per (sequence, KV head)
+    const int hpw = fd::valu_heads_per_wg(in_dtype, heads_q / heads_kv);
+    const long long units = (long long)batch * (p->vector ? heads_q / hpw : heads_kv);
+    p->gsz = p->vector ? hpw : heads_q / heads_kv;
     p->waves = p->vector ? 1 : fd::split_mfma_balanced_waves(head_dim, p->gsz);
     if (p->waves < 1)
         return fail(FD_ERR_INVALID, "group of %d too large for the balanced plan", p->gsz);
@@ -457,9 +461,11 @@ int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim
                                                 num_splits, cus)
                                   : 0;
         a.fused_waves = p->fused;
-        r.waves_per_group = vector_waves(a, cus);
+        r.waves_per_group = vector_waves(a, in_dtype, cus);
         r.query_tiles = 0;
-        r.work_groups = (int64_t)batch * heads_q * (p->fused > 0 ? 1 : num_splits);
+        r.work_groups = p->fused > 0 ? (int64_t)batch * heads_q
+                                     : (int64_t)batch * heads_q * num_splits /
+                                           fd::valu_heads_per_wg(in_dtype, group);
         break;
     case FD_KERNEL_GROUPED:
         r.waves_per_group = 1;
@@ -530,6 +536,8 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     // computed together, one per (sequence, KV head, tile group) when it takes
     // several tiles, else one per (sequence, query head)
     long long units = (long long)batch * (grouped ? heads_kv : heads_q);
+    if (!grouped)  // vector kernel: valu_heads_per_wg query heads per work-group
+        units /= fd::valu_heads_per_wg(in_dtype, group);
     int per_cu = grouped ? fd::kMfmaWgPerCU : kWorkGroupsPerCU;
     if (tiled) {
         const TiledShape t = tiled_shape(head_dim, group);

@@ -22,6 +22,21 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 #endif
 constexpr int kWavesPerCU = FD_WAVES_PER_CU;
 
+// Query heads per vector-kernel work-group (the kernel's HPW).  fp32 grouped
+// heads run on the vector kernel, one row of lanes per query head; taking up
+// to four heads of one KV head together puts their rows on the same token,
+// so one load instruction reads the same K/V addresses for all of them and
+// the memory path fetches those bytes once instead of once per query head.
+// One head otherwise (bf16/fp16 groups run on the matrix cores).
+#ifndef FD_VALU_HEAD_GROUP
+#define FD_VALU_HEAD_GROUP 1
+#endif
+inline int valu_heads_per_wg(int in_dtype, int group) {
+    if (!FD_VALU_HEAD_GROUP || in_dtype != kF32 || group < 2)
+        return 1;
+    return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
 // Resident one-wave work-groups per CU of the grouped (matrix-core) split
 // kernels; the token-balanced partition makes this many shares per CU.
 #ifndef FD_MFMA_WG_PER_CU

@@ -114,11 +114,11 @@ __device__ __forceinline__ void unpack_row(const uint32_t *w, float *f) {
 // FUSED: one work-group per (sequence, head group) whose wave w computes split
 // w (num_splits <= THREADS / 64); the LDS merge then combines the splits and
 // the work-group writes the final output (a combine stage in LDS).
-// BAL: token-balanced partition (partition_plan.h) with one query head per
-// unit: a one-wave work-group walks its share piece by piece, each piece of
-// unit (b, h) writing its (o, LSE) to slot w + rank(unit) and the unit's
-// first piece its descriptor {first slot, count}, as the matrix-core
-// balanced kernel does for a group.
+// BAL: token-balanced partition (partition_plan.h) over units of HPW query
+// heads: a one-wave work-group walks its share piece by piece, each piece of
+// unit (b, head group) writing its HPW (o, LSE) pairs to slot w + rank(unit)
+// and the unit's first piece its descriptor {first slot, count}, as the
+// matrix-core balanced kernel does for a group.
 template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED = false,
           bool BAL = false>
 __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     // or (FUSED) each wave's rows share that wave's split
     constexpr int TPS = (FUSED ? RPW : kRows) / HPW;
     static_assert(kRows % HPW == 0 && RPW % HPW == 0, "HPW must divide the row counts");
-    static_assert(!BAL || (THREADS == 64 && HPW == 1 && !FUSED),
-                  "balanced pieces run on one-wave work-groups of one head");
+    static_assert(!BAL || (THREADS == 64 && !FUSED),
+                  "balanced pieces run on one-wave work-groups");
 
     __shared__ float sm_acc[kRows][D];
     __shared__ float sm_m[kRows];
@@ -374,10 +374,10 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
             lse = (M + fast_log2(Ls)) * kLn2;
         }
         const size_t rowid = (size_t)b * a.heads_q + hg * HPW + hh;
-        if constexpr (BAL) {
-            a.o_part[(size_t)bslot * D + dd] = out;
+        if constexpr (BAL) {  // slot bslot holds the HPW heads' rows
+            a.o_part[((size_t)bslot * HPW + hh) * D + dd] = out;
             if (dd == 0)
-                a.lse_part[bslot] = lse;
+                a.lse_part[(size_t)bslot * HPW + hh] = lse;
         } else if (a.o_part) {
             const size_t slot =
                 rowid * (a.part_stride ? a.part_stride : a.num_splits) + a.part_offset + split;
@@ -402,14 +402,16 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         // share index (partition_plan.h: neighbouring work-groups take
         // consecutive heads of one token range when the heads come in
         // multiples of 8)
-        const int w = share_index((int)blockIdx.x, a.heads_q, a.num_wgs);
+        // units: (sequence, group of HPW query heads)
+        const int hx = a.heads_q / HPW;
+        const int w = share_index((int)blockIdx.x, hx, a.num_wgs);
         PieceCursor c;
-        if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, a.heads_q, w, a.num_wgs, c))
+        if (!balanced_start(a.kv_lens, a.batch, a.max_kv_len, hx, w, a.num_wgs, c))
             return;
-        walk_share(a.kv_lens, a.batch, a.max_kv_len, a.heads_q, w, c, [&](const Piece &p) {
+        walk_share(a.kv_lens, a.batch, a.max_kv_len, hx, w, c, [&](const Piece &p) {
             run(p.b, p.x, 0, p.t0, p.t1, p.slot);
             if (p.first && threadIdx.x == 0) {  // the unit's descriptor {first slot, count}
-                const size_t u = (size_t)p.b * a.heads_q + p.x;
+                const size_t u = (size_t)p.b * hx + p.x;
                 a.unit_desc[2 * u] = p.slot;
                 a.unit_desc[2 * u + 1] = p.desc_count;
             }
@@ -494,6 +496,25 @@ constexpr int lanes_per_row() {
     return r > 16 ? 16 : (r < 4 ? 4 : r);
 }
 
+// Every route but the fused one, HPW query heads per work-group.
+template <int DT, int D, int HPW>
+hipError_t launch_rows(const SplitArgs &a, hipStream_t stream) {
+    constexpr int LPR = lanes_per_row<DT, D>();
+    if (a.balanced) {  // token-balanced shares, one-wave work-groups
+        return a.block_table
+                   ? launch_cfg<DT, D, 64, HPW, LPR, true, false, true>(a, kWavesPerCU, stream)
+                   : launch_cfg<DT, D, 64, HPW, LPR, false, false, true>(a, kWavesPerCU, stream);
+    }
+    if (a.block_table) {
+        if (a.valu_waves > 1)
+            return launch_cfg<DT, D, 64 * kWavesPerCU, HPW, LPR, true>(a, 1, stream);
+        return launch_cfg<DT, D, 64, HPW, LPR, true>(a, kWavesPerCU, stream);
+    }
+    if (a.valu_waves > 1)
+        return launch_cfg<DT, D, 64 * kWavesPerCU, HPW, LPR, false>(a, 1, stream);
+    return launch_cfg<DT, D, 64, HPW, LPR, false>(a, kWavesPerCU, stream);
+}
+
 template <int DT, int D>
 hipError_t launch(const SplitArgs &a, hipStream_t stream) {
     constexpr int LPR = lanes_per_row<DT, D>();
@@ -513,19 +534,14 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
             return hipErrorInvalidValue;
         }
     }
-    if (a.balanced) {  // token-balanced shares, one-wave work-groups
-        return a.block_table
-                   ? launch_cfg<DT, D, 64, 1, LPR, true, false, true>(a, kWavesPerCU, stream)
-                   : launch_cfg<DT, D, 64, 1, LPR, false, false, true>(a, kWavesPerCU, stream);
+    if constexpr (DT == kF32) {  // grouped heads: HPW heads of one KV head per work-group
+        switch (valu_heads_per_wg(DT, a.heads_q / a.heads_kv)) {
+        case 4: return launch_rows<DT, D, 4>(a, stream);
+        case 2: return launch_rows<DT, D, 2>(a, stream);
+        default: break;
+        }
     }
-    if (a.block_table) {
-        if (a.valu_waves > 1)
-            return launch_cfg<DT, D, 64 * kWavesPerCU, 1, LPR, true>(a, 1, stream);
-        return launch_cfg<DT, D, 64, 1, LPR, true>(a, kWavesPerCU, stream);
-    }
-    if (a.valu_waves > 1)
-        return launch_cfg<DT, D, 64 * kWavesPerCU, 1, LPR, false>(a, 1, stream);
-    return launch_cfg<DT, D, 64, 1, LPR, false>(a, kWavesPerCU, stream);
+    return launch_rows<DT, D, 1>(a, stream);
 }
 
 template <int DT>

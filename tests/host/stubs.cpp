@@ -90,10 +90,10 @@ void check_balanced(const SplitArgs &a, int hx) {
 
 }  // namespace
 
-hipError_t launch_split_valu(const SplitArgs &a, int, hipStream_t) {
+hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t) {
     ++g_log.split_valu;
-    if (a.balanced) {  // one unit per (sequence, query head)
-        check_balanced(a, a.heads_q);
+    if (a.balanced) {  // one unit per (sequence, group of valu_heads_per_wg query heads)
+        check_balanced(a, a.heads_q / valu_heads_per_wg(in_dtype, a.heads_q / a.heads_kv));
         return hipSuccess;
     }
     if (a.num_splits < 1 || a.split_len < 1 ||
