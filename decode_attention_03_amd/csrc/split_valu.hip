@@ -14,8 +14,9 @@
 // holds one (head, token) pair at a time, every lane of the row owning d/16
 // contiguous elements of that token's K and V rows, so one 128-bit load per
 // lane fetches a whole 256-byte head row (d = 128, 16-bit types).  With
-// HPW > 1 the rows of one step read adjacent heads of the same token, i.e.
-// HPW * 256 contiguous bytes.  A row reduces its q.K partial sums with four
+// HPW > 1 (fp32 grouped heads) the rows of one step are HPW query heads of
+// one KV head on the same token, so their lanes read the same K/V bytes in
+// one instruction.  A row reduces its q.K partial sums with four
 // DPP adds and keeps a running (m, l, o) with the online update ([P1] §2.4.1
 // incremental form, o left unnormalised as in the block update of [P4]
 // §3.1); the rows of one head are merged in LDS with the same rule ([P4]
