@@ -23,11 +23,10 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int kWavesPerCU = FD_WAVES_PER_CU;
 
 // Query heads per vector-kernel work-group (the kernel's HPW).  fp32 grouped
-// heads run on the vector kernel, one row of lanes per query head; taking up
-// to four heads of one KV head together puts their rows on the same token,
-// so one load instruction reads the same K/V addresses for all of them and
-// the memory path fetches those bytes once instead of once per query head.
-// One head otherwise (bf16/fp16 groups run on the matrix cores).
+// heads run on the vector kernel; taking up to four heads of one KV head
+// together, every row of lanes holds their q rows and running states, so each
+// K/V row it loads serves all of them instead of being loaded once per query
+// head.  One head otherwise (bf16/fp16 groups run on the matrix cores).
 #ifndef FD_VALU_HEAD_GROUP
 #define FD_VALU_HEAD_GROUP 1
 #endif

@@ -14,9 +14,9 @@
 // holds one (head, token) pair at a time, every lane of the row owning d/16
 // contiguous elements of that token's K and V rows, so one 128-bit load per
 // lane fetches a whole 256-byte head row (d = 128, 16-bit types).  With
-// HPW > 1 (fp32 grouped heads) the rows of one step are HPW query heads of
-// one KV head on the same token, so their lanes read the same K/V bytes in
-// one instruction.  A row reduces its q.K partial sums with four
+// HPW > 1 (fp32 grouped heads) the work-group serves HPW query heads of one
+// KV head: every row holds all HPW q rows in registers and computes HPW dot
+// products, HPW running states, from each K/V row it loads once.  A row reduces its q.K partial sums with four
 // DPP adds and keeps a running (m, l, o) with the online update ([P1] §2.4.1
 // incremental form, o left unnormalised as in the block update of [P4]
 // §3.1); the rows of one head are merged in LDS with the same rule ([P4]
@@ -131,51 +131,56 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     constexpr int RPW = 64 / LPR;         // rows per wave
     // token slots per step position: the work-group's rows share one split,
     // or (FUSED) each wave's rows share that wave's split
-    constexpr int TPS = (FUSED ? RPW : kRows) / HPW;
-    static_assert(kRows % HPW == 0 && RPW % HPW == 0, "HPW must divide the row counts");
+    constexpr int TPS = FUSED ? RPW : kRows;
+    static_assert(HPW >= 1 && HPW <= 4, "one to four query heads per work-group");
     static_assert(!BAL || (THREADS == 64 && !FUSED),
                   "balanced pieces run on one-wave work-groups");
 
-    __shared__ float sm_acc[kRows][D];
-    __shared__ float sm_m[kRows];
-    __shared__ float sm_l[kRows];
+    __shared__ float sm_acc[HPW][kRows][D];
+    __shared__ float sm_m[HPW][kRows];
+    __shared__ float sm_l[HPW][kRows];
 
     const int tid = threadIdx.x;
     const int sub = tid % LPR;
     const int row = tid / LPR;
-    const int hoff = row % HPW;                          // head of this row within the group
-    const int tslot = (FUSED ? row % RPW : row) / HPW;  // token slot of this row
+    const int tslot = FUSED ? row % RPW : row;  // token slot of this row
 
-    // One piece: tokens [t0, t1) of sequence b for head group hg, written as
-    // split `split` of its rows (fixed splits) or to slot `bslot` (BAL).
+    // One piece: tokens [t0, t1) of sequence b for head group hg (query heads
+    // hg * HPW .. hg * HPW + HPW - 1, one KV head), written as split `split`
+    // of its rows (fixed splits) or to slot `bslot` (BAL).
     auto run = [&](int b, int hg, int split, long t0, long t1, long bslot) {
-    const int hq = hg * HPW + hoff;
-    const int kvh = hq / (a.heads_q / a.heads_kv);
+    const int kvh = hg * HPW / (a.heads_q / a.heads_kv);
 
-    float m = -INFINITY;  // running max of log2-domain scores in this row
-    float l = 0.f;        // running sum of exp2(s - m)
-    float acc[EPL];       // running sum of exp2(s - m) * V (unnormalised)
+    // per head of the group: running max of log2-domain scores in this row,
+    // running sum of exp2(s - m), and of exp2(s - m) * V (unnormalised)
+    float m[HPW], l[HPW], acc[HPW][EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        acc[i] = 0.f;
+    for (int h = 0; h < HPW; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            acc[h][i] = 0.f;
+    }
 
     if (t0 < t1) {
         const uint32_t lane_byte = L::HALF ? sub * 8u : sub * 16u;
-        // q row of this row's head.  fp32: pre-scaled into the log2 domain.
+        // q rows of the group's heads.  fp32: pre-scaled into the log2 domain.
         // 16-bit types: kept packed for the two-wide dot products (the
         // products of two bf16 or two fp16 values are exact in fp32), and the
         // scale is applied to the reduced score instead.
-        uint32_t qw[WORDS];
-        float qf[EPL];
-        {
+        uint32_t qw[HPW][WORDS];
+        float qf[HPW][EPL];
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
             const char *qrow = static_cast<const char *>(a.q) +
-                               ((size_t)b * a.heads_q + hq) * (size_t)L::ROW_BYTES;
-            load_row<DT, D, LPR>(qrow + lane_byte, qw);
+                               ((size_t)b * a.heads_q + hg * HPW + h) * (size_t)L::ROW_BYTES;
+            load_row<DT, D, LPR>(qrow + lane_byte, qw[h]);
             if constexpr (DT == kF32) {
-                unpack_row<DT, D, LPR>(qw, qf);
+                unpack_row<DT, D, LPR>(qw[h], qf[h]);
 #pragma unroll
                 for (int i = 0; i < EPL; ++i)
-                    qf[i] *= a.scale_log2;
+                    qf[h][i] *= a.scale_log2;
             }
         }
         // K/V addressing: a uniform (scalar) base per step plus a 32-bit
@@ -262,54 +267,57 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         // One step of arithmetic on the K/V words of step `st`.
         auto compute_step = [&](int st, const uint32_t (*kc)[WORDS],
                                 const uint32_t (*vc)[WORDS]) {
-            // scores s_u = (q * scale * log2e) . K_u, summed over the 16 lanes
-            float s[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float part = 0.f;
-                if constexpr (DT == kF32) {
-                    float kf[EPL];
-                    unpack_row<DT, D, LPR>(kc[u], kf);
+            for (int h = 0; h < HPW; ++h) {
+                // scores s_u = (q * scale * log2e) . K_u, summed over the row's lanes
+                float s[U];
 #pragma unroll
-                    for (int i = 0; i < EPL; ++i)
-                        part = __builtin_fmaf(qf[i], kf[i], part);
-                    s[u] = row_sum<LPR>(part);
-                } else {
+                for (int u = 0; u < U; ++u) {
+                    float part = 0.f;
+                    if constexpr (DT == kF32) {
+                        float kf[EPL];
+                        unpack_row<DT, D, LPR>(kc[u], kf);
 #pragma unroll
-                    for (int j = 0; j < WORDS; ++j)
-                        part = dot2<DT>(qw[j], kc[u][j], part);
-                    s[u] = row_sum<LPR>(part) * a.scale_log2;
+                        for (int i = 0; i < EPL; ++i)
+                            part = __builtin_fmaf(qf[h][i], kf[i], part);
+                        s[u] = row_sum<LPR>(part);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < WORDS; ++j)
+                            part = dot2<DT>(qw[h][j], kc[u][j], part);
+                        s[u] = row_sum<LPR>(part) * a.scale_log2;
+                    }
+                    const int rel = st * kStepTok + u * TPS + tslot;
+                    s[u] = rel < ntok ? s[u] : -INFINITY;
                 }
-                const int rel = st * kStepTok + u * TPS + tslot;
-                s[u] = rel < ntok ? s[u] : -INFINITY;
-            }
-            // online update of (m, l, acc) by U tokens
-            float mx = m;
+                // online update of (m, l, acc) of head h by U tokens
+                float mx = m[h];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                mx = fmaxf(mx, s[u]);
-            const float mref = mx == -INFINITY ? 0.f : mx;  // no token seen yet
-            const float alpha = fast_exp2(m - mref);
-            float p[U];
-            float psum = 0.f;
+                for (int u = 0; u < U; ++u)
+                    mx = fmaxf(mx, s[u]);
+                const float mref = mx == -INFINITY ? 0.f : mx;  // no token seen yet
+                const float alpha = fast_exp2(m[h] - mref);
+                float p[U];
+                float psum = 0.f;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                p[u] = fast_exp2(s[u] - mref);
-                psum += p[u];
-            }
-            l = __builtin_fmaf(l, alpha, psum);
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                acc[i] *= alpha;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float vf[EPL];
-                unpack_row<DT, D, LPR>(vc[u], vf);
+                for (int u = 0; u < U; ++u) {
+                    p[u] = fast_exp2(s[u] - mref);
+                    psum += p[u];
+                }
+                l[h] = __builtin_fmaf(l[h], alpha, psum);
 #pragma unroll
                 for (int i = 0; i < EPL; ++i)
-                    acc[i] = __builtin_fmaf(p[u], vf[i], acc[i]);
+                    acc[h][i] *= alpha;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float vf[EPL];
+                    unpack_row<DT, D, LPR>(vc[u], vf);
+#pragma unroll
+                    for (int i = 0; i < EPL; ++i)
+                        acc[h][i] = __builtin_fmaf(p[u], vf[i], acc[h][i]);
+                }
+                m[h] = mx;
             }
-            m = mx;
         };
 
         // Software pipeline over two register buffers: while step st is
@@ -340,19 +348,22 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
             compute_step(nsteps - 1, kw, vw);
     }
 
-    // Merge the TPS row states of each head (BAL: after the previous piece's
+    // Merge the row states of each head (BAL: after the previous piece's
     // merge has read the LDS rows this one overwrites).
     if constexpr (BAL)
         __syncthreads();
-    if (sub == 0) {
-        sm_m[row] = m;
-        sm_l[row] = l;
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        if (sub == 0) {
+            sm_m[h][row] = m[h];
+            sm_l[h][row] = l[h];
+        }
+#pragma unroll
+        for (int j = 0; j < WORDS; ++j)
+#pragma unroll
+            for (int e = 0; e < L::PW; ++e)
+                sm_acc[h][row][L::elem(sub, j, e)] = acc[h][j * L::PW + e];
     }
-#pragma unroll
-    for (int j = 0; j < WORDS; ++j)
-#pragma unroll
-        for (int e = 0; e < L::PW; ++e)
-            sm_acc[row][L::elem(sub, j, e)] = acc[j * L::PW + e];
     __syncthreads();
 
     for (int idx = tid; idx < HPW * D; idx += THREADS) {
@@ -360,16 +371,16 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
         const int dd = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int r = hh; r < kRows; r += HPW)
-            M = fmaxf(M, sm_m[r]);
+        for (int r = 0; r < kRows; ++r)
+            M = fmaxf(M, sm_m[hh][r]);
         float out = 0.f, lse = -INFINITY, Ls = 0.f;
         if (M != -INFINITY) {
             float Os = 0.f;
 #pragma unroll
-            for (int r = hh; r < kRows; r += HPW) {
-                const float w = fast_exp2(sm_m[r] - M);
-                Ls = __builtin_fmaf(w, sm_l[r], Ls);
-                Os = __builtin_fmaf(w, sm_acc[r][dd], Os);
+            for (int r = 0; r < kRows; ++r) {
+                const float w = fast_exp2(sm_m[hh][r] - M);
+                Ls = __builtin_fmaf(w, sm_l[hh][r], Ls);
+                Os = __builtin_fmaf(w, sm_acc[hh][r][dd], Os);
             }
             out = Os / Ls;
             lse = (M + fast_log2(Ls)) * kLn2;
@@ -457,7 +468,7 @@ template <int DT, int D, int THREADS, int HPW, int LPR, bool PAGED, bool FUSED =
           bool BAL = false>
 hipError_t launch_cfg(const SplitArgs &a, int wg_per_cu, hipStream_t stream) {
     constexpr int kRows = THREADS / LPR;
-    constexpr size_t kStatic = sizeof(float) * (size_t)(kRows * D + 2 * kRows);
+    constexpr size_t kStatic = sizeof(float) * (size_t)HPW * (kRows * D + 2 * kRows);
     const long grid =
         BAL ? (long)a.num_wgs : (long)a.batch * (a.heads_q / HPW) * (FUSED ? 1 : a.num_splits);
     auto kern = split_valu_kernel<DT, D, THREADS, HPW, LPR, PAGED, FUSED, BAL>;
