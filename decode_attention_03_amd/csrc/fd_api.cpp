@@ -24,7 +24,6 @@ namespace {
 
 constexpr int kVersion = 200;          // 0.2.0
 constexpr int kMaxSplits = 8192;       // combine keeps one weight per split in LDS
-constexpr int kWorkGroupsPerCU = fd::kWavesPerCU;  // resident one-wave work-groups per CU
 constexpr int kRaggedRounds = 4;       // work-group rounds aimed at for ragged batches
 constexpr int kMinSplitLenMha = 256;   // tokens; partial traffic ~0.8% of K/V at d = 128
 constexpr int kMinSplitLenPerHead = 64;  // grouped: tokens per query head of the group
@@ -295,7 +294,7 @@ int vector_waves(const fd::SplitArgs &a, int in_dtype, int cus) {
     // two-wave work-groups only where they all fit in the wave slots at once
     // (a work-group takes valu_heads_per_wg query heads)
     const long long wgs = (long long)a.batch * a.heads_q * a.num_splits /
-                          fd::valu_heads_per_wg(in_dtype, a.heads_q / a.heads_kv);
+                          fd::valu_heads_per_wg(in_dtype, a.head_dim, a.heads_q / a.heads_kv);
     return wgs <= cus ? fd::kWavesPerCU : 1;  // kWavesPerCU waves each on at most one per CU
 }
 
@@ -356,9 +355,9 @@ int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head
     // (batch * heads_q) are 32-bit in the kernels
     p->vector = balanced_vector(in_dtype, head_dim, heads_q / heads_kv);
     // vector kernel: one unit per (sequence, group of valu_heads_per_wg query
-    // heads), one-wave work-groups at kWavesPerCU per CU; matrix cores: one
-    // per (sequence, KV head)
-    const int hpw = fd::valu_heads_per_wg(in_dtype, heads_q / heads_kv);
+    // heads), one-wave work-groups at valu_wg_per_cu per CU; matrix cores:
+    // one per (sequence, KV head)
+    const int hpw = fd::valu_heads_per_wg(in_dtype, head_dim, heads_q / heads_kv);
     const long long units = (long long)batch * (p->vector ? heads_q / hpw : heads_kv);
     p->gsz = p->vector ? hpw : heads_q / heads_kv;
     p->waves = p->vector ? 1 : fd::split_mfma_balanced_waves(head_dim, p->gsz);
@@ -366,7 +365,7 @@ int balanced_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head
         return fail(FD_ERR_INVALID, "group of %d too large for the balanced plan", p->gsz);
     const long long wgs =
         (long long)cus *
-        (p->vector ? fd::kWavesPerCU : fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz)) *
+        (p->vector ? fd::valu_wg_per_cu(hpw) : fd::split_mfma_balanced_wg_per_cu(head_dim, p->gsz)) *
         kBalancedRounds;
     if (units + wgs > 0x7fffffffLL || (long long)batch * heads_q > 0x7fffffffLL)
         return fail(FD_ERR_INVALID, "batch * heads exceeds the launch limit of the balanced plan");
@@ -465,7 +464,7 @@ int make_plan(int batch, int heads_q, int heads_kv, int max_kv_len, int head_dim
         r.query_tiles = 0;
         r.work_groups = p->fused > 0 ? (int64_t)batch * heads_q
                                      : (int64_t)batch * heads_q * num_splits /
-                                           fd::valu_heads_per_wg(in_dtype, group);
+                                           fd::valu_heads_per_wg(in_dtype, head_dim, group);
         break;
     case FD_KERNEL_GROUPED:
         r.waves_per_group = 1;
@@ -537,8 +536,9 @@ int fd_choose_splits(int batch, int heads_q, int heads_kv, int max_kv_len, int h
     // several tiles, else one per (sequence, query head)
     long long units = (long long)batch * (grouped ? heads_kv : heads_q);
     if (!grouped)  // vector kernel: valu_heads_per_wg query heads per work-group
-        units /= fd::valu_heads_per_wg(in_dtype, group);
-    int per_cu = grouped ? fd::kMfmaWgPerCU : kWorkGroupsPerCU;
+        units /= fd::valu_heads_per_wg(in_dtype, head_dim, group);
+    int per_cu = grouped ? fd::kMfmaWgPerCU
+                         : fd::valu_wg_per_cu(fd::valu_heads_per_wg(in_dtype, head_dim, group));
     if (tiled) {
         const TiledShape t = tiled_shape(head_dim, group);
         units = (long long)batch * heads_kv * t.groups;

@@ -23,18 +23,27 @@ enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int kWavesPerCU = FD_WAVES_PER_CU;
 
 // Query heads per vector-kernel work-group (the kernel's HPW).  fp32 grouped
-// heads run on the vector kernel; taking up to four heads of one KV head
-// together, every row of lanes holds their q rows and running states, so each
-// K/V row it loads serves all of them instead of being loaded once per query
-// head.  One head otherwise (bf16/fp16 groups run on the matrix cores).
+// heads run on the vector kernel; taking up to eight heads of one KV head
+// together (eight at d <= 128, where their q rows and states fit the
+// registers, else four), every row of lanes holds their q rows and running
+// states, so each K/V row it loads serves all of them instead of being
+// loaded once per query head.  One head otherwise (bf16/fp16 groups run on
+// the matrix cores).
 #ifndef FD_VALU_HEAD_GROUP
 #define FD_VALU_HEAD_GROUP 1
 #endif
-inline int valu_heads_per_wg(int in_dtype, int group) {
+inline int valu_heads_per_wg(int in_dtype, int head_dim, int group) {
     if (!FD_VALU_HEAD_GROUP || in_dtype != kF32 || group < 2)
         return 1;
+    if (group % 8 == 0 && head_dim <= 128)
+        return 8;
     return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
 }
+
+// Resident one-wave vector-kernel work-groups per CU: kWavesPerCU, or four
+// (one per SIMD) with eight heads per work-group, whose steps are bound by
+// their arithmetic rather than by the load stream.
+inline int valu_wg_per_cu(int heads_per_wg) { return heads_per_wg >= 8 ? 4 : kWavesPerCU; }
 
 // Resident one-wave work-groups per CU of the grouped (matrix-core) split
 // kernels; the token-balanced partition makes this many shares per CU.

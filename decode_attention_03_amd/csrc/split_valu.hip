@@ -132,7 +132,7 @@ __global__ __launch_bounds__(THREADS) void split_valu_kernel(SplitArgs a) {
     // token slots per step position: the work-group's rows share one split,
     // or (FUSED) each wave's rows share that wave's split
     constexpr int TPS = FUSED ? RPW : kRows;
-    static_assert(HPW >= 1 && HPW <= 4, "one to four query heads per work-group");
+    static_assert(HPW >= 1 && HPW <= 8, "one to eight query heads per work-group");
     static_assert(!BAL || (THREADS == 64 && !FUSED),
                   "balanced pieces run on one-wave work-groups");
 
@@ -512,19 +512,20 @@ constexpr int lanes_per_row() {
 template <int DT, int D, int HPW>
 hipError_t launch_rows(const SplitArgs &a, hipStream_t stream) {
     constexpr int LPR = lanes_per_row<DT, D>();
+    const int per_cu = valu_wg_per_cu(HPW);  // one-wave work-groups per CU
     if (a.balanced) {  // token-balanced shares, one-wave work-groups
         return a.block_table
-                   ? launch_cfg<DT, D, 64, HPW, LPR, true, false, true>(a, kWavesPerCU, stream)
-                   : launch_cfg<DT, D, 64, HPW, LPR, false, false, true>(a, kWavesPerCU, stream);
+                   ? launch_cfg<DT, D, 64, HPW, LPR, true, false, true>(a, per_cu, stream)
+                   : launch_cfg<DT, D, 64, HPW, LPR, false, false, true>(a, per_cu, stream);
     }
     if (a.block_table) {
         if (a.valu_waves > 1)
             return launch_cfg<DT, D, 64 * kWavesPerCU, HPW, LPR, true>(a, 1, stream);
-        return launch_cfg<DT, D, 64, HPW, LPR, true>(a, kWavesPerCU, stream);
+        return launch_cfg<DT, D, 64, HPW, LPR, true>(a, per_cu, stream);
     }
     if (a.valu_waves > 1)
         return launch_cfg<DT, D, 64 * kWavesPerCU, HPW, LPR, false>(a, 1, stream);
-    return launch_cfg<DT, D, 64, HPW, LPR, false>(a, kWavesPerCU, stream);
+    return launch_cfg<DT, D, 64, HPW, LPR, false>(a, per_cu, stream);
 }
 
 template <int DT, int D>
@@ -547,7 +548,11 @@ hipError_t launch(const SplitArgs &a, hipStream_t stream) {
         }
     }
     if constexpr (DT == kF32) {  // grouped heads: HPW heads of one KV head per work-group
-        switch (valu_heads_per_wg(DT, a.heads_q / a.heads_kv)) {
+        switch (valu_heads_per_wg(DT, D, a.heads_q / a.heads_kv)) {
+        case 8:
+            if constexpr (D <= 128)
+                return launch_rows<DT, D, 8>(a, stream);
+            return hipErrorInvalidValue;
         case 4: return launch_rows<DT, D, 4>(a, stream);
         case 2: return launch_rows<DT, D, 2>(a, stream);
         default: break;

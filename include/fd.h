@@ -119,7 +119,7 @@ int fd_decode_workspace_bytes(int batch, int heads_q, int heads_kv, int max_kv_l
 #define FD_ROUTE_BALANCED 3 /* token-balanced pieces into the workspace, then the combine */
 
 /* Split kernels (fd_plan.kernel). */
-#define FD_KERNEL_VECTOR 0   /* vector ALUs (MHA, fp32; fp32 groups: up to four query
+#define FD_KERNEL_VECTOR 0   /* vector ALUs (MHA, fp32; fp32 groups: up to eight query
                                 heads of one KV head per work-group); on
                                 FD_ROUTE_BALANCED it walks the token-balanced shares */
 #define FD_KERNEL_GROUPED 1  /* matrix cores, one 16-query tile of a KV head's group */

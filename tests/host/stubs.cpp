@@ -93,7 +93,7 @@ void check_balanced(const SplitArgs &a, int hx) {
 hipError_t launch_split_valu(const SplitArgs &a, int in_dtype, hipStream_t) {
     ++g_log.split_valu;
     if (a.balanced) {  // one unit per (sequence, group of valu_heads_per_wg query heads)
-        check_balanced(a, a.heads_q / valu_heads_per_wg(in_dtype, a.heads_q / a.heads_kv));
+        check_balanced(a, a.heads_q / valu_heads_per_wg(in_dtype, a.head_dim, a.heads_q / a.heads_kv));
         return hipSuccess;
     }
     if (a.num_splits < 1 || a.split_len < 1 ||

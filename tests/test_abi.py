@@ -228,9 +228,10 @@ def test_decode_plan_routes(lib, case):
         # o and LSE slots for work-groups + units, and one descriptor per unit;
         # units are (sequence, KV head) of hq / hkv rows on the matrix cores,
         # (sequence, query head) of one row on the vector kernel, or for fp32
-        # groups (sequence, up to four query heads of one KV head)
+        # groups (sequence, up to eight query heads of one KV head)
         g = hq // hkv
-        hpw = 4 if dt == fd.F32 and g % 4 == 0 else (2 if dt == fd.F32 and g % 2 == 0 else 1)
+        hpw = (8 if dt == fd.F32 and g % 8 == 0 and d <= 128 else
+               4 if dt == fd.F32 and g % 4 == 0 else 2 if dt == fd.F32 and g % 2 == 0 else 1)
         units, gsz = (batch * hq // hpw, hpw) if p.kernel == 0 else (batch * hkv, g)
         slots = p.work_groups + units
         assert p.workspace_bytes >= slots * gsz * (d + 1) * 4 + units * 8

@@ -1,9 +1,10 @@
 """GPU parity of fp32 grouped-query heads on the vector kernel against the fp64
 oracle, through the C ABI.
 
-fp32 grouped heads run on the vector kernel with up to four query heads of
-one KV head per work-group (two when the group is only even, one when odd),
-their rows of lanes reading the same K/V token together.  These cases cover
+fp32 grouped heads run on the vector kernel with up to eight query heads of
+one KV head per work-group (eight at d <= 128 when the group divides by eight,
+else four, two when the group is only even, one when odd), every row of lanes
+holding all of their q rows and running states.  These cases cover
 each head count per work-group on every route the vector kernel serves: fixed
 splits (the split stage alone, the m/l/o format, the whole decode), one split
 per row, the automatic plan without lengths, the token-balanced partition for
@@ -29,6 +30,9 @@ CASES = [
     ("g8_d256", 3, 1, 8, 256, 1800, [1800, 700, 33]),
     ("g6_d64", 4, 2, 6, 64, 2000, [2000, 15, 1024, 0]),
     ("g3_d128", 4, 2, 3, 128, 1500, [1500, 3, 0, 777]),
+    ("g8_d128", 4, 2, 8, 128, 2200, [2200, 1, 1100, 0]),
+    ("g16_d64", 3, 2, 16, 64, 1700, [17, 1700, 900]),
+    ("g32_d64_mqa", 2, 1, 32, 64, 3000, [3000, 640]),
 ]
 
 
@@ -94,7 +98,7 @@ def test_f32_groups_every_route(gpu, case):
     assert (np.abs(gl[~empty] - rll[~empty]) / rll[~empty]).max() <= TOL_L
 
 
-@pytest.mark.parametrize("group,d", [(4, 128), (2, 64)])
+@pytest.mark.parametrize("group,d", [(4, 128), (2, 64), (8, 128)])
 def test_f32_groups_full_length_and_paged(gpu, group, d):
     """Every sequence full and no lengths: the automatic fixed-split plan; then
     the same cache in 16-token pages with ragged lengths (balanced) and fixed
