@@ -123,7 +123,11 @@ class Prepared:
             # units: (sequence, KV head) of hq / hkv rows on the matrix cores,
             # (sequence, query head) of one row on the vector kernel
             vec = self.dplan["kernel"] == "vector"
-            units, rows = (batch * hq, 1) if vec else (batch * hkv, hq // hkv)
+            g = hq // hkv  # fp32 groups: up to eight query heads per vector unit
+            hpw = 1
+            if vec and w.dtype == "f32":
+                hpw = 8 if g % 8 == 0 and d <= 128 else 4 if g % 4 == 0 else 2 if g % 2 == 0 else 1
+            units, rows = (batch * hq // hpw, hpw) if vec else (batch * hkv, g)
             pieces = self.dplan["work_groups"] + units
             self.part_bytes = pieces * rows * (d + 1) * 4
         else:
